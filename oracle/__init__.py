@@ -1,0 +1,16 @@
+"""Oracle (test infrastructure only): plain CPU statement of the NABLA forward path.
+
+Only ``tests/``, the smoke check and the bench's CPU baseline import this
+package.  The library under ``block_sparse_attention_blockmean_amd`` never does.
+"""
+from .nabla_oracle import (
+    fractal_index, reorder, block_mean, pooled_logits, row_softmax, cdf_values, cdf_keep,
+    block_tiles, sta_mask, block_mask, kv_lists, mask_from_lists, attention_block,
+    masked_attention, forward,
+)
+
+__all__ = [
+    "fractal_index", "reorder", "block_mean", "pooled_logits", "row_softmax", "cdf_values",
+    "cdf_keep", "block_tiles", "sta_mask", "block_mask", "kv_lists", "mask_from_lists",
+    "attention_block", "masked_attention", "forward",
+]

@@ -1,0 +1,317 @@
+"""Pins of the oracle against facts that the pages and plain mathematics fix.
+
+Each ``pin_*`` raises AssertionError when the oracle disagrees.  They look the
+oracle functions up at call time (``O.name``), so the mutation tests can plant a
+mistake in the oracle and check that some pin catches it.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle.nabla_oracle as O
+from conftest import read_golden
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- reorder
+
+def pin_reorder_golden():
+    lines = read_golden("fractal_T2_H4_W4_P2.txt")
+    T, H, W, P = map(int, lines[0].split())
+    seq = np.array(list(map(int, lines[1].split())))
+    L = T * H * W
+    x = np.arange(L, dtype=np.int64)[:, None]
+    y = O.reorder(x, T, H, W, P)
+    assert np.array_equal(y[:, 0], seq), (y[:, 0], seq)
+    assert np.array_equal(O.reorder(y, T, H, W, P, inverse=True)[:, 0], np.arange(L))
+
+
+def pin_reorder_roundtrip():
+    rng = _rng(1)
+    for T, H, W, P in [(1, 8, 8, 2), (3, 8, 16, 4), (2, 16, 8, 8), (2, 6, 9, 3), (1, 4, 4, 1)]:
+        L = T * H * W
+        x = rng.standard_normal((2, L, 3)).astype(np.float32)
+        y = O.reorder(x, T, H, W, P)
+        z = O.reorder(y, T, H, W, P, inverse=True)
+        assert np.array_equal(z, x)
+        pi = O.fractal_index(T, H, W, P)
+        assert np.array_equal(np.sort(pi), np.arange(L)), "not a bijection"
+
+
+def pin_reorder_identity_cases():
+    x = np.arange(2 * 8 * 8, dtype=np.int64)[:, None]
+    assert np.array_equal(O.reorder(x, 2, 8, 8, 1), x), "P = 1 must keep raster order"
+    assert np.array_equal(O.reorder(x, 2, 8, 8, 8), x), "P = H = W must keep raster order"
+
+
+def pin_reorder_runs_are_patches():
+    T, H, W, P = 3, 8, 12, 4
+    L = T * H * W
+    y = O.reorder(np.arange(L, dtype=np.int64)[:, None], T, H, W, P)[:, 0]
+    t, rem = np.divmod(y, H * W)
+    yy, xx = np.divmod(rem, W)
+    prev_t = -1
+    for r in range(L // (P * P)):
+        sl = slice(r * P * P, (r + 1) * P * P)
+        coords = set(zip(t[sl], yy[sl] // P, xx[sl] // P))
+        assert len(coords) == 1, "a run of P*P tokens must be one patch of one frame"
+        tt = int(t[sl][0])
+        assert tt >= prev_t, "time order must be kept"
+        prev_t = tt
+
+
+# ---------------------------------------------------------------- pooling / map
+
+def pin_pool_tile_mean():
+    """Pooled logit (i, j) = mean of the dense logits over the N x N tile (bilinearity)."""
+    rng = _rng(2)
+    for L, N, d in [(256, 64, 16), (192, 64, 8), (48, 16, 4)]:
+        q = rng.standard_normal((L, d)).astype(np.float32) + 0.3
+        k = rng.standard_normal((L, d)).astype(np.float32) * 1.7 - 0.2
+        scale = 1.0 / np.sqrt(d)
+        S = O.pooled_logits(O.block_mean(q, N), O.block_mean(k, N), scale)
+        nb = L // N
+        dense = np.zeros((L, L))
+        for a in range(L):
+            for b in range(L):
+                dense[a, b] = scale * sum(float(q[a, c]) * float(k[b, c]) for c in range(d))
+        tile_mean = dense.reshape(nb, N, nb, N).mean(axis=(1, 3))
+        assert np.allclose(S, tile_mean, rtol=1e-5, atol=1e-6), np.max(np.abs(S - tile_mean))
+
+
+def pin_pool_constant():
+    # a dyadic constant sums exactly, so the mean is exact
+    x = np.full((2, 256, 8), 0.75, dtype=np.float32)
+    p = O.block_mean(x, 64)
+    assert p.shape == (2, 4, 8)
+    assert np.all(p == np.float32(0.75)), p
+    # otherwise within the textbook bound of a sequential float32 sum, (N-1) u |c|
+    x = np.full((1, 128, 4), 0.7, dtype=np.float32)
+    p = O.block_mean(x, 64)
+    assert np.all(np.abs(p.astype(np.float64) - 0.7) <= 63 * 2.0 ** -24 * 0.7 + 2.0 ** -24), p
+
+
+def pin_softmax():
+    rng = _rng(3)
+    S = (rng.standard_normal((5, 37)) * 4).astype(np.float32)
+    A = O.row_softmax(S)
+    assert np.all(np.abs(A.sum(-1) - 1.0) <= 37 * 2.0 ** -24 + 1e-7)
+    ref = scipy.special.softmax(S.astype(np.float64), axis=-1)
+    assert np.max(np.abs(A - ref)) <= 1e-6
+    A2 = O.row_softmax(S + np.float32(3.5))
+    assert np.max(np.abs(A2 - A)) <= 1e-6
+    assert np.all(np.argmax(A, -1) == np.argmax(S, -1))
+
+
+# ---------------------------------------------------------------- CDF threshold
+
+def _golden_cdf_rows():
+    rows = []
+    for ln in read_golden("cdf_rows.txt"):
+        thr, vals, bits, fs = [s.strip() for s in ln.split("|")]
+        rows.append((float(thr), np.array(vals.split(), dtype=np.float32),
+                     np.array(bits.split(), dtype=int).astype(bool),
+                     np.array(fs.split(), dtype=np.float32)))
+    return rows
+
+
+def pin_cdf_golden():
+    for thr, row, bits, fs in _golden_cdf_rows():
+        Fv = O.cdf_values(row[None, :])[0]
+        assert np.array_equal(Fv, fs), (row, Fv, fs)
+        keep = O.cdf_keep(row[None, :], thr)[0]
+        assert np.array_equal(keep, bits), (thr, row, keep, bits)
+
+
+def _brute_F(A):
+    A = np.asarray(A, dtype=np.float64)
+    n = A.shape[-1]
+    out = np.zeros_like(A)
+    for r in range(A.shape[0]):
+        for j in range(n):
+            out[r, j] = sum(A[r, k] for k in range(n) if A[r, k] <= A[r, j])
+    return out
+
+
+def pin_cdf_bruteforce():
+    rng = _rng(4)
+    A = rng.random((40, 12))
+    A[:, 3] = A[:, 7]            # forced ties
+    A[::3, 1] = A[::3, 2] = A[::3, 5]
+    A /= A.sum(-1, keepdims=True)
+    assert np.max(np.abs(O.cdf_values(A) - _brute_F(A))) <= 1e-12
+
+
+def pin_cdf_invariants():
+    rng = _rng(5)
+    S = (rng.standard_normal((60, 24)) * 3).astype(np.float32)
+    S[:10, 4] = S[:10, 9]
+    A = O.row_softmax(S)
+    assert O.cdf_keep(A, 0.0).all(), "thr = 0 keeps every block"
+    prev = None
+    for thr in [0.0, 0.05, 0.1, 0.2, 0.4, 0.7, 0.95]:
+        keep = O.cdf_keep(A, thr)
+        kept_mass = np.where(keep, A, 0).astype(np.float64).sum(-1)
+        assert np.all(kept_mass >= 1.0 - thr - 1e-5), "kept mass must reach 1 - thr"
+        assert np.all(keep[np.arange(len(A)), np.argmax(A, -1)]), "row max is always kept"
+        for r in range(len(A)):
+            # minimality: re-adding the smallest kept group would be needed, i.e. the
+            # dropped mass plus that group exceeds thr
+            kept_vals = A[r][keep[r]]
+            vmin = kept_vals.min()
+            dropped_plus = A[r][A[r] <= vmin].astype(np.float64).sum()
+            assert dropped_plus > thr - 1e-6
+        if prev is not None:
+            assert np.all(prev >= keep), "kept set shrinks as thr grows"
+        prev = keep
+    uni = np.full((1, 16), 1.0 / 16, dtype=np.float32)
+    assert O.cdf_keep(uni, 0.9).all(), "a uniform row keeps every block"
+
+
+# ---------------------------------------------------------------- STA
+
+def pin_sta_counts():
+    for ln in read_golden("sta_counts.txt"):
+        T, H, W, P, wt, wh, ww, n = map(int, ln.split())
+        M = O.sta_mask(T, H, W, P, P * P, (wt, wh, ww))
+        assert int(M.sum()) == n, (ln, int(M.sum()))
+        assert np.array_equal(M, M.T)
+        assert M.diagonal().all()
+
+
+def pin_sta_brute():
+    """Against the tile numbering that the fractal order implies (block i sits at
+    tile (t, h, w) with i = (t*nH + h)*nW + w), enumerated directly."""
+    T, H, W, P = 3, 16, 24, 8
+    nH, nW = H // P, W // P
+    M = O.sta_mask(T, H, W, P, P * P, (3, 1, 3))
+    nb = T * nH * nW
+    ref = np.zeros((nb, nb), dtype=bool)
+    for (t1, h1, w1), (t2, h2, w2) in itertools.product(
+            itertools.product(range(T), range(nH), range(nW)), repeat=2):
+        i = (t1 * nH + h1) * nW + w1
+        j = (t2 * nH + h2) * nW + w2
+        ref[i, j] = abs(t1 - t2) <= 1 and h1 == h2 and abs(w1 - w2) <= 1
+    assert np.array_equal(M, ref)
+
+
+# ---------------------------------------------------------------- lists
+
+def pin_kv_lists():
+    rng = _rng(6)
+    m = rng.random((3, 10, 10)) < 0.4
+    m[:, np.arange(10), np.arange(10)] = True
+    cnt, idx = O.kv_lists(m)
+    assert np.array_equal(cnt, m.sum(-1))
+    for g in range(3):
+        for i in range(10):
+            row = idx[g, i, :cnt[g, i]]
+            assert np.all(np.diff(row) > 0), "ascending and unique"
+            assert np.array_equal(row, np.nonzero(m[g, i])[0])
+            assert np.all(idx[g, i, cnt[g, i]:] == -1)
+    assert np.array_equal(O.mask_from_lists(cnt, idx), m)
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa(q, k, v, tok_mask=None, scale=None):
+    qt, kt, vt = (torch.from_numpy(np.asarray(a, dtype=np.float64))[None] for a in (q, k, v))
+    am = None if tok_mask is None else torch.from_numpy(tok_mask)[None]
+    return F.scaled_dot_product_attention(qt, kt, vt, attn_mask=am, scale=scale)[0].numpy()
+
+
+def pin_attention_dense():
+    rng = _rng(7)
+    G, L, N, d = 2, 256, 64, 16
+    q, k, v = (rng.standard_normal((G, L, d)).astype(np.float32) for _ in range(3))
+    full = np.ones((G, L // N, L // N), dtype=bool)
+    out = O.masked_attention(q, k, v, full, N)
+    ref = _sdpa(q, k, v)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+def pin_attention_masked():
+    rng = _rng(8)
+    G, L, N, d = 2, 320, 64, 8
+    nb = L // N
+    q, k, v = (rng.standard_normal((G, L, d)).astype(np.float32) * 2 for _ in range(3))
+    m = rng.random((G, nb, nb)) < 0.5
+    m[:, np.arange(nb), (np.arange(nb) * 3) % nb] = True
+    out = O.masked_attention(q, k, v, m, N, scale=0.3)
+    tok = np.stack([np.kron(m[g], np.ones((N, N), dtype=bool)) for g in range(G)])
+    ref = _sdpa(q, k, v, tok, scale=0.3)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+    # convex hull: every output channel lies between the min and max of the kept values
+    for g in range(G):
+        for i in range(nb):
+            toks = np.concatenate([np.arange(j * N, (j + 1) * N) for j in np.nonzero(m[g, i])[0]])
+            lo, hi = v[g, toks].min(0), v[g, toks].max(0)
+            o = out[g, i * N:(i + 1) * N]
+            assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12)
+
+
+def pin_attention_diagonal():
+    rng = _rng(9)
+    L, N, d = 256, 64, 8
+    q, k, v = (rng.standard_normal((1, L, d)).astype(np.float32) for _ in range(3))
+    m = np.eye(L // N, dtype=bool)[None]
+    out = O.masked_attention(q, k, v, m, N)
+    for i in range(L // N):
+        sl = slice(i * N, (i + 1) * N)
+        ref = _sdpa(q[0, sl], k[0, sl], v[0, sl])
+        assert np.max(np.abs(out[0, sl] - ref)) <= 1e-12
+
+
+def pin_forward_thr0_is_full_attention():
+    """thr = 0 keeps every block; reorder -> attention -> inverse reorder is then
+    plain full attention in raster order."""
+    rng = _rng(10)
+    T, H, W, P, N, d = 2, 16, 16, 8, 64, 16
+    L = T * H * W
+    q, k, v = (rng.standard_normal((2, L, d)).astype(np.float32) for _ in range(3))
+    res = O.forward(q, k, v, T, H, W, P, N, thr=0.0)
+    assert res["mask"].all()
+    ref = _sdpa(q, k, v)
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12
+
+
+def pin_forward_permutation_equivariance():
+    """Attention in fractal order, mapped back, equals raster attention under the
+    token mask carried back through the same permutation."""
+    rng = _rng(11)
+    T, H, W, P, N, d = 2, 16, 16, 8, 64, 8
+    L = T * H * W
+    q, k, v = (rng.standard_normal((1, L, d)).astype(np.float32) for _ in range(3))
+    res = O.forward(q, k, v, T, H, W, P, N, thr=0.3)
+    assert not res["mask"].all()
+    pi = O.fractal_index(T, H, W, P)
+    blk = pi // N                                  # block of each raster token
+    tok = res["mask"][0][blk[:, None], blk[None, :]]
+    ref = _sdpa(q, k, v, tok[None])
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12
+
+
+def pin_mask_precision_band():
+    """The float32 mask equals the float64 one except where F lies within 1e-4 of thr."""
+    from synth import get_config, make_head
+    cfg = get_config("tiny")
+    q, k, _ = make_head(cfg, 0, 0)
+    qf = O.reorder(q, cfg.T, cfg.H, cfg.W, cfg.P)
+    kf = O.reorder(k, cfg.T, cfg.H, cfg.W, cfg.P)
+    for thr in (0.05, 0.1, 0.2, 0.5):
+        m32 = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, dtype=np.float32)
+        m64 = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, dtype=np.float64)
+        diff = m32["mask"] != m64["mask"]
+        assert np.all(np.abs(m64["F"][diff] - thr) <= 1e-4)
+        assert np.max(np.abs(m32["F"] - m64["F"])) <= 1e-5
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,117 @@
+"""Planted mistakes in the oracle (CPU only): each must make at least one pin fail.
+
+This shows the pins are strong enough that a plausible slip (a dropped term, a
+wrong sign or index, a transposed operand) in any oracle step would be caught."""
+import numpy as np
+import pytest
+
+import oracle.nabla_oracle as O
+import oracle_pins
+
+_orig_fractal = O.fractal_index
+_orig_pooled = O.pooled_logits
+_orig_cdf = O.cdf_values
+
+
+def _fractal_colmajor(T, H, W, P):
+    # patches taken column-major inside each frame
+    nH, nW = H // P, W // P
+    pi = _orig_fractal(T, H, W, P)
+    out = pi.copy()
+    for l in range(T * H * W):
+        t, rem = divmod(l, H * W)
+        y, x = divmod(rem, W)
+        patch = (t * nW + x // P) * nH + y // P
+        out[l] = patch * P * P + (y % P) * P + (x % P)
+    return out
+
+
+def _pooled_transposed(qp, kp, scale, dtype=np.float32):
+    return _orig_pooled(kp, qp, scale, dtype)
+
+
+def _pooled_unscaled(qp, kp, scale, dtype=np.float32):
+    return _orig_pooled(qp, kp, 1.0, dtype)
+
+
+def _softmax_sign(S):
+    m = np.max(S, axis=-1, keepdims=True)
+    e = np.exp(m - S)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _cdf_untied(A):
+    # ties broken by position instead of grouped
+    n = A.shape[-1]
+    A2 = A.reshape(-1, n)
+    order = np.argsort(A2, axis=1, kind="stable")
+    c = np.cumsum(np.take_along_axis(A2, order, 1), axis=1, dtype=A.dtype)
+    F = np.empty_like(c)
+    np.put_along_axis(F, order, c, 1)
+    return F.reshape(A.shape)
+
+
+def _cdf_descending(A):
+    # accumulates from the top instead of from the bottom
+    return (1.0 - _orig_cdf(A) + A).astype(A.dtype)
+
+
+def _keep_nonstrict(A, thr):
+    F = O.cdf_values(A)
+    return F >= F.dtype.type(thr)
+
+
+def _block_mean_off_by_one(x, N, dtype=np.float32):
+    L, d = x.shape[-2], x.shape[-1]
+    xb = np.asarray(x, dtype=dtype).reshape(x.shape[:-2] + (L // N, N, d))
+    return xb[..., 1:, :].sum(-2) / dtype(N)       # drops the first token of each block
+
+
+def _sta_strict(T, H, W, P, N, window):
+    r = np.array([(w - 1) // 2 for w in window])
+    tiles = O.block_tiles(T, H, W, P, N)
+    return np.all(np.abs(tiles[:, None] - tiles[None]) < np.maximum(r, 1), axis=-1)
+
+
+def _attn_no_scale(q, k, v, keep, i, N, scale, dtype=np.float64):
+    js = np.nonzero(keep)[0]
+    tok = (js[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+    s = np.asarray(q[i * N:(i + 1) * N], dtype) @ np.asarray(k[tok], dtype).T
+    p = np.exp(s - s.max(1, keepdims=True))
+    return (p @ np.asarray(v[tok], dtype)) / p.sum(1, keepdims=True)
+
+
+def _attn_keys_shifted(q, k, v, keep, i, N, scale, dtype=np.float64):
+    js = np.nonzero(keep)[0]
+    tok = (js[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+    tok_v = (tok + 1) % k.shape[0]                     # V rows one token off
+    s = (np.asarray(q[i * N:(i + 1) * N], dtype) @ np.asarray(k[tok], dtype).T) * scale
+    p = np.exp(s - s.max(1, keepdims=True))
+    return (p @ np.asarray(v[tok_v], dtype)) / p.sum(1, keepdims=True)
+
+
+MUTATIONS = [
+    ("fractal_index", _fractal_colmajor),
+    ("pooled_logits", _pooled_transposed),
+    ("pooled_logits", _pooled_unscaled),
+    ("row_softmax", _softmax_sign),
+    ("cdf_values", _cdf_untied),
+    ("cdf_values", _cdf_descending),
+    ("cdf_keep", _keep_nonstrict),
+    ("block_mean", _block_mean_off_by_one),
+    ("sta_mask", _sta_strict),
+    ("attention_block", _attn_no_scale),
+    ("attention_block", _attn_keys_shifted),
+]
+
+
+@pytest.mark.parametrize("name,bug", MUTATIONS, ids=[f"{n}:{b.__name__}" for n, b in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, bug):
+    monkeypatch.setattr(O, name, bug)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake in {name}"
