@@ -1,0 +1,173 @@
+"""ctypes binding of libnabla.so: marshals torch device tensors into the C ABI.
+
+Every function passes raw device pointers and torch's current HIP stream; all
+computation happens in the library's kernels.  There is no fallback: if the
+library is missing or a tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnabla.so")
+
+NABLA_OK, NABLA_E_INVAL, NABLA_E_UNSUPPORTED, NABLA_E_HIP, NABLA_E_WORKSPACE = range(5)
+NABLA_F32, NABLA_BF16 = 0, 1
+
+# Every symbol that include/nabla.h declares.
+EXPORTS = (
+    "nabla_reorder",
+    "nabla_build_mask_workspace_size",
+    "nabla_build_mask",
+    "block_sparse_attn_fwd",
+    "nabla_status_string",
+    "nabla_last_error",
+)
+
+
+class NablaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class StaWindow(ctypes.Structure):
+    _fields_ = [("wt", ctypes.c_int), ("wh", ctypes.c_int), ("ww", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libnabla.so and declare its signatures (no GPU needed to load)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m block_sparse_attention_blockmean_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.nabla_reorder.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, vp]
+    lib.nabla_reorder.restype = i
+    lib.nabla_build_mask_workspace_size.argtypes = [i, i, i, i, i]
+    lib.nabla_build_mask_workspace_size.restype = sz
+    lib.nabla_build_mask.argtypes = [vp, vp, i, i, i, i, i, i, i, i, f, ctypes.POINTER(StaWindow),
+                                     f, i, vp, vp, vp, vp, sz, vp]
+    lib.nabla_build_mask.restype = i
+    lib.block_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, f, i, vp]
+    lib.block_sparse_attn_fwd.restype = i
+    lib.nabla_status_string.argtypes = [i]
+    lib.nabla_status_string.restype = ctypes.c_char_p
+    lib.nabla_last_error.argtypes = []
+    lib.nabla_last_error.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(status: int, lib) -> None:
+    if status != NABLA_OK:
+        name = lib.nabla_status_string(status).decode()
+        msg = lib.nabla_last_error().decode()
+        raise NablaError(status, f"{name}: {msg}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return NABLA_BF16
+    if t.dtype == torch.float32:
+        return NABLA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def reorder(x: torch.Tensor, T: int, H: int, W: int, P: int, inverse: bool = False,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Raster <-> fractal token order of a [B, heads, T*H*W, d] tensor."""
+    lib = load_library()
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, heads, L, d]")
+    B, NH, L, d = x.shape
+    if L != T * H * W:
+        raise ValueError(f"L={L} does not match T*H*W={T * H * W}")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib.nabla_reorder(_dev(x, "x"), _dev(out, "out"), B, NH, T, H, W, d, P,
+                             _dtype_code(x), int(bool(inverse)), _stream()), lib)
+    return out
+
+
+def build_mask_workspace_size(batch: int, heads: int, L: int, d: int, N: int = 64) -> int:
+    return int(load_library().nabla_build_mask_workspace_size(batch, heads, L, d, N))
+
+
+def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int, N: int = 64,
+               thr: float = 0.1, sta: Optional[Tuple[int, int, int]] = None,
+               scale: Optional[float] = None, with_bitmap: bool = False,
+               workspace: Optional[torch.Tensor] = None, kv_count: Optional[torch.Tensor] = None,
+               kv_index: Optional[torch.Tensor] = None):
+    """NABLA block mask of fractal-ordered Q, K: returns (kv_count, kv_index[, bitmap])."""
+    lib = load_library()
+    B, NH, L, d = q.shape
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must have the same shape and dtype")
+    nb = L // N
+    dev = q.device
+    if kv_count is None:
+        kv_count = torch.empty((B, NH, nb), dtype=torch.int32, device=dev)
+    if kv_index is None:
+        kv_index = torch.empty((B, NH, nb, nb), dtype=torch.int32, device=dev)
+    bitmap = None
+    if with_bitmap:
+        bitmap = torch.empty((B, NH, nb, (nb + 31) // 32), dtype=torch.int32, device=dev)
+    ws_bytes = lib.nabla_build_mask_workspace_size(B, NH, L, d, N)
+    if workspace is None:
+        workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
+    win = None if sta is None else ctypes.byref(StaWindow(*sta))
+    _check(lib.nabla_build_mask(
+        _dev(q, "q"), _dev(k, "k"), B, NH, T, H, W, d, P, N, float(thr), win,
+        float(scale) if scale is not None else 0.0, _dtype_code(q),
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+        _dev(bitmap, "bitmap") if bitmap is not None else None,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()), lib)
+    if with_bitmap:
+        return kv_count, kv_index, bitmap
+    return kv_count, kv_index
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.Tensor,
+             kv_index: torch.Tensor, N: int = 64, scale: Optional[float] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-sparse attention over the kept N x N tiles listed in kv_count/kv_index."""
+    lib = load_library()
+    B, NH, L, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    nb = L // N
+    if kv_count.dtype != torch.int32 or kv_index.dtype != torch.int32:
+        raise TypeError("kv_count and kv_index must be int32")
+    if kv_count.numel() != B * NH * nb or kv_index.numel() != B * NH * nb * nb:
+        raise ValueError("kv_count / kv_index sizes do not match q")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.block_sparse_attn_fwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, NH, L, d, N,
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+        float(scale) if scale is not None else 0.0, _dtype_code(q), _stream()), lib)
+    return out

@@ -1,0 +1,184 @@
+// Host side of the C ABI declared in nabla.h: argument validation (before any HIP
+// call, so it also runs on machines without a GPU) and dispatch to the launchers.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "nabla_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+nabla_status fail(nabla_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+nabla_status hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return NABLA_OK;
+    return fail(NABLA_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_size(nabla_dtype dt) { return dt == NABLA_BF16 ? 2 : 4; }
+
+bool valid_dtype(nabla_dtype dt) { return dt == NABLA_F32 || dt == NABLA_BF16; }
+
+// Tokens per head times d must stay addressable with 32-bit chunk indices.
+constexpr long long kMaxHeadElems = 1ll << 33;
+
+}  // namespace
+
+extern "C" {
+
+const char* nabla_status_string(nabla_status st) {
+    switch (st) {
+        case NABLA_OK: return "NABLA_OK";
+        case NABLA_E_INVAL: return "NABLA_E_INVAL";
+        case NABLA_E_UNSUPPORTED: return "NABLA_E_UNSUPPORTED";
+        case NABLA_E_HIP: return "NABLA_E_HIP";
+        case NABLA_E_WORKSPACE: return "NABLA_E_WORKSPACE";
+    }
+    return "NABLA_E_UNKNOWN";
+}
+
+const char* nabla_last_error(void) { return g_last_error; }
+
+nabla_status nabla_reorder(const void* src, void* dst, int batch, int heads, int T, int H,
+                           int W, int d, int P, nabla_dtype dtype, int inverse,
+                           hipStream_t stream) {
+    if (!src || !dst) return fail(NABLA_E_INVAL, "nabla_reorder: null pointer");
+    if (src == dst) return fail(NABLA_E_INVAL, "nabla_reorder: src and dst must differ");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(NABLA_E_INVAL, "nabla_reorder: pointers must be 16-byte aligned");
+    if (batch <= 0 || heads <= 0 || T <= 0 || H <= 0 || W <= 0 || d <= 0 || P <= 0)
+        return fail(NABLA_E_INVAL, "nabla_reorder: sizes must be positive");
+    if (H % P || W % P)
+        return fail(NABLA_E_INVAL, "nabla_reorder: H=%d and W=%d must be multiples of P=%d", H, W, P);
+    if (inverse != 0 && inverse != 1) return fail(NABLA_E_INVAL, "nabla_reorder: inverse must be 0 or 1");
+    if (!valid_dtype(dtype)) return fail(NABLA_E_INVAL, "nabla_reorder: unknown dtype %d", (int)dtype);
+    const long long L = (long long)T * H * W;
+    const size_t row_bytes = (size_t)d * elem_size(dtype);
+    if (row_bytes % 16)
+        return fail(NABLA_E_UNSUPPORTED, "nabla_reorder: d*sizeof(dtype) = %zu is not a multiple of 16", row_bytes);
+    const long long chunks = L * (long long)(row_bytes / 16);
+    if (chunks >= (1ll << 31) || (long long)batch * heads > 65535)
+        return fail(NABLA_E_UNSUPPORTED, "nabla_reorder: tensor too large");
+    int chunk_shift = 0;
+    while ((size_t(16) << chunk_shift) < row_bytes) ++chunk_shift;
+    if ((size_t(16) << chunk_shift) != row_bytes)
+        return fail(NABLA_E_UNSUPPORTED, "nabla_reorder: d*sizeof(dtype) must be 16 bytes times a power of two");
+    nabla::ReorderArgs a{src, dst, batch * heads, T, H, W, P, (int)L, chunk_shift, inverse};
+    return hip_status(nabla::launch_reorder(a, stream), "nabla_reorder");
+}
+
+size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N) {
+    if (batch <= 0 || heads <= 0 || L <= 0 || d <= 0 || N <= 0 || L % N) return 0;
+    const size_t one = (size_t)batch * heads * (size_t)(L / N) * d * sizeof(float);
+    return ((2 * one) + 255) & ~(size_t)255;
+}
+
+nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads, int T, int H,
+                              int W, int d, int P, int N, float thr,
+                              const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !kv_count || !kv_index) return fail(NABLA_E_INVAL, "nabla_build_mask: null pointer");
+    if (!aligned16(q) || !aligned16(k) || ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3) ||
+        ((uintptr_t)bitmap & 3))
+        return fail(NABLA_E_INVAL, "nabla_build_mask: misaligned pointer");
+    if (batch <= 0 || heads <= 0 || T <= 0 || H <= 0 || W <= 0 || d <= 0 || P <= 0 || N <= 0)
+        return fail(NABLA_E_INVAL, "nabla_build_mask: sizes must be positive");
+    if (H % P || W % P)
+        return fail(NABLA_E_INVAL, "nabla_build_mask: H=%d and W=%d must be multiples of P=%d", H, W, P);
+    const long long L = (long long)T * H * W;
+    if (L % N) return fail(NABLA_E_INVAL, "nabla_build_mask: L=%lld is not a multiple of N=%d", L, N);
+    if (!(thr >= 0.f && thr < 1.f)) return fail(NABLA_E_INVAL, "nabla_build_mask: thr must lie in [0, 1)");
+    if (isnan(scale) || isinf(scale)) return fail(NABLA_E_INVAL, "nabla_build_mask: scale must be finite");
+    if (!valid_dtype(dtype)) return fail(NABLA_E_INVAL, "nabla_build_mask: unknown dtype %d", (int)dtype);
+    if (sta) {
+        if (sta->wt < 1 || sta->wh < 1 || sta->ww < 1 || !(sta->wt & 1) || !(sta->wh & 1) || !(sta->ww & 1))
+            return fail(NABLA_E_INVAL, "nabla_build_mask: STA window sizes must be odd and >= 1");
+        if (N != P * P)
+            return fail(NABLA_E_INVAL, "nabla_build_mask: an STA tile is one P x P patch, so N must equal P*P");
+    }
+    if (N != 64) return fail(NABLA_E_UNSUPPORTED, "nabla_build_mask: only N = 64 is implemented");
+    if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "nabla_build_mask: d must be 64 or 128");
+    const long long nb = L / N;
+    if (nb > NABLA_MAX_BLOCKS)
+        return fail(NABLA_E_UNSUPPORTED, "nabla_build_mask: %lld blocks per head exceed %d", nb, NABLA_MAX_BLOCKS);
+    if ((long long)batch * heads > 65535 || L * d >= kMaxHeadElems)
+        return fail(NABLA_E_UNSUPPORTED, "nabla_build_mask: tensor too large");
+    const size_t need = nabla_build_mask_workspace_size(batch, heads, (int)L, d, N);
+    if (!workspace || workspace_bytes < need)
+        return fail(NABLA_E_WORKSPACE, "nabla_build_mask: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace & 15)) return fail(NABLA_E_INVAL, "nabla_build_mask: misaligned workspace");
+
+    nabla::MaskArgs a{};
+    a.q = q;
+    a.k = k;
+    a.BH = batch * heads;
+    a.nb = (int)nb;
+    a.d = d;
+    a.N = N;
+    a.T = T;
+    a.nH = H / P;
+    a.nW = W / P;
+    a.thr = thr;
+    a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+    a.sta = sta ? 1 : 0;
+    a.rt = sta ? (sta->wt - 1) / 2 : 0;
+    a.rh = sta ? (sta->wh - 1) / 2 : 0;
+    a.rw = sta ? (sta->ww - 1) / 2 : 0;
+    a.kv_count = kv_count;
+    a.kv_index = kv_index;
+    a.bitmap = bitmap;
+    a.qp = (float*)workspace;
+    a.kp = a.qp + (size_t)a.BH * nb * d;
+    a.bf16 = dtype == NABLA_BF16;
+    return hip_status(nabla::launch_build_mask(a, stream), "nabla_build_mask");
+}
+
+nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                                   int batch, int heads, int L, int d, int N,
+                                   const int32_t* kv_count, const int32_t* kv_index,
+                                   float scale, nabla_dtype dtype, hipStream_t stream) {
+    if (!q || !k || !v || !o || !kv_count || !kv_index)
+        return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: null pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3))
+        return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: misaligned pointer");
+    if (batch <= 0 || heads <= 0 || L <= 0 || d <= 0 || N <= 0)
+        return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: sizes must be positive");
+    if (L % N) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: L=%d is not a multiple of N=%d", L, N);
+    if (isnan(scale) || isinf(scale)) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: scale must be finite");
+    if (!valid_dtype(dtype)) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: unknown dtype %d", (int)dtype);
+    if (N != 64) return fail(NABLA_E_UNSUPPORTED, "block_sparse_attn_fwd: only N = 64 is implemented");
+    if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "block_sparse_attn_fwd: d must be 64 or 128");
+    if ((long long)L * d >= kMaxHeadElems || (long long)batch * heads * (L / N) >= (1ll << 31))
+        return fail(NABLA_E_UNSUPPORTED, "block_sparse_attn_fwd: tensor too large");
+    nabla::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.BH = batch * heads;
+    a.L = L;
+    a.nb = L / N;
+    a.d = d;
+    a.kv_count = kv_count;
+    a.kv_index = kv_index;
+    a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+    hipError_t e = dtype == NABLA_BF16 ? nabla::launch_attn_bf16(a, stream)
+                                       : nabla::launch_attn_f32(a, stream);
+    return hip_status(e, "block_sparse_attn_fwd");
+}
+
+}  // extern "C"

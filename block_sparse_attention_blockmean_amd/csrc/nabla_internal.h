@@ -1,0 +1,79 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nabla.h"
+
+namespace nabla {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Divide-by-invariant-integer with one multiply-high (Granlund & Montgomery 1994,
+// "Division by invariant integers using multiplication", round-up variant):
+// for 1 <= d < 2^31 and n < 2^31, n / d = (umulhi(n, magic) + n) >> shift with
+// shift = ceil(log2 d) and magic = floor(2^32 (2^shift - d) / d) + 1.
+struct FastDiv {
+    uint32_t d, magic, shift;
+    FastDiv() : d(1), magic(0), shift(0) {}
+    explicit FastDiv(uint32_t div) : d(div) {
+        shift = 0;
+        while ((1u << shift) < div) ++shift;
+        magic = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << shift) - div)) / div + 1);
+        if (div == 1) magic = 0;
+    }
+    __host__ __device__ inline uint32_t div(uint32_t n) const {
+#ifdef __HIP_DEVICE_COMPILE__
+        uint32_t hi = __umulhi(n, magic);
+#else
+        uint32_t hi = (uint32_t)(((uint64_t)n * magic) >> 32);
+#endif
+        return (hi + n) >> shift;
+    }
+    __host__ __device__ inline void divmod(uint32_t n, uint32_t& q, uint32_t& r) const {
+        q = div(n);
+        r = n - q * d;
+    }
+};
+
+struct ReorderArgs {
+    const void* src;
+    void* dst;
+    int BH, T, H, W, P, L;
+    int chunk_shift;   // log2(16-byte chunks per token)
+    int inverse;
+};
+hipError_t launch_reorder(const ReorderArgs& a, hipStream_t s);
+
+struct MaskArgs {
+    const void* q;
+    const void* k;
+    int BH, nb, d, N;
+    int T, nH, nW;          // tile grid (frames, patch rows, patch columns) for STA
+    float thr, scale;
+    int sta;                // 0 = off
+    int rt, rh, rw;         // STA radii in tiles
+    int32_t* kv_count;
+    int32_t* kv_index;
+    uint32_t* bitmap;       // may be null
+    float* qp;              // workspace [BH, nb, d]
+    float* kp;              // workspace [BH, nb, d]
+    int bf16;
+};
+hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    int BH, L, nb, d;
+    const int32_t* kv_count;
+    const int32_t* kv_index;
+    float scale;
+};
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+}  // namespace nabla

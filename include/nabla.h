@@ -1,0 +1,158 @@
+/*
+ * nabla.h - C ABI of the MI355X (gfx950) NABLA block-sparse attention library.
+ *
+ * The operation is the forward pass of NABLA (Neighborhood-Adaptive Block-Level
+ * Attention) as the technical summary "NABLA - Atenção de Bloco Adaptativa de
+ * Vizinhança para Geração de Vídeo Eficiente" (gist.science, paper 2507.13546)
+ * states it in its section "Metodologia: NABLA":
+ *   1. fractal flattening of the T x H x W token grid,
+ *   2. block-mean pooling of Q and K, a reduced attention map with a row softmax,
+ *      per-row CDF thresholding to a binary block mask, expansion to N x N tiles,
+ *   3. an optional OR with a static Sliding Tile (STA) window,
+ * followed by softmax attention evaluated only on the kept N x N tiles (the
+ * summary runs that step through FlexAttention; here it is a HIP kernel).
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major [batch, heads, L, d] (d innermost), in device
+ *     memory, 16-byte aligned.  Q, K, V, O of one call share one dtype.
+ *   - The caller owns every buffer, including the workspace; the library allocates
+ *     no device memory and keeps no per-call state.
+ *   - Every call is asynchronous on `stream` (0 = the null stream) and never
+ *     synchronises the host.  Calls on distinct streams may run concurrently as long
+ *     as they do not write the same buffers.
+ *   - Arguments are validated on the host before anything is launched; a call that
+ *     returns an error other than NABLA_E_HIP has launched nothing and left every
+ *     output untouched.  NABLA_E_HIP reports a launch failure; errors raised later
+ *     by a kernel surface on the next synchronisation of the stream.
+ *   - nabla_last_error() returns a message for the calling thread's last failure.
+ */
+#ifndef NABLA_H
+#define NABLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NABLA_OK = 0,
+    NABLA_E_INVAL = 1,        /* bad pointer, shape, threshold, window or scale */
+    NABLA_E_UNSUPPORTED = 2,  /* valid request without a kernel (N != 64, d not 64/128, nb too large) */
+    NABLA_E_HIP = 3,          /* HIP launch or runtime error */
+    NABLA_E_WORKSPACE = 4     /* workspace missing or smaller than nabla_build_mask_workspace_size() */
+} nabla_status;
+
+typedef enum { NABLA_F32 = 0, NABLA_BF16 = 1 } nabla_dtype;
+
+/* Sliding Tile window, in tiles of 1 frame x P x P tokens; each size odd and >= 1.
+ * Block j is inside the window of block i when |dt| <= (wt-1)/2, |dh| <= (wh-1)/2
+ * and |dw| <= (ww-1)/2 between their tile coordinates; the window is centred and
+ * truncated at the grid border. */
+typedef struct { int wt, wh, ww; } nabla_sta_window;
+
+/* Largest number of N-token blocks per head that nabla_build_mask accepts. */
+#define NABLA_MAX_BLOCKS 2496
+
+/*
+ * nabla_reorder - fractal flattening of the token axis ("Metodologia: NABLA", item 1,
+ * "Reordenação de Tokens (Fractal Flattening)").
+ *
+ * src, dst  [batch, heads, L, d] with L = T*H*W; src != dst (no in-place).
+ * inverse=0 moves raster order (token (t, y, x) at l = (t*H + y)*W + x) to fractal
+ * order: frames in time order, inside a frame the P x P patches row-major, each
+ * patch's P*P tokens contiguous and row-major.  Position of raster token l:
+ *   ((t*(H/P) + y/P)*(W/P) + x/P)*P*P + (y%P)*P + x%P.
+ * inverse=1 applies the inverse permutation.  Bit-exact copy of every element.
+ * Errors: NABLA_E_INVAL for null or aliased pointers, non-positive sizes, H or W not
+ * a multiple of P, inverse not 0/1, a bad dtype, misaligned pointers;
+ * NABLA_E_UNSUPPORTED when d * sizeof(dtype) is not a multiple of 16 bytes.
+ */
+nabla_status nabla_reorder(const void* src, void* dst, int batch, int heads, int T, int H,
+                           int W, int d, int P, nabla_dtype dtype, int inverse,
+                           hipStream_t stream);
+
+/*
+ * nabla_build_mask_workspace_size - bytes of device workspace nabla_build_mask needs:
+ * the pooled Q and K in float32, 2 * batch*heads*(L/N)*d*4 bytes, rounded up to 256.
+ * Returns 0 for non-positive sizes or L not a multiple of N.
+ */
+size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N);
+
+/*
+ * nabla_build_mask - adaptive block mask ("Metodologia: NABLA", item 2, plus the
+ * STA union of item 3) for Q and K already in fractal order.
+ *
+ *   Qp, Kp  = mean of each run of N consecutive tokens (float32)      ("Downsampling")
+ *   S       = Qp Kp^T * scale, A = row softmax of S                   ("Atenção Reduzida")
+ *   F_ij    = sum of A_ik over k with A_ik <= A_ij (ties share one F)
+ *   keep    = F_ij > thr                                              ("Limiarização CDF")
+ *   mask    = keep OR (sta != NULL and block j inside the window of block i)
+ * so thr = 0 keeps every block, and the blocks dropped from a row carry at most thr
+ * of its pooled probability mass.  The largest block of each row is always kept.
+ *
+ * q, k        [batch, heads, L, d], L = T*H*W, fractal order, dtype `dtype`.
+ * N           tokens per block; nb = L / N blocks per head.
+ * thr         in [0, 1).
+ * sta         NULL for no window, else the window (requires N == P*P, one tile per block).
+ * scale       logit scale of the reduced map; <= 0 selects 1/sqrt(d).
+ * kv_count    out, int32 [batch, heads, nb]: kept blocks per query block.
+ * kv_index    out, int32 [batch, heads, nb, nb]: row (b, h, i) lists its kept KV blocks
+ *             in ascending order in its first kv_count entries; later entries are
+ *             not written.
+ * bitmap      optional out (NULL to skip), uint32 [batch, heads, nb, ceil(nb/32)]:
+ *             bit (j % 32) of word j / 32 of row i is the mask bit (i, j); unused high
+ *             bits of the last word are zero.
+ * workspace   device buffer of at least nabla_build_mask_workspace_size() bytes.
+ * Errors: NABLA_E_INVAL (null pointers, L != T*H*W, H or W not a multiple of P,
+ * L not a multiple of N, thr outside [0,1) or NaN, a window size even or < 1, a window
+ * with N != P*P, NaN or infinite scale, misaligned pointers); NABLA_E_UNSUPPORTED
+ * (N != 64, d not 64 or 128, nb > NABLA_MAX_BLOCKS); NABLA_E_WORKSPACE.
+ */
+nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads, int T, int H,
+                              int W, int d, int P, int N, float thr,
+                              const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * block_sparse_attn_fwd - softmax attention restricted to the kept N x N tiles
+ * ("Metodologia: NABLA", item 2, "Expansão": the expanded mask says which N x N
+ * blocks of the attention are computed; a dropped block leaves both the numerator
+ * and the softmax normaliser, as the AB-Attention page's section "Onde os esquemas
+ * esparsos anteriores falham" spells out).  Non-causal.
+ *
+ *   O[b,h,a,:] = sum over tokens t of kept blocks of row blk(a) of
+ *                softmax_t(scale * q_a . k_t) * v_t
+ *
+ * q, k, v, o  [batch, heads, L, d], any token order as long as blocks are runs of N
+ *             consecutive tokens (fractal order from nabla_reorder in the NABLA path).
+ * kv_count, kv_index  as written by nabla_build_mask (any lists with entries in
+ *             [0, nb) are accepted; duplicates are summed twice).  A query block with
+ *             kv_count 0 gets zero output.
+ * scale       <= 0 selects 1/sqrt(d).
+ * bf16: scores and the running softmax in float32, P rounded to bf16 for the P V
+ * product, float32 accumulation, output rounded to nearest-even bf16.
+ * f32: float32 throughout.
+ * Errors: NABLA_E_INVAL (null pointers, L not a multiple of N, NaN or infinite scale,
+ * misaligned pointers, bad dtype); NABLA_E_UNSUPPORTED (N != 64, d not 64 or 128).
+ */
+nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                                   int batch, int heads, int L, int d, int N,
+                                   const int32_t* kv_count, const int32_t* kv_index,
+                                   float scale, nabla_dtype dtype, hipStream_t stream);
+
+/* Static name of a status code ("NABLA_OK", ...). */
+const char* nabla_status_string(nabla_status status);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+const char* nabla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NABLA_H */

@@ -1,0 +1,53 @@
+"""Comparison helpers for the GPU parity tests (GPU results vs the oracle)."""
+from __future__ import annotations
+
+import numpy as np
+
+BAND = 1e-4          # |F_oracle - thr| within which a mask disagreement is tolerated
+MAX_BAND_FRAC = 1e-3  # tolerated disagreements, as a fraction of all blocks
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def lists_to_mask(count: np.ndarray, index: np.ndarray) -> np.ndarray:
+    """[..., nb] counts + [..., nb, nb] lists -> bool mask; also checks each list is
+    ascending, unique and in range."""
+    nb = index.shape[-1]
+    c2 = count.reshape(-1).astype(np.int64)
+    i2 = index.reshape(-1, nb)
+    assert np.all((c2 >= 0) & (c2 <= nb)), "count out of range"
+    valid = np.arange(nb)[None, :] < c2[:, None]
+    vals = np.where(valid, i2, 0)
+    assert np.all((vals >= 0) & (vals < nb)), "index out of range"
+    d = np.diff(vals, axis=1)
+    assert np.all((d > 0) | ~valid[:, 1:]), "lists must be strictly ascending"
+    rows, cols = np.nonzero(valid)
+    m = np.zeros((c2.size, nb), dtype=bool)
+    m[rows, i2[rows, cols]] = True
+    return m.reshape(index.shape)
+
+
+def bitmap_to_mask(bitmap: np.ndarray, nb: int) -> np.ndarray:
+    words = bitmap.astype(np.uint32)
+    bits = (words[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1
+    flat = bits.reshape(bits.shape[:-2] + (-1,)).astype(bool)
+    assert not flat[..., nb:].any(), "bits past nb must be zero"
+    return flat[..., :nb]
+
+
+def check_mask(gpu_mask: np.ndarray, oracle_mask: np.ndarray, oracle_F: np.ndarray, thr: float):
+    """Bit-exact except blocks with |F_oracle - thr| <= BAND, and those at most
+    MAX_BAND_FRAC of all blocks.  Returns (mismatches, band population)."""
+    assert gpu_mask.shape == oracle_mask.shape
+    mism = gpu_mask != oracle_mask
+    in_band = np.abs(oracle_F.astype(np.float64) - thr) <= BAND
+    outside = mism & ~in_band
+    assert not outside.any(), (
+        f"{int(outside.sum())} mask disagreements outside the band, e.g. at "
+        f"{np.argwhere(outside)[:5].tolist()}")
+    assert mism.sum() <= MAX_BAND_FRAC * mism.size, f"{int(mism.sum())} band disagreements"
+    return int(mism.sum()), int(in_band.sum())
+
+
+def max_abs(a, b) -> float:
+    return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))

@@ -1,0 +1,159 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every symbol the
+header declares, and rejects bad arguments before any HIP call (no kernel runs)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+import block_sparse_attention_blockmean_amd as nb_lib
+from block_sparse_attention_blockmean_amd._binding import (
+    NABLA_BF16, NABLA_E_INVAL, NABLA_E_UNSUPPORTED, NABLA_E_WORKSPACE, NABLA_F32, StaWindow,
+)
+
+HEADER = os.path.join(ROOT, "include", "nabla.h")
+
+# Fake, 256-byte aligned device addresses: validation rejects every call below before
+# anything dereferences them.
+A, B_, C, D_, E, F_, G = (ctypes.c_void_p(0x100000 * (i + 1)) for i in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)) - {"if"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nb_lib.load_library()
+
+
+def test_library_loads_without_gpu(lib):
+    assert lib is not None
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decl = declared_functions()
+    assert sorted(decl) == sorted(nb_lib.EXPORTS), decl
+    out = subprocess.run(["nm", "-D", "--defined-only", nb_lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in decl:
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    names = [lib.nabla_status_string(i).decode() for i in range(5)]
+    assert names == ["NABLA_OK", "NABLA_E_INVAL", "NABLA_E_UNSUPPORTED", "NABLA_E_HIP",
+                     "NABLA_E_WORKSPACE"]
+
+
+def test_workspace_size(lib):
+    # 2 * B*H*nb*d*4 bytes, rounded up to 256
+    assert lib.nabla_build_mask_workspace_size(1, 12, 32256, 128, 64) == 2 * 12 * 504 * 128 * 4
+    assert lib.nabla_build_mask_workspace_size(1, 2, 1024, 64, 64) == 2 * 2 * 16 * 64 * 4
+    assert lib.nabla_build_mask_workspace_size(1, 1, 1000, 64, 64) == 0
+    assert lib.nabla_build_mask_workspace_size(0, 1, 1024, 64, 64) == 0
+
+
+# ------------------------------------------------------------- nabla_reorder
+
+def reorder(lib, src=A, dst=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, dt=NABLA_F32,
+            inverse=0):
+    return lib.nabla_reorder(src, dst, batch, heads, T, H, W, d, P, dt, inverse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=None), NABLA_E_INVAL),
+    (dict(dst=None), NABLA_E_INVAL),
+    (dict(dst=A), NABLA_E_INVAL),
+    (dict(src=ctypes.c_void_p(0x100008)), NABLA_E_INVAL),
+    (dict(batch=0), NABLA_E_INVAL),
+    (dict(T=-1), NABLA_E_INVAL),
+    (dict(H=12), NABLA_E_INVAL),
+    (dict(W=20), NABLA_E_INVAL),
+    (dict(inverse=2), NABLA_E_INVAL),
+    (dict(dt=7), NABLA_E_INVAL),
+    (dict(d=2), NABLA_E_UNSUPPORTED),
+    (dict(d=24), NABLA_E_UNSUPPORTED),
+])
+def test_reorder_validation(lib, kw, status):
+    assert reorder(lib, **kw) == status
+    assert lib.nabla_last_error().decode().startswith("nabla_reorder")
+
+
+# ------------------------------------------------------------- nabla_build_mask
+
+def build_mask(lib, q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, thr=0.1,
+               sta=None, scale=0.0, dt=NABLA_F32, cnt=C, idx=D_, bitmap=None, ws=E,
+               ws_bytes=1 << 30):
+    win = None if sta is None else ctypes.byref(StaWindow(*sta))
+    return lib.nabla_build_mask(q, k, batch, heads, T, H, W, d, P, N, thr, win, scale, dt, cnt,
+                                idx, bitmap, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NABLA_E_INVAL),
+    (dict(k=None), NABLA_E_INVAL),
+    (dict(cnt=None), NABLA_E_INVAL),
+    (dict(idx=None), NABLA_E_INVAL),
+    (dict(q=ctypes.c_void_p(0x100004)), NABLA_E_INVAL),
+    (dict(heads=0), NABLA_E_INVAL),
+    (dict(H=20), NABLA_E_INVAL),
+    (dict(T=3, H=8, W=8, P=8, thr=2.0), NABLA_E_INVAL),  # valid shape, bad thr
+    (dict(T=1, H=8, W=12, P=4), NABLA_E_INVAL),         # L = 96 not a multiple of 64
+    (dict(thr=1.0), NABLA_E_INVAL),
+    (dict(thr=-0.1), NABLA_E_INVAL),
+    (dict(thr=float("nan")), NABLA_E_INVAL),
+    (dict(scale=float("nan")), NABLA_E_INVAL),
+    (dict(scale=float("inf")), NABLA_E_INVAL),
+    (dict(sta=(2, 3, 3)), NABLA_E_INVAL),
+    (dict(sta=(3, 0, 3)), NABLA_E_INVAL),
+    (dict(sta=(3, 3, 3), P=4, H=16, W=16), NABLA_E_INVAL),  # N != P*P
+    (dict(dt=5), NABLA_E_INVAL),
+    (dict(N=32, T=4), NABLA_E_UNSUPPORTED),
+    (dict(d=96), NABLA_E_UNSUPPORTED),
+    (dict(T=160, H=32, W=32), NABLA_E_UNSUPPORTED),     # 2560 blocks > NABLA_MAX_BLOCKS
+    (dict(ws=None), NABLA_E_WORKSPACE),
+    (dict(ws_bytes=100), NABLA_E_WORKSPACE),
+])
+def test_build_mask_validation(lib, kw, status):
+    assert build_mask(lib, **kw) == status
+    assert lib.nabla_last_error().decode().startswith("nabla_build_mask")
+
+
+# ------------------------------------------------------------- block_sparse_attn_fwd
+
+def attn(lib, q=A, k=B_, v=C, o=D_, batch=1, heads=2, L=1024, d=64, N=64, cnt=E, idx=F_,
+         scale=0.0, dt=NABLA_BF16):
+    return lib.block_sparse_attn_fwd(q, k, v, o, batch, heads, L, d, N, cnt, idx, scale, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NABLA_E_INVAL),
+    (dict(v=None), NABLA_E_INVAL),
+    (dict(o=None), NABLA_E_INVAL),
+    (dict(cnt=None), NABLA_E_INVAL),
+    (dict(idx=None), NABLA_E_INVAL),
+    (dict(o=ctypes.c_void_p(0x100002)), NABLA_E_INVAL),
+    (dict(L=1000), NABLA_E_INVAL),
+    (dict(L=0), NABLA_E_INVAL),
+    (dict(scale=float("nan")), NABLA_E_INVAL),
+    (dict(dt=3), NABLA_E_INVAL),
+    (dict(N=128), NABLA_E_UNSUPPORTED),
+    (dict(d=256), NABLA_E_UNSUPPORTED),
+])
+def test_attn_validation(lib, kw, status):
+    assert attn(lib, **kw) == status
+    assert lib.nabla_last_error().decode().startswith("block_sparse_attn_fwd")
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 1024, 64)
+    with pytest.raises(ValueError):
+        nb_lib.reorder(x, 4, 16, 16, 8)

@@ -1,0 +1,226 @@
+"""GPU parity: every step of the HIP path against the oracle on the same seeded inputs.
+
+Masks must match bit for bit except blocks whose oracle cumulative mass lies within
+1e-4 of thr (at most 0.1% of blocks); outputs must match the oracle evaluated with the
+GPU's own mask within 1e-4 (float32) / 2e-2 (bf16) max-abs.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import CONFIGS, Config, make_head, make_qkv
+import block_sparse_attention_blockmean_amd as nab
+from parity import (TOL_BF16, TOL_F32, bitmap_to_mask, check_mask, lists_to_mask, max_abs)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def tdtype(cfg: Config):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def small(name, T, H, W, P, d, dtype, thr, sta=None, heads=2, B=1, seed_index=7):
+    return Config(name, seed_index, B=B, heads=heads, d=d, dtype=dtype, T=T, H=H, W=W, P=P,
+                  N=64, thr=thr, sta=sta, scale_logits=(dtype == "bf16"))
+
+
+SMALL = [
+    CONFIGS[0],
+    dataclasses.replace(CONFIGS[0], name="tiny_thr0", thr=0.0),
+    dataclasses.replace(CONFIGS[0], name="tiny_thr05", thr=0.5),
+    small("bf16_d128_ragged", 5, 24, 40, 8, 128, "bf16", 0.2),
+    small("bf16_d128_ragged_sta", 5, 24, 40, 8, 128, "bf16", 0.2, sta=(3, 3, 3)),
+    small("bf16_d64", 3, 32, 32, 8, 64, "bf16", 0.05, heads=3),
+    small("bf16_P4", 2, 16, 16, 4, 128, "bf16", 0.1),
+    small("f32_d128_sta", 4, 16, 32, 8, 128, "f32", 0.3, sta=(1, 3, 5)),
+    small("bf16_nb130", 13, 16, 40, 8, 128, "bf16", 0.2, B=2, heads=1),
+]
+
+
+def run_gpu_path(cfg: Config, q, k, v, thr=None, with_bitmap=True):
+    """Raster CPU tensors -> GPU reorder, mask, attention, inverse reorder."""
+    thr = cfg.thr if thr is None else thr
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    qf = nab.reorder(qd, cfg.T, cfg.H, cfg.W, cfg.P)
+    kf = nab.reorder(kd, cfg.T, cfg.H, cfg.W, cfg.P)
+    vf = nab.reorder(vd, cfg.T, cfg.H, cfg.W, cfg.P)
+    cnt, idx, bm = nab.build_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, cfg.sta,
+                                  with_bitmap=True)
+    of = nab.attn_fwd(qf, kf, vf, cnt, idx, cfg.N)
+    o = nab.reorder(of, cfg.T, cfg.H, cfg.W, cfg.P, inverse=True)
+    torch.cuda.synchronize()
+    return dict(qf=qf, kf=kf, vf=vf, cnt=cnt, idx=idx, bitmap=bm, of=of, o=o)
+
+
+# ------------------------------------------------------------------ reorder
+
+@pytest.mark.parametrize("T,H,W,P,d,dt", [
+    (4, 16, 16, 8, 64, torch.float32), (3, 24, 40, 8, 128, torch.bfloat16),
+    (2, 12, 20, 4, 64, torch.bfloat16), (2, 8, 8, 1, 128, torch.float32),
+    (1, 16, 16, 16, 64, torch.bfloat16), (5, 6, 9, 3, 64, torch.float32),
+])
+def test_reorder_bitexact(T, H, W, P, d, dt):
+    say(f"reorder T{T} H{H} W{W} P{P} d{d} {dt}")
+    g = torch.Generator().manual_seed(T * 1000 + H * 10 + P)
+    x = torch.randn(2, 3, T * H * W, d, generator=g).to(dt)
+    y = nab.reorder(x.cuda(), T, H, W, P)
+    z = nab.reorder(y, T, H, W, P, inverse=True)
+    ref = O.reorder(x.view(torch.int16 if dt == torch.bfloat16 else torch.int32).numpy(), T, H, W, P)
+    yb = y.cpu().view(torch.int16 if dt == torch.bfloat16 else torch.int32).numpy()
+    assert np.array_equal(yb, ref)
+    assert torch.equal(z.cpu().view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                       x.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+
+
+# ------------------------------------------------------------------ mask + attention, small grids
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_small_grid_parity(cfg):
+    say(f"small-grid parity {cfg.name}: {cfg.B}x{cfg.heads} {cfg.T}x{cfg.H}x{cfg.W} P{cfg.P} "
+        f"d{cfg.d} {cfg.dtype} thr{cfg.thr} sta{cfg.sta} nb{cfg.nb}")
+    q, k, v = make_qkv(cfg)
+    res = run_gpu_path(cfg, q, k, v)
+    G = cfg.BH
+    qn, kn, vn = (to_np(t).reshape(G, cfg.L, cfg.d) for t in (q, k, v))
+    qf, kf, vf = (O.reorder(a, cfg.T, cfg.H, cfg.W, cfg.P) for a in (qn, kn, vn))
+    # the GPU reorder is exact, so the fractal tensors agree bit for bit
+    assert np.array_equal(to_np(res["qf"]).reshape(G, cfg.L, cfg.d), qf)
+    ref = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr, cfg.sta)
+    cnt = res["cnt"].cpu().numpy().reshape(G, cfg.nb)
+    idx = res["idx"].cpu().numpy().reshape(G, cfg.nb, cfg.nb)
+    gmask = lists_to_mask(cnt, idx)
+    assert np.array_equal(bitmap_to_mask(res["bitmap"].cpu().numpy().reshape(G, cfg.nb, -1), cfg.nb),
+                          gmask)
+    mism, band = check_mask(gmask, ref["mask"], ref["F"], cfg.thr)
+    assert np.all(cnt >= 1), "the largest block of every row is kept"
+    say(f"  kept {gmask.mean():.4f}  mismatches {mism}  band {band}")
+    # attention with the GPU's own mask
+    out = O.masked_attention(qf, kf, vf, gmask, cfg.N)
+    err = max_abs(to_np(res["of"]).reshape(G, cfg.L, cfg.d), out)
+    tol = TOL_BF16 if cfg.dtype == "bf16" else TOL_F32
+    say(f"  attention max-abs {err:.3e} (tol {tol})")
+    assert err <= tol
+    # the whole path, back in raster order
+    err_r = max_abs(to_np(res["o"]).reshape(G, cfg.L, cfg.d),
+                    O.reorder(out, cfg.T, cfg.H, cfg.W, cfg.P, inverse=True))
+    assert err_r <= tol
+
+
+def test_thr0_is_full_attention():
+    """thr = 0 keeps every block, so the path is dense attention in raster order."""
+    cfg = dataclasses.replace(CONFIGS[0], thr=0.0)
+    q, k, v = make_qkv(cfg)
+    res = run_gpu_path(cfg, q, k, v)
+    assert torch.all(res["cnt"] == cfg.nb)
+    qt, kt, vt = (t.double() for t in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).numpy()
+    assert max_abs(to_np(res["o"]), ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_attention_arbitrary_lists(dtype, d):
+    """Lists not produced by the mask step: random rows, full rows and empty rows."""
+    cfg = small("lists", 3, 16, 24, 8, d, dtype, 0.1, heads=2)
+    say(f"arbitrary lists {dtype} d{d}")
+    q, k, v = make_qkv(cfg)
+    G, nb = cfg.BH, cfg.nb
+    rng = np.random.default_rng(5)
+    m = rng.random((G, nb, nb)) < 0.3
+    m[:, 0, :] = True          # a full row
+    m[:, 1, :] = False         # an empty row -> zeros
+    m[:, 2, :] = False
+    m[:, 2, nb - 1] = True     # a single far block
+    cnt, idx = O.kv_lists(m)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o = nab.attn_fwd(qd, kd, vd, torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    ref = O.masked_attention(*(to_np(t).reshape(G, cfg.L, d) for t in (q, k, v)), m, cfg.N)
+    on = to_np(o).reshape(G, cfg.L, d)
+    assert np.all(on[:, 64:128] == 0)
+    assert max_abs(on, ref) <= (TOL_BF16 if dtype == "bf16" else TOL_F32)
+
+
+def test_determinism():
+    """Repeated runs give identical bits (no atomics or order-dependent reductions)."""
+    cfg = SMALL[4]
+    q, k, v = make_qkv(cfg)
+    a = run_gpu_path(cfg, q, k, v)
+    b = run_gpu_path(cfg, q, k, v)
+    assert torch.equal(a["cnt"], b["cnt"])
+    for key in ("bitmap", "o"):
+        assert torch.equal(a[key], b[key])
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sample_blocks(G, nb, cnt, rng, n_rand=48):
+    pairs = {(0, 0), (0, nb - 1), (G - 1, 0), (G - 1, nb - 1)}
+    flat = cnt.reshape(-1)
+    for f in (int(np.argmax(flat)), int(np.argmin(flat))):
+        pairs.add((f // nb, f % nb))
+    for _ in range(n_rand):
+        pairs.add((int(rng.integers(G)), int(rng.integers(nb))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS[1:], ids=lambda c: c.name)
+def test_full_config_parity(cfg):
+    """Full mask parity on every head; attention on a seeded sample of query blocks
+    (rows are independent given the mask, so sampled rows are exact checks)."""
+    say(f"full config {cfg.name}: {cfg.B}x{cfg.heads} L{cfg.L} nb{cfg.nb}")
+    q, k, v = make_qkv(cfg)
+    say("  inputs generated")
+    G = cfg.BH
+    for thr in (cfg.thr_list or (cfg.thr,)):
+        res = run_gpu_path(cfg, q, k, v, thr=thr)
+        cnt = res["cnt"].cpu().numpy().reshape(G, cfg.nb)
+        idx = res["idx"].cpu().numpy().reshape(G, cfg.nb, cfg.nb)
+        gmask = lists_to_mask(cnt, idx)
+        mism_tot = 0
+        band_tot = 0
+        # oracle mask, a few heads at a time to bound host memory
+        for g0 in range(0, G, 8):
+            sl = slice(g0, min(G, g0 + 8))
+            qn = to_np(q.reshape(G, cfg.L, cfg.d)[sl])
+            kn = to_np(k.reshape(G, cfg.L, cfg.d)[sl])
+            qf = O.reorder(qn, cfg.T, cfg.H, cfg.W, cfg.P)
+            kf = O.reorder(kn, cfg.T, cfg.H, cfg.W, cfg.P)
+            ref = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, cfg.sta)
+            mism, band = check_mask(gmask[sl], ref["mask"], ref["F"], thr)
+            mism_tot += mism
+            band_tot += band
+        assert mism_tot <= 1e-3 * gmask.size
+        say(f"  thr {thr}: kept {gmask.mean():.4f}  mismatches {mism_tot}  band {band_tot}")
+        rng = np.random.default_rng(cfg.index)
+        blocks = _sample_blocks(G, cfg.nb, cnt, rng)
+        of = res["of"].reshape(G, cfg.L, cfg.d)
+        worst = 0.0
+        heads = sorted({g for g, _ in blocks})
+        for g in heads:
+            qf, kf, vf = (O.reorder(to_np(t.reshape(G, cfg.L, cfg.d)[g]), cfg.T, cfg.H, cfg.W, cfg.P)
+                          for t in (q, k, v))
+            for gg, i in blocks:
+                if gg != g:
+                    continue
+                ref_o = O.attention_block(qf, kf, vf, gmask[g, i], i, cfg.N, 1.0 / np.sqrt(cfg.d))
+                got = to_np(of[g, i * cfg.N:(i + 1) * cfg.N])
+                worst = max(worst, max_abs(got, ref_o))
+        say(f"  attention on {len(blocks)} sampled blocks: max-abs {worst:.3e}")
+        assert worst <= TOL_BF16
+        del res
+        torch.cuda.empty_cache()
