@@ -35,12 +35,38 @@ def bitmap_to_mask(bitmap: np.ndarray, nb: int) -> np.ndarray:
     return flat[..., :nb]
 
 
-def check_mask(gpu_mask: np.ndarray, oracle_mask: np.ndarray, oracle_F: np.ndarray, thr: float):
-    """Bit-exact except blocks with |F_oracle - thr| <= BAND, and those at most
+TIE_EPS = 2e-5      # relative spread of pooled probabilities treated as a near tie
+
+
+def cutoff_ambiguity(A: np.ndarray, thr: float, eps: float = TIE_EPS) -> np.ndarray:
+    """Blocks whose keep bit float32 arithmetic cannot settle.
+
+    F_j = (mass of blocks <= A_j) is only known up to the order of blocks whose
+    values agree with A_j to within relative ``eps`` (about 5x the float32 error of
+    the pooled softmax): over those orders F_j ranges from
+        F_lo = mass of blocks < A_j (1 - eps), plus A_j
+        F_hi = mass of blocks <= A_j (1 + eps).
+    A block is at the cutoff when thr lies within BAND of [F_lo, F_hi].  Without
+    near ties F_lo = F_hi = F_j and this is |F_j - thr| <= BAND."""
+    nb = A.shape[-1]
+    a = np.asarray(A, dtype=np.float64).reshape(-1, nb)
+    f_lo = np.empty_like(a)
+    f_hi = np.empty_like(a)
+    for r in range(a.shape[0]):
+        s = np.sort(a[r])
+        c = np.concatenate([[0.0], np.cumsum(s)])      # c[n] = mass of the n smallest
+        f_hi[r] = c[np.searchsorted(s, a[r] * (1 + eps), side="right")]
+        f_lo[r] = c[np.searchsorted(s, a[r] * (1 - eps), side="left")] + a[r]
+    amb = (thr >= f_lo - BAND) & (thr <= f_hi + BAND)
+    return amb.reshape(A.shape)
+
+
+def check_mask(gpu_mask: np.ndarray, oracle_mask: np.ndarray, oracle_A: np.ndarray, thr: float):
+    """Bit-exact except blocks at the cutoff (see cutoff_ambiguity), and those at most
     MAX_BAND_FRAC of all blocks.  Returns (mismatches, band population)."""
     assert gpu_mask.shape == oracle_mask.shape
     mism = gpu_mask != oracle_mask
-    in_band = np.abs(oracle_F.astype(np.float64) - thr) <= BAND
+    in_band = cutoff_ambiguity(oracle_A, thr)
     outside = mism & ~in_band
     assert not outside.any(), (
         f"{int(outside.sum())} mask disagreements outside the band, e.g. at "

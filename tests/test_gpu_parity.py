@@ -106,7 +106,7 @@ def test_small_grid_parity(cfg):
     gmask = lists_to_mask(cnt, idx)
     assert np.array_equal(bitmap_to_mask(res["bitmap"].cpu().numpy().reshape(G, cfg.nb, -1), cfg.nb),
                           gmask)
-    mism, band = check_mask(gmask, ref["mask"], ref["F"], cfg.thr)
+    mism, band = check_mask(gmask, ref["mask"], ref["A"], cfg.thr)
     assert np.all(cnt >= 1), "the largest block of every row is kept"
     say(f"  kept {gmask.mean():.4f}  mismatches {mism}  band {band}")
     # attention with the GPU's own mask
@@ -201,9 +201,10 @@ def test_full_config_parity(cfg):
             qf = O.reorder(qn, cfg.T, cfg.H, cfg.W, cfg.P)
             kf = O.reorder(kn, cfg.T, cfg.H, cfg.W, cfg.P)
             ref = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, cfg.sta)
-            mism, band = check_mask(gmask[sl], ref["mask"], ref["F"], thr)
+            mism, band = check_mask(gmask[sl], ref["mask"], ref["A"], thr)
             mism_tot += mism
             band_tot += band
+            say(f"  heads {g0}..{sl.stop - 1}: mask mismatches {mism}, band {band}")
         assert mism_tot <= 1e-3 * gmask.size
         say(f"  thr {thr}: kept {gmask.mean():.4f}  mismatches {mism_tot}  band {band_tot}")
         rng = np.random.default_rng(cfg.index)
