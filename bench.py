@@ -1,0 +1,251 @@
+"""Benchmark of the NABLA forward path on one MI355X.
+
+One step = the whole path on one layer's worth of synthetic video-shaped Q/K/V
+already resident in HBM: fractal reorder of Q, K, V -> block mask (pooling, pooled
+map, softmax, CDF cutoff, lists) -> block-sparse attention -> inverse reorder of O.
+
+Prints one JSON line.  ``value`` is kept-tile TFLOP/s over the whole step
+(4 N^2 d FLOP per kept 64 x 64 tile / step time); the sub-phase times, the
+attention kernel's own TFLOP/s against the bf16 MFMA peak and the mask phase's
+GB/s against HBM peak ride along, with the oracle timed on the host beside it.
+
+    python bench.py [--steps K] [--warmup W] [--config 1] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import block_sparse_attention_blockmean_amd as nab  # noqa: E402
+from synth import GENERATOR_VERSION, get_config, make_qkv  # noqa: E402
+
+METRIC = "block-sparse attn ms/layer + kept-tile TFLOP/s (% MFMA peak); mask GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_blockmean_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per attention launch from the committed --pmc summary, valid only
+    if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for ln in open(TRAFFIC_FILE):
+        if ":" in ln and not ln.lstrip().startswith("#"):
+            key, val = ln.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, q, k, v, kept_flops_total, budget_s=12.0):
+    """The oracle (untuned) on a bounded sample of the same workload, extrapolated
+    to one whole step: reorder + mask of one head scaled by the head count, and
+    attention on as many query blocks of that head as fit the budget, scaled by
+    kept-tile FLOPs."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    G = cfg.BH
+    qn, kn, vn = (t[0, 0].float().numpy() for t in (q, k, v))
+    t0 = time.perf_counter()
+    qf, kf, vf = (O.reorder(a, cfg.T, cfg.H, cfg.W, cfg.P) for a in (qn, kn, vn))
+    t1 = time.perf_counter()
+    mk = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr, cfg.sta)
+    t2 = time.perf_counter()
+    scale = 1.0 / np.sqrt(cfg.d)
+    order = np.random.default_rng(0).permutation(cfg.nb)
+    done, flops = 0, 0.0
+    t3 = time.perf_counter()
+    for i in order:
+        O.attention_block(qf, kf, vf, mk["mask"][i], int(i), cfg.N, scale)
+        flops += float(mk["mask"][i].sum()) * 4 * cfg.N * cfg.N * cfg.d
+        done += 1
+        if time.perf_counter() - t3 > budget_s:
+            break
+    t4 = time.perf_counter()
+    t_step = G * ((t1 - t0) * 4 / 3 + (t2 - t1)) + (t4 - t3) * kept_flops_total / max(flops, 1.0)
+    return {
+        "value": kept_flops_total / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"head (0,0) of {G}: reorder of Q,K,V and the float32 mask; float64 attention on "
+                   f"{done} of {cfg.nb} query blocks; extrapolated to {G} heads and all kept tiles "
+                   f"({t4 - t0:.1f} s measured, est. {t_step:.0f} s per step)"),
+        "est_s_per_step": t_step,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="1", help="workload index or name")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only an identity reorder (P=1, a plain copy) of 1 GiB, for counter scaling")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the path shards by (batch, head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    nab.load_library()
+
+    if args.copy_calibration:
+        n = 1 << 29   # 1 GiB of bf16
+        x = torch.randn(n // 128, 128, device="cuda").to(torch.bfloat16).reshape(1, 1, -1, 128)
+        y = torch.empty_like(x)
+        L = x.shape[2]
+        for _ in range(max(1, args.steps)):
+            nab.reorder(x, 1, 1, L, 1, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": x.numel() * 2,
+                          "copy_calibration_bytes_written": y.numel() * 2, "launches": args.steps}))
+        return 0
+
+    cfg = get_config(int(args.config) if args.config.isdigit() else args.config)
+    print(f"# workload {cfg.name}: B{cfg.B} heads{cfg.heads} d{cfg.d} {cfg.dtype} "
+          f"{cfg.T}x{cfg.H}x{cfg.W} P{cfg.P} N{cfg.N} thr{cfg.thr} sta{cfg.sta}", file=sys.stderr,
+          flush=True)
+    q, k, v = make_qkv(cfg)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    qf, kf, vf, of, od = (torch.empty_like(qd) for _ in range(5))
+    nb = cfg.nb
+    cnt = torch.empty((cfg.B, cfg.heads, nb), dtype=torch.int32, device=dev)
+    idx = torch.empty((cfg.B, cfg.heads, nb, nb), dtype=torch.int32, device=dev)
+    ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, cfg.N),
+                     dtype=torch.uint8, device=dev)
+    T, H, W, P = cfg.T, cfg.H, cfg.W, cfg.P
+    # five events per timed step, all on torch's current stream, which is the stream
+    # every library call launches on
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        nab.reorder(qd, T, H, W, P, out=qf)
+        nab.reorder(kd, T, H, W, P, out=kf)
+        nab.reorder(vd, T, H, W, P, out=vf)
+        if ev:
+            ev[1].record()
+        nab.build_mask(qf, kf, T, H, W, P, cfg.N, cfg.thr, cfg.sta, workspace=ws, kv_count=cnt,
+                       kv_index=idx)
+        if ev:
+            ev[2].record()
+        nab.attn_fwd(qf, kf, vf, cnt, idx, cfg.N, out=of)
+        if ev:
+            ev[3].record()
+        nab.reorder(of, T, H, W, P, inverse=True, out=od)
+        if ev:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kept = int(cnt.sum().item())
+    kept_flops = kept * 4.0 * cfg.N * cfg.N * cfg.d
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    phase = np.mean([[ev[i].elapsed_time(ev[i + 1]) for i in range(4)] for ev in events], axis=0)
+    ms_reorder_in, ms_mask, ms_attn, ms_reorder_out = (float(x) for x in phase)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    esize = 2 if cfg.dtype == "bf16" else 4
+    tensor_bytes = cfg.BH * cfg.L * cfg.d * esize
+    mask_bytes = 2 * tensor_bytes + 4 * (kept + cfg.BH * nb)
+    attn_tflops = kept_flops / (ms_attn * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = read_traffic()
+
+    rec = {
+        "metric": METRIC,
+        "value": round(kept_flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": f"synthetic ({GENERATOR_VERSION}: smooth 3D cosine field + N(0,0.5^2) noise, seeded)",
+        "config": {
+            "workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "T": cfg.T,
+            "H": cfg.H, "W": cfg.W, "P": cfg.P, "N": cfg.N, "thr": cfg.thr,
+            "sta": list(cfg.sta) if cfg.sta else None, "L": cfg.L, "blocks_per_head": nb,
+        },
+        "ms_layer": round(float(ms_mask + ms_attn), 4),
+        "ms_attn": round(float(ms_attn), 4),
+        "ms_mask": round(float(ms_mask), 4),
+        "ms_reorder_qkv": round(float(ms_reorder_in), 4),
+        "ms_reorder_o": round(float(ms_reorder_out), 4),
+        "gpu_ms_per_step": round(float(phase.sum()), 4),
+        "kept_fraction": round(kept / (cfg.BH * nb * nb), 5),
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_frac_of_peak": round(attn_tflops / peak, 4),
+        "mask_GBps": round(mask_bytes / (ms_mask * 1e-3) / 1e9, 1),
+        "mask_frac_of_hbm": round(mask_bytes / (ms_mask * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "reorder_GBps": round(3 * 2 * tensor_bytes / (ms_reorder_in * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / peak, 4),
+            "traffic": traffic,
+        },
+        "device": torch.cuda.get_device_name(0),
+        "cus": torch.cuda.get_device_properties(0).multi_processor_count,
+    }
+    if not args.no_cpu:
+        print("# timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
+        cb = cpu_baseline(cfg, q, k, v, kept_flops)
+        cb["value"] = float(f"{cb['value']:.3g}")
+        rec["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -97,40 +97,92 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
 
 // ---------------------------------------------------------------------------
 // Reduced map + softmax + CDF cutoff + STA + lists.
-// A workgroup owns 16 query blocks (rows) of one head.
-// Phase 1: each wave computes 16x16 tiles of S with v_mfma_f32_16x16x4_f32 (float32
-//   operands, float32 accumulation) and parks them in LDS.
-// Phase 2: each wave takes whole rows: softmax, then the cutoff.  Keeping block j
-//   iff F_j > thr is the same as keeping every block whose value is at least v*, the
-//   smallest row value with g(v*) > thr, where g(u) = sum of the row values <= u.
-//   g only grows with u, and for non-negative floats the bit patterns order like
-//   the values, so v* is found by bisection over 32-bit patterns: 31 masked sums.
+// A workgroup (8 waves) owns 16 query blocks (rows) of one head.
+// Phase 1: the waves compute 16x16 tiles of S with v_mfma_f32_16x16x4_f32 (float32
+//   operands and accumulation) and park the 16 rows in LDS.
+// Phase 2: each wave takes whole rows.  Keeping block j iff F_j > thr is the same as
+//   keeping every block whose probability is at least v*, the smallest row value
+//   with g(v*) > thr, where g(u) = sum of the row values <= u.  g only grows with u,
+//   and non-negative floats order like their bit patterns, so v* is found by
+//   bisection over bit patterns.  The search starts at u0 = thr / nb (g(u0) <= nb u0
+//   = thr) and keeps only the values still inside the bracket (compacted into a
+//   per-wave LDS buffer), so each step touches fewer values and the search stops
+//   once a single candidate is left.  All sums run in a fixed order, so the result
+//   is deterministic.
 // ---------------------------------------------------------------------------
 constexpr int kRows = 16;
-constexpr int kMaxChunks = (NABLA_MAX_BLOCKS + 63) / 64;
+constexpr int kWaves = 8;
+constexpr int kCap = 512;   // candidates per wave held in LDS
 
+template <int K>
+__device__ inline float swz_xor(float x) {
+    // ds_swizzle bit-mask mode inside each 32-lane half: lane ^ K
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (K << 10) | 0x1f));
+}
+template <int K>
+__device__ inline int swz_xor_i(int x) {
+    return __builtin_amdgcn_ds_swizzle(x, (K << 10) | 0x1f);
+}
+// Wave-wide reductions: a butterfly inside each 32-lane half, then the two halves
+// combined from lanes 0 and 32, so every lane holds the same bits.
 __device__ inline float wave_sum(float x) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
-    return x;
+    x += swz_xor<1>(x);
+    x += swz_xor<2>(x);
+    x += swz_xor<4>(x);
+    x += swz_xor<8>(x);
+    x += swz_xor<16>(x);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+}
+__device__ inline int wave_sum_i(int x) {
+    x += swz_xor_i<1>(x);
+    x += swz_xor_i<2>(x);
+    x += swz_xor_i<4>(x);
+    x += swz_xor_i<8>(x);
+    x += swz_xor_i<16>(x);
+    return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 32);
 }
 __device__ inline float wave_max(float x) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+    x = fmaxf(x, swz_xor<1>(x));
+    x = fmaxf(x, swz_xor<2>(x));
+    x = fmaxf(x, swz_xor<4>(x));
+    x = fmaxf(x, swz_xor<8>(x));
+    x = fmaxf(x, swz_xor<16>(x));
+    return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
+                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)));
 }
-__device__ inline uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
-    return x;
+__device__ inline uint32_t wave_max_u(uint32_t x) {
+    x = max(x, (uint32_t)swz_xor_i<1>((int)x));
+    x = max(x, (uint32_t)swz_xor_i<2>((int)x));
+    x = max(x, (uint32_t)swz_xor_i<4>((int)x));
+    x = max(x, (uint32_t)swz_xor_i<8>((int)x));
+    x = max(x, (uint32_t)swz_xor_i<16>((int)x));
+    return max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 32));
+}
+
+// Writes the values of src[0..len) whose bit pattern lies in (lo, hi] to dst, in
+// order; src may equal dst (each write lands at or before its source).
+__device__ inline int compact(const float* src, int len, uint32_t lo, uint32_t hi, float* dst,
+                              int lane) {
+    int n = 0;
+    for (int j0 = 0; j0 < len; j0 += 64) {
+        const int j = j0 + lane;
+        const float x = (j < len) ? src[j] : 0.f;
+        const uint32_t b = __float_as_uint(x);
+        const bool in = (j < len) && b > lo && b <= hi;
+        const uint64_t ballot = __ballot(in);
+        if (in) dst[n + __popcll(ballot & ((1ull << lane) - 1ull))] = x;
+        n += __popcll(ballot);
+    }
+    return n;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void map_select_kernel(
+__global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp, int nb, int ld_s, float scale,
     float thr, int sta, int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
     int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap) {
-    extern __shared__ float s_lds[];   // [kRows][ld_s]
+    extern __shared__ float s_lds[];   // [kRows][ld_s] rows, then [kWaves][kCap] candidates
     constexpr int KC = D / 4;          // k values per lane per MFMA chain
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -138,11 +190,9 @@ __global__ __launch_bounds__(256) void map_select_kernel(
     const int row0 = blockIdx.x * kRows;
     const float* qh = qp + (size_t)bh * nb * D;
     const float* kh = kp + (size_t)bh * nb * D;
-    const int n_chunks = (nb + 63) >> 6;
-    const int ld_pad = n_chunks * 64;
 
-    // ---- phase 1: S tiles.  The k index of the MFMA (lane / 16) selects a
-    // contiguous quarter of d in both operands, so operand loads are 16-byte vectors.
+    // ---- phase 1: S tiles.  The MFMA's k index (lane / 16) selects a contiguous
+    // quarter of d in both operands, so operand loads are 16-byte vectors.
     {
         const int li = lane & 15;
         const int kq = lane >> 4;
@@ -159,8 +209,8 @@ __global__ __launch_bounds__(256) void map_select_kernel(
 #pragma unroll
             for (int v = 0; v < KC; ++v) a[v] = 0.f;
         }
-        const int n_ct = ld_pad / 16;
-        for (int ct = wave; ct < n_ct; ct += 4) {
+        const int n_ct = (nb + 15) / 16;
+        for (int ct = wave; ct < n_ct; ct += kWaves) {
             const int j = ct * 16 + li;
             float b[KC];
             if (j < nb) {
@@ -178,68 +228,102 @@ __global__ __launch_bounds__(256) void map_select_kernel(
 #pragma unroll
             for (int s = 0; s < KC; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
             // lane holds S[4*(lane/16) + r][16*ct + lane%16]
+            if (j < nb) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 4 * kq + r;
-                s_lds[i * ld_s + j] = (j < nb) ? acc[r] * scale : -INFINITY;
+                for (int r = 0; r < 4; ++r) s_lds[(4 * kq + r) * ld_s + j] = acc[r] * scale;
             }
         }
     }
     __syncthreads();
 
     // ---- phase 2: one row per wave at a time.
+    float* cand = s_lds + kRows * ld_s + wave * kCap;
     const int nwords = (nb + 31) >> 5;
-    for (int r = wave; r < kRows; r += 4) {
+    for (int r = wave; r < kRows; r += kWaves) {
         const int row = row0 + r;
         if (row >= nb) break;
-        const float* srow = s_lds + r * ld_s;
-        float v[kMaxChunks];
+        float* arow = s_lds + r * ld_s;
+        // softmax; the row is overwritten with the probabilities A
         float mx = -INFINITY;
-#pragma unroll
-        for (int m = 0; m < kMaxChunks; ++m) {
-            if (m < n_chunks) {
-                v[m] = srow[m * 64 + lane];
-                mx = fmaxf(mx, v[m]);
-            }
-        }
+        for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, arow[j]);
         mx = wave_max(mx);
         float sum = 0.f;
-#pragma unroll
-        for (int m = 0; m < kMaxChunks; ++m) {
-            if (m < n_chunks) {
-                v[m] = expf(v[m] - mx);      // padding (-inf) becomes 0
-                sum += v[m];
-            }
+        for (int j = lane; j < nb; j += 64) {
+            const float e = expf(arow[j] - mx);
+            arow[j] = e;
+            sum += e;
         }
         sum = wave_sum(sum);
-        uint32_t vmax_bits = 0;
-#pragma unroll
-        for (int m = 0; m < kMaxChunks; ++m) {
-            if (m < n_chunks) {
-                v[m] = v[m] / sum;
-                vmax_bits = max(vmax_bits, __float_as_uint(v[m]));
-            }
+        // start of the bracket: u0 = thr / nb, nudged down so rounding cannot push
+        // g(u0) above thr; it is verified below and dropped to 0 if it fails
+        uint32_t lo = __float_as_uint(thr / ((float)nb * 1.0001f));
+        float g_lo = 0.f;
+        int n_in = 0;
+        uint32_t maxb = 0;
+        for (int j = lane; j < nb; j += 64) {
+            const float p = arow[j] / sum;
+            arow[j] = p;
+            const uint32_t b = __float_as_uint(p);
+            maxb = max(maxb, b);
+            if (b <= lo) g_lo += p; else ++n_in;
         }
-        vmax_bits = wave_max_u32(vmax_bits);
-        // smallest bit pattern u with g(u) > thr, searched in (lo, hi]; g(0) = 0 <= thr.
-        uint32_t lo = 0, hi = vmax_bits;
-        while (hi - lo > 1) {
+        g_lo = wave_sum(g_lo);
+        n_in = wave_sum_i(n_in);
+        maxb = wave_max_u(maxb);
+        if (g_lo > thr) {   // cannot happen in exact arithmetic; fall back to g(0) = 0
+            lo = 0;
+            g_lo = 0.f;
+            int c = 0;
+            for (int j = lane; j < nb; j += 64) c += __float_as_uint(arow[j]) > 0u;
+            n_in = wave_sum_i(c);
+        }
+        uint32_t hi = maxb;
+        // bracket (lo, hi]: g(lo) = g_lo <= thr and, unless the whole row sums to at
+        // most thr, g(hi) > thr; n_in values lie inside it (always >= 1: the maximum)
+        const float* src = arow;
+        int len = nb;
+        if (n_in <= kCap) {
+            len = compact(arow, nb, lo, hi, cand, lane);
+            src = cand;
+        }
+        while (hi - lo > 1 && n_in > 1) {
             const uint32_t mid = lo + ((hi - lo) >> 1);
-            float g = 0.f;
-#pragma unroll
-            for (int m = 0; m < kMaxChunks; ++m) {
-                if (m < n_chunks) g += (__float_as_uint(v[m]) <= mid) ? v[m] : 0.f;
+            float s = 0.f;
+            int c = 0;
+            for (int j = lane; j < len; j += 64) {
+                const float x = src[j];
+                const uint32_t b = __float_as_uint(x);
+                if (b > lo && b <= mid) { s += x; ++c; }
             }
-            g = wave_sum(g);
-            if (g > thr) hi = mid; else lo = mid;
+            s = wave_sum(s);
+            c = wave_sum_i(c);
+            if (g_lo + s > thr) {
+                hi = mid;
+                n_in = c;
+            } else {
+                lo = mid;
+                g_lo += s;
+                n_in -= c;
+            }
+            if (n_in <= kCap && 2 * n_in <= len && n_in > 1) {
+                len = compact(src, len, lo, hi, cand, lane);
+                src = cand;
+            }
         }
-        // If even the whole row sums to <= thr (thr within rounding of 1), hi stays at
-        // the row maximum, which keeps the largest block.
-        const uint32_t cut = hi;
+        uint32_t cut = hi;
+        if (n_in == 1 && hi - lo > 1) {
+            // the single value left in (lo, hi] is where g crosses thr
+            uint32_t best = 0;
+            for (int j = lane; j < len; j += 64) {
+                const uint32_t b = __float_as_uint(src[j]);
+                if (b > lo && b <= hi) best = max(best, b);
+            }
+            cut = wave_max_u(best);
+        }
 
         int qt = 0, qh_ = 0, qw = 0;
+        const int pf = nH * nW;
         if (sta) {
-            const int pf = nH * nW;
             qt = row / pf;
             const int rem = row - qt * pf;
             qh_ = rem / nW;
@@ -248,30 +332,26 @@ __global__ __launch_bounds__(256) void map_select_kernel(
         int32_t* out_idx = kv_index + ((size_t)bh * nb + row) * nb;
         uint32_t* out_bits = bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr;
         int base = 0;
-#pragma unroll
-        for (int m = 0; m < kMaxChunks; ++m) {
-            if (m < n_chunks) {
-                const int j = m * 64 + lane;
-                bool keep = false;
-                if (j < nb) {
-                    keep = __float_as_uint(v[m]) >= cut;
-                    if (sta && !keep) {
-                        const int pf = nH * nW;
-                        const int kt = j / pf;
-                        const int rem = j - kt * pf;
-                        const int kh_ = rem / nW;
-                        const int kw = rem - kh_ * nW;
-                        keep = abs(kt - qt) <= rt && abs(kh_ - qh_) <= rh && abs(kw - qw) <= rw;
-                    }
+        for (int j0 = 0; j0 < nb; j0 += 64) {
+            const int j = j0 + lane;
+            bool keep = false;
+            if (j < nb) {
+                keep = __float_as_uint(arow[j]) >= cut;
+                if (sta && !keep) {
+                    const int kt = j / pf;
+                    const int rem = j - kt * pf;
+                    const int kh_ = rem / nW;
+                    const int kw = rem - kh_ * nW;
+                    keep = abs(kt - qt) <= rt && abs(kh_ - qh_) <= rh && abs(kw - qw) <= rw;
                 }
-                const uint64_t ballot = __ballot(keep);
-                const int pos = base + __popcll(ballot & ((1ull << lane) - 1ull));
-                if (keep) out_idx[pos] = j;
-                base += __popcll(ballot);
-                if (out_bits) {
-                    if (lane == 0 && 2 * m < nwords) out_bits[2 * m] = (uint32_t)ballot;
-                    if (lane == 1 && 2 * m + 1 < nwords) out_bits[2 * m + 1] = (uint32_t)(ballot >> 32);
-                }
+            }
+            const uint64_t ballot = __ballot(keep);
+            if (keep) out_idx[base + __popcll(ballot & ((1ull << lane) - 1ull))] = j;
+            base += __popcll(ballot);
+            if (out_bits) {
+                const int w = j0 >> 5;
+                if (lane == 0 && w < nwords) out_bits[w] = (uint32_t)ballot;
+                if (lane == 1 && w + 1 < nwords) out_bits[w + 1] = (uint32_t)(ballot >> 32);
             }
         }
         if (lane == 0) kv_count[(size_t)bh * nb + row] = base;
@@ -289,20 +369,20 @@ hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
-    const int n_chunks = (a.nb + 63) / 64;
-    const int ld_s = n_chunks * 64 + 16;
-    const size_t lds = (size_t)kRows * ld_s * sizeof(float);
+    const int ld_s = ((a.nb + 63) / 64) * 64 + 16;
+    const size_t lds = ((size_t)kRows * ld_s + (size_t)kWaves * kCap) * sizeof(float);
     static bool attr_set = false;
     if (!attr_set) {
+        const int max_lds = (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap) *
+                            (int)sizeof(float);
         hipError_t e = hipFuncSetAttribute((const void*)map_select_kernel<D>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           kRows * ((kMaxChunks * 64) + 16) * (int)sizeof(float));
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
-    hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(256), lds, s, a.qp, a.kp, a.nb, ld_s,
-                       a.scale, a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count,
+    hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.qp, a.kp, a.nb,
+                       ld_s, a.scale, a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count,
                        a.kv_index, a.bitmap);
     return hipGetLastError();
 }

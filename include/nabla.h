@@ -55,7 +55,7 @@ typedef enum { NABLA_F32 = 0, NABLA_BF16 = 1 } nabla_dtype;
 typedef struct { int wt, wh, ww; } nabla_sta_window;
 
 /* Largest number of N-token blocks per head that nabla_build_mask accepts. */
-#define NABLA_MAX_BLOCKS 2496
+#define NABLA_MAX_BLOCKS 2048
 
 /*
  * nabla_reorder - fractal flattening of the token axis ("Metodologia: NABLA", item 1,

@@ -117,7 +117,7 @@ def build_mask(lib, q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=6
     (dict(dt=5), NABLA_E_INVAL),
     (dict(N=32, T=4), NABLA_E_UNSUPPORTED),
     (dict(d=96), NABLA_E_UNSUPPORTED),
-    (dict(T=160, H=32, W=32), NABLA_E_UNSUPPORTED),     # 2560 blocks > NABLA_MAX_BLOCKS
+    (dict(T=129, H=32, W=32), NABLA_E_UNSUPPORTED),     # 2064 blocks > NABLA_MAX_BLOCKS
     (dict(ws=None), NABLA_E_WORKSPACE),
     (dict(ws_bytes=100), NABLA_E_WORKSPACE),
 ])

@@ -155,6 +155,34 @@ def test_attention_arbitrary_lists(dtype, d):
     assert max_abs(on, ref) <= (TOL_BF16 if dtype == "bf16" else TOL_F32)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_exact_ties_grouped(dtype):
+    """Blocks with identical keys get identical pooled probabilities on both sides;
+    tied blocks must be kept or dropped together, and with exact ties the plain
+    |F - thr| <= 1e-4 band applies."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(11)
+    L, d, N = 1024, 64, 64
+    q = torch.randn(1, 2, L, d, generator=g).to(tdt)
+    k = torch.randn(1, 2, L, d, generator=g).to(tdt) * 2
+    # 16 key blocks made of 4 distinct blocks, each repeated 4 times
+    kb = k.reshape(1, 2, 16, N, d)
+    for j in range(4, 16):
+        kb[:, :, j] = kb[:, :, j % 4]
+    k = kb.reshape(1, 2, L, d).contiguous()
+    qn = to_np(q).reshape(2, L, d)
+    kn = to_np(k).reshape(2, L, d)
+    for thr in (0.05, 0.2, 0.3, 0.45, 0.6, 0.8):
+        cnt, idx = nab.build_mask(q.cuda(), k.cuda(), 4, 16, 16, 8, N, thr)
+        torch.cuda.synchronize()
+        gm = lists_to_mask(cnt.cpu().numpy().reshape(2, 16), idx.cpu().numpy().reshape(2, 16, 16))
+        for j in range(4, 16):
+            assert np.array_equal(gm[..., j], gm[..., j % 4]), (thr, j)
+        ref = O.block_mask(qn, kn, 4, 16, 16, 8, N, thr)
+        mism = gm != ref["mask"]
+        assert np.all(np.abs(ref["F"][mism] - thr) <= 1e-4), thr
+
+
 def test_determinism():
     """Repeated runs give identical bits (no atomics or order-dependent reductions)."""
     cfg = SMALL[4]
