@@ -150,6 +150,7 @@ def main(argv=None):
     idx = torch.empty((cfg.B, cfg.heads, nb, nb), dtype=torch.int32, device=dev)
     ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, cfg.N),
                      dtype=torch.uint8, device=dev)
+    sched = torch.empty((cfg.BH * nb,), dtype=torch.int32, device=dev)
     T, H, W, P = cfg.T, cfg.H, cfg.W, cfg.P
     # five events per timed step, all on torch's current stream, which is the stream
     # every library call launches on
@@ -164,10 +165,10 @@ def main(argv=None):
         if ev:
             ev[1].record()
         nab.build_mask(qf, kf, T, H, W, P, cfg.N, cfg.thr, cfg.sta, workspace=ws, kv_count=cnt,
-                       kv_index=idx)
+                       kv_index=idx, schedule=sched)
         if ev:
             ev[2].record()
-        nab.attn_fwd(qf, kf, vf, cnt, idx, cfg.N, out=of)
+        nab.attn_fwd(qf, kf, vf, cnt, idx, cfg.N, out=of, schedule=sched)
         if ev:
             ev[3].record()
         nab.reorder(of, T, H, W, P, inverse=True, out=od)

@@ -56,9 +56,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_build_mask_workspace_size.argtypes = [i, i, i, i, i]
     lib.nabla_build_mask_workspace_size.restype = sz
     lib.nabla_build_mask.argtypes = [vp, vp, i, i, i, i, i, i, i, i, f, ctypes.POINTER(StaWindow),
-                                     f, i, vp, vp, vp, vp, sz, vp]
+                                     f, i, vp, vp, vp, vp, vp, sz, vp]
     lib.nabla_build_mask.restype = i
-    lib.block_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, f, i, vp]
+    lib.block_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, f, i, vp]
     lib.block_sparse_attn_fwd.restype = i
     lib.nabla_status_string.argtypes = [i]
     lib.nabla_status_string.restype = ctypes.c_char_p
@@ -119,9 +119,13 @@ def build_mask_workspace_size(batch: int, heads: int, L: int, d: int, N: int = 6
 def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int, N: int = 64,
                thr: float = 0.1, sta: Optional[Tuple[int, int, int]] = None,
                scale: Optional[float] = None, with_bitmap: bool = False,
-               workspace: Optional[torch.Tensor] = None, kv_count: Optional[torch.Tensor] = None,
-               kv_index: Optional[torch.Tensor] = None):
-    """NABLA block mask of fractal-ordered Q, K: returns (kv_count, kv_index[, bitmap])."""
+               with_schedule: bool = False, workspace: Optional[torch.Tensor] = None,
+               kv_count: Optional[torch.Tensor] = None, kv_index: Optional[torch.Tensor] = None,
+               schedule: Optional[torch.Tensor] = None):
+    """NABLA block mask of fractal-ordered Q, K.
+
+    Returns (kv_count, kv_index), plus the bitmap and/or the longest-first
+    schedule when asked for (in that order)."""
     lib = load_library()
     B, NH, L, d = q.shape
     if k.shape != q.shape or k.dtype != q.dtype:
@@ -135,6 +139,8 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
     bitmap = None
     if with_bitmap:
         bitmap = torch.empty((B, NH, nb, (nb + 31) // 32), dtype=torch.int32, device=dev)
+    if with_schedule and schedule is None:
+        schedule = torch.empty((B * NH * nb,), dtype=torch.int32, device=dev)
     ws_bytes = lib.nabla_build_mask_workspace_size(B, NH, L, d, N)
     if workspace is None:
         workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
@@ -144,15 +150,20 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
         float(scale) if scale is not None else 0.0, _dtype_code(q),
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
         _dev(bitmap, "bitmap") if bitmap is not None else None,
+        _dev(schedule, "schedule") if schedule is not None else None,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()), lib)
+    out = [kv_count, kv_index]
     if with_bitmap:
-        return kv_count, kv_index, bitmap
-    return kv_count, kv_index
+        out.append(bitmap)
+    if with_schedule or schedule is not None:
+        out.append(schedule)
+    return tuple(out)
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.Tensor,
              kv_index: torch.Tensor, N: int = 64, scale: Optional[float] = None,
-             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+             out: Optional[torch.Tensor] = None,
+             schedule: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Block-sparse attention over the kept N x N tiles listed in kv_count/kv_index."""
     lib = load_library()
     B, NH, L, d = q.shape
@@ -164,10 +175,14 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.
         raise TypeError("kv_count and kv_index must be int32")
     if kv_count.numel() != B * NH * nb or kv_index.numel() != B * NH * nb * nb:
         raise ValueError("kv_count / kv_index sizes do not match q")
+    if schedule is not None:
+        if schedule.dtype != torch.int32 or schedule.numel() != B * NH * nb:
+            raise ValueError("schedule must hold batch*heads*nb int32 entries")
     if out is None:
         out = torch.empty_like(q)
     _check(lib.block_sparse_attn_fwd(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, NH, L, d, N,
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+        _dev(schedule, "schedule") if schedule is not None else None,
         float(scale) if scale is not None else 0.0, _dtype_code(q), _stream()), lib)
     return out

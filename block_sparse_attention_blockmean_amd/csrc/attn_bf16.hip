@@ -4,17 +4,26 @@
 // "Metodologia: NABLA", item 2, "Expansão"); a dropped tile contributes neither to the
 // numerator nor to the normaliser.
 //
-// One workgroup = one 64-row query block, two waves of 32 query rows each.  For every
-// kept KV block the workgroup stages K (row-major) and V (transposed, d-major) in LDS
-// and each wave runs
+// One workgroup = one 64-row query block, two waves of 32 query rows each.  Per kept
+// KV block, each wave runs
 //     S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q from VGPRs
 //     online softmax   float32, exp2 with scale*log2(e) folded into one FMA
 //     O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, A = V^T from LDS, B = P from VGPRs
 // Computing the transposed products makes every lane own one query column: its S^T
 // accumulator already has the layout the P operand of the second product needs (the
 // MFMA's k index is permuted identically in both operands, which leaves the sum
-// unchanged), and the row statistics (max, sum, rescale) stay in the lane, with one
-// exchange between lanes l and l^32 that split the 64 keys of the tile.
+// unchanged), and the row statistics stay in the lane, with one exchange between
+// lanes l and l^32, which split the 64 keys of a tile.
+//
+// Memory pipeline: K and V tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, no VGPR staging), row-major with an XOR swizzle of the
+// 16-byte chunks.  V^T operands come out of the row-major V tile through the
+// transposing LDS read (ds_read_b64_tr_b16).  All copies for later tiles are issued
+// at the end of an iteration, after every LDS read of the current tile: K of the tile
+// after next (two K buffers), then V of the next tile (one V buffer).  Copies
+// complete in issue order, so the single wait for V before the P V product also
+// covers K of the next tile: K streams in for a whole iteration, V for S^T plus the
+// softmax.
 #include <math.h>
 
 #include "nabla_internal.h"
@@ -24,42 +33,77 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kBlk = 64;
 constexpr int kThreads = 128;
-constexpr int kPadK = 8;   // bf16 elements of padding per K row in LDS
-constexpr int kPadV = 8;   // bf16 elements of padding per V^T row in LDS
 
-// Position of key kv (0..63) inside a V^T row in LDS.  The S^T accumulator of lane l
-// (half h = l / 32) holds keys 32*T + 8*M + 4*h + C (register 4*M + C of tile T); the
-// P operand of k-step u is registers 8*(u%2) .. 8*(u%2)+7 of tile u/2, so k-step u,
-// half h, element e needs key 32*(u/2) + 8*(2*(u%2) + e/4) + 4*h + e%4.  Storing that
-// key at 16*u + 8*h + e makes the matching V^T operand one contiguous 16-byte read.
-__device__ inline int vt_pos(int kv) {
-    const int T = kv >> 5, M = (kv >> 3) & 3, H = (kv >> 2) & 1, C = kv & 3;
-    return 32 * T + 16 * (M >> 1) + 8 * H + 4 * (M & 1) + C;
+template <int D>
+struct Tile {
+    static constexpr int kRowBytes = 2 * D;             // one token row of K or V
+    static constexpr int kChunks = D / 8;               // 16-byte chunks per row
+    static constexpr int kRowsPerLine = 256 / kRowBytes;  // rows per 256-byte LDS bank line
+    static constexpr int kBytes = kBlk * kRowBytes;
+    static constexpr int kLoadsPerWave = kBytes / 1024 / 2;  // 1 KB per wave-wide load
+    // K is read 16 bytes per lane from 16 consecutive rows at one chunk: spread the
+    // rows over all chunk slots of a bank line.
+    __device__ static inline int k_swz(int row) { return (row / kRowsPerLine) & (kChunks - 1); }
+    // V is read 8 bytes per lane, 4 rows x 64 bytes per 16 lanes: spread groups of
+    // 4 chunks over the bank line.
+    __device__ static inline int v_swz(int row) { return 4 * ((row / kRowsPerLine) & (kChunks / 4 - 1)); }
+};
+
+// Wave-wide copy of one 64 x D tile from global memory into LDS.  Load u of wave w
+// fills bytes [1024 (2u + w), +1024) of the LDS tile, 16 bytes per lane in lane order;
+// the lane picks the global chunk that belongs in that slot under the swizzle.
+template <int D, bool kIsV>
+__device__ inline void load_tile(const __bf16* g_tile, char* lds_tile, int wave, int lane) {
+    using G = Tile<D>;
+    const char* src = reinterpret_cast<const char*>(g_tile);
+#pragma unroll
+    for (int u = 0; u < G::kLoadsPerWave; ++u) {
+        const int piece = 2 * u + wave;
+        const int o = piece * 1024 + lane * 16;
+        const int row = o / G::kRowBytes;
+        const int slot = (o % G::kRowBytes) / 16;
+        const int chunk = slot ^ (kIsV ? G::v_swz(row) : G::k_swz(row));
+        __builtin_amdgcn_global_load_lds(src + row * G::kRowBytes + chunk * 16,
+                                         (lds_void*)(lds_tile + piece * 1024), 16, 0, 0);
+    }
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, int L, int nb, const int32_t* __restrict__ kv_count,
-    const int32_t* __restrict__ kv_index, float scale_log2e) {
+    const int32_t* __restrict__ kv_index, const int32_t* __restrict__ schedule,
+    float scale_log2e) {
+    using G = Tile<D>;
     constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;        // 32-row d tiles of O^T
-    constexpr int LDK = D + kPadK;
-    constexpr int LDV = kBlk + kPadV;
-    __shared__ __attribute__((aligned(16))) __bf16 k_lds[kBlk * LDK];
-    __shared__ __attribute__((aligned(16))) __bf16 vt_lds[D * LDV];
+    __shared__ __attribute__((aligned(1024))) char k_lds[2][G::kBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds[G::kBytes];
 
     // Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD walks a
     // contiguous range of (head, query block) and neighbouring query blocks, which
     // keep similar KV lists, share that XCD's L2.
-    const int G = gridDim.x;
-    const int full = (G / 8) * 8;
+    // With a schedule, workgroups take query blocks in its order (longest lists first).
+    const int nwg = gridDim.x;
+    const int full = (nwg / 8) * 8;
     int logical = blockIdx.x;
-    if (logical < full) logical = (logical % 8) * (G / 8) + logical / 8;
+    if (schedule) {
+        logical = schedule[logical];
+    } else if (logical < full) {
+        logical = (logical % 8) * (nwg / 8) + logical / 8;
+    }
     const int bh = logical / nb;
     const int qb = logical - bh * nb;
 
@@ -74,6 +118,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const __bf16* kh = k + head_off;
     const __bf16* vh = v + head_off;
 
+    const int count = kv_count[(size_t)bh * nb + qb];
+    const int32_t* list = kv_index + ((size_t)bh * nb + qb) * nb;
     // Q operand: lane holds Q[row][16 s + 8 h .. + 7] for s = 0..KS-1.
     const int qrow = qb * kBlk + wave * 32 + c32;
     bf16x8 qreg[KS];
@@ -81,129 +127,137 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int s = 0; s < KS; ++s)
         qreg[s] = *reinterpret_cast<const bf16x8*>(qh + (size_t)qrow * D + 16 * s + 8 * h);
 
+    // issue order K0, K1, V0; iteration i issues K(i+2), V(i+1) at its end
+    if (count > 0) load_tile<D, false>(kh + (size_t)list[0] * kBlk * D, k_lds[0], wave, lane);
+    if (count > 1) load_tile<D, false>(kh + (size_t)list[1] * kBlk * D, k_lds[1], wave, lane);
+    if (count > 0) load_tile<D, true>(vh + (size_t)list[0] * kBlk * D, v_lds, wave, lane);
+
     f32x16 oacc[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
-    float m_run = -INFINITY;   // running max of scaled logits (log2 domain)
+    float m_run = -INFINITY;   // reference max of scaled logits (log2 domain)
     float l_run = 0.f;         // this lane's share of the running normaliser
 
-    const int count = kv_count[(size_t)bh * nb + qb];
-    const int32_t* list = kv_index + ((size_t)bh * nb + qb) * nb;
+    // per-lane LDS byte offsets that do not change from tile to tile
+    int k_off[2][KS];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int row = 32 * t + c32;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            k_off[t][s] = row * G::kRowBytes + (((2 * s + h) ^ G::k_swz(row)) * 16);
+    }
+    const int g16 = lane >> 4, j16 = lane & 15;
+    int v_off[DT][4][2];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int row = 16 * u + 4 * h + 8 * p + (j16 >> 2);
+                const int d = 32 * t + 16 * (g16 & 1) + 4 * (j16 & 3);
+                v_off[t][u][p] = row * G::kRowBytes + (((d >> 3) ^ G::v_swz(row)) * 16) + ((d >> 2) & 1) * 8;
+            }
+
+    // K0 has landed once only K1 and V0 may be pending
+    if (count > 1) wait_vmcnt<2 * G::kLoadsPerWave>(); else wait_vmcnt<G::kLoadsPerWave>();
+    __syncthreads();
 
     for (int it = 0; it < count; ++it) {
-        const int j = list[it];
-        const __bf16* kt = kh + (size_t)j * kBlk * D;
-        const __bf16* vt = vh + (size_t)j * kBlk * D;
-        __syncthreads();
-        // ---- stage K: 16-byte chunks, 16 lanes per 256-byte row
-        {
-            constexpr int CH = D / 8;                  // chunks per row
-            constexpr int PER = kBlk * CH / kThreads;  // chunks per thread
-            uint4 buf[PER];
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int id = tid + u * kThreads;
-                const int row = id / CH, ch = id % CH;
-                buf[u] = *reinterpret_cast<const uint4*>(kt + (size_t)row * D + ch * 8);
-            }
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int id = tid + u * kThreads;
-                const int row = id / CH, ch = id % CH;
-                *reinterpret_cast<uint4*>(k_lds + row * LDK + ch * 8) = buf[u];
-            }
-        }
-        // ---- stage V transposed: a unit is 4 consecutive keys x 8 consecutive d
-        {
-            constexpr int DC = D / 8;
-            constexpr int UNITS = 16 * DC;
-            constexpr int PER = UNITS / kThreads;
-            uint4 buf[PER][4];
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int id = tid + u * kThreads;
-                const int kg = id & 15, dc = id >> 4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    buf[u][i] = *reinterpret_cast<const uint4*>(vt + (size_t)(4 * kg + i) * D + 8 * dc);
-            }
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int id = tid + u * kThreads;
-                const int kg = id & 15, dc = id >> 4;
-                const int pos = vt_pos(4 * kg);
-                const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&buf[u][0]);
-                const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&buf[u][1]);
-                const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&buf[u][2]);
-                const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&buf[u][3]);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    // element c of each of the 4 rows: low or high half of word c/2
-                    const int sh = (c & 1) * 16;
-                    const uint32_t e0 = (w0[c >> 1] >> sh) & 0xffffu;
-                    const uint32_t e1 = (w1[c >> 1] >> sh) & 0xffffu;
-                    const uint32_t e2 = (w2[c >> 1] >> sh) & 0xffffu;
-                    const uint32_t e3 = (w3[c >> 1] >> sh) & 0xffffu;
-                    uint2 pk;
-                    pk.x = e0 | (e1 << 16);
-                    pk.y = e2 | (e3 << 16);
-                    *reinterpret_cast<uint2*>(vt_lds + (8 * dc + c) * LDV + pos) = pk;
-                }
-            }
-        }
-        __syncthreads();
+        // K(it) is in LDS and visible: it was issued before V(it-1), which every wave
+        // waited for before the previous P V product, followed by two barriers
+        const char* kbuf = k_lds[it & 1];
 
-        // ---- S^T = K Q^T for this wave's 32 query columns, 64 keys in two 32-key tiles
+        // ---- S^T = K Q^T for this wave's 32 query columns, 64 keys in two 32-key
+        // tiles.  All K operands are requested first so the MFMA chain never waits on
+        // a freshly issued LDS read.
+        bf16x8 ka[KS][2];
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) ka[s][t] = *reinterpret_cast<const bf16x8*>(kbuf + k_off[t][s]);
         f32x16 sacc[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(k_lds + (32 * t + c32) * LDK + 16 * s + 8 * h);
-                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[t], 0, 0, 0);
-            }
-        }
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][t], qreg[s], sacc[t], 0, 0, 0);
+        // keep the scheduler from folding the reads back into the MFMA chain
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);   // all K operand reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);   // then the MFMAs
 
-        // ---- online softmax for query column c32 (keys split between lanes l, l^32)
+        // ---- online softmax for query column c32 (keys split between lanes l, l^32).
+        // The reference maximum m_run only moves when a tile's maximum exceeds it by
+        // more than 8 (log2 units), so P stays below 2^8 and the rescale of O and l is
+        // rare; normalising by l at the end makes the result independent of m_run.
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * scale_log2e);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float psum = 0.f;
-        bf16x8 pb[4];
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2e;
+        if (__ballot(mx > m_run + 8.0f)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+            for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][8 * (u & 1) + e], scale_log2e, -m_new));
-                psum += p;
-                pb[u][e] = (__bf16)p;
-            }
+                for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
         }
-        l_run = l_run * alpha + psum;
+
+        // V(it), and K(it+1) issued before it, have landed
+        wait_vmcnt<0>();
+        __syncthreads();
+
+        // ---- O^T += V^T P^T, k-step by k-step: P of step u needs only its own 8 exps,
+        // and the V^T operands (two transposing 8-byte reads each) of step u+1 are
+        // requested while step u multiplies.
+        s16x4 vr[2][DT][2];
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-
-        // ---- O^T += V^T P^T
+            for (int p = 0; p < 2; ++p)
+                vr[0][t][p] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_lds + v_off[t][0][p]));
+        float psum = 0.f;
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
+        for (int u = 0; u < 4; ++u) {
+            if (u + 1 < 4) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt_lds + (32 * t + c32) * LDV + 16 * u + 8 * h);
-                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], oacc[t], 0, 0, 0);
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        vr[(u + 1) & 1][t][p] =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_lds + v_off[t][u + 1][p]));
+            }
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][8 * (u & 1) + e], scale_log2e, -m_run));
+                psum += pe;
+                pb[e] = (__bf16)pe;
+            }
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(vr[u & 1][t][0], vr[u & 1][t][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[t], 0, 0, 0);
             }
         }
+        l_run += psum;
+        // every wave is done with v_lds and k_lds[it & 1]: refill them
+        __syncthreads();
+        if (it + 2 < count)
+            load_tile<D, false>(kh + (size_t)list[it + 2] * kBlk * D, k_lds[it & 1], wave, lane);
+        if (it + 1 < count) load_tile<D, true>(vh + (size_t)list[it + 1] * kBlk * D, v_lds, wave, lane);
     }
 
     // ---- normalise and store: lane holds O[qrow][32 t + 8 g + 4 h + c], c = 0..3
@@ -227,7 +281,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     const float scale_log2e = a.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(a.BH * a.nb), dim3(kThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
-                       a.L, a.nb, a.kv_count, a.kv_index, scale_log2e);
+                       a.L, a.nb, a.kv_count, a.kv_index, a.schedule, scale_log2e);
     return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, int L, int nb, const int32_t* __restrict__ kv_count,
-    const int32_t* __restrict__ kv_index, float scale) {
+    const int32_t* __restrict__ kv_index, const int32_t* __restrict__ schedule,
+    float scale) {
     constexpr int LD = D + 1;
     extern __shared__ float lds[];
     float* q_s = lds;                   // [64][LD]
@@ -26,8 +27,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     float* v_s = k_s + kBlk * LD;       // [64][LD]
     float* p_s = v_s + kBlk * LD;       // [64][65]
 
-    const int bh = blockIdx.x / nb;
-    const int qb = blockIdx.x - bh * nb;
+    const int blk = schedule ? schedule[blockIdx.x] : (int)blockIdx.x;
+    const int bh = blk / nb;
+    const int qb = blk - bh * nb;
     const int tid = threadIdx.x;
     const int row = tid >> 2;
     const int part = tid & 3;
@@ -103,7 +105,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     }
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(a.BH * a.nb), dim3(kThreads), lds, s,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.L,
-                       a.nb, a.kv_count, a.kv_index, a.scale);
+                       a.nb, a.kv_count, a.kv_index, a.schedule, a.scale);
     return hipGetLastError();
 }
 

@@ -358,6 +358,50 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Work order for the attention launch: every query block once, longest kept list
+// first (a counting sort on nb + 1 count values by a single workgroup).  Starting
+// the long lists first leaves only short ones for the tail of the launch.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ kv_count,
+                                                         int total, int nb,
+                                                         int32_t* __restrict__ schedule) {
+    extern __shared__ int bins[];   // bins[nb - count]: descending counts come first
+    const int tid = threadIdx.x;
+    for (int i = tid; i <= nb; i += 1024) bins[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < total; i += 1024) {
+        const int c = min(max(kv_count[i], 0), nb);
+        atomicAdd(&bins[nb - c], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // exclusive prefix sum over the nb + 1 bins: one contiguous chunk per lane
+        const int per = (nb + 1 + 63) / 64;
+        const int b0 = tid * per;
+        const int b1 = min(b0 + per, nb + 1);
+        int local = 0;
+        for (int b = b0; b < b1; ++b) local += bins[b];
+        int incl = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (tid >= off) incl += y;
+        }
+        int run = incl - local;
+        for (int b = b0; b < b1; ++b) {
+            const int n = bins[b];
+            bins[b] = run;
+            run += n;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < total; i += 1024) {
+        const int c = min(max(kv_count[i], 0), nb);
+        schedule[atomicAdd(&bins[nb - c], 1)] = i;
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
     const int total = a.BH * a.nb;
@@ -397,7 +441,11 @@ hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
         e = (a.d == 128) ? launch_pool<float, 128>(a, s) : launch_pool<float, 64>(a, s);
     }
     if (e != hipSuccess) return e;
-    return (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
+    e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
+    if (e != hipSuccess || !a.schedule) return e;
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), (size_t)(a.nb + 1) * sizeof(int), s,
+                       a.kv_count, a.BH * a.nb, a.nb, a.schedule);
+    return hipGetLastError();
 }
 
 }  // namespace nabla

@@ -88,10 +88,11 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
                               int W, int d, int P, int N, float thr,
                               const nabla_sta_window* sta, float scale, nabla_dtype dtype,
                               int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
-                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                              int32_t* schedule, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
     if (!q || !k || !kv_count || !kv_index) return fail(NABLA_E_INVAL, "nabla_build_mask: null pointer");
     if (!aligned16(q) || !aligned16(k) || ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3) ||
-        ((uintptr_t)bitmap & 3))
+        ((uintptr_t)bitmap & 3) || ((uintptr_t)schedule & 3))
         return fail(NABLA_E_INVAL, "nabla_build_mask: misaligned pointer");
     if (batch <= 0 || heads <= 0 || T <= 0 || H <= 0 || W <= 0 || d <= 0 || P <= 0 || N <= 0)
         return fail(NABLA_E_INVAL, "nabla_build_mask: sizes must be positive");
@@ -140,6 +141,7 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
     a.kv_count = kv_count;
     a.kv_index = kv_index;
     a.bitmap = bitmap;
+    a.schedule = schedule;
     a.qp = (float*)workspace;
     a.kp = a.qp + (size_t)a.BH * nb * d;
     a.bf16 = dtype == NABLA_BF16;
@@ -149,11 +151,12 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
 nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
                                    int batch, int heads, int L, int d, int N,
                                    const int32_t* kv_count, const int32_t* kv_index,
-                                   float scale, nabla_dtype dtype, hipStream_t stream) {
+                                   const int32_t* schedule, float scale, nabla_dtype dtype,
+                                   hipStream_t stream) {
     if (!q || !k || !v || !o || !kv_count || !kv_index)
         return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: null pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-        ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3))
+        ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3) || ((uintptr_t)schedule & 3))
         return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: misaligned pointer");
     if (batch <= 0 || heads <= 0 || L <= 0 || d <= 0 || N <= 0)
         return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: sizes must be positive");
@@ -175,6 +178,7 @@ nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, 
     a.d = d;
     a.kv_count = kv_count;
     a.kv_index = kv_index;
+    a.schedule = schedule;
     a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
     hipError_t e = dtype == NABLA_BF16 ? nabla::launch_attn_bf16(a, stream)
                                        : nabla::launch_attn_f32(a, stream);

@@ -57,6 +57,7 @@ struct MaskArgs {
     int32_t* kv_count;
     int32_t* kv_index;
     uint32_t* bitmap;       // may be null
+    int32_t* schedule;      // may be null
     float* qp;              // workspace [BH, nb, d]
     float* kp;              // workspace [BH, nb, d]
     int bf16;
@@ -71,6 +72,7 @@ struct AttnArgs {
     int BH, L, nb, d;
     const int32_t* kv_count;
     const int32_t* kv_index;
+    const int32_t* schedule;   // may be null
     float scale;
 };
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);

@@ -106,6 +106,11 @@ size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N
  * bitmap      optional out (NULL to skip), uint32 [batch, heads, nb, ceil(nb/32)]:
  *             bit (j % 32) of word j / 32 of row i is the mask bit (i, j); unused high
  *             bits of the last word are zero.
+ * schedule    optional out (NULL to skip), int32 [batch*heads*nb]: every query block
+ *             (b*heads + h)*nb + i exactly once, in order of non-increasing kv_count
+ *             (order among equal counts unspecified).  Passed to block_sparse_attn_fwd
+ *             it makes the longest lists start first, which shortens the tail of the
+ *             launch; it never changes results.
  * workspace   device buffer of at least nabla_build_mask_workspace_size() bytes.
  * Errors: NABLA_E_INVAL (null pointers, L != T*H*W, H or W not a multiple of P,
  * L not a multiple of N, thr outside [0,1) or NaN, a window size even or < 1, a window
@@ -116,7 +121,8 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
                               int W, int d, int P, int N, float thr,
                               const nabla_sta_window* sta, float scale, nabla_dtype dtype,
                               int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
-                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+                              int32_t* schedule, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * block_sparse_attn_fwd - softmax attention restricted to the kept N x N tiles
@@ -133,6 +139,9 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
  * kv_count, kv_index  as written by nabla_build_mask (any lists with entries in
  *             [0, nb) are accepted; duplicates are summed twice).  A query block with
  *             kv_count 0 gets zero output.
+ * schedule    optional (NULL for natural order): a permutation of the batch*heads*nb
+ *             query blocks giving the order in which they are started, e.g. the one
+ *             nabla_build_mask writes.  Results do not depend on it.
  * scale       <= 0 selects 1/sqrt(d).
  * bf16: scores and the running softmax in float32, P rounded to bf16 for the P V
  * product, float32 accumulation, output rounded to nearest-even bf16.
@@ -143,7 +152,8 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
 nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
                                    int batch, int heads, int L, int d, int N,
                                    const int32_t* kv_count, const int32_t* kv_index,
-                                   float scale, nabla_dtype dtype, hipStream_t stream);
+                                   const int32_t* schedule, float scale, nabla_dtype dtype,
+                                   hipStream_t stream);
 
 /* Static name of a status code ("NABLA_OK", ...). */
 const char* nabla_status_string(nabla_status status);

@@ -89,11 +89,11 @@ def test_reorder_validation(lib, kw, status):
 # ------------------------------------------------------------- nabla_build_mask
 
 def build_mask(lib, q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, thr=0.1,
-               sta=None, scale=0.0, dt=NABLA_F32, cnt=C, idx=D_, bitmap=None, ws=E,
+               sta=None, scale=0.0, dt=NABLA_F32, cnt=C, idx=D_, bitmap=None, schedule=None, ws=E,
                ws_bytes=1 << 30):
     win = None if sta is None else ctypes.byref(StaWindow(*sta))
     return lib.nabla_build_mask(q, k, batch, heads, T, H, W, d, P, N, thr, win, scale, dt, cnt,
-                                idx, bitmap, ws, ws_bytes, None)
+                                idx, bitmap, schedule, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -118,6 +118,7 @@ def build_mask(lib, q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=6
     (dict(N=32, T=4), NABLA_E_UNSUPPORTED),
     (dict(d=96), NABLA_E_UNSUPPORTED),
     (dict(T=129, H=32, W=32), NABLA_E_UNSUPPORTED),     # 2064 blocks > NABLA_MAX_BLOCKS
+    (dict(schedule=ctypes.c_void_p(0x100002)), NABLA_E_INVAL),
     (dict(ws=None), NABLA_E_WORKSPACE),
     (dict(ws_bytes=100), NABLA_E_WORKSPACE),
 ])
@@ -129,8 +130,9 @@ def test_build_mask_validation(lib, kw, status):
 # ------------------------------------------------------------- block_sparse_attn_fwd
 
 def attn(lib, q=A, k=B_, v=C, o=D_, batch=1, heads=2, L=1024, d=64, N=64, cnt=E, idx=F_,
-         scale=0.0, dt=NABLA_BF16):
-    return lib.block_sparse_attn_fwd(q, k, v, o, batch, heads, L, d, N, cnt, idx, scale, dt, None)
+         schedule=None, scale=0.0, dt=NABLA_BF16):
+    return lib.block_sparse_attn_fwd(q, k, v, o, batch, heads, L, d, N, cnt, idx, schedule, scale,
+                                     dt, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -140,6 +142,7 @@ def attn(lib, q=A, k=B_, v=C, o=D_, batch=1, heads=2, L=1024, d=64, N=64, cnt=E,
     (dict(cnt=None), NABLA_E_INVAL),
     (dict(idx=None), NABLA_E_INVAL),
     (dict(o=ctypes.c_void_p(0x100002)), NABLA_E_INVAL),
+    (dict(schedule=ctypes.c_void_p(0x100001)), NABLA_E_INVAL),
     (dict(L=1000), NABLA_E_INVAL),
     (dict(L=0), NABLA_E_INVAL),
     (dict(scale=float("nan")), NABLA_E_INVAL),

@@ -59,12 +59,12 @@ def run_gpu_path(cfg: Config, q, k, v, thr=None, with_bitmap=True):
     qf = nab.reorder(qd, cfg.T, cfg.H, cfg.W, cfg.P)
     kf = nab.reorder(kd, cfg.T, cfg.H, cfg.W, cfg.P)
     vf = nab.reorder(vd, cfg.T, cfg.H, cfg.W, cfg.P)
-    cnt, idx, bm = nab.build_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, cfg.sta,
-                                  with_bitmap=True)
-    of = nab.attn_fwd(qf, kf, vf, cnt, idx, cfg.N)
+    cnt, idx, bm, sched = nab.build_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, cfg.sta,
+                                         with_bitmap=True, with_schedule=True)
+    of = nab.attn_fwd(qf, kf, vf, cnt, idx, cfg.N, schedule=sched)
     o = nab.reorder(of, cfg.T, cfg.H, cfg.W, cfg.P, inverse=True)
     torch.cuda.synchronize()
-    return dict(qf=qf, kf=kf, vf=vf, cnt=cnt, idx=idx, bitmap=bm, of=of, o=o)
+    return dict(qf=qf, kf=kf, vf=vf, cnt=cnt, idx=idx, bitmap=bm, sched=sched, of=of, o=o)
 
 
 # ------------------------------------------------------------------ reorder
@@ -181,6 +181,25 @@ def test_exact_ties_grouped(dtype):
         ref = O.block_mask(qn, kn, 4, 16, 16, 8, N, thr)
         mism = gm != ref["mask"]
         assert np.all(np.abs(ref["F"][mism] - thr) <= 1e-4), thr
+
+
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[3], SMALL[8]], ids=lambda c: c.name)
+def test_schedule(cfg):
+    """The schedule lists every query block once, longest kept list first, and the
+    attention output does not depend on the order the blocks are started in."""
+    q, k, v = make_qkv(cfg)
+    res = run_gpu_path(cfg, q, k, v)
+    sched = res["sched"].cpu().numpy()
+    cnt = res["cnt"].cpu().numpy().reshape(-1)
+    assert np.array_equal(np.sort(sched), np.arange(cfg.BH * cfg.nb))
+    assert np.all(np.diff(cnt[sched]) <= 0)
+    plain = nab.attn_fwd(res["qf"], res["kf"], res["vf"], res["cnt"], res["idx"], cfg.N)
+    rev = torch.flip(res["sched"], [0]).contiguous()
+    backwards = nab.attn_fwd(res["qf"], res["kf"], res["vf"], res["cnt"], res["idx"], cfg.N,
+                             schedule=rev)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, res["of"])
+    assert torch.equal(backwards, res["of"])
 
 
 def test_determinism():
