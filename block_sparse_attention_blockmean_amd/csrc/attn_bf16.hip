@@ -18,12 +18,10 @@
 // Memory pipeline: K and V tiles go from global memory straight into LDS
 // (global_load_lds_dwordx4, no VGPR staging), row-major with an XOR swizzle of the
 // 16-byte chunks.  V^T operands come out of the row-major V tile through the
-// transposing LDS read (ds_read_b64_tr_b16).  All copies for later tiles are issued
-// at the end of an iteration, after every LDS read of the current tile: K of the tile
-// after next (two K buffers), then V of the next tile (one V buffer).  Copies
-// complete in issue order, so the single wait for V before the P V product also
-// covers K of the next tile: K streams in for a whole iteration, V for S^T plus the
-// softmax.
+// transposing LDS read (ds_read_b64_tr_b16).  One K and one V buffer (32 KiB per
+// workgroup, so four workgroups = two waves per SIMD fit a CU): K of the next tile
+// streams in during the softmax, right after every wave has read the current K, and V
+// of the next tile during the next S^T and softmax.
 #include <math.h>
 
 #include "nabla_internal.h"
@@ -89,7 +87,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     using G = Tile<D>;
     constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;        // 32-row d tiles of O^T
-    __shared__ __attribute__((aligned(1024))) char k_lds[2][G::kBytes];
+    __shared__ __attribute__((aligned(1024))) char k_lds[G::kBytes];
     __shared__ __attribute__((aligned(1024))) char v_lds[G::kBytes];
 
     // Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD walks a
@@ -127,10 +125,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int s = 0; s < KS; ++s)
         qreg[s] = *reinterpret_cast<const bf16x8*>(qh + (size_t)qrow * D + 16 * s + 8 * h);
 
-    // issue order K0, K1, V0; iteration i issues K(i+2), V(i+1) at its end
-    if (count > 0) load_tile<D, false>(kh + (size_t)list[0] * kBlk * D, k_lds[0], wave, lane);
-    if (count > 1) load_tile<D, false>(kh + (size_t)list[1] * kBlk * D, k_lds[1], wave, lane);
-    if (count > 0) load_tile<D, true>(vh + (size_t)list[0] * kBlk * D, v_lds, wave, lane);
+    // issue order K0, V0; iteration i issues K(i+1) after its S^T and V(i+1) at its end
+    if (count > 0) {
+        load_tile<D, false>(kh + (size_t)list[0] * kBlk * D, k_lds, wave, lane);
+        load_tile<D, true>(vh + (size_t)list[0] * kBlk * D, v_lds, wave, lane);
+    }
 
     f32x16 oacc[DT];
 #pragma unroll
@@ -162,36 +161,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
                 v_off[t][u][p] = row * G::kRowBytes + (((d >> 3) ^ G::v_swz(row)) * 16) + ((d >> 2) & 1) * 8;
             }
 
-    // K0 has landed once only K1 and V0 may be pending
-    if (count > 1) wait_vmcnt<2 * G::kLoadsPerWave>(); else wait_vmcnt<G::kLoadsPerWave>();
+    // K0 has landed once only V0 may be pending
+    wait_vmcnt<G::kLoadsPerWave>();
     __syncthreads();
 
     for (int it = 0; it < count; ++it) {
-        // K(it) is in LDS and visible: it was issued before V(it-1), which every wave
-        // waited for before the previous P V product, followed by two barriers
-        const char* kbuf = k_lds[it & 1];
+        // K(it) is in LDS and visible: it was issued before V(it)... (iteration 0) or
+        // after S^T(it-1), and every wave waited for it before the previous P V product,
+        // followed by two barriers
+        const char* kbuf = k_lds;
 
-        // ---- S^T = K Q^T for this wave's 32 query columns, 64 keys in two 32-key
-        // tiles.  All K operands are requested first so the MFMA chain never waits on
-        // a freshly issued LDS read.
-        bf16x8 ka[KS][2];
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) ka[s][t] = *reinterpret_cast<const bf16x8*>(kbuf + k_off[t][s]);
+        // ---- S^T = K Q^T for this wave's 32 query columns, 64 keys in two 32-key tiles.
+        // Operands are requested half a tile ahead: 8 reads, then the 8 MFMAs that
+        // use them while the next 8 reads land.
         f32x16 sacc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int half = 0; half < 2; ++half) {
+            bf16x8 ka[KS / 2][2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][t], qreg[s], sacc[t], 0, 0, 0);
-        // keep the scheduler from folding the reads back into the MFMA chain
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);   // all K operand reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);   // then the MFMAs
+            for (int s = 0; s < KS / 2; ++s)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    ka[s][t] = *reinterpret_cast<const bf16x8*>(kbuf + k_off[t][half * (KS / 2) + s]);
+#pragma unroll
+            for (int s = 0; s < KS / 2; ++s)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][t], qreg[half * (KS / 2) + s],
+                                                                      sacc[t], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);   // this half's K reads
+            __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);   // then its MFMAs
+        }
+
+        // every wave is done with k_lds: stream in the next K during the softmax
+        __syncthreads();
+        if (it + 1 < count) load_tile<D, false>(kh + (size_t)list[it + 1] * kBlk * D, k_lds, wave, lane);
 
         // ---- online softmax for query column c32 (keys split between lanes l, l^32).
         // The reference maximum m_run only moves when a tile's maximum exceeds it by
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
                 for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
         }
 
-        // V(it), and K(it+1) issued before it, have landed
+        // V(it) and K(it+1) have landed
         wait_vmcnt<0>();
         __syncthreads();
 
@@ -253,10 +261,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
             }
         }
         l_run += psum;
-        // every wave is done with v_lds and k_lds[it & 1]: refill them
+        // every wave is done with v_lds: stream in the next V
         __syncthreads();
-        if (it + 2 < count)
-            load_tile<D, false>(kh + (size_t)list[it + 2] * kBlk * D, k_lds[it & 1], wave, lane);
         if (it + 1 < count) load_tile<D, true>(vh + (size_t)list[it + 1] * kBlk * D, v_lds, wave, lane);
     }
 
