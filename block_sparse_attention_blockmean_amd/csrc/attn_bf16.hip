@@ -20,8 +20,9 @@
 // 16-byte chunks.  V^T operands come out of the row-major V tile through the
 // transposing LDS read (ds_read_b64_tr_b16).  One K and one V buffer (32 KiB per
 // workgroup, so four workgroups = two waves per SIMD fit a CU): K of the next tile
-// streams in during the softmax, right after every wave has read the current K, and V
-// of the next tile during the next S^T and softmax.
+// streams in during the softmax and P V, right after every wave has read the current
+// K, and V of the next tile during the next S^T and softmax.  Barriers between waves
+// are plain s_barrier with explicit waits, so copies stay in flight across them.
 #include <math.h>
 
 #include "nabla_internal.h"
@@ -56,26 +57,47 @@ struct Tile {
 
 // Wave-wide copy of one 64 x D tile from global memory into LDS.  Load u of wave w
 // fills bytes [1024 (2u + w), +1024) of the LDS tile, 16 bytes per lane in lane order;
-// the lane picks the global chunk that belongs in that slot under the swizzle.
+// the lane picks the global chunk that belongs in that slot under the swizzle.  The
+// tile base is uniform and the lane offset 32-bit, so the load takes the scalar-base
+// form; the LDS destination (M0) is uniform as well.
+template <int D, bool kIsV>
+__device__ inline uint32_t tile_lane_offset(int u, int wave, int lane) {
+    using G = Tile<D>;
+    const int o = (2 * u + wave) * 1024 + lane * 16;
+    const int row = o / G::kRowBytes;
+    const int slot = (o % G::kRowBytes) / 16;
+    const int chunk = slot ^ (kIsV ? G::v_swz(row) : G::k_swz(row));
+    return (uint32_t)(row * G::kRowBytes + chunk * 16);
+}
+
 template <int D, bool kIsV>
 __device__ inline void load_tile(const __bf16* g_tile, char* lds_tile, int wave, int lane) {
     using G = Tile<D>;
     const char* src = reinterpret_cast<const char*>(g_tile);
 #pragma unroll
     for (int u = 0; u < G::kLoadsPerWave; ++u) {
-        const int piece = 2 * u + wave;
-        const int o = piece * 1024 + lane * 16;
-        const int row = o / G::kRowBytes;
-        const int slot = (o % G::kRowBytes) / 16;
-        const int chunk = slot ^ (kIsV ? G::v_swz(row) : G::k_swz(row));
-        __builtin_amdgcn_global_load_lds(src + row * G::kRowBytes + chunk * 16,
-                                         (lds_void*)(lds_tile + piece * 1024), 16, 0, 0);
+        uint32_t off = tile_lane_offset<D, kIsV>(u, wave, lane);
+        // keep the offset a 32-bit register at the load, so it is not widened to a
+        // 64-bit pointer and hoisted out of the tile loop
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(lds_tile + (2 * u + wave) * 1024),
+                                         16, 0, 0);
     }
 }
 
 template <int N>
 __device__ inline void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS hand-offs that leaves tile copies in flight.  A
+// __syncthreads() is a fenced barrier and drains every outstanding vector-memory
+// operation first, which would cancel the prefetch; here only this wave's LDS reads
+// are completed (lgkmcnt), and every place that needs a copy to have landed waits for
+// it explicitly with wait_vmcnt before the barrier.  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int D>
@@ -106,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const int qb = logical - bh * nb;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int lane = tid & 63;
     const int h = lane >> 5;
     const int c32 = lane & 31;
@@ -163,43 +185,44 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
     // K0 has landed once only V0 may be pending
     wait_vmcnt<G::kLoadsPerWave>();
-    __syncthreads();
+    lds_barrier();
 
     for (int it = 0; it < count; ++it) {
-        // K(it) is in LDS and visible: it was issued before V(it)... (iteration 0) or
-        // after S^T(it-1), and every wave waited for it before the previous P V product,
-        // followed by two barriers
+        // K(it) is in LDS and visible: every wave waited for it (in the prologue or at
+        // the end of the previous iteration) before a barrier
         const char* kbuf = k_lds;
 
         // ---- S^T = K Q^T for this wave's 32 query columns, 64 keys in two 32-key tiles.
-        // Operands are requested half a tile ahead: 8 reads, then the 8 MFMAs that
-        // use them while the next 8 reads land.
+        // Operands are requested a quarter tile ahead: a group of reads, then the
+        // MFMAs that use them while the next group lands.
+        constexpr int KG = KS / 4;   // k-steps per group
         f32x16 sacc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            bf16x8 ka[KS / 2][2];
+        for (int grp = 0; grp < 4; ++grp) {
+            bf16x8 ka[KG][2];
 #pragma unroll
-            for (int s = 0; s < KS / 2; ++s)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    ka[s][t] = *reinterpret_cast<const bf16x8*>(kbuf + k_off[t][half * (KS / 2) + s]);
-#pragma unroll
-            for (int s = 0; s < KS / 2; ++s)
+            for (int s = 0; s < KG; ++s)
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
-                    sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][t], qreg[half * (KS / 2) + s],
+                    ka[s][t] = *reinterpret_cast<const bf16x8*>(kbuf + k_off[t][grp * KG + s]);
+#pragma unroll
+            for (int s = 0; s < KG; ++s)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][t], qreg[grp * KG + s],
                                                                       sacc[t], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);   // this half's K reads
-            __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);   // then its MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KG, 0);   // this group's K reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * KG, 0);   // then its MFMAs
         }
 
-        // every wave is done with k_lds: stream in the next K during the softmax
-        __syncthreads();
-        if (it + 1 < count) load_tile<D, false>(kh + (size_t)list[it + 1] * kBlk * D, k_lds, wave, lane);
+        // every wave is done with k_lds: stream in the next K during the softmax and P V
+        lds_barrier();
+        const bool more = it + 1 < count;
+        if (more) load_tile<D, false>(kh + (size_t)list[it + 1] * kBlk * D, k_lds, wave, lane);
 
         // ---- online softmax for query column c32 (keys split between lanes l, l^32).
         // The reference maximum m_run only moves when a tile's maximum exceeds it by
@@ -222,9 +245,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
                 for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
         }
 
-        // V(it) and K(it+1) have landed
-        wait_vmcnt<0>();
-        __syncthreads();
+        // V(it) has landed once at most K(it+1), issued after it, is pending
+        if (more) wait_vmcnt<G::kLoadsPerWave>(); else wait_vmcnt<0>();
+        lds_barrier();
 
         // ---- O^T += V^T P^T, k-step by k-step: P of step u needs only its own 8 exps,
         // and the V^T operands (two transposing 8-byte reads each) of step u+1 are
@@ -261,9 +284,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
             }
         }
         l_run += psum;
-        // every wave is done with v_lds: stream in the next V
-        __syncthreads();
-        if (it + 1 < count) load_tile<D, true>(vh + (size_t)list[it + 1] * kBlk * D, v_lds, wave, lane);
+        // K(it+1) has landed (nothing was issued after it); after the barrier every
+        // wave is done with v_lds and sees K(it+1): stream in the next V
+        if (more) wait_vmcnt<0>();
+        lds_barrier();
+        if (more) load_tile<D, true>(vh + (size_t)list[it + 1] * kBlk * D, v_lds, wave, lane);
     }
 
     // ---- normalise and store: lane holds O[qrow][32 t + 8 g + 4 h + c], c = 0..3

@@ -359,34 +359,35 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Work order for the attention launch: every query block once, longest kept list
-// first (a counting sort on nb + 1 count values by a single workgroup).  Starting
-// the long lists first leaves only short ones for the tail of the launch.
+// Work order for the attention launch: heads one after another, and inside a head its
+// query blocks by decreasing kept count.  Consecutive workgroups are dealt round-robin
+// to the 8 XCDs, so all of them work on the same one or two heads at any time: the
+// K/V tiles in flight are those of one or two heads (tens of MB at the 720p shapes),
+// which the last-level cache holds, and each head's short lists run last, which keeps
+// the tail of the launch short.  One wave per head (counting sort on nb + 1 bins).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ kv_count,
-                                                         int total, int nb,
-                                                         int32_t* __restrict__ schedule) {
-    extern __shared__ int bins[];   // bins[nb - count]: descending counts come first
-    const int tid = threadIdx.x;
-    for (int i = tid; i <= nb; i += 1024) bins[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < total; i += 1024) {
-        const int c = min(max(kv_count[i], 0), nb);
-        atomicAdd(&bins[nb - c], 1);
-    }
-    __syncthreads();
-    if (tid < 64) {
+constexpr int kSchedWaves = 16;
+
+__global__ __launch_bounds__(kSchedWaves * 64) void schedule_kernel(
+    const int32_t* __restrict__ kv_count, int heads, int nb, int32_t* __restrict__ schedule) {
+    extern __shared__ int sh[];
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    int* bins = sh + w * (nb + 1);
+    for (int h = w; h < heads; h += kSchedWaves) {
+        const int32_t* cnt = kv_count + (size_t)h * nb;
+        for (int b = lane; b <= nb; b += 64) bins[b] = 0;
+        for (int i = lane; i < nb; i += 64) atomicAdd(&bins[nb - min(max(cnt[i], 0), nb)], 1);
         // exclusive prefix sum over the nb + 1 bins: one contiguous chunk per lane
         const int per = (nb + 1 + 63) / 64;
-        const int b0 = tid * per;
-        const int b1 = min(b0 + per, nb + 1);
+        const int b0 = lane * per, b1 = min(b0 + per, nb + 1);
         int local = 0;
         for (int b = b0; b < b1; ++b) local += bins[b];
         int incl = local;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int y = __shfl_up(incl, off);
-            if (tid >= off) incl += y;
+            if (lane >= off) incl += y;
         }
         int run = incl - local;
         for (int b = b0; b < b1; ++b) {
@@ -394,11 +395,10 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
             bins[b] = run;
             run += n;
         }
-    }
-    __syncthreads();
-    for (int i = tid; i < total; i += 1024) {
-        const int c = min(max(kv_count[i], 0), nb);
-        schedule[atomicAdd(&bins[nb - c], 1)] = i;
+        for (int i = lane; i < nb; i += 64) {
+            const int pos = atomicAdd(&bins[nb - min(max(cnt[i], 0), nb)], 1);
+            schedule[(size_t)h * nb + pos] = h * nb + i;
+        }
     }
 }
 
@@ -443,8 +443,17 @@ hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
     if (e != hipSuccess || !a.schedule) return e;
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), (size_t)(a.nb + 1) * sizeof(int), s,
-                       a.kv_count, a.BH * a.nb, a.nb, a.schedule);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e2 = hipFuncSetAttribute((const void*)schedule_kernel,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            kSchedWaves * (NABLA_MAX_BLOCKS + 1) * (int)sizeof(int));
+        if (e2 != hipSuccess) return e2;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedWaves * 64),
+                       (size_t)kSchedWaves * (a.nb + 1) * sizeof(int), s, a.kv_count, a.BH, a.nb,
+                       a.schedule);
     return hipGetLastError();
 }
 

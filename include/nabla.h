@@ -107,10 +107,12 @@ size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N
  *             bit (j % 32) of word j / 32 of row i is the mask bit (i, j); unused high
  *             bits of the last word are zero.
  * schedule    optional out (NULL to skip), int32 [batch*heads*nb]: every query block
- *             (b*heads + h)*nb + i exactly once, in order of non-increasing kv_count
- *             (order among equal counts unspecified).  Passed to block_sparse_attn_fwd
- *             it makes the longest lists start first, which shortens the tail of the
- *             launch; it never changes results.
+ *             (b*heads + h)*nb + i exactly once, as a start order for
+ *             block_sparse_attn_fwd: heads in order, each head's blocks by decreasing
+ *             kv_count (order among equal counts unspecified).  Consecutive workgroups
+ *             spread over all XCDs, so the whole GPU works on one or two heads at a
+ *             time (their K/V stay in the last-level cache) and each head's short lists
+ *             run last.  It never changes results.
  * workspace   device buffer of at least nabla_build_mask_workspace_size() bytes.
  * Errors: NABLA_E_INVAL (null pointers, L != T*H*W, H or W not a multiple of P,
  * L not a multiple of N, thr outside [0,1) or NaN, a window size even or < 1, a window

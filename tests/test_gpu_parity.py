@@ -185,14 +185,18 @@ def test_exact_ties_grouped(dtype):
 
 @pytest.mark.parametrize("cfg", [SMALL[0], SMALL[3], SMALL[8]], ids=lambda c: c.name)
 def test_schedule(cfg):
-    """The schedule lists every query block once, longest kept list first, and the
-    attention output does not depend on the order the blocks are started in."""
+    """The schedule lists every query block once, head by head, longest kept list first
+    inside a head, and the attention output does not depend on the start order."""
     q, k, v = make_qkv(cfg)
     res = run_gpu_path(cfg, q, k, v)
     sched = res["sched"].cpu().numpy()
     cnt = res["cnt"].cpu().numpy().reshape(-1)
     assert np.array_equal(np.sort(sched), np.arange(cfg.BH * cfg.nb))
-    assert np.all(np.diff(cnt[sched]) <= 0)
+    # heads in order, inside a head the blocks by non-increasing kept count
+    for g in range(cfg.BH):
+        part = sched[g * cfg.nb:(g + 1) * cfg.nb]
+        assert np.array_equal(np.sort(part), np.arange(g * cfg.nb, (g + 1) * cfg.nb))
+        assert np.all(np.diff(cnt[part]) <= 0)
     plain = nab.attn_fwd(res["qf"], res["kf"], res["vf"], res["cnt"], res["idx"], cfg.N)
     rev = torch.flip(res["sched"], [0]).contiguous()
     backwards = nab.attn_fwd(res["qf"], res["kf"], res["vf"], res["cnt"], res["idx"], cfg.N,
