@@ -61,11 +61,11 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(cfg, q, k, v, kept_flops_total, budget_s=12.0):
-    """The oracle (untuned) on a bounded sample of the same workload, extrapolated
-    to one whole step: reorder + mask of one head scaled by the head count, and
-    attention on as many query blocks of that head as fit the budget, scaled by
-    kept-tile FLOPs."""
+def cpu_baseline(cfg, q, k, v, kept_flops_total, budget_s=15.0):
+    """The oracle (untuned) on a bounded sample of the same workload, extrapolated to
+    one whole step: whole heads (reorder of Q, K, V, the float32 mask, float64 attention
+    over every kept tile), one after another until the budget is spent, scaled by the
+    head count."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -73,32 +73,29 @@ def cpu_baseline(cfg, q, k, v, kept_flops_total, budget_s=12.0):
     except Exception:
         threads = 1
     G = cfg.BH
-    qn, kn, vn = (t[0, 0].float().numpy() for t in (q, k, v))
-    t0 = time.perf_counter()
-    qf, kf, vf = (O.reorder(a, cfg.T, cfg.H, cfg.W, cfg.P) for a in (qn, kn, vn))
-    t1 = time.perf_counter()
-    mk = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr, cfg.sta)
-    t2 = time.perf_counter()
     scale = 1.0 / np.sqrt(cfg.d)
-    order = np.random.default_rng(0).permutation(cfg.nb)
-    done, flops = 0, 0.0
-    t3 = time.perf_counter()
-    for i in order:
-        O.attention_block(qf, kf, vf, mk["mask"][i], int(i), cfg.N, scale)
-        flops += float(mk["mask"][i].sum()) * 4 * cfg.N * cfg.N * cfg.d
-        done += 1
-        if time.perf_counter() - t3 > budget_s:
+    t0 = time.perf_counter()
+    heads = 0
+    for g in range(G):
+        b, h = divmod(g, cfg.heads)
+        qn, kn, vn = (t[b, h].float().numpy() for t in (q, k, v))
+        qf, kf, vf = (O.reorder(a, cfg.T, cfg.H, cfg.W, cfg.P) for a in (qn, kn, vn))
+        mk = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr, cfg.sta)
+        for i in range(cfg.nb):
+            O.attention_block(qf, kf, vf, mk["mask"][i], int(i), cfg.N, scale)
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
             break
-    t4 = time.perf_counter()
-    t_step = G * ((t1 - t0) * 4 / 3 + (t2 - t1)) + (t4 - t3) * kept_flops_total / max(flops, 1.0)
+    elapsed = time.perf_counter() - t0
+    t_step = elapsed * G / heads
     return {
         "value": kept_flops_total / t_step / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"head (0,0) of {G}: reorder of Q,K,V and the float32 mask; float64 attention on "
-                   f"{done} of {cfg.nb} query blocks; extrapolated to {G} heads and all kept tiles "
-                   f"({t4 - t0:.1f} s measured, est. {t_step:.0f} s per step)"),
+        "sample": (f"{heads} of {G} (batch, head) slices, each whole: reorder of Q,K,V, the float32 "
+                   f"mask and float64 attention over all its kept tiles; {elapsed:.1f} s measured, "
+                   f"scaled by {G}/{heads} to est. {t_step:.0f} s per step"),
         "est_s_per_step": t_step,
     }
 
