@@ -114,50 +114,38 @@ constexpr int kRows = 16;
 constexpr int kWaves = 8;
 constexpr int kCap = 512;   // candidates per wave held in LDS
 
-template <int K>
-__device__ inline float swz_xor(float x) {
-    // ds_swizzle bit-mask mode inside each 32-lane half: lane ^ K
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (K << 10) | 0x1f));
+// Wave-wide reductions on DPP: shifts of 1, 2, 4, 8 lanes inside each 16-lane row, then
+// the row broadcasts of lanes 15 and 31 (a fixed order, so the result is deterministic);
+// lane 63 ends with the total, which every lane then reads.  VALU latency only, no LDS.
+template <int CTRL, int ROWS>
+__device__ inline int dpp_i(int identity, int x) {
+    return __builtin_amdgcn_update_dpp(identity, x, CTRL, ROWS, 0xf, false);
 }
-template <int K>
-__device__ inline int swz_xor_i(int x) {
-    return __builtin_amdgcn_ds_swizzle(x, (K << 10) | 0x1f);
+template <typename Op>
+__device__ inline int wave_reduce_bits(int x, int identity, Op op) {
+    x = op(x, dpp_i<0x111, 0xf>(identity, x));   // row_shr:1
+    x = op(x, dpp_i<0x112, 0xf>(identity, x));   // row_shr:2
+    x = op(x, dpp_i<0x114, 0xf>(identity, x));   // row_shr:4
+    x = op(x, dpp_i<0x118, 0xf>(identity, x));   // row_shr:8
+    x = op(x, dpp_i<0x142, 0xa>(identity, x));   // row_bcast:15 into rows 1, 3
+    x = op(x, dpp_i<0x143, 0xc>(identity, x));   // row_bcast:31 into rows 2, 3
+    return __builtin_amdgcn_readlane(x, 63);
 }
-// Wave-wide reductions: a butterfly inside each 32-lane half, then the two halves
-// combined from lanes 0 and 32, so every lane holds the same bits.
 __device__ inline float wave_sum(float x) {
-    x += swz_xor<1>(x);
-    x += swz_xor<2>(x);
-    x += swz_xor<4>(x);
-    x += swz_xor<8>(x);
-    x += swz_xor<16>(x);
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
-           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    return __int_as_float(wave_reduce_bits(__float_as_int(x), 0, [](int a, int b) {
+        return __float_as_int(__int_as_float(a) + __int_as_float(b));
+    }));
 }
 __device__ inline int wave_sum_i(int x) {
-    x += swz_xor_i<1>(x);
-    x += swz_xor_i<2>(x);
-    x += swz_xor_i<4>(x);
-    x += swz_xor_i<8>(x);
-    x += swz_xor_i<16>(x);
-    return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 32);
+    return wave_reduce_bits(x, 0, [](int a, int b) { return a + b; });
 }
 __device__ inline float wave_max(float x) {
-    x = fmaxf(x, swz_xor<1>(x));
-    x = fmaxf(x, swz_xor<2>(x));
-    x = fmaxf(x, swz_xor<4>(x));
-    x = fmaxf(x, swz_xor<8>(x));
-    x = fmaxf(x, swz_xor<16>(x));
-    return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
-                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)));
+    return __int_as_float(wave_reduce_bits(__float_as_int(x), __float_as_int(-INFINITY), [](int a, int b) {
+        return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+    }));
 }
 __device__ inline uint32_t wave_max_u(uint32_t x) {
-    x = max(x, (uint32_t)swz_xor_i<1>((int)x));
-    x = max(x, (uint32_t)swz_xor_i<2>((int)x));
-    x = max(x, (uint32_t)swz_xor_i<4>((int)x));
-    x = max(x, (uint32_t)swz_xor_i<8>((int)x));
-    x = max(x, (uint32_t)swz_xor_i<16>((int)x));
-    return max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 32));
+    return (uint32_t)wave_reduce_bits((int)x, 0, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
 }
 
 // Writes the values of src[0..len) whose bit pattern lies in (lo, hi] to dst, in
@@ -210,9 +198,9 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
             for (int v = 0; v < KC; ++v) a[v] = 0.f;
         }
         const int n_ct = (nb + 15) / 16;
-        for (int ct = wave; ct < n_ct; ct += kWaves) {
+        // K operand of column tile ct: rows 16 ct + lane % 16, quarter lane / 16 of d
+        auto load_b = [&](int ct, float (&b)[KC]) {
             const int j = ct * 16 + li;
-            float b[KC];
             if (j < nb) {
                 const f32x4* src = reinterpret_cast<const f32x4*>(kh + (size_t)j * D + kq * KC);
 #pragma unroll
@@ -224,14 +212,29 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
 #pragma unroll
                 for (int v = 0; v < KC; ++v) b[v] = 0.f;
             }
+        };
+        auto tile = [&](int ct, const float (&b)[KC]) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KC; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
             // lane holds S[4*(lane/16) + r][16*ct + lane%16]
+            const int j = ct * 16 + li;
             if (j < nb) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) s_lds[(4 * kq + r) * ld_s + j] = acc[r] * scale;
             }
+        };
+        // the wave's column tiles ct = wave, wave + 8, ...: the next tile's operand is
+        // loaded while the current one multiplies
+        float b0[KC], b1[KC];
+        if (wave < n_ct) load_b(wave, b0);
+        for (int ct = wave; ct < n_ct; ct += 2 * kWaves) {
+            const bool has1 = ct + kWaves < n_ct;
+            if (has1) load_b(ct + kWaves, b1);
+            tile(ct, b0);
+            if (!has1) break;
+            if (ct + 2 * kWaves < n_ct) load_b(ct + 2 * kWaves, b0);
+            tile(ct + kWaves, b1);
         }
     }
     __syncthreads();
@@ -366,39 +369,37 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
 // which the last-level cache holds, and each head's short lists run last, which keeps
 // the tail of the launch short.  One wave per head (counting sort on nb + 1 bins).
 // ---------------------------------------------------------------------------
-constexpr int kSchedWaves = 16;
-
-__global__ __launch_bounds__(kSchedWaves * 64) void schedule_kernel(
-    const int32_t* __restrict__ kv_count, int heads, int nb, int32_t* __restrict__ schedule) {
-    extern __shared__ int sh[];
-    const int w = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    int* bins = sh + w * (nb + 1);
-    for (int h = w; h < heads; h += kSchedWaves) {
-        const int32_t* cnt = kv_count + (size_t)h * nb;
-        for (int b = lane; b <= nb; b += 64) bins[b] = 0;
-        for (int i = lane; i < nb; i += 64) atomicAdd(&bins[nb - min(max(cnt[i], 0), nb)], 1);
-        // exclusive prefix sum over the nb + 1 bins: one contiguous chunk per lane
-        const int per = (nb + 1 + 63) / 64;
-        const int b0 = lane * per, b1 = min(b0 + per, nb + 1);
-        int local = 0;
-        for (int b = b0; b < b1; ++b) local += bins[b];
-        int incl = local;
+__global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict__ kv_count, int nb,
+                                                      int32_t* __restrict__ schedule) {
+    extern __shared__ int bins[];   // nb + 1 counters
+    const int h = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int32_t* cnt = kv_count + (size_t)h * nb;
+    for (int b = lane; b <= nb; b += 64) bins[b] = 0;
+    __syncthreads();
+    for (int i = lane; i < nb; i += 64) atomicAdd(&bins[nb - min(max(cnt[i], 0), nb)], 1);
+    __syncthreads();
+    // exclusive prefix sum over the nb + 1 bins: one contiguous chunk per lane
+    const int per = (nb + 1 + 63) / 64;
+    const int b0 = lane * per, b1 = min(b0 + per, nb + 1);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += bins[b];
+    int incl = local;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off);
-            if (lane >= off) incl += y;
-        }
-        int run = incl - local;
-        for (int b = b0; b < b1; ++b) {
-            const int n = bins[b];
-            bins[b] = run;
-            run += n;
-        }
-        for (int i = lane; i < nb; i += 64) {
-            const int pos = atomicAdd(&bins[nb - min(max(cnt[i], 0), nb)], 1);
-            schedule[(size_t)h * nb + pos] = h * nb + i;
-        }
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    int run = incl - local;
+    for (int b = b0; b < b1; ++b) {
+        const int n = bins[b];
+        bins[b] = run;
+        run += n;
+    }
+    __syncthreads();
+    for (int i = lane; i < nb; i += 64) {
+        const int pos = atomicAdd(&bins[nb - min(max(cnt[i], 0), nb)], 1);
+        schedule[(size_t)h * nb + pos] = h * nb + i;
     }
 }
 
@@ -443,17 +444,9 @@ hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
     if (e != hipSuccess || !a.schedule) return e;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e2 = hipFuncSetAttribute((const void*)schedule_kernel,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            kSchedWaves * (NABLA_MAX_BLOCKS + 1) * (int)sizeof(int));
-        if (e2 != hipSuccess) return e2;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedWaves * 64),
-                       (size_t)kSchedWaves * (a.nb + 1) * sizeof(int), s, a.kv_count, a.BH, a.nb,
-                       a.schedule);
+    // one wave per head; its bins fit the default LDS limit (NABLA_MAX_BLOCKS + 1 ints)
+    hipLaunchKernelGGL(schedule_kernel, dim3(a.BH), dim3(64), (size_t)(a.nb + 1) * sizeof(int), s,
+                       a.kv_count, a.nb, a.schedule);
     return hipGetLastError();
 }
 
