@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
 
 // ---------------------------------------------------------------------------
 // Reduced map + softmax + CDF cutoff + STA + lists.
-// A workgroup (8 waves) owns 16 query blocks (rows) of one head.
+// A workgroup (16 waves) owns 16 query blocks (rows) of one head.
 // Phase 1: the waves compute 16x16 tiles of S with v_mfma_f32_16x16x4_f32 (float32
 //   operands and accumulation) and park the 16 rows in LDS.
 // Phase 2: each wave takes whole rows.  Keeping block j iff F_j > thr is the same as
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
 //   is deterministic.
 // ---------------------------------------------------------------------------
 constexpr int kRows = 16;
-constexpr int kWaves = 8;
-constexpr int kCap = 512;   // candidates per wave held in LDS
+constexpr int kWaves = 16;
+constexpr int kCap = 256;   // candidates per wave held in LDS
 
 // Wave-wide reductions on DPP: shifts of 1, 2, 4, 8 lanes inside each 16-lane row, then
 // the row broadcasts of lanes 15 and 31 (a fixed order, so the result is deterministic);
@@ -135,9 +135,6 @@ __device__ inline float wave_sum(float x) {
     return __int_as_float(wave_reduce_bits(__float_as_int(x), 0, [](int a, int b) {
         return __float_as_int(__int_as_float(a) + __int_as_float(b));
     }));
-}
-__device__ inline int wave_sum_i(int x) {
-    return wave_reduce_bits(x, 0, [](int a, int b) { return a + b; });
 }
 __device__ inline float wave_max(float x) {
     return __int_as_float(wave_reduce_bits(__float_as_int(x), __float_as_int(-INFINITY), [](int a, int b) {
@@ -250,35 +247,43 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
         float mx = -INFINITY;
         for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, arow[j]);
         mx = wave_max(mx);
+        constexpr float kLog2e = 1.4426950408889634f;
+        const float mx2 = mx * kLog2e;
         float sum = 0.f;
         for (int j = lane; j < nb; j += 64) {
-            const float e = expf(arow[j] - mx);
+            const float e = __builtin_amdgcn_exp2f(fmaf(arow[j], kLog2e, -mx2));
             arow[j] = e;
             sum += e;
         }
-        sum = wave_sum(sum);
+        const float inv_sum = 1.0f / wave_sum(sum);
         // start of the bracket: u0 = thr / nb, nudged down so rounding cannot push
         // g(u0) above thr; it is verified below and dropped to 0 if it fails
         uint32_t lo = __float_as_uint(thr / ((float)nb * 1.0001f));
         float g_lo = 0.f;
         int n_in = 0;
         uint32_t maxb = 0;
-        for (int j = lane; j < nb; j += 64) {
-            const float p = arow[j] / sum;
-            arow[j] = p;
-            const uint32_t b = __float_as_uint(p);
-            maxb = max(maxb, b);
-            if (b <= lo) g_lo += p; else ++n_in;
+        for (int j0 = 0; j0 < nb; j0 += 64) {
+            const int j = j0 + lane;
+            bool in = false;
+            if (j < nb) {
+                const float p = arow[j] * inv_sum;
+                arow[j] = p;
+                const uint32_t b = __float_as_uint(p);
+                maxb = max(maxb, b);
+                if (b <= lo) g_lo += p; else in = true;
+            }
+            n_in += __popcll(__ballot(in));
         }
         g_lo = wave_sum(g_lo);
-        n_in = wave_sum_i(n_in);
         maxb = wave_max_u(maxb);
         if (g_lo > thr) {   // cannot happen in exact arithmetic; fall back to g(0) = 0
             lo = 0;
             g_lo = 0.f;
-            int c = 0;
-            for (int j = lane; j < nb; j += 64) c += __float_as_uint(arow[j]) > 0u;
-            n_in = wave_sum_i(c);
+            n_in = 0;
+            for (int j0 = 0; j0 < nb; j0 += 64) {
+                const int j = j0 + lane;
+                n_in += __popcll(__ballot(j < nb && __float_as_uint(arow[j]) > 0u));
+            }
         }
         uint32_t hi = maxb;
         // bracket (lo, hi]: g(lo) = g_lo <= thr and, unless the whole row sums to at
@@ -289,39 +294,49 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
             len = compact(arow, nb, lo, hi, cand, lane);
             src = cand;
         }
-        while (hi - lo > 1 && n_in > 1) {
+        // bisection until at most 64 values are left in the bracket
+        while (hi - lo > 1 && n_in > 64) {
             const uint32_t mid = lo + ((hi - lo) >> 1);
-            float s = 0.f;
+            float s_ = 0.f;
             int c = 0;
-            for (int j = lane; j < len; j += 64) {
-                const float x = src[j];
+            for (int j0 = 0; j0 < len; j0 += 64) {
+                const int j = j0 + lane;
+                const float x = (j < len) ? src[j] : 0.f;
                 const uint32_t b = __float_as_uint(x);
-                if (b > lo && b <= mid) { s += x; ++c; }
+                const bool in = (j < len) && b > lo && b <= mid;
+                if (in) s_ += x;
+                c += __popcll(__ballot(in));
             }
-            s = wave_sum(s);
-            c = wave_sum_i(c);
-            if (g_lo + s > thr) {
+            s_ = wave_sum(s_);
+            if (g_lo + s_ > thr) {
                 hi = mid;
                 n_in = c;
             } else {
                 lo = mid;
-                g_lo += s;
+                g_lo += s_;
                 n_in -= c;
             }
-            if (n_in <= kCap && 2 * n_in <= len && n_in > 1) {
+            if (n_in <= kCap && 2 * n_in <= len) {
                 len = compact(src, len, lo, hi, cand, lane);
                 src = cand;
             }
         }
         uint32_t cut = hi;
-        if (n_in == 1 && hi - lo > 1) {
-            // the single value left in (lo, hi] is where g crosses thr
-            uint32_t best = 0;
-            for (int j = lane; j < len; j += 64) {
-                const uint32_t b = __float_as_uint(src[j]);
-                if (b > lo && b <= hi) best = max(best, b);
+        if (n_in <= 64) {
+            // one candidate per lane: F(x) = g_lo + (sum of the candidates <= x), tied
+            // values together; the cut is the smallest candidate with F(x) > thr
+            len = compact(src, len, lo, hi, cand, lane);
+            const float x = lane < len ? cand[lane] : 0.f;
+            const uint32_t bx = __float_as_uint(x);
+            float below = 0.f;
+            for (int m = 0; m < len; ++m) {
+                const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), m));
+                if (__float_as_uint(y) <= bx) below += y;
             }
-            cut = wave_max_u(best);
+            const bool crosses = lane < len && g_lo + below > thr;
+            const uint32_t pick = crosses ? bx : 0xffffffffu;
+            const uint32_t best = ~wave_max_u(~pick);   // smallest pattern among the crossing ones
+            if (best != 0xffffffffu) cut = best;
         }
 
         int qt = 0, qh_ = 0, qw = 0;
