@@ -229,6 +229,34 @@ def _sample_blocks(G, nb, cnt, rng, n_rand=48):
     return sorted(pairs)
 
 
+def test_max_blocks_per_head():
+    """The largest mask the library accepts: 2048 blocks per head (16 frames of 8 x 16
+    patches), where the select step holds 16 rows of 2048 pooled logits in LDS."""
+    cfg = small("nb2048", 16, 64, 128, 8, 64, "bf16", 0.2, heads=1)
+    assert cfg.nb == 2048
+    say(f"max blocks per head: nb {cfg.nb}, L {cfg.L}")
+    q, k, v = make_qkv(cfg)
+    res = run_gpu_path(cfg, q, k, v)
+    nb = cfg.nb
+    cnt = res["cnt"].cpu().numpy().reshape(1, nb)
+    idx = res["idx"].cpu().numpy().reshape(1, nb, nb)
+    gmask = lists_to_mask(cnt, idx)
+    assert np.array_equal(bitmap_to_mask(res["bitmap"].cpu().numpy().reshape(1, nb, -1), nb), gmask)
+    qf, kf, vf = (O.reorder(to_np(t.reshape(1, cfg.L, cfg.d)[0]), cfg.T, cfg.H, cfg.W, cfg.P)
+                  for t in (q, k, v))
+    ref = O.block_mask(qf[None], kf[None], cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr)
+    mism, band = check_mask(gmask, ref["mask"], ref["A"], cfg.thr)
+    say(f"  kept {gmask.mean():.4f}  mismatches {mism}  band {band}")
+    assert mism <= 1e-3 * gmask.size
+    of = res["of"].reshape(1, cfg.L, cfg.d)
+    worst = 0.0
+    for _, i in _sample_blocks(1, nb, cnt, np.random.default_rng(11), n_rand=12):
+        ref_o = O.attention_block(qf, kf, vf, gmask[0, i], i, cfg.N, 1.0 / np.sqrt(cfg.d))
+        worst = max(worst, max_abs(to_np(of[0, i * cfg.N:(i + 1) * cfg.N]), ref_o))
+    say(f"  attention on sampled blocks: max-abs {worst:.3e}")
+    assert worst <= TOL_BF16
+
+
 @pytest.mark.parametrize("cfg", CONFIGS[1:], ids=lambda c: c.name)
 def test_full_config_parity(cfg):
     """Full mask parity on every head; attention on a seeded sample of query blocks
