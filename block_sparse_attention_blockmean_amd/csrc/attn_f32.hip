@@ -96,13 +96,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
 template <int D>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
     const size_t lds = (3 * kBlk * (D + 1) + kBlk * 65) * sizeof(float);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_f32_kernel<D>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = set_max_dynamic_lds((const void*)attn_fwd_f32_kernel<D>, (int)lds, lds_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(a.BH * a.nb), dim3(kThreads), lds, s,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.L,
                        a.nb, a.kv_count, a.kv_index, a.schedule, a.scale);

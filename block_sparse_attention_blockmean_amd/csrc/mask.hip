@@ -431,15 +431,10 @@ template <int D>
 hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
     const int ld_s = ((a.nb + 63) / 64) * 64 + 16;
     const size_t lds = ((size_t)kRows * ld_s + (size_t)kWaves * kCap) * sizeof(float);
-    static bool attr_set = false;
-    if (!attr_set) {
-        const int max_lds = (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap) *
-                            (int)sizeof(float);
-        hipError_t e = hipFuncSetAttribute((const void*)map_select_kernel<D>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const int max_lds = (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap) * (int)sizeof(float);
+    hipError_t e = set_max_dynamic_lds((const void*)map_select_kernel<D>, max_lds, lds_set);
+    if (e != hipSuccess) return e;
     dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
     hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.qp, a.kp, a.nb,
                        ld_s, a.scale, a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "nabla.h"
 
 namespace nabla {
@@ -36,6 +38,20 @@ struct FastDiv {
         r = n - q * d;
     }
 };
+
+// Raises a kernel's dynamic-LDS limit on the current device.  The attribute is per
+// device, so `done` remembers (one bit per device id below 64) where it has been set;
+// concurrent first calls may both set it, which is harmless.
+inline hipError_t set_max_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 struct ReorderArgs {
     const void* src;
