@@ -4,26 +4,31 @@
 // "Metodologia: NABLA", item 2, "Expansão"); a dropped tile contributes neither to the
 // numerator nor to the normaliser.
 //
-// One workgroup = one 64-row query block, two waves of 32 query rows each.  Per kept
-// KV block, each wave runs
-//     S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q from VGPRs
+// One workgroup = one 64-row query block, four waves.  Wave (qh, kh) takes query rows
+// [32 qh, 32 qh + 32) against keys [32 kh, 32 kh + 32) of every kept KV tile, with its
+// own running maximum, normaliser and output; the two key halves of each query half are
+// merged once at the end.  Per tile, each wave runs
+//     S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = 32 keys of K from LDS, B = Q (VGPRs)
 //     online softmax   float32, exp2 with scale*log2(e) folded into one FMA
-//     O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, A = V^T from LDS, B = P from VGPRs
+//     O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, A = V^T from LDS, B = P (VGPRs)
 // Computing the transposed products makes every lane own one query column: its S^T
 // accumulator already has the layout the P operand of the second product needs (the
 // MFMA's k index is permuted identically in both operands, which leaves the sum
-// unchanged), and the row statistics stay in the lane, with one exchange between
-// lanes l and l^32, which split the 64 keys of a tile.
+// unchanged), and the row statistics stay in the lane, with one exchange between lanes
+// l and l^32, which split the wave's 32 keys.
 //
-// Memory pipeline: K and V tiles go from global memory straight into LDS
-// (global_load_lds_dwordx4, no VGPR staging), row-major with an XOR swizzle of the
-// 16-byte chunks.  V^T operands come out of the row-major V tile through the
-// transposing LDS read (ds_read_b64_tr_b16).  One K and one V buffer (32 KiB per
-// workgroup, so four workgroups = two waves per SIMD fit a CU): K of the next tile
-// streams in during the softmax and P V, right after every wave has read the current
-// K, and V of the next tile during the next S^T and softmax.  Barriers between waves
-// are plain s_barrier with explicit waits, so copies stay in flight across them.
+// Memory pipeline: K and V tiles go from global memory straight into LDS with the
+// buffer form of the LDS DMA (buffer_load_dwordx4 ... lds, no VGPR staging), row-major
+// with an XOR swizzle of the 16-byte chunks, and are double-buffered: at the top of
+// iteration i, after one barrier, the workgroup issues K(i+1) and V(i+1), which have the
+// whole iteration to land.  64 KiB of LDS per workgroup and ~170 VGPRs per wave put two
+// workgroups on a CU, two waves on every SIMD.  V^T operands come out of the row-major V
+// tile through the transposing LDS read (ds_read_b64_tr_b16).  The four buffers are
+// separate LDS objects, so the compiler sees that reading one never waits for a copy
+// into another.
 #include <math.h>
+
+#include <type_traits>
 
 #include "nabla_internal.h"
 
@@ -38,7 +43,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kBlk = 64;
-constexpr int kThreads = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+// Third dword of a raw buffer resource on gfx9-family GPUs: 32-bit data format, no
+// swizzle, no stride.
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D>
 struct Tile {
@@ -46,7 +55,7 @@ struct Tile {
     static constexpr int kChunks = D / 8;               // 16-byte chunks per row
     static constexpr int kRowsPerLine = 256 / kRowBytes;  // rows per 256-byte LDS bank line
     static constexpr int kBytes = kBlk * kRowBytes;
-    static constexpr int kLoadsPerWave = kBytes / 1024 / 2;  // 1 KB per wave-wide load
+    static constexpr int kCopiesPerWave = kBytes / 1024 / kWaves;  // 1 KiB per copy
     // K is read 16 bytes per lane from 16 consecutive rows at one chunk: spread the
     // rows over all chunk slots of a bank line.
     __device__ static inline int k_swz(int row) { return (row / kRowsPerLine) & (kChunks - 1); }
@@ -55,39 +64,42 @@ struct Tile {
     __device__ static inline int v_swz(int row) { return 4 * ((row / kRowsPerLine) & (kChunks / 4 - 1)); }
 };
 
-// Wave-wide copy of one 64 x D tile from global memory into LDS.  Load u of wave w
-// fills bytes [1024 (2u + w), +1024) of the LDS tile, 16 bytes per lane in lane order;
-// the lane picks the global chunk that belongs in that slot under the swizzle.  The
-// tile base is uniform and the lane offset 32-bit, so the load takes the scalar-base
-// form; the LDS destination (M0) is uniform as well.
+// Copy u of wave w fills bytes [1024 (4u + w), +1024) of the LDS tile, 16 bytes per lane
+// in lane order; the lane fetches the global chunk that belongs in that slot under the
+// swizzle.  Copy u covers rows 4 KiB further down than copy u - 1 and the swizzle of a
+// row depends only on its position within 16 rows (d = 128) or 32 rows (d = 64), which
+// copy u shares with copy 0, so the lane part is that of copy 0 and u adds 4 KiB.
 template <int D, bool kIsV>
-__device__ inline uint32_t tile_lane_offset(int u, int wave, int lane) {
+__device__ inline uint32_t copy_lane_offset(int wave, int lane) {
     using G = Tile<D>;
-    const int o = (2 * u + wave) * 1024 + lane * 16;
+    const int o = wave * 1024 + lane * 16;
     const int row = o / G::kRowBytes;
     const int slot = (o % G::kRowBytes) / 16;
     const int chunk = slot ^ (kIsV ? G::v_swz(row) : G::k_swz(row));
     return (uint32_t)(row * G::kRowBytes + chunk * 16);
 }
 
-template <int D, bool kIsV>
-__device__ inline void load_tile(const __bf16* g_tile, char* lds_tile, int wave, int lane) {
+// The wave's share of one tile copy (buffer form of the LDS DMA: uniform tile offset in
+// soffset, 32-bit lane offset, uniform LDS destination in M0; offsets past the buffer
+// read zeros).
+template <int D>
+__device__ inline void copy_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t tile_byte, char* lds_tile, int wave,
+                                 uint32_t lane_off) {
     using G = Tile<D>;
-    const char* src = reinterpret_cast<const char*>(g_tile);
 #pragma unroll
-    for (int u = 0; u < G::kLoadsPerWave; ++u) {
-        uint32_t off = tile_lane_offset<D, kIsV>(u, wave, lane);
-        // keep the offset a 32-bit register at the load, so it is not widened to a
-        // 64-bit pointer and hoisted out of the tile loop
-        asm volatile("" : "+v"(off));
-        __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(lds_tile + (2 * u + wave) * 1024),
-                                         16, 0, 0);
-    }
+    for (int u = 0; u < G::kCopiesPerWave; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + (4 * u + wave) * 1024), 16,
+                                                 lane_off, tile_byte + u * 4096, 0, 0);
 }
 
+// s_waitcnt vmcnt(N) through the builtin, which the compiler's own wait accounting
+// understands (an asm wait would leave it assuming the copies are still pending).
+// gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their
+// maxima (no wait).
 template <int N>
 __device__ inline void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
 // Workgroup barrier for LDS hand-offs that leaves tile copies in flight.  A
@@ -101,21 +113,23 @@ __device__ inline void lds_barrier() {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, int L, int nb, const int32_t* __restrict__ kv_count,
-    const int32_t* __restrict__ kv_index, const int32_t* __restrict__ schedule,
-    float scale_log2e) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                          const __bf16* __restrict__ v, __bf16* __restrict__ o, int L, int nb,
+                          const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_index,
+                          const int32_t* __restrict__ schedule, float scale_log2e) {
     using G = Tile<D>;
     constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;        // 32-row d tiles of O^T
-    __shared__ __attribute__((aligned(1024))) char k_lds[G::kBytes];
-    __shared__ __attribute__((aligned(1024))) char v_lds[G::kBytes];
+    constexpr uint32_t kTileBytes = kBlk * D * 2;
+    __shared__ __attribute__((aligned(1024))) char k_lds0[G::kBytes];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[G::kBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[G::kBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[G::kBytes];
 
-    // Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD walks a
-    // contiguous range of (head, query block) and neighbouring query blocks, which
-    // keep similar KV lists, share that XCD's L2.
-    // With a schedule, workgroups take query blocks in its order (longest lists first).
+    // Workgroups are dealt round-robin to the 8 XCDs; without a schedule, remap so that
+    // each XCD walks a contiguous range of (head, query block).  With a schedule,
+    // workgroups take query blocks in its order (heads in turn, longest lists first).
     const int nwg = gridDim.x;
     const int full = (nwg / 8) * 8;
     int logical = blockIdx.x;
@@ -129,100 +143,88 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int qhalf = wave & 1;
+    const int khalf = wave >> 1;
     const int lane = tid & 63;
     const int h = lane >> 5;
     const int c32 = lane & 31;
 
     const size_t head_off = (size_t)bh * L * D;
     const __bf16* qh = q + head_off;
-    const __bf16* kh = k + head_off;
-    const __bf16* vh = v + head_off;
+    const int head_bytes = L * D * 2;
+    const __amdgpu_buffer_rsrc_t k_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(k + head_off), 0, head_bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t v_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(v + head_off), 0, head_bytes, kBufferFlags);
+    const uint32_t k_copy = copy_lane_offset<D, false>(wave, lane);
+    const uint32_t v_copy = copy_lane_offset<D, true>(wave, lane);
 
     const int count = kv_count[(size_t)bh * nb + qb];
     const int32_t* list = kv_index + ((size_t)bh * nb + qb) * nb;
+
+    if (count > 0) {
+        copy_tile<D>(k_rsrc, list[0] * kTileBytes, k_lds0, wave, k_copy);
+        copy_tile<D>(v_rsrc, list[0] * kTileBytes, v_lds0, wave, v_copy);
+    }
+
     // Q operand: lane holds Q[row][16 s + 8 h .. + 7] for s = 0..KS-1.
-    const int qrow = qb * kBlk + wave * 32 + c32;
+    const int qrow = qb * kBlk + 32 * qhalf + c32;
     bf16x8 qreg[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
         qreg[s] = *reinterpret_cast<const bf16x8*>(qh + (size_t)qrow * D + 16 * s + 8 * h);
-
-    // issue order K0, V0; iteration i issues K(i+1) after its S^T and V(i+1) at its end
-    if (count > 0) {
-        load_tile<D, false>(kh + (size_t)list[0] * kBlk * D, k_lds, wave, lane);
-        load_tile<D, true>(vh + (size_t)list[0] * kBlk * D, v_lds, wave, lane);
-    }
 
     f32x16 oacc[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
-    float m_run = -INFINITY;   // reference max of scaled logits (log2 domain)
+    float m_run = -INFINITY;   // reference max of scaled logits (log2 domain), same in l, l^32
     float l_run = 0.f;         // this lane's share of the running normaliser
 
     // per-lane LDS byte offsets that do not change from tile to tile
-    int k_off[2][KS];
+    const int krow = 32 * khalf + c32;
+    int k_off[KS];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int row = 32 * t + c32;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            k_off[t][s] = row * G::kRowBytes + (((2 * s + h) ^ G::k_swz(row)) * 16);
-    }
+    for (int s = 0; s < KS; ++s) k_off[s] = krow * G::kRowBytes + (((2 * s + h) ^ G::k_swz(krow)) * 16);
+    // V^T operand of d tile t, k-step u, half p: rows 32 kh + 16 u + 8 p + 4 h + j16 / 4;
+    // only the d tile changes the swizzled part, (16 u + 8 p) rows are a constant offset
     const int g16 = lane >> 4, j16 = lane & 15;
-    int v_off[DT][4][2];
+    int v_off[DT];
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int row = 16 * u + 4 * h + 8 * p + (j16 >> 2);
-                const int d = 32 * t + 16 * (g16 & 1) + 4 * (j16 & 3);
-                v_off[t][u][p] = row * G::kRowBytes + (((d >> 3) ^ G::v_swz(row)) * 16) + ((d >> 2) & 1) * 8;
-            }
+    for (int t = 0; t < DT; ++t) {
+        const int row = 32 * khalf + 4 * h + (j16 >> 2);
+        const int d = 32 * t + 16 * (g16 & 1) + 4 * (j16 & 3);
+        v_off[t] = row * G::kRowBytes + (((d >> 3) ^ G::v_swz(row)) * 16) + ((d >> 2) & 1) * 8;
+    }
 
-    // K0 has landed once only V0 may be pending
-    wait_vmcnt<G::kLoadsPerWave>();
-    lds_barrier();
+    int next_tile = count > 1 ? list[1] : 0;   // KV block copied at the top of iteration i: list[i+1]
 
-    for (int it = 0; it < count; ++it) {
-        // K(it) is in LDS and visible: every wave waited for it (in the prologue or at
-        // the end of the previous iteration) before a barrier
-        const char* kbuf = k_lds;
-
-        // ---- S^T = K Q^T for this wave's 32 query columns, 64 keys in two 32-key tiles.
-        // Operands are requested a quarter tile ahead: a group of reads, then the
-        // MFMAs that use them while the next group lands.
-        constexpr int KG = KS / 4;   // k-steps per group
-        f32x16 sacc[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-            bf16x8 ka[KG][2];
-#pragma unroll
-            for (int s = 0; s < KG; ++s)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    ka[s][t] = *reinterpret_cast<const bf16x8*>(kbuf + k_off[t][grp * KG + s]);
-#pragma unroll
-            for (int s = 0; s < KG; ++s)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][t], qreg[grp * KG + s],
-                                                                      sacc[t], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KG, 0);   // this group's K reads
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * KG, 0);   // then its MFMAs
+    // One tile; PAR = i % 2 selects the buffers holding K(i) and V(i).
+    auto step = [&](auto par, int i) {
+        constexpr int PAR = decltype(par)::value;
+        const char* kbuf = PAR ? k_lds1 : k_lds0;
+        const char* vbuf = PAR ? v_lds1 : v_lds0;
+        // K(i) and V(i) have landed (issued one iteration ago); after the barrier every
+        // wave sees them and is done with the buffers of tile i - 1, refilled now
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (i + 1 < count) {
+            const uint32_t nxt = next_tile * kTileBytes;
+            copy_tile<D>(k_rsrc, nxt, PAR ? k_lds0 : k_lds1, wave, k_copy);
+            copy_tile<D>(v_rsrc, nxt, PAR ? v_lds0 : v_lds1, wave, v_copy);
         }
 
-        // every wave is done with k_lds: stream in the next K during the softmax and P V
-        lds_barrier();
-        const bool more = it + 1 < count;
-        if (more) load_tile<D, false>(kh + (size_t)list[it + 1] * kBlk * D, k_lds, wave, lane);
+        // ---- S^T = K Q^T for this wave's 32 keys and 32 query columns (all K operands
+        // requested first; each MFMA waits only for its own)
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        bf16x8 ka[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ka[s] = *reinterpret_cast<const bf16x8*>(kbuf + k_off[s]);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qreg[s], sacc, 0, 0, 0);
 
         // ---- online softmax for query column c32 (keys split between lanes l, l^32).
         // The reference maximum m_run only moves when a tile's maximum exceeds it by
@@ -230,10 +232,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         // rare; normalising by l at the end makes the result independent of m_run.
         float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2e;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+        {
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * scale_log2e;
+        }
         if (__ballot(mx > m_run + 8.0f)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -245,65 +248,84 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
                 for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
         }
 
-        // V(it) has landed once at most K(it+1), issued after it, is pending
-        if (more) wait_vmcnt<G::kLoadsPerWave>(); else wait_vmcnt<0>();
-        lds_barrier();
+        // ---- O^T += V^T P^T over the wave's two 16-key k-steps; P of k-step u is
+        // accumulator entries 8u .. 8u+7
+        bf16x8 pb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[8 * u + e], scale_log2e, -m_run));
+                l_run += pe;
+                pb[u][e] = (__bf16)pe;
+            }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(vbuf + v_off[t] + (16 * u) * G::kRowBytes));
+                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(vbuf + v_off[t] + (16 * u + 8) * G::kRowBytes));
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], oacc[t], 0, 0, 0);
+            }
+        // the tile the next iteration copies, read after this one's last LDS wait so that
+        // the scalar load is done by the barrier that opens the next iteration
+        __builtin_amdgcn_sched_barrier(0);
+        next_tile = list[min(i + 2, count - 1)];
+    };
 
-        // ---- O^T += V^T P^T, k-step by k-step: P of step u needs only its own 8 exps,
-        // and the V^T operands (two transposing 8-byte reads each) of step u+1 are
-        // requested while step u multiplies.
-        s16x4 vr[2][DT][2];
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    for (int i = 0; i < count; i += 2) {
+        step(P0{}, i);
+        if (i + 1 < count) step(P1{}, i + 1);
+    }
+
+    // ---- merge the key halves: wave (qh, 1) hands its partial output, maximum and
+    // normaliser to wave (qh, 0), which finishes query rows 32 qh .. 32 qh + 31.  Every
+    // copy has landed (the last iteration issued none and waited for the rest) and the
+    // barrier below ends every read of the tile buffers.
+    lds_barrier();
+    float* xo = reinterpret_cast<float*>(qhalf ? k_lds1 : k_lds0);   // DT*16*64 floats
+    float* xs = reinterpret_cast<float*>(v_lds0) + qhalf * 128;      // m, l per lane
+    static_assert(DT * 16 * 64 * 4 <= G::kBytes, "partial output exceeds one tile buffer");
+    if (khalf == 1) {
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int p = 0; p < 2; ++p)
-                vr[0][t][p] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_lds + v_off[t][0][p]));
-        float psum = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (u + 1 < 4) {
-#pragma unroll
-                for (int t = 0; t < DT; ++t)
-#pragma unroll
-                    for (int p = 0; p < 2; ++p)
-                        vr[(u + 1) & 1][t][p] =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_lds + v_off[t][u + 1][p]));
-            }
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][8 * (u & 1) + e], scale_log2e, -m_run));
-                psum += pe;
-                pb[e] = (__bf16)pe;
-            }
-#pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(vr[u & 1][t][0], vr[u & 1][t][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[t], 0, 0, 0);
-            }
-        }
-        l_run += psum;
-        // K(it+1) has landed (nothing was issued after it); after the barrier every
-        // wave is done with v_lds and sees K(it+1): stream in the next V
-        if (more) wait_vmcnt<0>();
-        lds_barrier();
-        if (more) load_tile<D, true>(vh + (size_t)list[it + 1] * kBlk * D, v_lds, wave, lane);
+            for (int r = 0; r < 16; ++r) xo[(t * 16 + r) * 64 + lane] = oacc[t][r];
+        xs[lane] = m_run;
+        xs[64 + lane] = l_run;
     }
-
-    // ---- normalise and store: lane holds O[qrow][32 t + 8 g + 4 h + c], c = 0..3
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-    __bf16* orow = o + head_off + (size_t)qrow * D;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            bf16x4 pk;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) pk[c] = (__bf16)(oacc[t][4 * g + c] * inv);
-            *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * h) = pk;
+    lds_barrier();
+    if (khalf == 0) {
+        const float m_p = xs[lane];
+        const float l_p = xs[64 + lane];
+        const float m = fmaxf(m_run, m_p);
+        const float a_s = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+        const float a_p = m_p == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_p - m);
+        float l = l_run * a_s + l_p * a_p;
+        {
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+            l = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
         }
+        const float inv = (l > 0.f) ? 1.0f / l : 0.f;
+        // lane holds O[qrow][32 t + 8 g + 4 h + c], c = 0..3
+        __bf16* orow = o + head_off + (size_t)qrow * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 pk;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int r = 4 * g + c;
+                    pk[c] = (__bf16)((oacc[t][r] * a_s + xo[(t * 16 + r) * 64 + lane] * a_p) * inv);
+                }
+                *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * h) = pk;
+            }
     }
 }
 
