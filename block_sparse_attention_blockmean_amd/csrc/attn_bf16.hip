@@ -198,7 +198,9 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         v_off[t] = row * G::kRowBytes + (((d >> 3) ^ G::v_swz(row)) * 16) + ((d >> 2) & 1) * 8;
     }
 
-    int next_tile = count > 1 ? list[1] : 0;   // KV block copied at the top of iteration i: list[i+1]
+    // KV block copied during iteration i: list[i+1], and the last block again at the last
+    // iteration (into the buffer nothing reads any more), which keeps the copies unconditional
+    int next_tile = list[count > 1 ? 1 : 0];   // in bounds also when count is 0 (then unused)
 
     // One tile; PAR = i % 2 selects the buffers holding K(i) and V(i).
     auto step = [&](auto par, int i) {
@@ -209,11 +211,9 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         // wave sees them and is done with the buffers of tile i - 1, refilled now
         wait_vmcnt<0>();
         lds_barrier();
-        if (i + 1 < count) {
-            const uint32_t nxt = next_tile * kTileBytes;
-            copy_tile<D>(k_rsrc, nxt, PAR ? k_lds0 : k_lds1, wave, k_copy);
-            copy_tile<D>(v_rsrc, nxt, PAR ? v_lds0 : v_lds1, wave, v_copy);
-        }
+        const uint32_t nxt = next_tile * kTileBytes;
+        char* k_dst = PAR ? k_lds0 : k_lds1;
+        char* v_dst = PAR ? v_lds0 : v_lds1;
 
         // ---- S^T = K Q^T for this wave's 32 keys and 32 query columns (all K operands
         // requested first; each MFMA waits only for its own)
@@ -223,8 +223,17 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         bf16x8 ka[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) ka[s] = *reinterpret_cast<const bf16x8*>(kbuf + k_off[s]);
+        __builtin_amdgcn_sched_barrier(0);
+        // the wave's copies of K(i+1), one after every other MFMA
 #pragma unroll
-        for (int s = 0; s < KS; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qreg[s], sacc, 0, 0, 0);
+        for (int s = 0; s < KS; ++s) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qreg[s], sacc, 0, 0, 0);
+            constexpr int kEvery = KS / G::kCopiesPerWave;
+            if (s % kEvery == 0)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(k_dst + (4 * (s / kEvery) + wave) * 1024), 16,
+                                                         k_copy, nxt + (s / kEvery) * 4096, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 
         // ---- online softmax for query column c32 (keys split between lanes l, l^32).
         // The reference maximum m_run only moves when a tile's maximum exceeds it by
@@ -263,6 +272,12 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
+                // the wave's copies of V(i+1), one after every other MFMA
+                constexpr int kEveryV = 2 * DT / G::kCopiesPerWave;
+                const int m = u * DT + t;
+                if (m % kEveryV == 0)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)(v_dst + (4 * (m / kEveryV) + wave) * 1024), 16,
+                                                             v_copy, nxt + (m / kEveryV) * 4096, 0, 0);
                 const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s16x4*)(vbuf + v_off[t] + (16 * u) * G::kRowBytes));
                 const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -284,9 +299,10 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     }
 
     // ---- merge the key halves: wave (qh, 1) hands its partial output, maximum and
-    // normaliser to wave (qh, 0), which finishes query rows 32 qh .. 32 qh + 31.  Every
-    // copy has landed (the last iteration issued none and waited for the rest) and the
-    // barrier below ends every read of the tile buffers.
+    // normaliser to wave (qh, 0), which finishes query rows 32 qh .. 32 qh + 31.  The
+    // last iteration's copies (of the last block again, into buffers no longer read) must
+    // land before the buffers are reused; the barrier then ends every read of them.
+    wait_vmcnt<0>();
     lds_barrier();
     float* xo = reinterpret_cast<float*>(qhalf ? k_lds1 : k_lds0);   // DT*16*64 floats
     float* xs = reinterpret_cast<float*>(v_lds0) + qhalf * 128;      // m, l per lane
