@@ -10,6 +10,8 @@ attention kernel's own TFLOP/s against the bf16 MFMA peak and the mask phase's
 GB/s against HBM peak ride along, with the oracle timed on the host beside it.
 
     python bench.py [--steps K] [--warmup W] [--config 1] [--no-cpu]
+    python bench.py --no-cpu --loop-seconds 12      # steady load for power / clock readings
+    python bench.py --gemm-reference                # dense bf16 GEMM of the vendor library
 """
 from __future__ import annotations
 
@@ -109,6 +111,13 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only an identity reorder (P=1, a plain copy) of 1 GiB, for counter scaling")
+    ap.add_argument("--loop-seconds", type=float, default=0.0,
+                    help="after the warm-up, repeat the step for this long (a progress line per "
+                         "second, no JSON line): a steady load for power and clock readings")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="time only a dense 8192^3 bf16 GEMM of the vendor library (torch.matmul) "
+                         "for --loop-seconds (default 10): the rate a plain GEMM sustains on this "
+                         "GPU, as context for the attention kernel's MFMA fraction")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -132,6 +141,32 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": x.numel() * 2,
                           "copy_calibration_bytes_written": y.numel() * 2, "launches": args.steps}))
+        return 0
+
+    if args.gemm_reference:
+        n = 8192
+        a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        secs = args.loop_seconds if args.loop_seconds > 0 else 10.0
+        t0 = time.perf_counter()
+        rates = []
+        while time.perf_counter() - t0 < secs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                torch.matmul(a, b, out=c)
+            e1.record()
+            torch.cuda.synchronize()
+            rates.append(2.0 * n ** 3 / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12)
+            print(f"# t={time.perf_counter() - t0:.1f}s gemm {rates[-1]:.1f} TFLOP/s", file=sys.stderr,
+                  flush=True)
+        tail = rates[len(rates) // 2:]
+        print(json.dumps({"gemm_reference": "torch.matmul bf16 (hipBLASLt)", "m": n, "n": n, "k": n,
+                          "tflops_steady": round(float(np.mean(tail)), 1), "seconds": round(secs, 1)}))
         return 0
 
     cfg = get_config(int(args.config) if args.config.isdigit() else args.config)
@@ -175,6 +210,20 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.loop_seconds > 0:
+        t0 = time.perf_counter()
+        n, last = 0, t0
+        while time.perf_counter() - t0 < args.loop_seconds:
+            for _ in range(50):
+                step()
+            torch.cuda.synchronize()
+            n += 50
+            now = time.perf_counter()
+            if now - last >= 1.0:
+                print(f"# t={now - t0:.1f}s steps={n} ms/step={(now - t0) * 1e3 / n:.3f}", file=sys.stderr,
+                      flush=True)
+                last = now
+        return 0
     kept = int(cnt.sum().item())
     kept_flops = kept * 4.0 * cfg.N * cfg.N * cfg.d
 
