@@ -1,4 +1,5 @@
-"""Oracle for NABLA block-mean adaptive block-sparse attention (forward).
+"""Oracle for NABLA block-mean adaptive block-sparse attention (forward, and the
+gradient of its attention step).
 
 TEST INFRASTRUCTURE ONLY.  This module is a plain, slow CPU statement of what the
 GPU path computes.  Only the test suite, the smoke check and the bench's CPU
@@ -273,6 +274,75 @@ def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarr
             out[g, i * N:(i + 1) * N] = attention_block(q[g], k[g], v[g], mask[g, i], i, N,
                                                         scale, dtype)
     return out
+
+
+def block_lse(q: np.ndarray, k: np.ndarray, keep: np.ndarray, i: int, N: int, scale: float,
+              dtype=np.float64) -> np.ndarray:
+    """Natural-log log-sum-exp of the kept logits of each query row of block ``i``:
+    lse_a = log sum over kept keys b of exp(scale * q_a . k_b); -inf for a block with
+    no kept KV block.  Row max first, then the sum of exponentials."""
+    js = np.nonzero(keep)[0]
+    if len(js) == 0:
+        return np.full(N, -np.inf, dtype=dtype)
+    tok = (js[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+    s = (np.asarray(q[i * N:(i + 1) * N], dtype=dtype) @ np.asarray(k[tok], dtype=dtype).T) * dtype(scale)
+    m = np.max(s, axis=1)
+    return m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
+
+
+def masked_attention_lse(q: np.ndarray, k: np.ndarray, mask: np.ndarray, N: int,
+                         scale: Optional[float] = None, dtype=np.float64) -> np.ndarray:
+    """[G, L] log-sum-exp of every query row over its kept keys (see ``block_lse``)."""
+    d = q.shape[-1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    G, L, _ = q.shape
+    out = np.empty((G, L), dtype=dtype)
+    for g in range(G):
+        for i in range(L // N):
+            out[g, i * N:(i + 1) * N] = block_lse(q[g], k[g], mask[g, i], i, N, scale, dtype)
+    return out
+
+
+def masked_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                              mask: np.ndarray, N: int, scale: Optional[float] = None,
+                              dtype=np.float64):
+    """Gradients (dq, dk, dv) of sum(O * dout) for O = block-masked softmax attention
+    (``masked_attention``) of [G, L, d] inputs under a [G, nb, nb] mask.
+
+    The pages define the forward only; this is its gradient, written per query block
+    i over the tokens of its kept KV blocks:
+        P   = softmax of scale * Q_i K^T over the kept keys (row by row)
+        O_i = P V,   D = rowsum(dO_i * O_i)
+        dV  += P^T dO_i,   dP = dO_i V^T,   dS = P * (dP - D)
+        dQ_i = scale * dS K,   dK += scale * dS^T Q_i
+    A query block with no kept block has zero output, so it passes no gradient."""
+    d = q.shape[-1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    G, L, _ = q.shape
+    dq = np.zeros((G, L, d), dtype=dtype)
+    dk = np.zeros((G, L, d), dtype=dtype)
+    dv = np.zeros((G, L, v.shape[-1]), dtype=dtype)
+    for g in range(G):
+        for i in range(L // N):
+            js = np.nonzero(mask[g, i])[0]
+            if len(js) == 0:
+                continue
+            tok = (js[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+            rows = slice(i * N, (i + 1) * N)
+            qi = np.asarray(q[g, rows], dtype=dtype)
+            kk = np.asarray(k[g, tok], dtype=dtype)
+            vv = np.asarray(v[g, tok], dtype=dtype)
+            doi = np.asarray(dout[g, rows], dtype=dtype)
+            s = (qi @ kk.T) * dtype(scale)
+            e = np.exp(s - np.max(s, axis=1, keepdims=True))
+            p = e / np.sum(e, axis=1, keepdims=True)
+            o = p @ vv
+            D = np.sum(doi * o, axis=1, keepdims=True)
+            dv[g, tok] += p.T @ doi
+            ds = p * (doi @ vv.T - D)
+            dq[g, rows] = dtype(scale) * (ds @ kk)
+            dk[g, tok] += dtype(scale) * (ds.T @ qi)
+    return dq, dk, dv
 
 
 def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, T: int, H: int, W: int, P: int,

@@ -314,4 +314,101 @@ def pin_mask_precision_band():
         assert np.max(np.abs(m32["F"] - m64["F"])) <= 1e-5
 
 
+# ---------------------------------------------------------------- backward (gradient of attention)
+
+def _tok_mask(m, N):
+    return np.stack([np.kron(m[g], np.ones((N, N), dtype=bool)) for g in range(m.shape[0])])
+
+
+def _autograd_grads(q, k, v, dout, tok, scale):
+    """Gradients of sum(O * dout) by torch autograd through the float64 SDPA math
+    path with a boolean token mask (an implementation independent of the oracle)."""
+    qt, kt, vt = (torch.from_numpy(np.asarray(a, dtype=np.float64)).requires_grad_(True)
+                  for a in (q, k, v))
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(tok), scale=scale)
+    (o * torch.from_numpy(np.asarray(dout, dtype=np.float64))).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def pin_lse_logsumexp():
+    rng = _rng(20)
+    G, L, N, d = 2, 320, 64, 8
+    nb = L // N
+    q, k = (rng.standard_normal((G, L, d)).astype(np.float32) * 2 for _ in range(2))
+    m = rng.random((G, nb, nb)) < 0.4
+    m[:, np.arange(nb), np.arange(nb)] = True
+    m[1, 2] = False                                   # an empty row
+    lse = O.masked_attention_lse(q, k, m, N, scale=0.4)
+    tok = _tok_mask(m, N)
+    s = np.einsum("gad,gbd->gab", q.astype(np.float64), k.astype(np.float64)) * 0.4
+    ref = scipy.special.logsumexp(np.where(tok, s, -np.inf), axis=-1)
+    ok = np.isfinite(ref)
+    assert np.array_equal(ok, np.isfinite(lse))
+    assert np.all(lse[~ok] == -np.inf)
+    assert np.max(np.abs(lse[ok] - ref[ok])) <= 1e-12
+
+
+def pin_backward_autograd():
+    rng = _rng(21)
+    G, L, N, d = 2, 320, 64, 8
+    nb = L // N
+    q, k, v, do = (rng.standard_normal((G, L, d)).astype(np.float32) * 1.5 for _ in range(4))
+    for trial, density in enumerate((1.0, 0.45)):
+        m = rng.random((G, nb, nb)) < density
+        m[:, np.arange(nb), (np.arange(nb) * 2 + trial) % nb] = True   # no empty row
+        dq, dk, dv = O.masked_attention_backward(q, k, v, do, m, N, scale=0.35)
+        rq, rk, rv = _autograd_grads(q, k, v, do, _tok_mask(m, N), 0.35)
+        for a, b in ((dq, rq), (dk, rk), (dv, rv)):
+            assert np.max(np.abs(a - b)) <= 1e-10 * max(1.0, np.max(np.abs(b)))
+
+
+def pin_backward_finite_difference():
+    rng = _rng(22)
+    G, L, N, d = 1, 192, 64, 4
+    nb = L // N
+    q, k, v, do = (rng.standard_normal((G, L, d)) for _ in range(4))
+    m = np.array([[[1, 0, 1], [1, 1, 0], [0, 0, 1]]], dtype=bool)
+    scale = 0.7
+    dq, dk, dv = O.masked_attention_backward(q, k, v, do, m, N, scale=scale)
+
+    def f(q_, k_, v_):
+        return float(np.sum(O.masked_attention(q_, k_, v_, m, N, scale=scale) * do))
+
+    eps = 1e-6
+    for which, g in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(3):
+            u = rng.standard_normal((G, L, d))
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which] = args_p[which] + eps * u
+            args_m[which] = args_m[which] - eps * u
+            fd = (f(*args_p) - f(*args_m)) / (2 * eps)
+            an = float(np.sum(g * u))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, fd, an)
+
+
+def pin_backward_sums_and_empty_rows():
+    """Rows of dS sum to zero, so the dK of a head sums to zero over its keys; P's
+    rows sum to one, so dV sums to the dO of the rows that keep something.  A query
+    block with no kept block passes no gradient at all."""
+    rng = _rng(23)
+    G, L, N, d = 2, 384, 64, 8
+    nb = L // N
+    q, k, v, do = (rng.standard_normal((G, L, d)) for _ in range(4))
+    m = rng.random((G, nb, nb)) < 0.5
+    m[:, np.arange(nb), np.arange(nb)] = True
+    m[0, 3] = False
+    dq, dk, dv = O.masked_attention_backward(q, k, v, do, m, N)
+    assert np.max(np.abs(dk.sum(axis=1))) <= 1e-10
+    live = np.repeat(m.any(axis=2), N, axis=1)          # [G, L] rows that keep a block
+    assert np.max(np.abs(dv.sum(axis=1) - (do * live[..., None]).sum(axis=1))) <= 1e-10
+    assert np.all(dq[0, 3 * N:4 * N] == 0)
+    m2 = m.copy()
+    m2[0, 3] = False
+    do2 = do.copy()
+    do2[0, 3 * N:4 * N] = rng.standard_normal((N, d))   # dO of the empty block is irrelevant
+    dq2, dk2, dv2 = O.masked_attention_backward(q, k, v, do2, m2, N)
+    assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -90,6 +90,41 @@ def _attn_keys_shifted(q, k, v, keep, i, N, scale, dtype=np.float64):
     return (p @ np.asarray(v[tok_v], dtype)) / p.sum(1, keepdims=True)
 
 
+def _backward_with(bug):
+    """A copy of the oracle's backward with one planted slip."""
+    def bwd(q, k, v, dout, mask, N, scale=None, dtype=np.float64):
+        d = q.shape[-1]
+        scale = 1.0 / np.sqrt(d) if scale is None else scale
+        G, L, _ = q.shape
+        dq, dk, dv = (np.zeros((G, L, d), dtype=dtype) for _ in range(3))
+        for g in range(G):
+            for i in range(L // N):
+                js = np.nonzero(mask[g, i])[0]
+                if len(js) == 0:
+                    continue
+                tok = (js[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+                rows = slice(i * N, (i + 1) * N)
+                qi, kk, vv, doi = (np.asarray(a, dtype) for a in (q[g, rows], k[g, tok], v[g, tok], dout[g, rows]))
+                s = (qi @ kk.T) * scale
+                e = np.exp(s - s.max(1, keepdims=True))
+                p = e / e.sum(1, keepdims=True)
+                D = np.sum(doi * (p @ vv), axis=1, keepdims=True)
+                dP = doi @ vv.T
+                ds = p * dP if bug == "no_D" else p * (dP - D)
+                dv[g, tok] += (p.T @ doi) if bug != "dv_from_dp" else (ds.T @ doi)
+                dq[g, rows] = (ds @ kk) * (1.0 if bug == "dq_unscaled" else scale)
+                dk[g, tok] += scale * ((ds.T @ qi) if bug != "dk_from_p" else (p.T @ qi))
+        return dq, dk, dv
+    bwd.__name__ = f"_backward_{bug}"
+    return bwd
+
+
+def _lse_log2(q, k, keep, i, N, scale, dtype=np.float64):
+    return _orig_block_lse(q, k, keep, i, N, scale, dtype) / np.log(2.0)
+
+
+_orig_block_lse = O.block_lse
+
 MUTATIONS = [
     ("fractal_index", _fractal_colmajor),
     ("pooled_logits", _pooled_transposed),
@@ -102,6 +137,11 @@ MUTATIONS = [
     ("sta_mask", _sta_strict),
     ("attention_block", _attn_no_scale),
     ("attention_block", _attn_keys_shifted),
+    ("masked_attention_backward", _backward_with("no_D")),
+    ("masked_attention_backward", _backward_with("dv_from_dp")),
+    ("masked_attention_backward", _backward_with("dq_unscaled")),
+    ("masked_attention_backward", _backward_with("dk_from_p")),
+    ("block_lse", _lse_log2),
 ]
 
 
