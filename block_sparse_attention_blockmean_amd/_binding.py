@@ -24,6 +24,9 @@ EXPORTS = (
     "nabla_build_mask_workspace_size",
     "nabla_build_mask",
     "block_sparse_attn_fwd",
+    "block_sparse_attn_fwd_lse",
+    "nabla_attn_bwd_workspace_size",
+    "block_sparse_attn_bwd",
     "nabla_status_string",
     "nabla_last_error",
 )
@@ -60,6 +63,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_build_mask.restype = i
     lib.block_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, f, i, vp]
     lib.block_sparse_attn_fwd.restype = i
+    lib.block_sparse_attn_fwd_lse.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, f, i, vp, vp]
+    lib.block_sparse_attn_fwd_lse.restype = i
+    lib.nabla_attn_bwd_workspace_size.argtypes = [i, i, i, i]
+    lib.nabla_attn_bwd_workspace_size.restype = sz
+    lib.block_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, f, i,
+                                          vp, sz, vp]
+    lib.block_sparse_attn_bwd.restype = i
     lib.nabla_status_string.argtypes = [i]
     lib.nabla_status_string.restype = ctypes.c_char_p
     lib.nabla_last_error.argtypes = []
@@ -160,11 +170,43 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
     return tuple(out)
 
 
+def _check_lists(q: torch.Tensor, kv_count: torch.Tensor, kv_index: torch.Tensor, N: int) -> None:
+    B, NH, L, d = q.shape
+    nb = L // N
+    if kv_count.dtype != torch.int32 or kv_index.dtype != torch.int32:
+        raise TypeError("kv_count and kv_index must be int32")
+    if kv_count.numel() != B * NH * nb or kv_index.numel() != B * NH * nb * nb:
+        raise ValueError("kv_count / kv_index sizes do not match q")
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.Tensor,
              kv_index: torch.Tensor, N: int = 64, scale: Optional[float] = None,
              out: Optional[torch.Tensor] = None,
-             schedule: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Block-sparse attention over the kept N x N tiles listed in kv_count/kv_index."""
+             schedule: Optional[torch.Tensor] = None, with_lse: bool = False,
+             lse: Optional[torch.Tensor] = None):
+    """Block-sparse attention over the kept N x N tiles listed in kv_count/kv_index.
+
+    With ``with_lse`` (or an ``lse`` tensor) it also returns the float32 [B, heads, L]
+    log-sum-exp of every query row, as (out, lse), which ``attn_bwd`` needs."""
+    if with_lse or lse is not None:
+        lib = load_library()
+        B, NH, L, d = q.shape
+        if lse is None:
+            lse = torch.empty((B, NH, L), dtype=torch.float32, device=q.device)
+        if lse.dtype != torch.float32 or lse.numel() != B * NH * L:
+            raise ValueError("lse must hold batch*heads*L float32 values")
+        for name, t in (("k", k), ("v", v)):
+            if t.shape != q.shape or t.dtype != q.dtype:
+                raise ValueError(f"{name} must match q in shape and dtype")
+        _check_lists(q, kv_count, kv_index, N)
+        if out is None:
+            out = torch.empty_like(q)
+        _check(lib.block_sparse_attn_fwd_lse(
+            _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, NH, L, d, N,
+            _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+            _dev(schedule, "schedule") if schedule is not None else None,
+            float(scale) if scale is not None else 0.0, _dtype_code(q), _dev(lse, "lse"), _stream()), lib)
+        return out, lse
     lib = load_library()
     B, NH, L, d = q.shape
     for name, t in (("k", k), ("v", v)):
@@ -186,3 +228,37 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.
         _dev(schedule, "schedule") if schedule is not None else None,
         float(scale) if scale is not None else 0.0, _dtype_code(q), _stream()), lib)
     return out
+
+
+def attn_bwd_workspace_size(batch: int, heads: int, L: int, N: int = 64) -> int:
+    return int(load_library().nabla_attn_bwd_workspace_size(batch, heads, L, N))
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+             lse: torch.Tensor, kv_count: torch.Tensor, kv_index: torch.Tensor, N: int = 64,
+             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for o = attn_fwd(q, k, v, ...) under the
+    same lists; ``o`` and ``lse`` come from ``attn_fwd(..., with_lse=True)``."""
+    lib = load_library()
+    B, NH, L, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    if lse.dtype != torch.float32 or lse.numel() != B * NH * L:
+        raise ValueError("lse must hold batch*heads*L float32 values")
+    _check_lists(q, kv_count, kv_index, N)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    ws_bytes = int(lib.nabla_attn_bwd_workspace_size(B, NH, L, N))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.block_sparse_attn_bwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(dout, "dout"), _dev(lse, "lse"),
+        _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), B, NH, L, d, N,
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+        float(scale) if scale is not None else 0.0, _dtype_code(q),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()), lib)
+    return dq, dk, dv

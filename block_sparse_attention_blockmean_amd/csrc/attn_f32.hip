@@ -19,7 +19,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, int L, int nb, const int32_t* __restrict__ kv_count,
     const int32_t* __restrict__ kv_index, const int32_t* __restrict__ schedule,
-    float scale) {
+    float scale, float* __restrict__ lse) {
     constexpr int LD = D + 1;
     extern __shared__ float lds[];
     float* q_s = lds;                   // [64][LD]
@@ -88,6 +88,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     float l_tot = l_run + __shfl_xor(l_run, 1);
     l_tot += __shfl_xor(l_tot, 2);
     const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+    if (lse && part == 0)
+        lse[(size_t)bh * L + (size_t)qb * kBlk + row] = l_tot > 0.f ? m_run + logf(l_tot) : -INFINITY;
     float* orow = o + head_off + ((size_t)qb * kBlk + row) * D;
 #pragma unroll
     for (int c = 0; c < D / 4; ++c) orow[part + 4 * c] = acc[c] * inv;
@@ -101,7 +103,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(a.BH * a.nb), dim3(kThreads), lds, s,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.L,
-                       a.nb, a.kv_count, a.kv_index, a.schedule, a.scale);
+                       a.nb, a.kv_count, a.kv_index, a.schedule, a.scale, a.lse);
     return hipGetLastError();
 }
 

@@ -455,8 +455,12 @@ hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
     e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
     if (e != hipSuccess || !a.schedule) return e;
     // one wave per head; its bins fit the default LDS limit (NABLA_MAX_BLOCKS + 1 ints)
-    hipLaunchKernelGGL(schedule_kernel, dim3(a.BH), dim3(64), (size_t)(a.nb + 1) * sizeof(int), s,
-                       a.kv_count, a.nb, a.schedule);
+    return launch_schedule(a.kv_count, a.BH, a.nb, a.schedule, s);
+}
+
+hipError_t launch_schedule(const int32_t* counts, int BH, int nb, int32_t* schedule, hipStream_t s) {
+    hipLaunchKernelGGL(schedule_kernel, dim3(BH), dim3(64), (size_t)(nb + 1) * sizeof(int), s, counts, nb,
+                       schedule);
     return hipGetLastError();
 }
 

@@ -148,25 +148,134 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
     return hip_status(nabla::launch_build_mask(a, stream), "nabla_build_mask");
 }
 
+namespace {
+
+nabla_status attn_fwd_impl(const char* who, const void* q, const void* k, const void* v, void* o,
+                           int batch, int heads, int L, int d, int N, const int32_t* kv_count,
+                           const int32_t* kv_index, const int32_t* schedule, float scale,
+                           nabla_dtype dtype, float* lse, hipStream_t stream);
+
+}  // namespace
+
 nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
                                    int batch, int heads, int L, int d, int N,
                                    const int32_t* kv_count, const int32_t* kv_index,
                                    const int32_t* schedule, float scale, nabla_dtype dtype,
                                    hipStream_t stream) {
+    return attn_fwd_impl("block_sparse_attn_fwd", q, k, v, o, batch, heads, L, d, N, kv_count, kv_index,
+                         schedule, scale, dtype, nullptr, stream);
+}
+
+nabla_status block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v, void* o,
+                                       int batch, int heads, int L, int d, int N,
+                                       const int32_t* kv_count, const int32_t* kv_index,
+                                       const int32_t* schedule, float scale, nabla_dtype dtype,
+                                       float* lse, hipStream_t stream) {
+    if (!lse) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd_lse: null lse");
+    if (!aligned16(lse)) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd_lse: misaligned lse");
+    return attn_fwd_impl("block_sparse_attn_fwd_lse", q, k, v, o, batch, heads, L, d, N, kv_count,
+                         kv_index, schedule, scale, dtype, lse, stream);
+}
+
+size_t nabla_attn_bwd_workspace_size(int batch, int heads, int L, int N) {
+    if (batch <= 0 || heads <= 0 || L <= 0 || N <= 0 || L % N) return 0;
+    const size_t BH = (size_t)batch * heads, nb = (size_t)(L / N), words = (nb + 31) / 32;
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    return up(BH * L * 4) + up(BH * nb * words * 4) + up(BH * nb * 4) + up(BH * nb * nb * 4) +
+           2 * up(BH * nb * 4);
+}
+
+nabla_status block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                   int batch, int heads, int L, int d, int N,
+                                   const int32_t* kv_count, const int32_t* kv_index, float scale,
+                                   nabla_dtype dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    const char* who = "block_sparse_attn_bwd";
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !kv_count || !kv_index)
+        return fail(NABLA_E_INVAL, "%s: null pointer", who);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+        !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)kv_count & 3) ||
+        ((uintptr_t)kv_index & 3))
+        return fail(NABLA_E_INVAL, "%s: misaligned pointer", who);
+    const void* ins[] = {q, k, v, o, dout, lse};
+    for (const void* out : {(const void*)dq, (const void*)dk, (const void*)dv}) {
+        for (const void* in : ins)
+            if (out == in) return fail(NABLA_E_INVAL, "%s: an output aliases an input", who);
+    }
+    if (dq == dk || dq == dv || dk == dv) return fail(NABLA_E_INVAL, "%s: outputs must differ", who);
+    if (batch <= 0 || heads <= 0 || L <= 0 || d <= 0 || N <= 0)
+        return fail(NABLA_E_INVAL, "%s: sizes must be positive", who);
+    if (L % N) return fail(NABLA_E_INVAL, "%s: L=%d is not a multiple of N=%d", who, L, N);
+    if (isnan(scale) || isinf(scale)) return fail(NABLA_E_INVAL, "%s: scale must be finite", who);
+    if (!valid_dtype(dtype)) return fail(NABLA_E_INVAL, "%s: unknown dtype %d", who, (int)dtype);
+    if (N != 64) return fail(NABLA_E_UNSUPPORTED, "%s: only N = 64 is implemented", who);
+    if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "%s: d must be 64 or 128", who);
+    if (L / N > NABLA_MAX_BLOCKS)
+        return fail(NABLA_E_UNSUPPORTED, "%s: %d blocks per head exceed %d", who, L / N, NABLA_MAX_BLOCKS);
+    if ((long long)L * d >= kMaxHeadElems || (long long)batch * heads * (L / N) >= (1ll << 31))
+        return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
+    const size_t need = nabla_attn_bwd_workspace_size(batch, heads, L, N);
+    if (!workspace || workspace_bytes < need)
+        return fail(NABLA_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if ((uintptr_t)workspace & 255) return fail(NABLA_E_INVAL, "%s: workspace must be 256-byte aligned", who);
+
+    nabla::AttnBwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.BH = batch * heads;
+    a.L = L;
+    a.nb = L / N;
+    a.d = d;
+    a.kv_count = kv_count;
+    a.kv_index = kv_index;
+    a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+    a.bf16 = dtype == NABLA_BF16;
+    const size_t BH = (size_t)a.BH, nb = (size_t)a.nb, words = (nb + 31) / 32;
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    char* w = (char*)workspace;
+    a.drow = (float*)w;
+    w += up(BH * L * 4);
+    a.bits = (uint32_t*)w;
+    w += up(BH * nb * words * 4);
+    a.q_count = (int32_t*)w;
+    w += up(BH * nb * 4);
+    a.q_index = (int32_t*)w;
+    w += up(BH * nb * nb * 4);
+    a.sched_q = (int32_t*)w;
+    w += up(BH * nb * 4);
+    a.sched_k = (int32_t*)w;
+    return hip_status(nabla::launch_attn_bwd(a, stream), who);
+}
+
+namespace {
+
+nabla_status attn_fwd_impl(const char* who, const void* q, const void* k, const void* v, void* o,
+                           int batch, int heads, int L, int d, int N, const int32_t* kv_count,
+                           const int32_t* kv_index, const int32_t* schedule, float scale,
+                           nabla_dtype dtype, float* lse, hipStream_t stream) {
     if (!q || !k || !v || !o || !kv_count || !kv_index)
-        return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: null pointer");
+        return fail(NABLA_E_INVAL, "%s: null pointer", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
         ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3) || ((uintptr_t)schedule & 3))
-        return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: misaligned pointer");
+        return fail(NABLA_E_INVAL, "%s: misaligned pointer", who);
     if (batch <= 0 || heads <= 0 || L <= 0 || d <= 0 || N <= 0)
-        return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: sizes must be positive");
-    if (L % N) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: L=%d is not a multiple of N=%d", L, N);
-    if (isnan(scale) || isinf(scale)) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: scale must be finite");
-    if (!valid_dtype(dtype)) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd: unknown dtype %d", (int)dtype);
-    if (N != 64) return fail(NABLA_E_UNSUPPORTED, "block_sparse_attn_fwd: only N = 64 is implemented");
-    if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "block_sparse_attn_fwd: d must be 64 or 128");
+        return fail(NABLA_E_INVAL, "%s: sizes must be positive", who);
+    if (L % N) return fail(NABLA_E_INVAL, "%s: L=%d is not a multiple of N=%d", who, L, N);
+    if (isnan(scale) || isinf(scale)) return fail(NABLA_E_INVAL, "%s: scale must be finite", who);
+    if (!valid_dtype(dtype)) return fail(NABLA_E_INVAL, "%s: unknown dtype %d", who, (int)dtype);
+    if (N != 64) return fail(NABLA_E_UNSUPPORTED, "%s: only N = 64 is implemented", who);
+    if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "%s: d must be 64 or 128", who);
     if ((long long)L * d >= kMaxHeadElems || (long long)batch * heads * (L / N) >= (1ll << 31))
-        return fail(NABLA_E_UNSUPPORTED, "block_sparse_attn_fwd: tensor too large");
+        return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
     nabla::AttnArgs a{};
     a.q = q;
     a.k = k;
@@ -180,9 +289,12 @@ nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, 
     a.kv_index = kv_index;
     a.schedule = schedule;
     a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+    a.lse = lse;
     hipError_t e = dtype == NABLA_BF16 ? nabla::launch_attn_bf16(a, stream)
                                        : nabla::launch_attn_f32(a, stream);
-    return hip_status(e, "block_sparse_attn_fwd");
+    return hip_status(e, who);
 }
+
+}  // namespace
 
 }  // extern "C"

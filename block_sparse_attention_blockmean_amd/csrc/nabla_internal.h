@@ -90,8 +90,37 @@ struct AttnArgs {
     const int32_t* kv_index;
     const int32_t* schedule;   // may be null
     float scale;
+    float* lse;                // may be null: natural-log log-sum-exp per query row [BH, L]
 };
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+// Start order of BH*nb items, heads in turn, each head's items by decreasing count.
+hipError_t launch_schedule(const int32_t* counts, int BH, int nb, int32_t* schedule, hipStream_t s);
+
+struct AttnBwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;          // [BH, L], natural log
+    void* dq;
+    void* dk;
+    void* dv;
+    int BH, L, nb, d;
+    const int32_t* kv_count;
+    const int32_t* kv_index;
+    float scale;
+    int bf16;
+    // workspace
+    float* drow;               // [BH, L]   rowsum(dO * O)
+    uint32_t* bits;            // [BH, nb, ceil(nb/32)]  transposed mask
+    int32_t* q_count;          // [BH, nb]
+    int32_t* q_index;          // [BH, nb, nb]
+    int32_t* sched_q;          // [BH * nb]  start order of the dQ sweep
+    int32_t* sched_k;          // [BH * nb]  start order of the dK/dV sweep
+};
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 
 }  // namespace nabla

@@ -157,6 +157,66 @@ nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, 
                                    const int32_t* schedule, float scale, nabla_dtype dtype,
                                    hipStream_t stream);
 
+/*
+ * block_sparse_attn_fwd_lse - block_sparse_attn_fwd that also writes what the gradient
+ * needs: the natural-log log-sum-exp of every query row over its kept keys,
+ *   lse[b,h,a] = log( sum over tokens t of kept blocks of row blk(a) of exp(scale * q_a . k_t) ),
+ * -inf for the rows of a query block with no kept block.
+ * lse         out, float32 [batch, heads, L], 16-byte aligned.
+ * Other arguments, results and errors as block_sparse_attn_fwd (a null lse is
+ * NABLA_E_INVAL).
+ */
+nabla_status block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v, void* o,
+                                       int batch, int heads, int L, int d, int N,
+                                       const int32_t* kv_count, const int32_t* kv_index,
+                                       const int32_t* schedule, float scale, nabla_dtype dtype,
+                                       float* lse, hipStream_t stream);
+
+/*
+ * nabla_attn_bwd_workspace_size - bytes of device workspace block_sparse_attn_bwd needs
+ * (nb = L/N, BH = batch*heads): the row dots D (BH*L floats), the transposed mask
+ * (BH*nb*ceil(nb/32) words), the transposed lists (BH*nb counts, BH*nb*nb entries) and
+ * two start orders (2*BH*nb ints), each section rounded up to 256 bytes.
+ * Returns 0 for non-positive sizes or L not a multiple of N.
+ */
+size_t nabla_attn_bwd_workspace_size(int batch, int heads, int L, int N);
+
+/*
+ * block_sparse_attn_bwd - gradient of the block-sparse attention: for
+ * O = block_sparse_attn_fwd(Q, K, V) under the lists kv_count / kv_index and an
+ * upstream gradient dO, the gradients of sum(O * dO) with respect to Q, K and V.  The
+ * summary claims the method speeds up training as well as inference (section
+ * "Principais Contribuições", dual-phase acceleration; "Resultados Experimentais",
+ * item 2, pre-training); the backward pass uses the same kept tiles, and a dropped
+ * tile passes no gradient.
+ * With P_at = exp(scale q_a . k_t - lse_a) on the kept tiles:
+ *   D_a  = sum_c dO_ac O_ac
+ *   dV_t = sum_a P_at dO_a
+ *   dS_at = P_at (dO_a . v_t - D_a)
+ *   dQ_a = scale * sum_t dS_at k_t,   dK_t = scale * sum_a dS_at q_a
+ * q, k, v, o, dout  [batch, heads, L, d], dtype `dtype` (o and lse from
+ *             block_sparse_attn_fwd_lse on the same inputs and lists).
+ * lse         float32 [batch, heads, L], 16-byte aligned.
+ * dq, dk, dv  out, [batch, heads, L, d], dtype `dtype`; every element is written.
+ * kv_count, kv_index  the forward's lists; entries in [0, nb), no duplicates within a
+ *             row (nabla_build_mask writes them that way).  dQ follows each row's list;
+ *             dK and dV follow its transpose, which records a block once per row.
+ * scale       <= 0 selects 1/sqrt(d); must equal the forward's.
+ * bf16: S, dP in float32 from bf16 MFMAs, P and dS rounded to bf16 as operands of the
+ * second products, float32 accumulation, gradients rounded to nearest-even bf16.
+ * f32: float32 throughout.  Deterministic: no atomics on the gradients.
+ * workspace   device buffer of at least nabla_attn_bwd_workspace_size() bytes.
+ * Errors: as block_sparse_attn_fwd, plus NABLA_E_INVAL for a null or misaligned lse,
+ * output aliasing an input, nb > NABLA_MAX_BLOCKS giving NABLA_E_UNSUPPORTED, and
+ * NABLA_E_WORKSPACE.
+ */
+nabla_status block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                   int batch, int heads, int L, int d, int N,
+                                   const int32_t* kv_count, const int32_t* kv_index, float scale,
+                                   nabla_dtype dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* Static name of a status code ("NABLA_OK", ...). */
 const char* nabla_status_string(nabla_status status);
 

@@ -155,6 +155,75 @@ def test_attn_validation(lib, kw, status):
     assert lib.nabla_last_error().decode().startswith("block_sparse_attn_fwd")
 
 
+def attn_lse(lib, lse=G, **kw):
+    a = dict(q=A, k=B_, v=C, o=D_, batch=1, heads=2, L=1024, d=64, N=64, cnt=E, idx=F_,
+             schedule=None, scale=0.0, dt=NABLA_BF16)
+    a.update(kw)
+    return lib.block_sparse_attn_fwd_lse(a["q"], a["k"], a["v"], a["o"], a["batch"], a["heads"], a["L"],
+                                         a["d"], a["N"], a["cnt"], a["idx"], a["schedule"], a["scale"],
+                                         a["dt"], lse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=None), NABLA_E_INVAL),
+    (dict(lse=ctypes.c_void_p(0x100004)), NABLA_E_INVAL),
+    (dict(q=None), NABLA_E_INVAL),
+    (dict(L=1000), NABLA_E_INVAL),
+    (dict(d=96), NABLA_E_UNSUPPORTED),
+])
+def test_attn_lse_validation(lib, kw, status):
+    assert attn_lse(lib, **kw) == status
+    assert lib.nabla_last_error().decode().startswith("block_sparse_attn_fwd_lse")
+
+
+# ------------------------------------------------------------- block_sparse_attn_bwd
+
+H_, I_, J_, K_, M_ = (ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(5))
+
+
+def test_bwd_workspace_size(lib):
+    # D, bitmap, counts, lists, two orders; each rounded up to 256 bytes
+    BH, L, nb = 12, 32256, 504
+    up = lambda b: (b + 255) // 256 * 256
+    want = up(BH * L * 4) + up(BH * nb * 16 * 4) + up(BH * nb * 4) + up(BH * nb * nb * 4) + 2 * up(BH * nb * 4)
+    assert lib.nabla_attn_bwd_workspace_size(1, 12, L, 64) == want
+    assert lib.nabla_attn_bwd_workspace_size(1, 1, 1000, 64) == 0
+    assert lib.nabla_attn_bwd_workspace_size(1, 0, 1024, 64) == 0
+
+
+def attn_bwd(lib, **kw):
+    a = dict(q=A, k=B_, v=C, o=D_, dout=E, lse=F_, dq=G, dk=H_, dv=I_, batch=1, heads=2, L=1024, d=64,
+             N=64, cnt=J_, idx=K_, scale=0.0, dt=NABLA_BF16, ws=M_, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.block_sparse_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                                     a["dv"], a["batch"], a["heads"], a["L"], a["d"], a["N"], a["cnt"],
+                                     a["idx"], a["scale"], a["dt"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NABLA_E_INVAL),
+    (dict(dout=None), NABLA_E_INVAL),
+    (dict(lse=None), NABLA_E_INVAL),
+    (dict(dk=None), NABLA_E_INVAL),
+    (dict(lse=ctypes.c_void_p(0x100008)), NABLA_E_INVAL),
+    (dict(dq=A), NABLA_E_INVAL),            # output aliases q
+    (dict(dv=E), NABLA_E_INVAL),            # output aliases dout
+    (dict(dk=G), NABLA_E_INVAL),            # dk == dq
+    (dict(L=1000), NABLA_E_INVAL),
+    (dict(scale=float("inf")), NABLA_E_INVAL),
+    (dict(dt=4), NABLA_E_INVAL),
+    (dict(N=32), NABLA_E_UNSUPPORTED),
+    (dict(d=32), NABLA_E_UNSUPPORTED),
+    (dict(L=64 * 2049), NABLA_E_UNSUPPORTED),
+    (dict(ws=None), NABLA_E_WORKSPACE),
+    (dict(ws_bytes=1000), NABLA_E_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100010)), NABLA_E_INVAL),
+])
+def test_attn_bwd_validation(lib, kw, status):
+    assert attn_bwd(lib, **kw) == status
+    assert lib.nabla_last_error().decode().startswith("block_sparse_attn_bwd")
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 1024, 64)
