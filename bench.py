@@ -12,6 +12,7 @@ GB/s against HBM peak ride along, with the oracle timed on the host beside it.
     python bench.py [--steps K] [--warmup W] [--config 1] [--no-cpu]
     python bench.py --no-cpu --loop-seconds 12      # steady load for power / clock readings
     python bench.py --gemm-reference                # dense bf16 GEMM of the vendor library
+    python bench.py --backward --no-cpu             # the gradient of the attention step
 """
 from __future__ import annotations
 
@@ -37,12 +38,17 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_blockmean_amd", "csrc", "attn_bf16.hip")
+ATTN_TILE = os.path.join(ROOT, "block_sparse_attention_blockmean_amd", "csrc", "attn_tile.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.txt")
 
 
 def kernel_source_hash() -> str:
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernel's sources (the kernel file and the tile header)."""
+    h = hashlib.sha256()
+    for path in (ATTN_SRC, ATTN_TILE):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -102,6 +108,66 @@ def cpu_baseline(cfg, q, k, v, kept_flops_total, budget_s=15.0):
     }
 
 
+def bench_backward(args, cfg, qd, kd, vd) -> int:
+    """Gradient of the attention step on the same workload: the mask and the forward
+    (with its log-sum-exp) run once untimed; then K calls of block_sparse_attn_bwd (row
+    dots, transposed lists, start orders, the dQ sweep and the dK/dV sweep), each
+    bracketed by HIP events on the launch stream."""
+    T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
+    qf, kf, vf = (nab.reorder(t, T, H, W, P) for t in (qd, kd, vd))
+    cnt, idx, sched = nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True)
+    o, lse = nab.attn_fwd(qf, kf, vf, cnt, idx, N, schedule=sched, with_lse=True)
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    dout = torch.randn(qf.shape, device="cuda", generator=g).to(qf.dtype)
+    ws = torch.empty(nab.attn_bwd_workspace_size(cfg.B, cfg.heads, cfg.L, N), dtype=torch.uint8,
+                     device="cuda")
+    dq, dk, dv = (torch.empty_like(qf) for _ in range(3))
+
+    def call():
+        nab.attn_bwd(qf, kf, vf, o, dout, lse, cnt, idx, N, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    kept = int(cnt.sum().item())
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    alg = kept * 10.0 * N * N * cfg.d          # five products of 2 N^2 d per kept tile
+    exe = kept * 14.0 * N * N * cfg.d          # seven: S and dP are formed in both sweeps
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    rec = {
+        "metric": "block-sparse attn backward (dQ, dK, dV) kept-tile TFLOP/s",
+        "value": round(alg / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": f"synthetic ({GENERATOR_VERSION}), dO ~ N(0, 1) seeded",
+        "config": {"workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "L": cfg.L,
+                   "blocks_per_head": cfg.nb, "thr": cfg.thr},
+        "ms_bwd": round(ms, 4),
+        "kept_fraction": round(kept / (cfg.BH * cfg.nb * cfg.nb), 5),
+        "flop_convention": "algorithmic 10 N^2 d per kept tile (5 products); executed 14 N^2 d",
+        "executed_tflops": round(exe / (ms * 1e-3) / 1e12, 2),
+        "executed_frac_of_peak": round(exe / (ms * 1e-3) / 1e12 / peak, 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +180,9 @@ def main(argv=None):
     ap.add_argument("--loop-seconds", type=float, default=0.0,
                     help="after the warm-up, repeat the step for this long (a progress line per "
                          "second, no JSON line): a steady load for power and clock readings")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the gradient of the attention step (block_sparse_attn_bwd) instead of "
+                         "the forward path; prints its own JSON line")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="time only a dense 8192^3 bf16 GEMM of the vendor library (torch.matmul) "
                          "for --loop-seconds (default 10): the rate a plain GEMM sustains on this "
@@ -206,6 +275,9 @@ def main(argv=None):
         nab.reorder(of, T, H, W, P, inverse=True, out=od)
         if ev:
             ev[4].record()
+
+    if args.backward:
+        return bench_backward(args, cfg, qd, kd, vd)
 
     for _ in range(args.warmup):
         step()
