@@ -302,10 +302,13 @@ void bwd_dq_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 //     dP = dO V^T      A = dO rows (LDS),  B = V rows (LDS, resident)
 //     P = exp2(S scale log2(e) - lse log2(e)),  dS = P (dP - D)   (per query row)
 //     dV^T += dO^T P   A = dO^T through the transposing LDS read, B = P (VGPRs)
+// then, after a barrier that frees the dO tile for the next query block's copy,
 //     dK^T += Q^T dS   A = Q^T through the transposing LDS read, B = dS (VGPRs)
-// K and V stay in LDS for the whole sweep; each query block's Q and dO tiles are
-// copied in after every wave is done with the previous ones.  The two query halves
-// are summed through LDS at the end.
+// K and V stay in LDS for the whole sweep.  Q is double-buffered (the next query
+// block's Q is copied at the top of an iteration); dO has one buffer, refilled once
+// every wave has formed its dV.  16 + 16 + 2 x 16 + 16 KiB = 80 KiB of LDS at d = 128:
+// two workgroups fill a CU's 160 KiB.  The two query halves are summed through LDS at
+// the end.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -320,7 +323,8 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     constexpr uint32_t kTileBytes = kBlk * D * 2;
     __shared__ __attribute__((aligned(1024))) char k_t[G::kBytes];
     __shared__ __attribute__((aligned(1024))) char v_t[G::kBytes];
-    __shared__ __attribute__((aligned(1024))) char q_t[G::kBytes];
+    __shared__ __attribute__((aligned(1024))) char q_t0[G::kBytes];
+    __shared__ __attribute__((aligned(1024))) char q_t1[G::kBytes];
     __shared__ __attribute__((aligned(1024))) char do_t[G::kBytes];
 
     const int logical = logical_item(schedule);
@@ -352,7 +356,7 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     copy_tile<D>(k_rsrc, kb * kTileBytes, k_t, wave, lane_copy);
     copy_tile<D>(v_rsrc, kb * kTileBytes, v_t, wave, lane_copy);
     if (count > 0) {
-        copy_tile<D>(q_rsrc, list[0] * kTileBytes, q_t, wave, lane_copy);
+        copy_tile<D>(q_rsrc, list[0] * kTileBytes, q_t0, wave, lane_copy);
         copy_tile<D>(do_rsrc, list[0] * kTileBytes, do_t, wave, lane_copy);
     }
 
@@ -365,15 +369,16 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
             dkacc[t][r] = 0.f;
         }
 
-    // A rows (queries) of the Q / dO tiles and B rows (keys) of the K / V tiles
+    // A rows (queries) of the Q / dO tiles and B rows (keys) of the K / V tiles.  The
+    // two rows differ by a multiple of 32, over which the row swizzle repeats, so the B
+    // offsets are the A offsets plus one wave-uniform constant.
     const int arow = 32 * qhalf + c32;
     const int brow = 32 * khalf + c32;
-    int a_off[KS], b_off[KS];
+    const int b_shift = (brow - arow) * G::kRowBytes;
+    static_assert(32 % (G::kRowsPerLine * G::kChunks) == 0, "row swizzle period must divide 32");
+    int a_off[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        a_off[s] = arow * G::kRowBytes + (((2 * s + h) ^ G::k_swz(arow)) * 16);
-        b_off[s] = brow * G::kRowBytes + (((2 * s + h) ^ G::k_swz(brow)) * 16);
-    }
+    for (int s = 0; s < KS; ++s) a_off[s] = arow * G::kRowBytes + (((2 * s + h) ^ G::k_swz(arow)) * 16);
     // dO^T / Q^T operand of d tile t, k-step u, half p: rows 32 qh + 16 u + 8 p + 4 h + j16 / 4
     // (the row swizzle repeats every 16 rows: u is a constant offset, p is not)
     int t_off[DT][2];
@@ -388,35 +393,33 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     // the lane's 16 query rows of a block: 32 qh + 8 g + 4 h + c for accumulator entry 4 g + c
     const size_t stat_off = (size_t)bh * L + 32 * qhalf + 4 * h;
 
-    for (int i = 0; i < count; ++i) {
+    auto step = [&](auto par, int i) {
+        constexpr int PAR = decltype(par)::value;
+        const char* qbuf = PAR ? q_t1 : q_t0;
+        char* q_next = PAR ? q_t0 : q_t1;
         const int qblk = list[i];
-        // Q and dO of query block qblk have landed
+        // Q and dO of query block qblk have landed; every wave is done with the previous
+        // block, so the other Q buffer takes the next block's Q now
         wait_vmcnt<0>();
         lds_barrier();
+        const bool more = i + 1 < count;
+        const uint32_t nxt = more ? list[i + 1] * kTileBytes : 0u;
+        if (more) copy_tile<D>(q_rsrc, nxt, q_next, wave, lane_copy);
         float4 ls[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             ls[g] = *reinterpret_cast<const float4*>(lse + stat_off + (size_t)qblk * kBlk + 8 * g);
 
-        f32x16 sacc, dpacc;
+        // S, then P (the log-sum-exp and S die here), then dV, then dP and dS
+        f32x16 sacc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            sacc[r] = 0.f;
-            dpacc[r] = 0.f;
-        }
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(q_t + a_off[s]);
-            const bf16x8 b = *reinterpret_cast<const bf16x8*>(k_t + b_off[s]);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(qbuf + a_off[s]);
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(k_t + b_shift + a_off[s]);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, sacc, 0, 0, 0);
         }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(do_t + a_off[s]);
-            const bf16x8 b = *reinterpret_cast<const bf16x8*>(v_t + b_off[s]);
-            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dpacc, 0, 0, 0);
-        }
-
         float p[16];
         bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -424,12 +427,6 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
             const float l2 = ls[r / 4][r % 4] * kLog2e;
             p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2e, -l2));
             pb[r / 8][r % 8] = (__bf16)p[r];
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 dr = *reinterpret_cast<const float4*>(drow + stat_off + (size_t)qblk * kBlk + 8 * g);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) dsb[g / 2][4 * (g % 2) + c] = (__bf16)(p[4 * g + c] * (dpacc[4 * g + c] - dr[c]));
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -442,31 +439,49 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
                 const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
                 dvacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], dvacc[t], 0, 0, 0);
             }
+        f32x16 dpacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dpacc[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(do_t + a_off[s]);
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(v_t + b_shift + a_off[s]);
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dpacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 dr = *reinterpret_cast<const float4*>(drow + stat_off + (size_t)qblk * kBlk + 8 * g);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dsb[g / 2][4 * (g % 2) + c] = (__bf16)(p[4 * g + c] * (dpacc[4 * g + c] - dr[c]));
+        }
+        // every wave has read this dO: its buffer takes the next block's dO
+        lds_barrier();
+        if (more) copy_tile<D>(do_rsrc, nxt, do_t, wave, lane_copy);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
                 const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(q_t + t_off[t][0] + (16 * u) * G::kRowBytes));
+                    (lds_s16x4*)(qbuf + t_off[t][0] + (16 * u) * G::kRowBytes));
                 const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(q_t + t_off[t][1] + (16 * u) * G::kRowBytes));
+                    (lds_s16x4*)(qbuf + t_off[t][1] + (16 * u) * G::kRowBytes));
                 const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
                 dkacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[u], dkacc[t], 0, 0, 0);
             }
-        // every wave is done with this Q and dO: copy the next query block's
-        lds_barrier();
-        if (i + 1 < count) {
-            const uint32_t nxt = list[i + 1] * kTileBytes;
-            copy_tile<D>(q_rsrc, nxt, q_t, wave, lane_copy);
-            copy_tile<D>(do_rsrc, nxt, do_t, wave, lane_copy);
-        }
+    };
+
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    for (int i = 0; i < count; i += 2) {
+        step(P0{}, i);
+        if (i + 1 < count) step(P1{}, i + 1);
     }
 
     // sum the query halves: wave (kh, 1) hands its partial dV^T, dK^T to wave (kh, 0)
     wait_vmcnt<0>();
     lds_barrier();
-    float* xv = reinterpret_cast<float*>(khalf ? q_t : k_t);
-    float* xk = reinterpret_cast<float*>(khalf ? do_t : v_t);
+    float* xv = reinterpret_cast<float*>(khalf ? q_t0 : k_t);
+    float* xk = reinterpret_cast<float*>(khalf ? q_t1 : v_t);
     static_assert(DT * 16 * 64 * 4 <= G::kBytes, "partial dK / dV exceeds one tile buffer");
     if (qhalf == 1) {
 #pragma unroll
