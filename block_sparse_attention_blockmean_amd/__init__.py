@@ -7,11 +7,12 @@ device tensors, pass their pointers and the current HIP stream to the C ABI in
 ``python -m block_sparse_attention_blockmean_amd.build``.
 """
 from ._binding import (
-    EXPORTS, LIB_PATH, NablaError, StaWindow, attn_bwd, attn_bwd_workspace_size, attn_fwd, build_mask,
-    build_mask_workspace_size, load_library, reorder,
+    EXPORTS, LIB_PATH, NablaError, StaWindow, attn_bwd, attn_bwd_workspace_size, attn_fwd,
+    attn_fwd_raster, build_mask, build_mask_workspace_size, load_library, reorder,
 )
 
 __all__ = [
     "EXPORTS", "LIB_PATH", "NablaError", "StaWindow", "attn_bwd", "attn_bwd_workspace_size",
-    "attn_fwd", "build_mask", "build_mask_workspace_size", "load_library", "reorder",
+    "attn_fwd", "attn_fwd_raster", "build_mask", "build_mask_workspace_size", "load_library",
+    "reorder",
 ]

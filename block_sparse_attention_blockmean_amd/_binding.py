@@ -23,7 +23,9 @@ EXPORTS = (
     "nabla_reorder",
     "nabla_build_mask_workspace_size",
     "nabla_build_mask",
+    "nabla_build_mask_raster",
     "block_sparse_attn_fwd",
+    "block_sparse_attn_fwd_raster",
     "block_sparse_attn_fwd_lse",
     "nabla_attn_bwd_workspace_size",
     "block_sparse_attn_bwd",
@@ -61,6 +63,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_build_mask.argtypes = [vp, vp, i, i, i, i, i, i, i, i, f, ctypes.POINTER(StaWindow),
                                      f, i, vp, vp, vp, vp, vp, sz, vp]
     lib.nabla_build_mask.restype = i
+    lib.nabla_build_mask_raster.argtypes = lib.nabla_build_mask.argtypes
+    lib.nabla_build_mask_raster.restype = i
+    lib.block_sparse_attn_fwd_raster.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, f, i, vp]
+    lib.block_sparse_attn_fwd_raster.restype = i
     lib.block_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, f, i, vp]
     lib.block_sparse_attn_fwd.restype = i
     lib.block_sparse_attn_fwd_lse.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, f, i, vp, vp]
@@ -131,8 +137,9 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
                scale: Optional[float] = None, with_bitmap: bool = False,
                with_schedule: bool = False, workspace: Optional[torch.Tensor] = None,
                kv_count: Optional[torch.Tensor] = None, kv_index: Optional[torch.Tensor] = None,
-               schedule: Optional[torch.Tensor] = None):
-    """NABLA block mask of fractal-ordered Q, K.
+               schedule: Optional[torch.Tensor] = None, raster: bool = False):
+    """NABLA block mask of fractal-ordered Q, K (``raster=True``: Q, K in raster order,
+    the fractal flattening applied in the addressing; needs N == P*P).
 
     Returns (kv_count, kv_index), plus the bitmap and/or the longest-first
     schedule when asked for (in that order)."""
@@ -155,7 +162,8 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
     if workspace is None:
         workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
     win = None if sta is None else ctypes.byref(StaWindow(*sta))
-    _check(lib.nabla_build_mask(
+    entry = lib.nabla_build_mask_raster if raster else lib.nabla_build_mask
+    _check(entry(
         _dev(q, "q"), _dev(k, "k"), B, NH, T, H, W, d, P, N, float(thr), win,
         float(scale) if scale is not None else 0.0, _dtype_code(q),
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
@@ -224,6 +232,32 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.
         out = torch.empty_like(q)
     _check(lib.block_sparse_attn_fwd(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, NH, L, d, N,
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+        _dev(schedule, "schedule") if schedule is not None else None,
+        float(scale) if scale is not None else 0.0, _dtype_code(q), _stream()), lib)
+    return out
+
+
+def attn_fwd_raster(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.Tensor,
+                    kv_index: torch.Tensor, T: int, H: int, W: int, P: int, N: int = 64,
+                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    schedule: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-sparse attention of raster-ordered Q, K, V (output in raster order) under
+    lists that number blocks in fractal order (``build_mask(..., raster=True)``)."""
+    lib = load_library()
+    B, NH, L, d = q.shape
+    if L != T * H * W:
+        raise ValueError(f"L={L} does not match T*H*W={T * H * W}")
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    _check_lists(q, kv_count, kv_index, N)
+    if schedule is not None and (schedule.dtype != torch.int32 or schedule.numel() != B * NH * (L // N)):
+        raise ValueError("schedule must hold batch*heads*nb int32 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.block_sparse_attn_fwd_raster(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, NH, T, H, W, d, P, N,
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
         _dev(schedule, "schedule") if schedule is not None else None,
         float(scale) if scale is not None else 0.0, _dtype_code(q), _stream()), lib)

@@ -38,17 +38,17 @@ namespace {
 
 using namespace attn;
 
-template <int D>
+template <int D, bool RASTER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                           const __bf16* __restrict__ v, __bf16* __restrict__ o, int L, int nb,
                           const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_index,
-                          const int32_t* __restrict__ schedule, float scale_log2e,
+                          const int32_t* __restrict__ schedule, RasterGrid grid, float scale_log2e,
                           float* __restrict__ lse) {
     using G = Tile<D>;
     constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;        // 32-row d tiles of O^T
-    constexpr uint32_t kTileBytes = kBlk * D * 2;
+    const uint32_t stride = copy_stride<RASTER>(grid);   // between a tile's 4 KiB copies
     __shared__ __attribute__((aligned(1024))) char k_lds0[G::kBytes];
     __shared__ __attribute__((aligned(1024))) char k_lds1[G::kBytes];
     __shared__ __attribute__((aligned(1024))) char v_lds0[G::kBytes];
@@ -83,19 +83,21 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         __builtin_amdgcn_make_buffer_rsrc((void*)(k + head_off), 0, head_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t v_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(v + head_off), 0, head_bytes, kBufferFlags);
-    const uint32_t k_copy = copy_lane_offset<D, false>(wave, lane);
-    const uint32_t v_copy = copy_lane_offset<D, true>(wave, lane);
+    const uint32_t k_copy = copy_lane_offset_in<D, false, RASTER>(grid, wave, lane);
+    const uint32_t v_copy = copy_lane_offset_in<D, true, RASTER>(grid, wave, lane);
 
     const int count = kv_count[(size_t)bh * nb + qb];
     const int32_t* list = kv_index + ((size_t)bh * nb + qb) * nb;
 
     if (count > 0) {
-        copy_tile<D>(k_rsrc, list[0] * kTileBytes, k_lds0, wave, k_copy);
-        copy_tile<D>(v_rsrc, list[0] * kTileBytes, v_lds0, wave, v_copy);
+        const uint32_t first = block_row<RASTER>(grid, list[0]) * G::kRowBytes;
+        copy_tile<D>(k_rsrc, first, k_lds0, wave, k_copy, stride);
+        copy_tile<D>(v_rsrc, first, v_lds0, wave, v_copy, stride);
     }
 
     // Q operand: lane holds Q[row][16 s + 8 h .. + 7] for s = 0..KS-1.
-    const int qrow = qb * kBlk + 32 * qhalf + c32;
+    // the lane's query row in the head (fractal or raster order)
+    const uint32_t qrow = block_row<RASTER>(grid, qb) + row_in_block<RASTER>(grid, 32 * qhalf + c32);
     bf16x8 qreg[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
@@ -138,7 +140,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         // wave sees them and is done with the buffers of tile i - 1, refilled now
         wait_vmcnt<0>();
         lds_barrier();
-        const uint32_t nxt = next_tile * kTileBytes;
+        const uint32_t nxt = block_row<RASTER>(grid, next_tile) * G::kRowBytes;
         char* k_dst = PAR ? k_lds0 : k_lds1;
         char* v_dst = PAR ? v_lds0 : v_lds1;
 
@@ -158,7 +160,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
             constexpr int kEvery = KS / G::kCopiesPerWave;
             if (s % kEvery == 0)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(k_dst + (4 * (s / kEvery) + wave) * 1024), 16,
-                                                         k_copy, nxt + (s / kEvery) * 4096, 0, 0);
+                                                         k_copy, nxt + (s / kEvery) * stride, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -204,7 +206,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
                 const int m = u * DT + t;
                 if (m % kEveryV == 0)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)(v_dst + (4 * (m / kEveryV) + wave) * 1024), 16,
-                                                             v_copy, nxt + (m / kEveryV) * 4096, 0, 0);
+                                                             v_copy, nxt + (m / kEveryV) * stride, 0, 0);
                 const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s16x4*)(vbuf + v_off[t] + (16 * u) * G::kRowBytes));
                 const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -276,19 +278,27 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     }
 }
 
-template <int D>
+template <int D, bool RASTER>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
     const float scale_log2e = a.scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(a.BH * a.nb), dim3(kThreads), 0, s,
+    RasterGrid grid{};
+    if (RASTER) {
+        grid.W = (uint32_t)a.W;
+        grid.HW = (uint32_t)(a.H * a.W);
+        grid.nHW = FastDiv((uint32_t)((a.H / 8) * (a.W / 8)));
+        grid.nW = FastDiv((uint32_t)(a.W / 8));
+    }
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, RASTER>), dim3(a.BH * a.nb), dim3(kThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
-                       a.L, a.nb, a.kv_count, a.kv_index, a.schedule, scale_log2e, a.lse);
+                       a.L, a.nb, a.kv_count, a.kv_index, a.schedule, grid, scale_log2e, a.lse);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-    return a.d == 128 ? launch<128>(a, s) : launch<64>(a, s);
+    if (a.raster) return a.d == 128 ? launch<128, true>(a, s) : launch<64, true>(a, s);
+    return a.d == 128 ? launch<128, false>(a, s) : launch<64, false>(a, s);
 }
 
 }  // namespace nabla

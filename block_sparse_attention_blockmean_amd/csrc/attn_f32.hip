@@ -6,6 +6,7 @@
 // each scoring 16 of the 64 keys of a tile and accumulating d/4 output columns.
 #include <math.h>
 
+#include "attn_tile.h"
 #include "nabla_internal.h"
 
 namespace nabla {
@@ -14,12 +15,16 @@ namespace {
 constexpr int kBlk = 64;
 constexpr int kThreads = 256;
 
-template <int D>
+using attn::RasterGrid;
+using attn::block_row;
+using attn::row_in_block;
+
+template <int D, bool RASTER>
 __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, int L, int nb, const int32_t* __restrict__ kv_count,
     const int32_t* __restrict__ kv_index, const int32_t* __restrict__ schedule,
-    float scale, float* __restrict__ lse) {
+    RasterGrid grid, float scale, float* __restrict__ lse) {
     constexpr int LD = D + 1;
     extern __shared__ float lds[];
     float* q_s = lds;                   // [64][LD]
@@ -35,8 +40,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     const int part = tid & 3;
     const size_t head_off = (size_t)bh * L * D;
 
+    const uint32_t qbase = block_row<RASTER>(grid, qb);
     for (int i = tid; i < kBlk * D; i += kThreads)
-        q_s[(i / D) * LD + i % D] = q[head_off + (size_t)qb * kBlk * D + i];
+        q_s[(i / D) * LD + i % D] = q[head_off + (size_t)(qbase + row_in_block<RASTER>(grid, i / D)) * D + i % D];
 
     float m_run = -INFINITY, l_run = 0.f;
     float acc[D / 4];
@@ -46,11 +52,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     const int count = kv_count[(size_t)bh * nb + qb];
     const int32_t* list = kv_index + ((size_t)bh * nb + qb) * nb;
     for (int it = 0; it < count; ++it) {
-        const int j = list[it];
+        const uint32_t jbase = block_row<RASTER>(grid, list[it]);
         __syncthreads();
         for (int i = tid; i < kBlk * D; i += kThreads) {
-            k_s[(i / D) * LD + i % D] = k[head_off + (size_t)j * kBlk * D + i];
-            v_s[(i / D) * LD + i % D] = v[head_off + (size_t)j * kBlk * D + i];
+            const size_t src = head_off + (size_t)(jbase + row_in_block<RASTER>(grid, i / D)) * D + i % D;
+            k_s[(i / D) * LD + i % D] = k[src];
+            v_s[(i / D) * LD + i % D] = v[src];
         }
         __syncthreads();
         float s[16];
@@ -88,29 +95,37 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     float l_tot = l_run + __shfl_xor(l_run, 1);
     l_tot += __shfl_xor(l_tot, 2);
     const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-    if (lse && part == 0)
-        lse[(size_t)bh * L + (size_t)qb * kBlk + row] = l_tot > 0.f ? m_run + logf(l_tot) : -INFINITY;
-    float* orow = o + head_off + ((size_t)qb * kBlk + row) * D;
+    const uint32_t orow_idx = qbase + row_in_block<RASTER>(grid, row);
+    if (lse && part == 0) lse[(size_t)bh * L + orow_idx] = l_tot > 0.f ? m_run + logf(l_tot) : -INFINITY;
+    float* orow = o + head_off + (size_t)orow_idx * D;
 #pragma unroll
     for (int c = 0; c < D / 4; ++c) orow[part + 4 * c] = acc[c] * inv;
 }
 
-template <int D>
+template <int D, bool RASTER>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
     const size_t lds = (3 * kBlk * (D + 1) + kBlk * 65) * sizeof(float);
     static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = set_max_dynamic_lds((const void*)attn_fwd_f32_kernel<D>, (int)lds, lds_set);
+    hipError_t e = set_max_dynamic_lds((const void*)attn_fwd_f32_kernel<D, RASTER>, (int)lds, lds_set);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(a.BH * a.nb), dim3(kThreads), lds, s,
+    RasterGrid grid{};
+    if (RASTER) {
+        grid.W = (uint32_t)a.W;
+        grid.HW = (uint32_t)(a.H * a.W);
+        grid.nHW = FastDiv((uint32_t)((a.H / 8) * (a.W / 8)));
+        grid.nW = FastDiv((uint32_t)(a.W / 8));
+    }
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, RASTER>), dim3(a.BH * a.nb), dim3(kThreads), lds, s,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.L,
-                       a.nb, a.kv_count, a.kv_index, a.schedule, a.scale, a.lse);
+                       a.nb, a.kv_count, a.kv_index, a.schedule, grid, a.scale, a.lse);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
-    return a.d == 128 ? launch<128>(a, s) : launch<64>(a, s);
+    if (a.raster) return a.d == 128 ? launch<128, true>(a, s) : launch<64, true>(a, s);
+    return a.d == 128 ? launch<128, false>(a, s) : launch<64, false>(a, s);
 }
 
 }  // namespace nabla

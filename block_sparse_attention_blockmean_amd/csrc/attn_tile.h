@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "nabla_internal.h"
+
 namespace nabla {
 namespace attn {
 
@@ -53,17 +55,59 @@ __device__ inline uint32_t copy_lane_offset(int wave, int lane) {
     return (uint32_t)(row * G::kRowBytes + chunk * 16);
 }
 
+// Where the 64 tokens of block b sit in a [L, D] head.
+//   Fractal order: block b is rows [64 b, 64 b + 64).
+//   Raster order with 8 x 8 patches (one patch per block): block b is patch
+//   (t, ph, pw) = (b / nHW, (b % nHW) / nW, b % nW), and its row r is raster token
+//   t HW + (8 ph + r / 8) W + 8 pw + r % 8 - eight runs of eight consecutive tokens.
+struct RasterGrid {
+    uint32_t W, HW;       // tokens per raster row, per frame
+    FastDiv nHW, nW;      // patches per frame, per patch row
+};
+
+template <bool RASTER>
+__device__ inline uint32_t block_row(const RasterGrid& g, uint32_t b) {
+    if (!RASTER) return b * kBlk;
+    uint32_t t, rem, ph, pw;
+    g.nHW.divmod(b, t, rem);
+    g.nW.divmod(rem, ph, pw);
+    return t * g.HW + 8 * (ph * g.W + pw);
+}
+
+template <bool RASTER>
+__device__ inline uint32_t row_in_block(const RasterGrid& g, int r) {
+    return RASTER ? (uint32_t)((r >> 3) * g.W + (r & 7)) : (uint32_t)r;
+}
+
+// Byte distance in the head between copy u and copy u + 1 of a tile: 4 KiB of rows,
+// which in raster order is 4096 / (2 D) / 8 patch rows, 512 W bytes for any D.
+template <bool RASTER>
+__device__ inline uint32_t copy_stride(const RasterGrid& g) {
+    return RASTER ? 512u * g.W : 4096u;
+}
+
+// copy_lane_offset for either token order (the swizzle is that of the LDS row).
+template <int D, bool kIsV, bool RASTER>
+__device__ inline uint32_t copy_lane_offset_in(const RasterGrid& g, int wave, int lane) {
+    using G = Tile<D>;
+    const int o = wave * 1024 + lane * 16;
+    const int row = o / G::kRowBytes;
+    const int slot = (o % G::kRowBytes) / 16;
+    const int chunk = slot ^ (kIsV ? G::v_swz(row) : G::k_swz(row));
+    return row_in_block<RASTER>(g, row) * G::kRowBytes + chunk * 16;
+}
+
 // The wave's share of one tile copy (buffer form of the LDS DMA: uniform tile offset in
 // soffset, 32-bit lane offset, uniform LDS destination in M0; offsets past the buffer
-// read zeros).
+// read zeros).  `stride` is the byte distance between consecutive 4 KiB copies.
 template <int D>
 __device__ inline void copy_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t tile_byte, char* lds_tile, int wave,
-                                 uint32_t lane_off) {
+                                 uint32_t lane_off, uint32_t stride = 4096) {
     using G = Tile<D>;
 #pragma unroll
     for (int u = 0; u < G::kCopiesPerWave; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + (4 * u + wave) * 1024), 16,
-                                                 lane_off, tile_byte + u * 4096, 0, 0);
+                                                 lane_off, tile_byte + u * stride, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) through the builtin, which the compiler's own wait accounting

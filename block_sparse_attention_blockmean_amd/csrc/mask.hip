@@ -6,6 +6,7 @@
 //                      STA OR, and compaction of each row into an ascending kept list.
 #include <math.h>
 
+#include "attn_tile.h"
 #include "nabla_internal.h"
 
 namespace nabla {
@@ -44,11 +45,12 @@ struct Elem<float> {
     }
 };
 
-template <typename T, int D, int N>
+template <typename T, int D, int N, bool RASTER>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
                                                     const T* __restrict__ k,
                                                     float* __restrict__ qp,
-                                                    float* __restrict__ kp, int total_blocks) {
+                                                    float* __restrict__ kp, int total_blocks, int nb,
+                                                    int L, attn::RasterGrid grid) {
     constexpr int EPC = Elem<T>::kPerChunk;
     constexpr int CHUNKS = D / EPC;          // 16-byte chunks per token
     constexpr int G = 64 / CHUNKS;           // tokens per load instruction
@@ -58,7 +60,14 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
     if (wave >= 2 * total_blocks) return;
     const bool is_k = wave >= total_blocks;
     const int blk = is_k ? wave - total_blocks : wave;
-    const T* src = (is_k ? k : q) + (size_t)blk * N * D;
+    // the block's first row: fractal order, runs of N rows; raster order, one 8 x 8 patch
+    const T* src;
+    if (RASTER) {
+        const int bh = blk / nb;
+        src = (is_k ? k : q) + ((size_t)bh * L + attn::block_row<true>(grid, blk - bh * nb)) * D;
+    } else {
+        src = (is_k ? k : q) + (size_t)blk * N * D;
+    }
     float* dst = (is_k ? kp : qp) + (size_t)blk * D;
     const int c = lane % CHUNKS;
     const int g = lane / CHUNKS;
@@ -67,7 +76,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
 #pragma unroll
     for (int r = 0; r < ITERS; ++r) {
         raw[r] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(src + (size_t)(r * G + g) * D) + c);
+            reinterpret_cast<const u32x4*>(src + (size_t)attn::row_in_block<RASTER>(grid, r * G + g) * D) + c);
     }
     float acc[EPC];
 #pragma unroll
@@ -422,8 +431,18 @@ template <typename T, int D>
 hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
     const int total = a.BH * a.nb;
     const int waves = 2 * total;
-    hipLaunchKernelGGL((pool_kernel<T, D, 64>), dim3((waves + 3) / 4), dim3(256), 0, s,
-                       (const T*)a.q, (const T*)a.k, a.qp, a.kp, total);
+    attn::RasterGrid grid{};
+    if (a.raster) {
+        grid.W = (uint32_t)a.W;
+        grid.HW = (uint32_t)(a.H * a.W);
+        grid.nHW = FastDiv((uint32_t)(a.nH * a.nW));
+        grid.nW = FastDiv((uint32_t)a.nW);
+        hipLaunchKernelGGL((pool_kernel<T, D, 64, true>), dim3((waves + 3) / 4), dim3(256), 0, s,
+                           (const T*)a.q, (const T*)a.k, a.qp, a.kp, total, a.nb, a.nb * 64, grid);
+    } else {
+        hipLaunchKernelGGL((pool_kernel<T, D, 64, false>), dim3((waves + 3) / 4), dim3(256), 0, s,
+                           (const T*)a.q, (const T*)a.k, a.qp, a.kp, total, a.nb, a.nb * 64, grid);
+    }
     return hipGetLastError();
 }
 

@@ -84,43 +84,79 @@ size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N
     return ((2 * one) + 255) & ~(size_t)255;
 }
 
+namespace {
+
+nabla_status build_mask_impl(const char* who, int raster, const void* q, const void* k, int batch,
+                             int heads, int T, int H, int W, int d, int P, int N, float thr,
+                             const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                             int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                             int32_t* schedule, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+}  // namespace
+
 nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads, int T, int H,
                               int W, int d, int P, int N, float thr,
                               const nabla_sta_window* sta, float scale, nabla_dtype dtype,
                               int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                               int32_t* schedule, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
-    if (!q || !k || !kv_count || !kv_index) return fail(NABLA_E_INVAL, "nabla_build_mask: null pointer");
+    return build_mask_impl("nabla_build_mask", 0, q, k, batch, heads, T, H, W, d, P, N, thr, sta, scale,
+                           dtype, kv_count, kv_index, bitmap, schedule, workspace, workspace_bytes, stream);
+}
+
+nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, int heads, int T, int H,
+                                     int W, int d, int P, int N, float thr,
+                                     const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                                     int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                                     int32_t* schedule, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+    return build_mask_impl("nabla_build_mask_raster", 1, q, k, batch, heads, T, H, W, d, P, N, thr, sta,
+                           scale, dtype, kv_count, kv_index, bitmap, schedule, workspace, workspace_bytes,
+                           stream);
+}
+
+namespace {
+
+nabla_status build_mask_impl(const char* who, int raster, const void* q, const void* k, int batch,
+                             int heads, int T, int H, int W, int d, int P, int N, float thr,
+                             const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                             int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                             int32_t* schedule, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    if (!q || !k || !kv_count || !kv_index) return fail(NABLA_E_INVAL, "%s: null pointer", who);
     if (!aligned16(q) || !aligned16(k) || ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3) ||
         ((uintptr_t)bitmap & 3) || ((uintptr_t)schedule & 3))
-        return fail(NABLA_E_INVAL, "nabla_build_mask: misaligned pointer");
+        return fail(NABLA_E_INVAL, "%s: misaligned pointer", who);
     if (batch <= 0 || heads <= 0 || T <= 0 || H <= 0 || W <= 0 || d <= 0 || P <= 0 || N <= 0)
-        return fail(NABLA_E_INVAL, "nabla_build_mask: sizes must be positive");
+        return fail(NABLA_E_INVAL, "%s: sizes must be positive", who);
     if (H % P || W % P)
-        return fail(NABLA_E_INVAL, "nabla_build_mask: H=%d and W=%d must be multiples of P=%d", H, W, P);
+        return fail(NABLA_E_INVAL, "%s: H=%d and W=%d must be multiples of P=%d", who, H, W, P);
     const long long L = (long long)T * H * W;
-    if (L % N) return fail(NABLA_E_INVAL, "nabla_build_mask: L=%lld is not a multiple of N=%d", L, N);
-    if (!(thr >= 0.f && thr < 1.f)) return fail(NABLA_E_INVAL, "nabla_build_mask: thr must lie in [0, 1)");
-    if (isnan(scale) || isinf(scale)) return fail(NABLA_E_INVAL, "nabla_build_mask: scale must be finite");
-    if (!valid_dtype(dtype)) return fail(NABLA_E_INVAL, "nabla_build_mask: unknown dtype %d", (int)dtype);
+    if (L % N) return fail(NABLA_E_INVAL, "%s: L=%lld is not a multiple of N=%d", who, L, N);
+    if (!(thr >= 0.f && thr < 1.f)) return fail(NABLA_E_INVAL, "%s: thr must lie in [0, 1)", who);
+    if (isnan(scale) || isinf(scale)) return fail(NABLA_E_INVAL, "%s: scale must be finite", who);
+    if (!valid_dtype(dtype)) return fail(NABLA_E_INVAL, "%s: unknown dtype %d", who, (int)dtype);
     if (sta) {
         if (sta->wt < 1 || sta->wh < 1 || sta->ww < 1 || !(sta->wt & 1) || !(sta->wh & 1) || !(sta->ww & 1))
-            return fail(NABLA_E_INVAL, "nabla_build_mask: STA window sizes must be odd and >= 1");
+            return fail(NABLA_E_INVAL, "%s: STA window sizes must be odd and >= 1", who);
         if (N != P * P)
-            return fail(NABLA_E_INVAL, "nabla_build_mask: an STA tile is one P x P patch, so N must equal P*P");
+            return fail(NABLA_E_INVAL, "%s: an STA tile is one P x P patch, so N must equal P*P", who);
     }
-    if (N != 64) return fail(NABLA_E_UNSUPPORTED, "nabla_build_mask: only N = 64 is implemented");
-    if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "nabla_build_mask: d must be 64 or 128");
+    if (raster && N != P * P)
+        return fail(NABLA_E_INVAL, "%s: raster order needs one P x P patch per block (N == P*P)", who);
+    if (N != 64) return fail(NABLA_E_UNSUPPORTED, "%s: only N = 64 is implemented", who);
+    if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "%s: d must be 64 or 128", who);
     const long long nb = L / N;
     if (nb > NABLA_MAX_BLOCKS)
-        return fail(NABLA_E_UNSUPPORTED, "nabla_build_mask: %lld blocks per head exceed %d", nb, NABLA_MAX_BLOCKS);
+        return fail(NABLA_E_UNSUPPORTED, "%s: %lld blocks per head exceed %d", who, nb, NABLA_MAX_BLOCKS);
     if ((long long)batch * heads > 65535 || L * d >= kMaxHeadElems)
-        return fail(NABLA_E_UNSUPPORTED, "nabla_build_mask: tensor too large");
+        return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
     const size_t need = nabla_build_mask_workspace_size(batch, heads, (int)L, d, N);
     if (!workspace || workspace_bytes < need)
-        return fail(NABLA_E_WORKSPACE, "nabla_build_mask: workspace of %zu bytes needed, %zu given", need,
+        return fail(NABLA_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
                     workspace ? workspace_bytes : (size_t)0);
-    if (((uintptr_t)workspace & 15)) return fail(NABLA_E_INVAL, "nabla_build_mask: misaligned workspace");
+    if (((uintptr_t)workspace & 15)) return fail(NABLA_E_INVAL, "%s: misaligned workspace", who);
 
     nabla::MaskArgs a{};
     a.q = q;
@@ -145,15 +181,20 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
     a.qp = (float*)workspace;
     a.kp = a.qp + (size_t)a.BH * nb * d;
     a.bf16 = dtype == NABLA_BF16;
-    return hip_status(nabla::launch_build_mask(a, stream), "nabla_build_mask");
+    a.raster = raster;
+    a.H = H;
+    a.W = W;
+    return hip_status(nabla::launch_build_mask(a, stream), who);
 }
+
+}  // namespace
 
 namespace {
 
 nabla_status attn_fwd_impl(const char* who, const void* q, const void* k, const void* v, void* o,
                            int batch, int heads, int L, int d, int N, const int32_t* kv_count,
                            const int32_t* kv_index, const int32_t* schedule, float scale,
-                           nabla_dtype dtype, float* lse, hipStream_t stream);
+                           nabla_dtype dtype, float* lse, int raster, int H, int W, hipStream_t stream);
 
 }  // namespace
 
@@ -163,7 +204,25 @@ nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, 
                                    const int32_t* schedule, float scale, nabla_dtype dtype,
                                    hipStream_t stream) {
     return attn_fwd_impl("block_sparse_attn_fwd", q, k, v, o, batch, heads, L, d, N, kv_count, kv_index,
-                         schedule, scale, dtype, nullptr, stream);
+                         schedule, scale, dtype, nullptr, 0, 0, 0, stream);
+}
+
+nabla_status block_sparse_attn_fwd_raster(const void* q, const void* k, const void* v, void* o,
+                                          int batch, int heads, int T, int H, int W, int d, int P, int N,
+                                          const int32_t* kv_count, const int32_t* kv_index,
+                                          const int32_t* schedule, float scale, nabla_dtype dtype,
+                                          hipStream_t stream) {
+    const char* who = "block_sparse_attn_fwd_raster";
+    if (T <= 0 || H <= 0 || W <= 0 || P <= 0 || N <= 0)
+        return fail(NABLA_E_INVAL, "%s: sizes must be positive", who);
+    if (H % P || W % P)
+        return fail(NABLA_E_INVAL, "%s: H=%d and W=%d must be multiples of P=%d", who, H, W, P);
+    if (N != P * P)
+        return fail(NABLA_E_INVAL, "%s: raster order needs one P x P patch per block (N == P*P)", who);
+    const long long L = (long long)T * H * W;
+    if (L >= (1ll << 31)) return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
+    return attn_fwd_impl(who, q, k, v, o, batch, heads, (int)L, d, N, kv_count, kv_index, schedule, scale,
+                         dtype, nullptr, 1, H, W, stream);
 }
 
 nabla_status block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v, void* o,
@@ -174,7 +233,7 @@ nabla_status block_sparse_attn_fwd_lse(const void* q, const void* k, const void*
     if (!lse) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd_lse: null lse");
     if (!aligned16(lse)) return fail(NABLA_E_INVAL, "block_sparse_attn_fwd_lse: misaligned lse");
     return attn_fwd_impl("block_sparse_attn_fwd_lse", q, k, v, o, batch, heads, L, d, N, kv_count,
-                         kv_index, schedule, scale, dtype, lse, stream);
+                         kv_index, schedule, scale, dtype, lse, 0, 0, 0, stream);
 }
 
 size_t nabla_attn_bwd_workspace_size(int batch, int heads, int L, int N) {
@@ -261,7 +320,7 @@ namespace {
 nabla_status attn_fwd_impl(const char* who, const void* q, const void* k, const void* v, void* o,
                            int batch, int heads, int L, int d, int N, const int32_t* kv_count,
                            const int32_t* kv_index, const int32_t* schedule, float scale,
-                           nabla_dtype dtype, float* lse, hipStream_t stream) {
+                           nabla_dtype dtype, float* lse, int raster, int H, int W, hipStream_t stream) {
     if (!q || !k || !v || !o || !kv_count || !kv_index)
         return fail(NABLA_E_INVAL, "%s: null pointer", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -290,6 +349,9 @@ nabla_status attn_fwd_impl(const char* who, const void* q, const void* k, const 
     a.schedule = schedule;
     a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
     a.lse = lse;
+    a.raster = raster;
+    a.H = H;
+    a.W = W;
     hipError_t e = dtype == NABLA_BF16 ? nabla::launch_attn_bf16(a, stream)
                                        : nabla::launch_attn_f32(a, stream);
     return hip_status(e, who);

@@ -77,6 +77,8 @@ struct MaskArgs {
     float* qp;              // workspace [BH, nb, d]
     float* kp;              // workspace [BH, nb, d]
     int bf16;
+    int raster;             // 0: q, k in fractal order; 1: raster order, 8 x 8 patches per block
+    int H, W;               // token grid, for the raster order
 };
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
 
@@ -91,6 +93,8 @@ struct AttnArgs {
     const int32_t* schedule;   // may be null
     float scale;
     float* lse;                // may be null: natural-log log-sum-exp per query row [BH, L]
+    int raster;                // 0: blocks are runs of 64 rows; 1: raster T x H x W with 8 x 8 patches
+    int H, W;                  // grid of the raster order
 };
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);

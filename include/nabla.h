@@ -158,6 +158,38 @@ nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, 
                                    hipStream_t stream);
 
 /*
+ * nabla_build_mask_raster - nabla_build_mask for Q and K in raster order
+ * (token (t, y, x) at l = (t*H + y)*W + x): the fractal flattening ("Metodologia: NABLA",
+ * item 1) is applied in the addressing instead of by a separate nabla_reorder pass.
+ * Block b is the P x P patch that fractal order would place at rows [N b, N b + N),
+ * read as P runs of P consecutive tokens; requires N == P*P.  Results (counts, lists,
+ * bitmap, schedule) are identical to nabla_reorder followed by nabla_build_mask.
+ * Errors: as nabla_build_mask, plus NABLA_E_INVAL when N != P*P.
+ */
+nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, int heads, int T,
+                                     int H, int W, int d, int P, int N, float thr,
+                                     const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                                     int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                                     int32_t* schedule, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/*
+ * block_sparse_attn_fwd_raster - block_sparse_attn_fwd for Q, K, V and O in raster order,
+ * with blocks numbered as fractal order numbers them (the lists of
+ * nabla_build_mask_raster): the permutation is applied while reading tiles and writing
+ * rows, so no reorder pass runs before or after.  The output equals nabla_reorder of Q,
+ * K, V, block_sparse_attn_fwd, and the inverse nabla_reorder of O, bit for bit.
+ * T, H, W     token grid, L = T*H*W; P patch size with N == P*P.
+ * Errors: as block_sparse_attn_fwd, plus NABLA_E_INVAL for non-positive T, H, W, P, H or
+ * W not a multiple of P, or N != P*P.
+ */
+nabla_status block_sparse_attn_fwd_raster(const void* q, const void* k, const void* v, void* o,
+                                          int batch, int heads, int T, int H, int W, int d, int P,
+                                          int N, const int32_t* kv_count, const int32_t* kv_index,
+                                          const int32_t* schedule, float scale, nabla_dtype dtype,
+                                          hipStream_t stream);
+
+/*
  * block_sparse_attn_fwd_lse - block_sparse_attn_fwd that also writes what the gradient
  * needs: the natural-log log-sum-exp of every query row over its kept keys,
  *   lse[b,h,a] = log( sum over tokens t of kept blocks of row blk(a) of exp(scale * q_a . k_t) ),

@@ -224,6 +224,39 @@ def test_attn_bwd_validation(lib, kw, status):
     assert lib.nabla_last_error().decode().startswith("block_sparse_attn_bwd")
 
 
+# ------------------------------------------------------------- raster-order entry points
+
+def test_build_mask_raster_validation(lib):
+    win = None
+    def call(**kw):
+        a = dict(q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, thr=0.1, scale=0.0,
+                 dt=NABLA_F32, cnt=C, idx=D_, ws=E, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.nabla_build_mask_raster(a["q"], a["k"], a["batch"], a["heads"], a["T"], a["H"], a["W"],
+                                           a["d"], a["P"], a["N"], a["thr"], win, a["scale"], a["dt"], a["cnt"],
+                                           a["idx"], None, None, a["ws"], a["ws_bytes"], None)
+    for kw, st in ((dict(q=None), NABLA_E_INVAL), (dict(P=4, H=16, W=16), NABLA_E_INVAL),
+                   (dict(thr=1.5), NABLA_E_INVAL), (dict(d=96), NABLA_E_UNSUPPORTED),
+                   (dict(ws_bytes=10), NABLA_E_WORKSPACE)):
+        assert call(**kw) == st, kw
+        assert lib.nabla_last_error().decode().startswith("nabla_build_mask_raster")
+
+
+def test_attn_raster_validation(lib):
+    def call(**kw):
+        a = dict(q=A, k=B_, v=C, o=D_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, cnt=E, idx=F_,
+                 scale=0.0, dt=NABLA_BF16)
+        a.update(kw)
+        return lib.block_sparse_attn_fwd_raster(a["q"], a["k"], a["v"], a["o"], a["batch"], a["heads"], a["T"],
+                                                a["H"], a["W"], a["d"], a["P"], a["N"], a["cnt"], a["idx"], None,
+                                                a["scale"], a["dt"], None)
+    for kw, st in ((dict(o=None), NABLA_E_INVAL), (dict(P=4), NABLA_E_INVAL), (dict(H=20), NABLA_E_INVAL),
+                   (dict(T=0), NABLA_E_INVAL), (dict(d=32), NABLA_E_UNSUPPORTED),
+                   (dict(scale=float("nan")), NABLA_E_INVAL)):
+        assert call(**kw) == st, kw
+        assert lib.nabla_last_error().decode().startswith("block_sparse_attn_fwd_raster")
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 1024, 64)
