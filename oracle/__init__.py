@@ -8,11 +8,12 @@ from .nabla_oracle import (
     fractal_index, reorder, block_mean, pooled_logits, row_softmax, cdf_values, cdf_keep,
     block_tiles, sta_mask, block_mask, kv_lists, mask_from_lists, attention_block,
     masked_attention, forward, block_lse, masked_attention_lse, masked_attention_backward,
+    sip_probabilities, sip_mask, weighted_block_attention,
 )
 
 __all__ = [
     "fractal_index", "reorder", "block_mean", "pooled_logits", "row_softmax", "cdf_values",
     "cdf_keep", "block_tiles", "sta_mask", "block_mask", "kv_lists", "mask_from_lists",
     "attention_block", "masked_attention", "forward", "block_lse", "masked_attention_lse",
-    "masked_attention_backward",
+    "masked_attention_backward", "sip_probabilities", "sip_mask", "weighted_block_attention",
 ]

@@ -345,6 +345,95 @@ def masked_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout:
     return dq, dk, dv
 
 
+# ---------------------------------------------------------------------------
+# SIP: sampling with inclusion-probability weighting (AB-Attention page, "Os três
+# recursos do AB-Attention", second feature), on NABLA's block scores
+# ---------------------------------------------------------------------------
+
+def sip_probabilities(A: np.ndarray, budget: int) -> np.ndarray:
+    """Inclusion probabilities of one row of block scores A (>= 0) for an expected
+    budget of ``budget`` blocks: a block's probability is proportional to its score,
+    capped at 1, and the highest-scoring block is always included.
+
+    Reading: the row's top block (smallest index among equal maxima) gets pi = 1; the
+    other blocks share budget - 1 by pi_j = min(1, c A_j) with c chosen so that their
+    probabilities sum to budget - 1 (blocks whose c A_j reaches 1 are certain).  With
+    budget >= nb every block is certain.  Solved by sorting the scores in decreasing
+    order and taking the smallest number m of certain blocks for which the next block
+    stays below 1."""
+    A = np.asarray(A, dtype=np.float64)
+    nb = A.shape[-1]
+    pi = np.zeros(nb)
+    if budget >= nb:
+        return np.ones(nb)
+    t = int(np.argmax(A))
+    pi[t] = 1.0
+    rest = np.array([j for j in range(nb) if j != t])
+    kp = budget - 1
+    if kp <= 0 or len(rest) == 0:
+        return pi
+    w = A[rest]
+    order = np.argsort(-w, kind="stable")
+    ws = w[order]
+    tail = np.concatenate([np.cumsum(ws[::-1])[::-1], [0.0]])    # tail[m] = sum of ws[m:]
+    c = 0.0
+    m_cert = 0
+    for m in range(0, min(kp, len(ws)) + 1):
+        if m == kp or tail[m] <= 0.0:
+            c, m_cert = 0.0, m
+            break
+        cm = (kp - m) / tail[m]
+        if cm * ws[m] < 1.0:
+            c, m_cert = cm, m
+            break
+    p_rest = np.minimum(1.0, c * ws)
+    p_rest[:m_cert] = 1.0
+    out = np.empty(len(rest))
+    out[order] = p_rest
+    pi[rest] = out
+    return pi
+
+
+def sip_mask(A: np.ndarray, budget: int, uniforms: np.ndarray):
+    """Sampled mask and weights for rows of scores A [..., nb]: block j of a row is
+    kept when its uniform draw u_j (in [0, 1), given) is below pi_j, and a kept block
+    carries the logit shift log(1 / pi_j), so that exp(s + log(1/pi)) = exp(s) / pi:
+    the Horvitz-Thompson weight of the sampled block in both the numerator and the
+    normaliser of the softmax.  Returns (mask, logw, pi); logw is 0 where not kept."""
+    A = np.asarray(A, dtype=np.float64)
+    nb = A.shape[-1]
+    flat = A.reshape(-1, nb)
+    u = np.asarray(uniforms, dtype=np.float64).reshape(-1, nb)
+    pi = np.stack([sip_probabilities(r, budget) for r in flat])
+    keep = u < pi
+    logw = np.where(keep, -np.log(np.where(keep, pi, 1.0)), 0.0)
+    return keep.reshape(A.shape), logw.reshape(A.shape), pi.reshape(A.shape)
+
+
+def weighted_block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
+                             logw: np.ndarray, N: int, scale: Optional[float] = None,
+                             dtype=np.float64) -> np.ndarray:
+    """Block-sparse attention with a per-tile additive logit shift: for query block i,
+    the logits of the tokens of kept KV block j are scale * q . k + logw[i, j]; dropped
+    blocks are out of the numerator and the normaliser.  [G, L, d] inputs, [G, nb, nb]
+    mask and shifts."""
+    d = q.shape[-1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    G, L, _ = q.shape
+    out = np.zeros((G, L, v.shape[-1]), dtype=dtype)
+    for g in range(G):
+        for i in range(L // N):
+            js = np.nonzero(mask[g, i])[0]
+            if len(js) == 0:
+                continue
+            tok = (js[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+            s = (np.asarray(q[g, i * N:(i + 1) * N], dtype) @ np.asarray(k[g, tok], dtype).T) * dtype(scale)
+            s = s + np.repeat(np.asarray(logw[g, i, js], dtype), N)[None, :]
+            e = np.exp(s - np.max(s, axis=1, keepdims=True))
+            out[g, i * N:(i + 1) * N] = (e @ np.asarray(v[g, tok], dtype)) / np.sum(e, axis=1, keepdims=True)
+    return out
+
+
 def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, T: int, H: int, W: int, P: int,
             N: int, thr: float, sta: Optional[Tuple[int, int, int]] = None,
             scale: Optional[float] = None) -> Dict[str, np.ndarray]:

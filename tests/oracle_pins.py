@@ -411,4 +411,106 @@ def pin_backward_sums_and_empty_rows():
     assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
 
 
+# ---------------------------------------------------------------- SIP (sampling + HT weights)
+
+def _sip_rows(rng):
+    rows = [rng.random(24) ** 4, rng.random(40), np.full(16, 1.0 / 16), rng.random(30) ** 8]
+    z = rng.random(20)
+    z[[3, 7, 11]] = 0.0                                   # zero-score blocks
+    rows.append(z)
+    t = rng.random(18)
+    t[[2, 5, 9]] = t.max()                                # tied maxima: the smallest index is certain
+    rows.append(t)
+    return [r / r.sum() for r in rows]
+
+
+def pin_sip_probabilities():
+    """Budget, caps, the certain top block, monotonicity, and proportionality to the
+    score among the blocks that are neither certain nor zero."""
+    rng = _rng(30)
+    for A in _sip_rows(rng):
+        nb = len(A)
+        top = int(np.argmax(A))
+        pos = int(np.count_nonzero(A))
+        for k in (1, 2, 5, nb // 2, nb - 1, nb, nb + 3):
+            pi = O.sip_probabilities(A, k)
+            assert np.all(pi >= 0) and np.all(pi <= 1 + 1e-15)
+            assert pi[top] == 1.0
+            if k >= nb:
+                assert np.all(pi == 1.0)
+                continue
+            assert abs(pi.sum() - min(k, pos)) <= 1e-9, (k, pi.sum(), pos)
+            others = np.array([j for j in range(nb) if j != top])
+            a, p = A[others], pi[others]
+            order = np.argsort(a)
+            assert np.all(np.diff(p[order]) >= -1e-15), "pi must not decrease with the score"
+            mid = (p > 0) & (p < 1)
+            if mid.sum() >= 2:
+                ratio = p[mid] / a[mid]
+                assert np.max(ratio) - np.min(ratio) <= 1e-9 * np.max(ratio)
+            assert np.all(p[a == 0] == 0)
+            if k > 1 and mid.any():
+                assert np.all(p[~mid & (a > 0)] == 1.0)
+
+
+def pin_sip_horvitz_thompson_unbiased():
+    """Kept blocks weighted by exp(logw) = 1/pi give an unbiased sum: the expectation
+    over all inclusion outcomes (independent, P(keep j) = pi_j) of sum_j keep_j x_j / pi_j
+    equals sum_j x_j, enumerated exactly on small rows."""
+    rng = _rng(31)
+    for nb, k in ((6, 3), (7, 2), (8, 5)):
+        A = rng.random(nb) ** 3
+        A /= A.sum()
+        pi = O.sip_probabilities(A, k)
+        x = rng.standard_normal(nb)
+        expect = 0.0
+        total_p = 0.0
+        for outcome in range(1 << nb):
+            keep = np.array([(outcome >> j) & 1 for j in range(nb)], dtype=bool)
+            prob = np.prod(np.where(keep, pi, 1.0 - pi))
+            if prob == 0.0:
+                continue
+            # uniforms that realise this outcome under the rule keep iff u < pi
+            u = np.where(keep, 0.0, np.minimum(pi + (1.0 - pi) * 0.5, np.nextafter(1.0, 0.0)))
+            m, logw, _ = O.sip_mask(A[None], k, u[None])
+            assert np.array_equal(m[0], keep)
+            expect += prob * float(np.sum(m[0] * np.exp(logw[0]) * x))
+            total_p += prob
+        assert abs(total_p - 1.0) <= 1e-12
+        assert abs(expect - x[pi > 0].sum()) <= 1e-10 * max(1.0, np.abs(x).sum())
+
+
+def pin_weighted_attention_sdpa():
+    """Per-tile logit shifts = SDPA with an additive float mask (shift on kept tokens,
+    -inf on dropped ones)."""
+    rng = _rng(32)
+    G, L, N, d = 2, 320, 64, 8
+    nb = L // N
+    q, k, v = (rng.standard_normal((G, L, d)).astype(np.float32) for _ in range(3))
+    m = rng.random((G, nb, nb)) < 0.5
+    m[:, np.arange(nb), np.arange(nb)] = True
+    logw = np.where(m, rng.random((G, nb, nb)) * 3.0, 0.0)
+    out = O.weighted_block_attention(q, k, v, m, logw, N, scale=0.4)
+    bias = np.where(m, logw, -np.inf)
+    tb = np.stack([np.kron(bias[g], np.ones((N, N))) for g in range(G)])
+    qt, kt, vt = (torch.from_numpy(a.astype(np.float64))[None] for a in (q, k, v))
+    ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(tb)[None], scale=0.4)[0].numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+def pin_sip_full_budget_is_plain_attention():
+    """With a budget of every block, every block is certain with shift 0: the SIP path
+    is the plain block attention over all blocks, i.e. dense attention."""
+    rng = _rng(33)
+    G, L, N, d = 1, 256, 64, 8
+    nb = L // N
+    q, k, v = (rng.standard_normal((G, L, d)).astype(np.float32) for _ in range(3))
+    A = rng.random((G, nb, nb))
+    A /= A.sum(-1, keepdims=True)
+    m, logw, pi = O.sip_mask(A, nb, rng.random((G, nb, nb)))
+    assert m.all() and np.all(logw == 0) and np.all(pi == 1)
+    out = O.weighted_block_attention(q, k, v, m, logw, N)
+    assert np.max(np.abs(out - _sdpa(q, k, v))) <= 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

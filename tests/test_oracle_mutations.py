@@ -124,6 +124,34 @@ def _lse_log2(q, k, keep, i, N, scale, dtype=np.float64):
 
 
 _orig_block_lse = O.block_lse
+_orig_sip_p = O.sip_probabilities
+_orig_sip_mask = O.sip_mask
+_orig_wattn = O.weighted_block_attention
+
+
+def _sip_uncapped(A, budget):
+    # proportional allocation without the cap at 1 (and no certain blocks)
+    A = np.asarray(A, dtype=np.float64)
+    if budget >= len(A):
+        return np.ones(len(A))
+    return np.minimum(budget * A / A.sum(), 1.5)
+
+
+def _sip_no_certain_top(A, budget):
+    p = _orig_sip_p(A, budget).copy()
+    t = int(np.argmax(A))
+    if budget < len(A):
+        p[t] = min(1.0, p[t] * 0.5)
+    return p
+
+
+def _sip_logw_sign(A, budget, uniforms):
+    m, logw, pi = _orig_sip_mask(A, budget, uniforms)
+    return m, -logw, pi
+
+
+def _wattn_shift_ignored(q, k, v, mask, logw, N, scale=None, dtype=np.float64):
+    return _orig_wattn(q, k, v, mask, np.zeros_like(logw), N, scale, dtype)
 
 MUTATIONS = [
     ("fractal_index", _fractal_colmajor),
@@ -142,6 +170,10 @@ MUTATIONS = [
     ("masked_attention_backward", _backward_with("dq_unscaled")),
     ("masked_attention_backward", _backward_with("dk_from_p")),
     ("block_lse", _lse_log2),
+    ("sip_probabilities", _sip_uncapped),
+    ("sip_probabilities", _sip_no_certain_top),
+    ("sip_mask", _sip_logw_sign),
+    ("weighted_block_attention", _wattn_shift_ignored),
 ]
 
 
