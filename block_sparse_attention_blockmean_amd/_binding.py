@@ -24,6 +24,8 @@ EXPORTS = (
     "nabla_build_mask_workspace_size",
     "nabla_build_mask",
     "nabla_build_mask_raster",
+    "nabla_build_mask_sip",
+    "block_sparse_attn_fwd_weighted",
     "block_sparse_attn_fwd",
     "block_sparse_attn_fwd_raster",
     "block_sparse_attn_fwd_lse",
@@ -67,6 +69,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_build_mask_raster.restype = i
     lib.block_sparse_attn_fwd_raster.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, f, i, vp]
     lib.block_sparse_attn_fwd_raster.restype = i
+    lib.nabla_build_mask_sip.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, vp, f, i, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.nabla_build_mask_sip.restype = i
+    lib.block_sparse_attn_fwd_weighted.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, i, vp]
+    lib.block_sparse_attn_fwd_weighted.restype = i
     lib.block_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, f, i, vp]
     lib.block_sparse_attn_fwd.restype = i
     lib.block_sparse_attn_fwd_lse.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, f, i, vp, vp]
@@ -233,6 +239,67 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.
     _check(lib.block_sparse_attn_fwd(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, NH, L, d, N,
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+        _dev(schedule, "schedule") if schedule is not None else None,
+        float(scale) if scale is not None else 0.0, _dtype_code(q), _stream()), lib)
+    return out
+
+
+def build_mask_sip(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int, budget: int,
+                   uniforms: torch.Tensor, N: int = 64, scale: Optional[float] = None,
+                   with_bitmap: bool = False, with_schedule: bool = False,
+                   workspace: Optional[torch.Tensor] = None):
+    """SIP block selection of fractal-ordered Q, K: returns (kv_count, kv_index, kv_logw),
+    plus the bitmap and/or schedule when asked for.  ``uniforms`` is a float32
+    [B, heads, nb, nb] tensor of draws in [0, 1)."""
+    lib = load_library()
+    B, NH, L, d = q.shape
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must have the same shape and dtype")
+    nb = L // N
+    if uniforms.dtype != torch.float32 or uniforms.numel() != B * NH * nb * nb:
+        raise ValueError("uniforms must hold batch*heads*nb*nb float32 values")
+    dev = q.device
+    kv_count = torch.empty((B, NH, nb), dtype=torch.int32, device=dev)
+    kv_index = torch.empty((B, NH, nb, nb), dtype=torch.int32, device=dev)
+    kv_logw = torch.empty((B, NH, nb, nb), dtype=torch.float32, device=dev)
+    bitmap = torch.empty((B, NH, nb, (nb + 31) // 32), dtype=torch.int32, device=dev) if with_bitmap else None
+    schedule = torch.empty((B * NH * nb,), dtype=torch.int32, device=dev) if with_schedule else None
+    ws_bytes = lib.nabla_build_mask_workspace_size(B, NH, L, d, N)
+    if workspace is None:
+        workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
+    _check(lib.nabla_build_mask_sip(
+        _dev(q, "q"), _dev(k, "k"), B, NH, T, H, W, d, P, N, int(budget), _dev(uniforms, "uniforms"),
+        float(scale) if scale is not None else 0.0, _dtype_code(q), _dev(kv_count, "kv_count"),
+        _dev(kv_index, "kv_index"), _dev(kv_logw, "kv_logw"),
+        _dev(bitmap, "bitmap") if bitmap is not None else None,
+        _dev(schedule, "schedule") if schedule is not None else None,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()), lib)
+    out = [kv_count, kv_index, kv_logw]
+    if with_bitmap:
+        out.append(bitmap)
+    if with_schedule:
+        out.append(schedule)
+    return tuple(out)
+
+
+def attn_fwd_weighted(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.Tensor,
+                      kv_index: torch.Tensor, kv_logw: torch.Tensor, N: int = 64,
+                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                      schedule: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-sparse attention with the per-tile logit shifts ``kv_logw`` (SIP weights)."""
+    lib = load_library()
+    B, NH, L, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    _check_lists(q, kv_count, kv_index, N)
+    if kv_logw.dtype != torch.float32 or kv_logw.numel() != kv_index.numel():
+        raise ValueError("kv_logw must be float32 shaped like kv_index")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.block_sparse_attn_fwd_weighted(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, NH, L, d, N,
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), _dev(kv_logw, "kv_logw"),
         _dev(schedule, "schedule") if schedule is not None else None,
         float(scale) if scale is not None else 0.0, _dtype_code(q), _stream()), lib)
     return out

@@ -38,13 +38,13 @@ namespace {
 
 using namespace attn;
 
-template <int D, bool RASTER>
+template <int D, bool RASTER, bool WEIGHTED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                           const __bf16* __restrict__ v, __bf16* __restrict__ o, int L, int nb,
                           const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_index,
                           const int32_t* __restrict__ schedule, RasterGrid grid, float scale_log2e,
-                          float* __restrict__ lse) {
+                          float* __restrict__ lse, const float* __restrict__ kv_logw) {
     using G = Tile<D>;
     constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;        // 32-row d tiles of O^T
@@ -140,6 +140,8 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         // wave sees them and is done with the buffers of tile i - 1, refilled now
         wait_vmcnt<0>();
         lds_barrier();
+        // the tile's additive logit shift (log2 units): a sampled block's log(1 / pi)
+        const float wl = WEIGHTED ? kv_logw[((size_t)bh * nb + qb) * nb + i] * 1.4426950408889634f : 0.f;
         const uint32_t nxt = block_row<RASTER>(grid, next_tile) * G::kRowBytes;
         char* k_dst = PAR ? k_lds0 : k_lds1;
         char* v_dst = PAR ? v_lds0 : v_lds1;
@@ -173,7 +175,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
         {
             const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * scale_log2e;
+            mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * scale_log2e + wl;
         }
         if (__ballot(mx > m_run + 8.0f)) {
             const float m_new = fmaxf(m_run, mx);
@@ -193,7 +195,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[8 * u + e], scale_log2e, -m_run));
+                const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[8 * u + e], scale_log2e, wl - m_run));
                 l_run += pe;
                 pb[u][e] = (__bf16)pe;
             }
@@ -278,7 +280,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     }
 }
 
-template <int D, bool RASTER>
+template <int D, bool RASTER, bool WEIGHTED>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
     const float scale_log2e = a.scale * 1.4426950408889634f;
     RasterGrid grid{};
@@ -288,17 +290,18 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
         grid.nHW = FastDiv((uint32_t)((a.H / 8) * (a.W / 8)));
         grid.nW = FastDiv((uint32_t)(a.W / 8));
     }
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, RASTER>), dim3(a.BH * a.nb), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, RASTER, WEIGHTED>), dim3(a.BH * a.nb), dim3(kThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
-                       a.L, a.nb, a.kv_count, a.kv_index, a.schedule, grid, scale_log2e, a.lse);
+                       a.L, a.nb, a.kv_count, a.kv_index, a.schedule, grid, scale_log2e, a.lse, a.kv_logw);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-    if (a.raster) return a.d == 128 ? launch<128, true>(a, s) : launch<64, true>(a, s);
-    return a.d == 128 ? launch<128, false>(a, s) : launch<64, false>(a, s);
+    if (a.kv_logw) return a.d == 128 ? launch<128, false, true>(a, s) : launch<64, false, true>(a, s);
+    if (a.raster) return a.d == 128 ? launch<128, true, false>(a, s) : launch<64, true, false>(a, s);
+    return a.d == 128 ? launch<128, false, false>(a, s) : launch<64, false, false>(a, s);
 }
 
 }  // namespace nabla

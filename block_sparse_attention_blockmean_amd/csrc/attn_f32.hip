@@ -19,12 +19,12 @@ using attn::RasterGrid;
 using attn::block_row;
 using attn::row_in_block;
 
-template <int D, bool RASTER>
+template <int D, bool RASTER, bool WEIGHTED>
 __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, int L, int nb, const int32_t* __restrict__ kv_count,
     const int32_t* __restrict__ kv_index, const int32_t* __restrict__ schedule,
-    RasterGrid grid, float scale, float* __restrict__ lse) {
+    RasterGrid grid, float scale, float* __restrict__ lse, const float* __restrict__ kv_logw) {
     constexpr int LD = D + 1;
     extern __shared__ float lds[];
     float* q_s = lds;                   // [64][LD]
@@ -53,6 +53,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     const int32_t* list = kv_index + ((size_t)bh * nb + qb) * nb;
     for (int it = 0; it < count; ++it) {
         const uint32_t jbase = block_row<RASTER>(grid, list[it]);
+        const float wl = WEIGHTED ? kv_logw[((size_t)bh * nb + qb) * nb + it] : 0.f;
         __syncthreads();
         for (int i = tid; i < kBlk * D; i += kThreads) {
             const size_t src = head_off + (size_t)(jbase + row_in_block<RASTER>(grid, i / D)) * D + i % D;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
             const int kv = part + 4 * c;
             float dot = 0.f;
             for (int e = 0; e < D; ++e) dot = fmaf(q_s[row * LD + e], k_s[kv * LD + e], dot);
-            s[c] = dot * scale;
+            s[c] = dot * scale + wl;   // a sampled tile's log(1 / pi) shift
             mx = fmaxf(mx, s[c]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 1));
@@ -102,11 +103,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     for (int c = 0; c < D / 4; ++c) orow[part + 4 * c] = acc[c] * inv;
 }
 
-template <int D, bool RASTER>
+template <int D, bool RASTER, bool WEIGHTED>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
     const size_t lds = (3 * kBlk * (D + 1) + kBlk * 65) * sizeof(float);
     static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = set_max_dynamic_lds((const void*)attn_fwd_f32_kernel<D, RASTER>, (int)lds, lds_set);
+    hipError_t e = set_max_dynamic_lds((const void*)attn_fwd_f32_kernel<D, RASTER, WEIGHTED>, (int)lds, lds_set);
     if (e != hipSuccess) return e;
     RasterGrid grid{};
     if (RASTER) {
@@ -115,17 +116,18 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
         grid.nHW = FastDiv((uint32_t)((a.H / 8) * (a.W / 8)));
         grid.nW = FastDiv((uint32_t)(a.W / 8));
     }
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, RASTER>), dim3(a.BH * a.nb), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, RASTER, WEIGHTED>), dim3(a.BH * a.nb), dim3(kThreads), lds, s,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.L,
-                       a.nb, a.kv_count, a.kv_index, a.schedule, grid, a.scale, a.lse);
+                       a.nb, a.kv_count, a.kv_index, a.schedule, grid, a.scale, a.lse, a.kv_logw);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
-    if (a.raster) return a.d == 128 ? launch<128, true>(a, s) : launch<64, true>(a, s);
-    return a.d == 128 ? launch<128, false>(a, s) : launch<64, false>(a, s);
+    if (a.kv_logw) return a.d == 128 ? launch<128, false, true>(a, s) : launch<64, false, true>(a, s);
+    if (a.raster) return a.d == 128 ? launch<128, true, false>(a, s) : launch<64, true, false>(a, s);
+    return a.d == 128 ? launch<128, false, false>(a, s) : launch<64, false, false>(a, s);
 }
 
 }  // namespace nabla

@@ -171,11 +171,98 @@ __device__ inline int compact(const float* src, int len, uint32_t lo, uint32_t h
     return n;
 }
 
+// ---------------------------------------------------------------------------
+// SIP (AB-Attention page, "Os três recursos do AB-Attention", second feature) on one
+// row of block scores A (the pooled softmax), in one wave: block j is kept with
+// probability pi_j proportional to A_j and capped at 1, and carries the logit shift
+// log(1 / pi_j), the Horvitz-Thompson weight.  The row's top block (smallest index
+// among equal maxima) is certain; the others share budget - 1 through
+// pi_j = min(1, c A_j), the water level c found by growing the set of certain blocks
+// (c only increases as blocks become certain, so the set only grows).  Kept iff the
+// given uniform draw u_j < pi_j.
+// ---------------------------------------------------------------------------
+__device__ void sip_row(float* arow, int nb, float inv_sum, int budget, const float* u, int32_t* out_idx,
+                        float* out_logw, uint32_t* out_bits, int nwords, int32_t* out_count, int lane) {
+    float best = -1.f;
+    int bj = nb;
+    for (int j = lane; j < nb; j += 64) {
+        const float p = arow[j] * inv_sum;
+        arow[j] = p;
+        if (p > best) {
+            best = p;
+            bj = j;
+        }
+    }
+    const float amax = wave_max(best);
+    const int top = (int)~wave_max_u(~(uint32_t)(best == amax ? bj : nb));
+    const int kp = budget - 1;
+    const bool all = budget >= nb;
+    // water level over the blocks other than the top one
+    float c = 0.f, c_cert = 0.f;
+    if (!all && kp > 0) {
+        float rest = 0.f;
+        for (int j = lane; j < nb; j += 64)
+            if (j != top) rest += arow[j];
+        rest = wave_sum(rest);
+        c = rest > 0.f ? (float)kp / rest : 0.f;
+        c_cert = c;
+        int m = 0;
+        for (int it = 0; it < 64; ++it) {
+            float unc = 0.f;   // mass of the blocks still below 1
+            int cnt = 0;
+            for (int j0 = 0; j0 < nb; j0 += 64) {
+                const int j = j0 + lane;
+                const bool other = j < nb && j != top;
+                const bool cert = other && c * arow[j] >= 1.f;
+                if (other && !cert) unc += arow[j];
+                cnt += __popcll(__ballot(cert));
+            }
+            unc = wave_sum(unc);
+            if (cnt == m) {
+                c_cert = c;
+                break;
+            }
+            m = cnt;
+            c_cert = c;
+            if (m >= kp || !(unc > 0.f)) {
+                c = 0.f;
+                break;
+            }
+            c = (float)(kp - m) / unc;
+        }
+    }
+    int base = 0;
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+        const int j = j0 + lane;
+        bool keep = false;
+        float pi = 0.f;
+        if (j < nb) {
+            const float a = arow[j];
+            pi = (all || j == top || c_cert * a >= 1.f) ? 1.f : c * a;
+            keep = u[j] < pi;
+        }
+        const uint64_t ballot = __ballot(keep);
+        if (keep) {
+            const int pos = base + __popcll(ballot & ((1ull << lane) - 1ull));
+            out_idx[pos] = j;
+            out_logw[pos] = -logf(pi);
+        }
+        base += __popcll(ballot);
+        if (out_bits) {
+            const int w = j0 >> 5;
+            if (lane == 0 && w < nwords) out_bits[w] = (uint32_t)ballot;
+            if (lane == 1 && w + 1 < nwords) out_bits[w + 1] = (uint32_t)(ballot >> 32);
+        }
+    }
+    if (lane == 0) *out_count = base;
+}
+
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp, int nb, int ld_s, float scale,
     float thr, int sta, int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
-    int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap) {
+    int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int sip_budget,
+    const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
     extern __shared__ float s_lds[];   // [kRows][ld_s] rows, then [kWaves][kCap] candidates
     constexpr int KC = D / 4;          // k values per lane per MFMA chain
     const int wave = threadIdx.x >> 6;
@@ -265,6 +352,13 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
             sum += e;
         }
         const float inv_sum = 1.0f / wave_sum(sum);
+        if (sip_budget > 0) {
+            sip_row(arow, nb, inv_sum, sip_budget, uniforms + ((size_t)bh * nb + row) * nb,
+                    kv_index + ((size_t)bh * nb + row) * nb, kv_logw + ((size_t)bh * nb + row) * nb,
+                    bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr, nwords,
+                    kv_count + (size_t)bh * nb + row, lane);
+            continue;
+        }
         // start of the bracket: u0 = thr / nb, nudged down so rounding cannot push
         // g(u0) above thr; it is verified below and dropped to 0 if it fails
         uint32_t lo = __float_as_uint(thr / ((float)nb * 1.0001f));
@@ -457,7 +551,7 @@ hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
     dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
     hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.qp, a.kp, a.nb,
                        ld_s, a.scale, a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count,
-                       a.kv_index, a.bitmap);
+                       a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
     return hipGetLastError();
 }
 

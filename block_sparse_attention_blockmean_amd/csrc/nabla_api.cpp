@@ -91,7 +91,8 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
                              const nabla_sta_window* sta, float scale, nabla_dtype dtype,
                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                              int32_t* schedule, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream);
+                             hipStream_t stream, int sip_budget = 0, const float* uniforms = nullptr,
+                             float* kv_logw = nullptr);
 
 }  // namespace
 
@@ -103,6 +104,21 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
                               hipStream_t stream) {
     return build_mask_impl("nabla_build_mask", 0, q, k, batch, heads, T, H, W, d, P, N, thr, sta, scale,
                            dtype, kv_count, kv_index, bitmap, schedule, workspace, workspace_bytes, stream);
+}
+
+nabla_status nabla_build_mask_sip(const void* q, const void* k, int batch, int heads, int T, int H,
+                                  int W, int d, int P, int N, int budget, const float* uniforms,
+                                  float scale, nabla_dtype dtype, int32_t* kv_count, int32_t* kv_index,
+                                  float* kv_logw, uint32_t* bitmap, int32_t* schedule, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    const char* who = "nabla_build_mask_sip";
+    if (!uniforms || !kv_logw) return fail(NABLA_E_INVAL, "%s: null pointer", who);
+    if (((uintptr_t)uniforms & 3) || ((uintptr_t)kv_logw & 3))
+        return fail(NABLA_E_INVAL, "%s: misaligned pointer", who);
+    if (budget < 1) return fail(NABLA_E_INVAL, "%s: budget must be at least 1", who);
+    return build_mask_impl(who, 0, q, k, batch, heads, T, H, W, d, P, N, 0.0f, nullptr, scale, dtype,
+                           kv_count, kv_index, bitmap, schedule, workspace, workspace_bytes, stream, budget,
+                           uniforms, kv_logw);
 }
 
 nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, int heads, int T, int H,
@@ -123,7 +139,8 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
                              const nabla_sta_window* sta, float scale, nabla_dtype dtype,
                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                              int32_t* schedule, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+                             hipStream_t stream, int sip_budget, const float* uniforms,
+                             float* kv_logw) {
     if (!q || !k || !kv_count || !kv_index) return fail(NABLA_E_INVAL, "%s: null pointer", who);
     if (!aligned16(q) || !aligned16(k) || ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3) ||
         ((uintptr_t)bitmap & 3) || ((uintptr_t)schedule & 3))
@@ -184,6 +201,9 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     a.raster = raster;
     a.H = H;
     a.W = W;
+    a.sip_budget = sip_budget;
+    a.uniforms = uniforms;
+    a.kv_logw = kv_logw;
     return hip_status(nabla::launch_build_mask(a, stream), who);
 }
 
@@ -194,7 +214,8 @@ namespace {
 nabla_status attn_fwd_impl(const char* who, const void* q, const void* k, const void* v, void* o,
                            int batch, int heads, int L, int d, int N, const int32_t* kv_count,
                            const int32_t* kv_index, const int32_t* schedule, float scale,
-                           nabla_dtype dtype, float* lse, int raster, int H, int W, hipStream_t stream);
+                           nabla_dtype dtype, float* lse, int raster, int H, int W, hipStream_t stream,
+                           const float* kv_logw = nullptr);
 
 }  // namespace
 
@@ -205,6 +226,18 @@ nabla_status block_sparse_attn_fwd(const void* q, const void* k, const void* v, 
                                    hipStream_t stream) {
     return attn_fwd_impl("block_sparse_attn_fwd", q, k, v, o, batch, heads, L, d, N, kv_count, kv_index,
                          schedule, scale, dtype, nullptr, 0, 0, 0, stream);
+}
+
+nabla_status block_sparse_attn_fwd_weighted(const void* q, const void* k, const void* v, void* o,
+                                            int batch, int heads, int L, int d, int N,
+                                            const int32_t* kv_count, const int32_t* kv_index,
+                                            const float* kv_logw, const int32_t* schedule, float scale,
+                                            nabla_dtype dtype, hipStream_t stream) {
+    const char* who = "block_sparse_attn_fwd_weighted";
+    if (!kv_logw) return fail(NABLA_E_INVAL, "%s: null kv_logw", who);
+    if ((uintptr_t)kv_logw & 3) return fail(NABLA_E_INVAL, "%s: misaligned kv_logw", who);
+    return attn_fwd_impl(who, q, k, v, o, batch, heads, L, d, N, kv_count, kv_index, schedule, scale, dtype,
+                         nullptr, 0, 0, 0, stream, kv_logw);
 }
 
 nabla_status block_sparse_attn_fwd_raster(const void* q, const void* k, const void* v, void* o,
@@ -320,7 +353,8 @@ namespace {
 nabla_status attn_fwd_impl(const char* who, const void* q, const void* k, const void* v, void* o,
                            int batch, int heads, int L, int d, int N, const int32_t* kv_count,
                            const int32_t* kv_index, const int32_t* schedule, float scale,
-                           nabla_dtype dtype, float* lse, int raster, int H, int W, hipStream_t stream) {
+                           nabla_dtype dtype, float* lse, int raster, int H, int W, hipStream_t stream,
+                           const float* kv_logw) {
     if (!q || !k || !v || !o || !kv_count || !kv_index)
         return fail(NABLA_E_INVAL, "%s: null pointer", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -352,6 +386,7 @@ nabla_status attn_fwd_impl(const char* who, const void* q, const void* k, const 
     a.raster = raster;
     a.H = H;
     a.W = W;
+    a.kv_logw = kv_logw;
     hipError_t e = dtype == NABLA_BF16 ? nabla::launch_attn_bf16(a, stream)
                                        : nabla::launch_attn_f32(a, stream);
     return hip_status(e, who);

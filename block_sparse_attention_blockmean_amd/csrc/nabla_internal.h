@@ -79,6 +79,9 @@ struct MaskArgs {
     int bf16;
     int raster;             // 0: q, k in fractal order; 1: raster order, 8 x 8 patches per block
     int H, W;               // token grid, for the raster order
+    int sip_budget;         // > 0: sampled selection with this expected budget per row (no CDF cut)
+    const float* uniforms;  // SIP draws [BH, nb, nb]
+    float* kv_logw;         // SIP out: log(1 / pi) per list entry [BH, nb, nb]
 };
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
 
@@ -95,6 +98,7 @@ struct AttnArgs {
     float* lse;                // may be null: natural-log log-sum-exp per query row [BH, L]
     int raster;                // 0: blocks are runs of 64 rows; 1: raster T x H x W with 8 x 8 patches
     int H, W;                  // grid of the raster order
+    const float* kv_logw;      // may be null: additive logit shift per list entry [BH, nb, nb]
 };
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);

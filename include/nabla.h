@@ -190,6 +190,48 @@ nabla_status block_sparse_attn_fwd_raster(const void* q, const void* k, const vo
                                           hipStream_t stream);
 
 /*
+ * nabla_build_mask_sip - sampled block selection with inclusion-probability weights
+ * (SIP), the second feature of the AB-Attention page ("Os três recursos do
+ * AB-Attention"), on NABLA's block scores: the pooled, row-softmaxed map A of
+ * nabla_build_mask ("Downsampling", "Atenção Reduzida"), Q and K in fractal order.
+ * For each row, block j gets the inclusion probability
+ *   pi_j = 1 for the row's top block (smallest index among equal maxima),
+ *   pi_j = min(1, c A_j) for the others, c such that their pi sum to budget - 1
+ *          (every block is certain when budget >= nb),
+ * and is kept iff uniforms[b,h,i,j] < pi_j.  A kept block's list entry carries
+ * kv_logw = log(1 / pi_j) (natural log), the additive logit shift that makes
+ * block_sparse_attn_fwd_weighted the Horvitz-Thompson estimate of the numerator and
+ * the normaliser of the full softmax (a block with pi = 1/4 counts four times).
+ * budget      expected number of kept blocks per row, >= 1.
+ * uniforms    float32 [batch, heads, nb, nb] draws in [0, 1), caller's random numbers.
+ * kv_count, kv_index, bitmap, schedule  as nabla_build_mask.
+ * kv_logw     out, float32 [batch, heads, nb, nb]: first kv_count entries of each row,
+ *             aligned with kv_index.
+ * No STA window.  Errors: as nabla_build_mask, plus NABLA_E_INVAL for a null or
+ * misaligned uniforms / kv_logw or budget < 1.
+ */
+nabla_status nabla_build_mask_sip(const void* q, const void* k, int batch, int heads, int T, int H,
+                                  int W, int d, int P, int N, int budget, const float* uniforms,
+                                  float scale, nabla_dtype dtype, int32_t* kv_count,
+                                  int32_t* kv_index, float* kv_logw, uint32_t* bitmap,
+                                  int32_t* schedule, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * block_sparse_attn_fwd_weighted - block_sparse_attn_fwd with an additive logit shift
+ * per kept tile: the logits of the tokens of list entry e of row i are
+ * scale * q . k + kv_logw[b,h,i,e] (the SIP weights of nabla_build_mask_sip; the
+ * computation stays an ordinary softmax).  kv_logw float32 [batch, heads, nb, nb].
+ * Errors: as block_sparse_attn_fwd, plus NABLA_E_INVAL for a null or misaligned
+ * kv_logw.
+ */
+nabla_status block_sparse_attn_fwd_weighted(const void* q, const void* k, const void* v, void* o,
+                                            int batch, int heads, int L, int d, int N,
+                                            const int32_t* kv_count, const int32_t* kv_index,
+                                            const float* kv_logw, const int32_t* schedule,
+                                            float scale, nabla_dtype dtype, hipStream_t stream);
+
+/*
  * block_sparse_attn_fwd_lse - block_sparse_attn_fwd that also writes what the gradient
  * needs: the natural-log log-sum-exp of every query row over its kept keys,
  *   lse[b,h,a] = log( sum over tokens t of kept blocks of row blk(a) of exp(scale * q_a . k_t) ),

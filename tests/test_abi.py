@@ -257,6 +257,37 @@ def test_attn_raster_validation(lib):
         assert lib.nabla_last_error().decode().startswith("block_sparse_attn_fwd_raster")
 
 
+# ------------------------------------------------------------- SIP entry points
+
+def test_build_mask_sip_validation(lib):
+    def call(**kw):
+        a = dict(q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, budget=4, u=G, scale=0.0,
+                 dt=NABLA_BF16, cnt=C, idx=D_, logw=E, ws=F_, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.nabla_build_mask_sip(a["q"], a["k"], a["batch"], a["heads"], a["T"], a["H"], a["W"], a["d"],
+                                        a["P"], a["N"], a["budget"], a["u"], a["scale"], a["dt"], a["cnt"],
+                                        a["idx"], a["logw"], None, None, a["ws"], a["ws_bytes"], None)
+    for kw, st in ((dict(u=None), NABLA_E_INVAL), (dict(logw=None), NABLA_E_INVAL), (dict(budget=0), NABLA_E_INVAL),
+                   (dict(u=ctypes.c_void_p(0x100002)), NABLA_E_INVAL), (dict(q=None), NABLA_E_INVAL),
+                   (dict(d=96), NABLA_E_UNSUPPORTED), (dict(ws=None), NABLA_E_WORKSPACE)):
+        assert call(**kw) == st, kw
+        assert lib.nabla_last_error().decode().startswith("nabla_build_mask_sip")
+
+
+def test_attn_weighted_validation(lib):
+    def call(**kw):
+        a = dict(q=A, k=B_, v=C, o=D_, batch=1, heads=2, L=1024, d=64, N=64, cnt=E, idx=F_, logw=G, scale=0.0,
+                 dt=NABLA_BF16)
+        a.update(kw)
+        return lib.block_sparse_attn_fwd_weighted(a["q"], a["k"], a["v"], a["o"], a["batch"], a["heads"], a["L"],
+                                                  a["d"], a["N"], a["cnt"], a["idx"], a["logw"], None, a["scale"],
+                                                  a["dt"], None)
+    for kw, st in ((dict(logw=None), NABLA_E_INVAL), (dict(logw=ctypes.c_void_p(0x100001)), NABLA_E_INVAL),
+                   (dict(L=1000), NABLA_E_INVAL), (dict(N=32), NABLA_E_UNSUPPORTED)):
+        assert call(**kw) == st, kw
+        assert lib.nabla_last_error().decode().startswith("block_sparse_attn_fwd_weighted")
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 1024, 64)
