@@ -16,6 +16,7 @@ GB/s against HBM peak ride along, with the oracle timed on the host beside it.
     python bench.py --no-cpu --loop-seconds 12      # steady load for power / clock readings
     python bench.py --gemm-reference                # dense bf16 GEMM of the vendor library
     python bench.py --backward --no-cpu             # the gradient of the attention step
+    python bench.py --sip 185 --no-cpu              # SIP selection + weighted attention
 """
 from __future__ import annotations
 
@@ -171,6 +172,69 @@ def bench_backward(args, cfg, qd, kd, vd) -> int:
     return 0
 
 
+def bench_sip(args, cfg, qd, kd, vd) -> int:
+    """SIP variant of the step on fractal-order tensors: nabla_build_mask_sip (pooling,
+    pooled map, inclusion probabilities, sampling against seeded draws) and
+    block_sparse_attn_fwd_weighted, each bracketed by HIP events."""
+    T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
+    qf, kf, vf = (nab.reorder(t, T, H, W, P) for t in (qd, kd, vd))
+    g = torch.Generator(device="cuda").manual_seed(4321)
+    u = torch.rand((cfg.B, cfg.heads, cfg.nb, cfg.nb), device="cuda", generator=g)
+    ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, N), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(qf)
+    state = {}
+
+    def mask():
+        state["lists"] = nab.build_mask_sip(qf, kf, T, H, W, P, args.sip, u, N, with_schedule=True, workspace=ws)
+
+    def attn():
+        cnt, idx, logw, sched = state["lists"]
+        nab.attn_fwd_weighted(qf, kf, vf, cnt, idx, logw, N, out=o, schedule=sched)
+
+    for _ in range(args.warmup):
+        mask()
+        attn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        mask()
+        e[1].record()
+        attn()
+        e[2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_mask = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    kept = int(state["lists"][0].sum().item())
+    flops = kept * 4.0 * N * N * cfg.d
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    rec = {
+        "metric": "SIP block-sparse attn: kept-tile TFLOP/s (weighted attention), ms/layer",
+        "value": round(flops / (ms_attn * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": f"synthetic ({GENERATOR_VERSION}), draws U[0,1) seeded",
+        "config": {"workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "L": cfg.L,
+                   "blocks_per_head": cfg.nb, "budget": args.sip},
+        "ms_mask_sip": round(ms_mask, 4),
+        "ms_attn_weighted": round(ms_attn, 4),
+        "mean_kept_per_row": round(kept / (cfg.BH * cfg.nb), 2),
+        "attn_frac_of_peak": round(flops / (ms_attn * 1e-3) / 1e12 / peak, 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +250,10 @@ def main(argv=None):
     ap.add_argument("--backward", action="store_true",
                     help="time the gradient of the attention step (block_sparse_attn_bwd) instead of "
                          "the forward path; prints its own JSON line")
+    ap.add_argument("--sip", type=int, default=0, metavar="BUDGET",
+                    help="time the SIP variant instead: sampled selection with this expected number "
+                         "of blocks per row and attention with the Horvitz-Thompson logit shifts; "
+                         "prints its own JSON line")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="time only a dense 8192^3 bf16 GEMM of the vendor library (torch.matmul) "
                          "for --loop-seconds (default 10): the rate a plain GEMM sustains on this "
@@ -299,6 +367,8 @@ def main(argv=None):
 
     if args.backward:
         return bench_backward(args, cfg, qd, kd, vd)
+    if args.sip > 0:
+        return bench_sip(args, cfg, qd, kd, vd)
 
     for _ in range(args.warmup):
         step()
