@@ -8,7 +8,8 @@ from .nabla_oracle import (
     fractal_index, reorder, block_mean, pooled_logits, row_softmax, cdf_values, cdf_keep,
     block_tiles, sta_mask, block_mask, kv_lists, mask_from_lists, attention_block,
     masked_attention, forward, block_lse, masked_attention_lse, masked_attention_backward,
-    sip_probabilities, sip_mask, weighted_block_attention,
+    sip_probabilities, sip_mask, weighted_block_attention, ibcs_clusters, ibcs_scores,
+    ibcs_block_mask,
 )
 
 __all__ = [
@@ -16,4 +17,5 @@ __all__ = [
     "cdf_keep", "block_tiles", "sta_mask", "block_mask", "kv_lists", "mask_from_lists",
     "attention_block", "masked_attention", "forward", "block_lse", "masked_attention_lse",
     "masked_attention_backward", "sip_probabilities", "sip_mask", "weighted_block_attention",
+    "ibcs_clusters", "ibcs_scores", "ibcs_block_mask",
 ]

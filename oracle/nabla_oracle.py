@@ -346,6 +346,84 @@ def masked_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout:
 
 
 # ---------------------------------------------------------------------------
+# IBCS: intra-block clustering selector (AB-Attention page, "Os três recursos do
+# AB-Attention", first feature) as an alternative block score for NABLA's CDF cut
+# ---------------------------------------------------------------------------
+
+IBCS_CLUSTERS = 8
+IBCS_ITERS = 4
+
+
+def _sq_dist_f32(x: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """Squared Euclidean distances [n, k] in float32: per coordinate, difference, then
+    square, each rounded to float32, summed over d in index order (no fused
+    multiply-add, no pairwise summation)."""
+    diff = (x[:, None, :].astype(np.float32) - c[None, :, :].astype(np.float32)).astype(np.float32)
+    sq = (diff * diff).astype(np.float32)
+    return np.add.accumulate(sq, axis=-1, dtype=np.float32)[..., -1]
+
+
+def ibcs_clusters(qblock: np.ndarray, n_clusters: int = IBCS_CLUSTERS, iters: int = IBCS_ITERS):
+    """k-means of one query block's N queries ([N, d]) into n_clusters clusters.
+
+    Readings (the page gives the cluster count, not the algorithm's steps): Lloyd's
+    algorithm; initial centroids are the queries at rows 0, N/k, 2N/k, ...; ``iters``
+    rounds of assign-then-update; a query joins its nearest centroid by squared
+    Euclidean distance, ties to the lowest cluster index; a centroid becomes the mean of
+    its queries (summed in row order in float32, then divided by their count), and an
+    empty cluster keeps its centroid.  Returns (centroids [k, d] float32, weights [k] =
+    fraction of the block's queries in each cluster under the last assignment)."""
+    x = np.asarray(qblock, dtype=np.float32)
+    n = x.shape[0]
+    step = n // n_clusters
+    cent = x[np.arange(n_clusters) * step].copy()
+    assign = np.zeros(n, dtype=np.int64)
+    for _ in range(iters):
+        dist = _sq_dist_f32(x, cent)
+        assign = np.argmin(dist, axis=1)          # first minimum: lowest index on ties
+        for c in range(n_clusters):
+            rows = x[assign == c]
+            if len(rows):
+                total = np.add.accumulate(rows, axis=0, dtype=np.float32)[-1]
+                cent[c] = (total / np.float32(len(rows))).astype(np.float32)
+    weights = np.bincount(assign, minlength=n_clusters).astype(np.float64) / n
+    return cent, weights
+
+
+def ibcs_scores(q: np.ndarray, k: np.ndarray, N: int, scale: Optional[float] = None) -> np.ndarray:
+    """IBCS block scores for [..., L, d] Q, K in fractal order: for query block i with
+    centroids mu_c and weights w_c, A_ij = sum_c w_c softmax_j(scale * mu_c . Kp_j),
+    Kp_j the mean key of block j - the weighted attention of the centroids to the mean
+    keys.  Rows sum to one like NABLA's pooled softmax, so the same CDF cut applies."""
+    d = q.shape[-1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    L = q.shape[-2]
+    nb = L // N
+    lead = q.shape[:-2]
+    qf = np.asarray(q, dtype=np.float32).reshape((-1, L, d))
+    kp = block_mean(np.asarray(k).reshape((-1, L, d)), N, np.float64)
+    A = np.zeros((qf.shape[0], nb, nb))
+    for g in range(qf.shape[0]):
+        for i in range(nb):
+            cent, w = ibcs_clusters(qf[g, i * N:(i + 1) * N])
+            S = (cent.astype(np.float64) @ kp[g].T) * scale                      # [k, nb]
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            A[g, i] = w @ P
+    return A.reshape(lead + (nb, nb))
+
+
+def ibcs_block_mask(q: np.ndarray, k: np.ndarray, N: int, thr: float,
+                    scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """NABLA's CDF cut on the IBCS scores: keep block j of row i iff the mass of the
+    blocks scoring at most A_ij exceeds thr.  Returns mask, F and A."""
+    A = ibcs_scores(q, k, N, scale)
+    A32 = A.astype(np.float32)
+    F = cdf_values(A32)
+    return {"mask": F > F.dtype.type(thr), "F": F, "A": A32}
+
+
+# ---------------------------------------------------------------------------
 # SIP: sampling with inclusion-probability weighting (AB-Attention page, "Os três
 # recursos do AB-Attention", second feature), on NABLA's block scores
 # ---------------------------------------------------------------------------

@@ -513,4 +513,73 @@ def pin_sip_full_budget_is_plain_attention():
     assert np.max(np.abs(out - _sdpa(q, k, v))) <= 1e-12
 
 
+# ---------------------------------------------------------------- IBCS (intra-block clustering)
+
+def pin_ibcs_identical_queries_is_block_mean():
+    """A block whose queries are all equal forms one cluster whose centroid is the block
+    mean: IBCS's row is then exactly NABLA's pooled softmax row."""
+    rng = _rng(40)
+    G, L, N, d = 1, 256, 64, 16
+    nb = L // N
+    q = np.repeat(rng.standard_normal((G, nb, 1, d)), N, axis=2).reshape(G, L, d).astype(np.float32)
+    k = rng.standard_normal((G, L, d)).astype(np.float32) * 2
+    A = O.ibcs_scores(q, k, N, scale=0.3)
+    qp = O.block_mean(q, N, np.float64)
+    kp = O.block_mean(k, N, np.float64)
+    S = qp @ kp.transpose(0, 2, 1) * 0.3
+    ref = np.exp(S - S.max(-1, keepdims=True))
+    ref /= ref.sum(-1, keepdims=True)
+    # the centroid is a float32 running sum of 64 equal queries over 64, which may round
+    # away from the query by a few float32 ulps
+    assert np.max(np.abs(A - ref)) <= 1e-6
+    for i in range(nb):
+        _, w = O.ibcs_clusters(q[0, i * N:(i + 1) * N])
+        # one cluster holds the whole block (which one depends on float32 rounding of the
+        # running mean: a query ties at distance 0 with the untouched initial centroids)
+        assert np.count_nonzero(w) == 1 and w.max() == 1.0
+
+
+def pin_ibcs_separated_groups():
+    """Eight well-separated groups of eight consecutive queries (the initial centroids
+    fall one per group) are recovered: weights 1/8, centroids the group means."""
+    rng = _rng(41)
+    N, d = 64, 12
+    centers = rng.standard_normal((8, d)) * 20
+    x = (np.repeat(centers, 8, axis=0) + rng.standard_normal((N, d)) * 0.1).astype(np.float32)
+    perm = np.concatenate([[g * 8] for g in range(8)] + [[g * 8 + r for r in range(1, 8)] for g in range(8)])
+    cent, w = O.ibcs_clusters(x)
+    assert np.allclose(w, 1.0 / 8)
+    assert np.max(np.abs(cent - x.reshape(8, 8, d).mean(axis=1))) <= 1e-5
+    assert len(perm) == N
+
+
+def pin_ibcs_matches_library_kmeans():
+    """Lloyd's k-means from the same initial centroids, by scikit-learn's implementation."""
+    from sklearn.cluster import KMeans
+    rng = _rng(42)
+    for trial in range(4):
+        N, d = 64, 16
+        x = (rng.standard_normal((N, d)) + (rng.random((N, 1)) > 0.5) * 3).astype(np.float32)
+        cent, w = O.ibcs_clusters(x)
+        init = x[np.arange(8) * 8].astype(np.float64)
+        km = KMeans(n_clusters=8, init=init, n_init=1, max_iter=O.IBCS_ITERS, tol=0.0,
+                    algorithm="lloyd").fit(x.astype(np.float64))
+        assert np.max(np.abs(cent - km.cluster_centers_)) <= 1e-5, trial
+
+
+def pin_ibcs_rows_and_threshold():
+    rng = _rng(43)
+    G, L, N, d = 2, 384, 64, 8
+    q, k = (rng.standard_normal((G, L, d)).astype(np.float32) for _ in range(2))
+    A = O.ibcs_scores(q, k, N)
+    assert np.max(np.abs(A.sum(-1) - 1.0)) <= 1e-12 and np.all(A > 0)
+    r0 = O.ibcs_block_mask(q, k, N, 0.0)
+    assert r0["mask"].all()
+    r = O.ibcs_block_mask(q, k, N, 0.3)
+    # kept mass >= 1 - thr, and the row's largest score is kept
+    kept_mass = np.where(r["mask"], r["A"], 0).sum(-1)
+    assert np.all(kept_mass >= 0.7 - 1e-6)
+    assert np.all(np.take_along_axis(r["mask"], np.argmax(r["A"], -1)[..., None], -1))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -153,6 +153,29 @@ def _sip_logw_sign(A, budget, uniforms):
 def _wattn_shift_ignored(q, k, v, mask, logw, N, scale=None, dtype=np.float64):
     return _orig_wattn(q, k, v, mask, np.zeros_like(logw), N, scale, dtype)
 
+_orig_ibcs_clusters = O.ibcs_clusters
+_orig_ibcs_scores = O.ibcs_scores
+
+
+def _ibcs_uniform_weights(qblock, n_clusters=8, iters=4):
+    cent, w = _orig_ibcs_clusters(qblock, n_clusters, iters)
+    return cent, np.full(n_clusters, 1.0 / n_clusters)
+
+
+def _ibcs_first_rows_init(qblock, n_clusters=8, iters=4):
+    # initial centroids from the first k rows instead of evenly spaced ones
+    x = np.asarray(qblock, dtype=np.float32)
+    y = x.copy()
+    idx = np.arange(n_clusters) * (len(x) // n_clusters)
+    y[idx], y[np.arange(n_clusters)] = x[np.arange(n_clusters)], x[idx]
+    return _orig_ibcs_clusters(y, n_clusters, iters)
+
+
+def _ibcs_softmax_over_centroids(q, k, N, scale=None):
+    A = _orig_ibcs_scores(q, k, N, scale)
+    return np.exp(A) / np.exp(A).sum(-1, keepdims=True)
+
+
 MUTATIONS = [
     ("fractal_index", _fractal_colmajor),
     ("pooled_logits", _pooled_transposed),
@@ -174,6 +197,9 @@ MUTATIONS = [
     ("sip_probabilities", _sip_no_certain_top),
     ("sip_mask", _sip_logw_sign),
     ("weighted_block_attention", _wattn_shift_ignored),
+    ("ibcs_clusters", _ibcs_uniform_weights),
+    ("ibcs_clusters", _ibcs_first_rows_init),
+    ("ibcs_scores", _ibcs_softmax_over_centroids),
 ]
 
 
