@@ -17,6 +17,7 @@ GB/s against HBM peak ride along, with the oracle timed on the host beside it.
     python bench.py --gemm-reference                # dense bf16 GEMM of the vendor library
     python bench.py --backward --no-cpu             # the gradient of the attention step
     python bench.py --sip 185 --no-cpu              # SIP selection + weighted attention
+    python bench.py --ibcs --no-cpu                 # IBCS block scores + attention
 """
 from __future__ import annotations
 
@@ -235,6 +236,77 @@ def bench_sip(args, cfg, qd, kd, vd) -> int:
     return 0
 
 
+def bench_ibcs(args, cfg, qd, kd, vd) -> int:
+    """IBCS variant of the step on fractal-order tensors: nabla_build_mask_ibcs (K
+    pooling, 8 query clusters per block, centroid map, CDF cut, lists) and
+    block_sparse_attn_fwd on its lists, each bracketed by HIP events; the plain NABLA
+    mask on the same inputs is timed beside it."""
+    T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
+    qf, kf, vf = (nab.reorder(t, T, H, W, P) for t in (qd, kd, vd))
+    ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, N, ibcs=True),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(qf)
+    state = {}
+
+    def mask():
+        state["lists"] = nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True,
+                                        workspace=ws, ibcs=True)
+
+    def mask_nabla():
+        nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws)
+
+    def attn():
+        cnt, idx, sched = state["lists"]
+        nab.attn_fwd(qf, kf, vf, cnt, idx, N, out=o, schedule=sched)
+
+    for _ in range(args.warmup):
+        mask()
+        attn()
+        mask_nabla()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        mask()
+        e[1].record()
+        attn()
+        e[2].record()
+        mask_nabla()
+        e[3].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_mask = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_nabla = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    kept = int(state["lists"][0].sum().item())
+    flops = kept * 4.0 * N * N * cfg.d
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    rec = {
+        "metric": "IBCS block-sparse attn: kept-tile TFLOP/s over mask + attention, ms/layer",
+        "value": round(flops / ((ms_mask + ms_attn) * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": f"synthetic ({GENERATOR_VERSION})",
+        "config": {"workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "L": cfg.L,
+                   "blocks_per_head": cfg.nb, "thr": cfg.thr, "sta": cfg.sta},
+        "ms_mask_ibcs": round(ms_mask, 4),
+        "ms_mask_nabla_same_inputs": round(ms_nabla, 4),
+        "ms_attn": round(ms_attn, 4),
+        "kept_fraction": round(kept / (cfg.BH * cfg.nb * cfg.nb), 4),
+        "attn_frac_of_peak": round(flops / (ms_attn * 1e-3) / 1e12 / peak, 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +326,9 @@ def main(argv=None):
                     help="time the SIP variant instead: sampled selection with this expected number "
                          "of blocks per row and attention with the Horvitz-Thompson logit shifts; "
                          "prints its own JSON line")
+    ap.add_argument("--ibcs", action="store_true",
+                    help="time the IBCS variant instead: block scores from 8 query clusters per block, "
+                         "NABLA's CDF cut, attention on the kept tiles; prints its own JSON line")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="time only a dense 8192^3 bf16 GEMM of the vendor library (torch.matmul) "
                          "for --loop-seconds (default 10): the rate a plain GEMM sustains on this "
@@ -369,6 +444,8 @@ def main(argv=None):
         return bench_backward(args, cfg, qd, kd, vd)
     if args.sip > 0:
         return bench_sip(args, cfg, qd, kd, vd)
+    if args.ibcs:
+        return bench_ibcs(args, cfg, qd, kd, vd)
 
     for _ in range(args.warmup):
         step()

@@ -25,6 +25,8 @@ EXPORTS = (
     "nabla_build_mask",
     "nabla_build_mask_raster",
     "nabla_build_mask_sip",
+    "nabla_build_mask_ibcs_workspace_size",
+    "nabla_build_mask_ibcs",
     "block_sparse_attn_fwd_weighted",
     "block_sparse_attn_fwd",
     "block_sparse_attn_fwd_raster",
@@ -67,6 +69,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_build_mask.restype = i
     lib.nabla_build_mask_raster.argtypes = lib.nabla_build_mask.argtypes
     lib.nabla_build_mask_raster.restype = i
+    lib.nabla_build_mask_ibcs.argtypes = lib.nabla_build_mask.argtypes
+    lib.nabla_build_mask_ibcs.restype = i
+    lib.nabla_build_mask_ibcs_workspace_size.argtypes = [i, i, i, i, i]
+    lib.nabla_build_mask_ibcs_workspace_size.restype = sz
     lib.block_sparse_attn_fwd_raster.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, f, i, vp]
     lib.block_sparse_attn_fwd_raster.restype = i
     lib.nabla_build_mask_sip.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, vp, f, i, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -134,8 +140,11 @@ def reorder(x: torch.Tensor, T: int, H: int, W: int, P: int, inverse: bool = Fal
     return out
 
 
-def build_mask_workspace_size(batch: int, heads: int, L: int, d: int, N: int = 64) -> int:
-    return int(load_library().nabla_build_mask_workspace_size(batch, heads, L, d, N))
+def build_mask_workspace_size(batch: int, heads: int, L: int, d: int, N: int = 64,
+                              ibcs: bool = False) -> int:
+    lib = load_library()
+    fn = lib.nabla_build_mask_ibcs_workspace_size if ibcs else lib.nabla_build_mask_workspace_size
+    return int(fn(batch, heads, L, d, N))
 
 
 def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int, N: int = 64,
@@ -143,9 +152,11 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
                scale: Optional[float] = None, with_bitmap: bool = False,
                with_schedule: bool = False, workspace: Optional[torch.Tensor] = None,
                kv_count: Optional[torch.Tensor] = None, kv_index: Optional[torch.Tensor] = None,
-               schedule: Optional[torch.Tensor] = None, raster: bool = False):
+               schedule: Optional[torch.Tensor] = None, raster: bool = False,
+               ibcs: bool = False):
     """NABLA block mask of fractal-ordered Q, K (``raster=True``: Q, K in raster order,
-    the fractal flattening applied in the addressing; needs N == P*P).
+    the fractal flattening applied in the addressing; needs N == P*P; ``ibcs=True``: the
+    block scores come from 8 query clusters per block instead of the mean query).
 
     Returns (kv_count, kv_index), plus the bitmap and/or the longest-first
     schedule when asked for (in that order)."""
@@ -164,11 +175,13 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
         bitmap = torch.empty((B, NH, nb, (nb + 31) // 32), dtype=torch.int32, device=dev)
     if with_schedule and schedule is None:
         schedule = torch.empty((B * NH * nb,), dtype=torch.int32, device=dev)
-    ws_bytes = lib.nabla_build_mask_workspace_size(B, NH, L, d, N)
+    if raster and ibcs:
+        raise ValueError("IBCS scores are implemented for fractal-ordered inputs only")
+    ws_bytes = build_mask_workspace_size(B, NH, L, d, N, ibcs=ibcs)
     if workspace is None:
         workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
     win = None if sta is None else ctypes.byref(StaWindow(*sta))
-    entry = lib.nabla_build_mask_raster if raster else lib.nabla_build_mask
+    entry = lib.nabla_build_mask_raster if raster else (lib.nabla_build_mask_ibcs if ibcs else lib.nabla_build_mask)
     _check(entry(
         _dev(q, "q"), _dev(k, "k"), B, NH, T, H, W, d, P, N, float(thr), win,
         float(scale) if scale is not None else 0.0, _dtype_code(q),

@@ -4,6 +4,9 @@
 //   map_select_kernel  reduced map S = Qp Kp^T * scale on float32 MFMA, row softmax,
 //                      the CDF cutoff found by bisection on float32 bit patterns, the
 //                      STA OR, and compaction of each row into an ascending kept list.
+// With IBCS block scores the rows of the map are the 8 cluster centroids of each query
+// block (ibcs.hip) instead of its mean, and a block's score row is the weighted sum of
+// its centroids' softmax rows; the cut and the lists are the same.
 #include <math.h>
 
 #include "attn_tile.h"
@@ -50,12 +53,12 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
                                                     const T* __restrict__ k,
                                                     float* __restrict__ qp,
                                                     float* __restrict__ kp, int total_blocks, int nb,
-                                                    int L, attn::RasterGrid grid) {
+                                                    int L, attn::RasterGrid grid, int first_wave) {
     constexpr int EPC = Elem<T>::kPerChunk;
     constexpr int CHUNKS = D / EPC;          // 16-byte chunks per token
     constexpr int G = 64 / CHUNKS;           // tokens per load instruction
     constexpr int ITERS = N / G;
-    const int wave = (blockIdx.x * 256 + threadIdx.x) >> 6;
+    const int wave = first_wave + ((blockIdx.x * 256 + threadIdx.x) >> 6);
     const int lane = threadIdx.x & 63;
     if (wave >= 2 * total_blocks) return;
     const bool is_k = wave >= total_blocks;
@@ -257,20 +260,26 @@ __device__ void sip_row(float* arow, int nb, float inv_sum, int budget, const fl
     if (lane == 0) *out_count = base;
 }
 
+// `arows` holds the map's rows: n_arows = nb pooled queries per head, or with IBCS
+// (cw != null) n_arows = 8 nb centroids per head, cw their weights.
+static_assert(kRows % kIbcsClusters == 0, "a workgroup holds whole query blocks' centroids");
+
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
-    const float* __restrict__ qp, const float* __restrict__ kp, int nb, int ld_s, float scale,
-    float thr, int sta, int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
-    int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int sip_budget,
-    const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
+    const float* __restrict__ arows, int n_arows, const float* __restrict__ cw, const float* __restrict__ kp,
+    int nb, int ld_s, float scale, float thr, int sta, int nH, int nW, int rt, int rh, int rw,
+    int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap,
+    int sip_budget, const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
     extern __shared__ float s_lds[];   // [kRows][ld_s] rows, then [kWaves][kCap] candidates
     constexpr int KC = D / 4;          // k values per lane per MFMA chain
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kRows;
-    const float* qh = qp + (size_t)bh * nb * D;
+    const bool ibcs = cw != nullptr;
+    const float* qh = arows + (size_t)bh * n_arows * D;
     const float* kh = kp + (size_t)bh * nb * D;
+    constexpr float kLog2e = 1.4426950408889634f;
 
     // ---- phase 1: S tiles.  The MFMA's k index (lane / 16) selects a contiguous
     // quarter of d in both operands, so operand loads are 16-byte vectors.
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
         const int kq = lane >> 4;
         float a[KC];
         const int qrow = row0 + li;
-        if (qrow < nb) {
+        if (qrow < n_arows) {
             const f32x4* src = reinterpret_cast<const f32x4*>(qh + (size_t)qrow * D + kq * KC);
 #pragma unroll
             for (int v = 0; v < KC / 4; ++v) {
@@ -332,26 +341,61 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
     }
     __syncthreads();
 
-    // ---- phase 2: one row per wave at a time.
+    // ---- IBCS: each centroid row becomes w_c softmax(row), one row per wave
+    if (ibcs) {
+        for (int r = wave; r < kRows; r += kWaves) {
+            const int crow = row0 + r;
+            if (crow >= n_arows) break;
+            float* srow = s_lds + r * ld_s;
+            float mx = -INFINITY;
+            for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, srow[j]);
+            const float mx2 = wave_max(mx) * kLog2e;
+            float sum = 0.f;
+            for (int j = lane; j < nb; j += 64) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(srow[j], kLog2e, -mx2));
+                srow[j] = e;
+                sum += e;
+            }
+            const float f = cw[(size_t)bh * n_arows + crow] / wave_sum(sum);
+            for (int j = lane; j < nb; j += 64) srow[j] *= f;
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 2: one row (query block) per wave at a time.
     float* cand = s_lds + kRows * ld_s + wave * kCap;
     const int nwords = (nb + 31) >> 5;
-    for (int r = wave; r < kRows; r += kWaves) {
-        const int row = row0 + r;
+    const int out_rows = ibcs ? kRows / kIbcsClusters : kRows;
+    for (int r = wave; r < out_rows; r += kWaves) {
+        const int row = (ibcs ? row0 / kIbcsClusters : row0) + r;
         if (row >= nb) break;
-        float* arow = s_lds + r * ld_s;
-        // softmax; the row is overwritten with the probabilities A
-        float mx = -INFINITY;
-        for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, arow[j]);
-        mx = wave_max(mx);
-        constexpr float kLog2e = 1.4426950408889634f;
-        const float mx2 = mx * kLog2e;
-        float sum = 0.f;
-        for (int j = lane; j < nb; j += 64) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(arow[j], kLog2e, -mx2));
-            arow[j] = e;
-            sum += e;
+        float* arow;
+        float inv_sum;
+        if (ibcs) {
+            // A = sum over the block's clusters, in cluster order; rows already sum to one
+            arow = s_lds + r * kIbcsClusters * ld_s;
+            for (int j = lane; j < nb; j += 64) {
+                float a = arow[j];
+#pragma unroll
+                for (int c = 1; c < kIbcsClusters; ++c) a += arow[c * ld_s + j];
+                arow[j] = a;
+            }
+            inv_sum = 1.0f;
+        } else {
+            // softmax; the row is overwritten with the probabilities A
+            arow = s_lds + r * ld_s;
+            float mx = -INFINITY;
+            for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, arow[j]);
+            mx = wave_max(mx);
+            const float mx2 = mx * kLog2e;
+            float sum = 0.f;
+            for (int j = lane; j < nb; j += 64) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(arow[j], kLog2e, -mx2));
+                arow[j] = e;
+                sum += e;
+            }
+            inv_sum = 1.0f / wave_sum(sum);
         }
-        const float inv_sum = 1.0f / wave_sum(sum);
         if (sip_budget > 0) {
             sip_row(arow, nb, inv_sum, sip_budget, uniforms + ((size_t)bh * nb + row) * nb,
                     kv_index + ((size_t)bh * nb + row) * nb, kv_logw + ((size_t)bh * nb + row) * nb,
@@ -525,17 +569,18 @@ template <typename T, int D>
 hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
     const int total = a.BH * a.nb;
     const int waves = 2 * total;
+    const int first = a.ibcs ? total : 0;   // IBCS clusters Q instead of pooling it
     attn::RasterGrid grid{};
     if (a.raster) {
         grid.W = (uint32_t)a.W;
         grid.HW = (uint32_t)(a.H * a.W);
         grid.nHW = FastDiv((uint32_t)(a.nH * a.nW));
         grid.nW = FastDiv((uint32_t)a.nW);
-        hipLaunchKernelGGL((pool_kernel<T, D, 64, true>), dim3((waves + 3) / 4), dim3(256), 0, s,
-                           (const T*)a.q, (const T*)a.k, a.qp, a.kp, total, a.nb, a.nb * 64, grid);
+        hipLaunchKernelGGL((pool_kernel<T, D, 64, true>), dim3((waves - first + 3) / 4), dim3(256), 0, s,
+                           (const T*)a.q, (const T*)a.k, a.qp, a.kp, total, a.nb, a.nb * 64, grid, first);
     } else {
-        hipLaunchKernelGGL((pool_kernel<T, D, 64, false>), dim3((waves + 3) / 4), dim3(256), 0, s,
-                           (const T*)a.q, (const T*)a.k, a.qp, a.kp, total, a.nb, a.nb * 64, grid);
+        hipLaunchKernelGGL((pool_kernel<T, D, 64, false>), dim3((waves - first + 3) / 4), dim3(256), 0, s,
+                           (const T*)a.q, (const T*)a.k, a.qp, a.kp, total, a.nb, a.nb * 64, grid, first);
     }
     return hipGetLastError();
 }
@@ -548,10 +593,11 @@ hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
     const int max_lds = (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap) * (int)sizeof(float);
     hipError_t e = set_max_dynamic_lds((const void*)map_select_kernel<D>, max_lds, lds_set);
     if (e != hipSuccess) return e;
-    dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
-    hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.qp, a.kp, a.nb,
-                       ld_s, a.scale, a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count,
-                       a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
+    const int n_arows = a.ibcs ? a.nb * kIbcsClusters : a.nb;
+    dim3 grid((n_arows + kRows - 1) / kRows, a.BH);
+    hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.ibcs ? a.cent : a.qp, n_arows,
+                       a.ibcs ? a.cent_w : nullptr, a.kp, a.nb, ld_s, a.scale, a.thr, a.sta, a.nH, a.nW, a.rt,
+                       a.rh, a.rw, a.kv_count, a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
     return hipGetLastError();
 }
 
@@ -565,6 +611,7 @@ hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
         e = (a.d == 128) ? launch_pool<float, 128>(a, s) : launch_pool<float, 64>(a, s);
     }
     if (e != hipSuccess) return e;
+    if (a.ibcs && (e = launch_ibcs_cluster(a, s)) != hipSuccess) return e;
     e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
     if (e != hipSuccess || !a.schedule) return e;
     // one wave per head; its bins fit the default LDS limit (NABLA_MAX_BLOCKS + 1 ints)

@@ -84,6 +84,15 @@ size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N
     return ((2 * one) + 255) & ~(size_t)255;
 }
 
+size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, int N) {
+    if (batch <= 0 || heads <= 0 || L <= 0 || d <= 0 || N <= 0 || L % N) return 0;
+    const size_t blocks = (size_t)batch * heads * (size_t)(L / N);
+    const size_t kp = (blocks * d * sizeof(float) + 255) & ~(size_t)255;
+    const size_t cent = (blocks * nabla::kIbcsClusters * d * sizeof(float) + 255) & ~(size_t)255;
+    const size_t cw = (blocks * nabla::kIbcsClusters * sizeof(float) + 255) & ~(size_t)255;
+    return kp + cent + cw;
+}
+
 namespace {
 
 nabla_status build_mask_impl(const char* who, int raster, const void* q, const void* k, int batch,
@@ -92,7 +101,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                              int32_t* schedule, void* workspace, size_t workspace_bytes,
                              hipStream_t stream, int sip_budget = 0, const float* uniforms = nullptr,
-                             float* kv_logw = nullptr);
+                             float* kv_logw = nullptr, int ibcs = 0);
 
 }  // namespace
 
@@ -121,6 +130,17 @@ nabla_status nabla_build_mask_sip(const void* q, const void* k, int batch, int h
                            uniforms, kv_logw);
 }
 
+nabla_status nabla_build_mask_ibcs(const void* q, const void* k, int batch, int heads, int T, int H,
+                                   int W, int d, int P, int N, float thr,
+                                   const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                                   int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                                   int32_t* schedule, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    return build_mask_impl("nabla_build_mask_ibcs", 0, q, k, batch, heads, T, H, W, d, P, N, thr, sta, scale,
+                           dtype, kv_count, kv_index, bitmap, schedule, workspace, workspace_bytes, stream, 0,
+                           nullptr, nullptr, 1);
+}
+
 nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, int heads, int T, int H,
                                      int W, int d, int P, int N, float thr,
                                      const nabla_sta_window* sta, float scale, nabla_dtype dtype,
@@ -140,7 +160,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                              int32_t* schedule, void* workspace, size_t workspace_bytes,
                              hipStream_t stream, int sip_budget, const float* uniforms,
-                             float* kv_logw) {
+                             float* kv_logw, int ibcs) {
     if (!q || !k || !kv_count || !kv_index) return fail(NABLA_E_INVAL, "%s: null pointer", who);
     if (!aligned16(q) || !aligned16(k) || ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3) ||
         ((uintptr_t)bitmap & 3) || ((uintptr_t)schedule & 3))
@@ -167,9 +187,11 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     const long long nb = L / N;
     if (nb > NABLA_MAX_BLOCKS)
         return fail(NABLA_E_UNSUPPORTED, "%s: %lld blocks per head exceed %d", who, nb, NABLA_MAX_BLOCKS);
-    if ((long long)batch * heads > 65535 || L * d >= kMaxHeadElems)
+    // the launches cover up to 256 threads per block of every head with 32-bit thread ids
+    if ((long long)batch * heads > 65535 || L * d >= kMaxHeadElems || (long long)batch * heads * nb >= (1ll << 24))
         return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
-    const size_t need = nabla_build_mask_workspace_size(batch, heads, (int)L, d, N);
+    const size_t need = ibcs ? nabla_build_mask_ibcs_workspace_size(batch, heads, (int)L, d, N)
+                             : nabla_build_mask_workspace_size(batch, heads, (int)L, d, N);
     if (!workspace || workspace_bytes < need)
         return fail(NABLA_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -195,8 +217,21 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     a.kv_index = kv_index;
     a.bitmap = bitmap;
     a.schedule = schedule;
-    a.qp = (float*)workspace;
-    a.kp = a.qp + (size_t)a.BH * nb * d;
+    if (ibcs) {
+        // [Kp | centroids | weights], sections 256-byte aligned
+        const size_t blocks = (size_t)a.BH * nb;
+        char* base = (char*)workspace;
+        a.qp = nullptr;
+        a.kp = (float*)base;
+        base += (blocks * d * sizeof(float) + 255) & ~(size_t)255;
+        a.cent = (float*)base;
+        base += (blocks * nabla::kIbcsClusters * d * sizeof(float) + 255) & ~(size_t)255;
+        a.cent_w = (float*)base;
+        a.ibcs = 1;
+    } else {
+        a.qp = (float*)workspace;
+        a.kp = a.qp + (size_t)a.BH * nb * d;
+    }
     a.bf16 = dtype == NABLA_BF16;
     a.raster = raster;
     a.H = H;

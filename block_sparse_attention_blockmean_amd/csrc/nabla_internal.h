@@ -62,6 +62,10 @@ struct ReorderArgs {
 };
 hipError_t launch_reorder(const ReorderArgs& a, hipStream_t s);
 
+// IBCS clustering: centroids per query block and Lloyd rounds.
+constexpr int kIbcsClusters = 8;
+constexpr int kIbcsIters = 4;
+
 struct MaskArgs {
     const void* q;
     const void* k;
@@ -82,8 +86,12 @@ struct MaskArgs {
     int sip_budget;         // > 0: sampled selection with this expected budget per row (no CDF cut)
     const float* uniforms;  // SIP draws [BH, nb, nb]
     float* kv_logw;         // SIP out: log(1 / pi) per list entry [BH, nb, nb]
+    int ibcs;               // 1: rows of the map are IBCS centroids (Q is clustered, not pooled)
+    float* cent;            // IBCS workspace [BH, nb * kIbcsClusters, d] centroids
+    float* cent_w;          // IBCS workspace [BH, nb * kIbcsClusters] cluster weights
 };
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
+hipError_t launch_ibcs_cluster(const MaskArgs& a, hipStream_t s);
 
 struct AttnArgs {
     const void* q;

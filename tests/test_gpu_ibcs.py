@@ -1,0 +1,173 @@
+"""GPU parity of the IBCS block scores (8 query clusters per block scoring the mean keys)
+against the oracle.
+
+The clustering is a fixed sequence of individually rounded float32 operations, so the
+centroids and weights the kernels leave in the workspace ([Kp | centroids | weights],
+sections 256-byte aligned) must equal the oracle's bit for bit.  The mask must equal the
+oracle's CDF cut of its float64 scores except at the cutoff (the band of the NABLA mask
+test: the GPU's scores are float32)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import CONFIGS, Config, make_qkv
+import block_sparse_attention_blockmean_amd as nab
+from parity import bitmap_to_mask, check_mask, lists_to_mask
+
+pytestmark = pytest.mark.gpu
+
+K = O.IBCS_CLUSTERS
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(name, T, H, W, d, dtype, thr, sta=None, heads=2, B=1):
+    return Config(name, 12, B=B, heads=heads, d=d, dtype=dtype, T=T, H=H, W=W, P=8, N=64, thr=thr,
+                  sta=sta, scale_logits=(dtype == "bf16"))
+
+
+def _up256(n):
+    return (n + 255) // 256 * 256
+
+
+def gpu_ibcs(cfg, qf, kf, thr, sta=None):
+    """IBCS mask of fractal-ordered GPU tensors; returns lists, bitmap, and the
+    centroids [G, nb, 8, d] and weights [G, nb, 8] read back from the workspace."""
+    G, nb, d = cfg.BH, cfg.nb, cfg.d
+    nbytes = nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, d, cfg.N, ibcs=True)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=qf.device)
+    cnt, idx, bm = nab.build_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, sta, with_bitmap=True,
+                                  workspace=ws, ibcs=True)
+    torch.cuda.synchronize()
+    o_cent = _up256(G * nb * d * 4)
+    o_w = o_cent + _up256(G * nb * K * d * 4)
+    host = ws.cpu()
+    cent = host[o_cent:o_cent + G * nb * K * d * 4].view(torch.float32).numpy().reshape(G, nb, K, d)
+    w = host[o_w:o_w + G * nb * K * 4].view(torch.float32).numpy().reshape(G, nb, K)
+    m = lists_to_mask(cnt.cpu().numpy().reshape(G, nb), idx.cpu().numpy().reshape(G, nb, nb))
+    assert np.array_equal(bitmap_to_mask(bm.cpu().numpy().reshape(G, nb, -1), nb), m)
+    return dict(cnt=cnt, idx=idx, mask=m, cent=cent, w=w)
+
+
+def check_clusters(res, qf_np, N, heads, blocks=None):
+    """Centroids bit for bit, weights exactly, for the given heads (and blocks)."""
+    nb = res["cent"].shape[1]
+    n = 0
+    for g in heads:
+        for i in (range(nb) if blocks is None else blocks):
+            cent, w = O.ibcs_clusters(qf_np[g, i * N:(i + 1) * N])
+            gc = res["cent"][g, i]
+            assert np.array_equal(gc.view(np.uint32), cent.view(np.uint32)), (
+                f"head {g} block {i}: centroids differ, max-abs {np.max(np.abs(gc - cent)):.3e}")
+            assert np.array_equal(res["w"][g, i].astype(np.float64), w), (g, i, res["w"][g, i], w)
+            n += 1
+    return n
+
+
+def oracle_mask(cfg, qf_np, kf_np, thr, sta=None):
+    ref = O.ibcs_block_mask(qf_np, kf_np, cfg.N, thr)
+    mask = ref["mask"]
+    if sta is not None:
+        mask = mask | O.sta_mask(cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, sta)[None]
+    return mask, ref["A"]
+
+
+CASES = [
+    small("bf16_d128_nb75", 5, 24, 40, 128, "bf16", 0.2, heads=1, B=2),
+    small("bf16_d64", 3, 32, 16, 64, "bf16", 0.1, heads=3),
+    small("bf16_d128_sta", 4, 16, 32, 128, "bf16", 0.3, sta=(3, 3, 3)),
+    small("f32_d64", 4, 16, 32, 64, "f32", 0.2),
+    small("f32_d128_nb3", 3, 8, 8, 128, "f32", 0.05),
+]
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+def test_ibcs_parity(cfg):
+    say(f"IBCS {cfg.name}: {cfg.B}x{cfg.heads} nb {cfg.nb} d{cfg.d} {cfg.dtype} thr {cfg.thr} sta {cfg.sta}")
+    q, k, v = make_qkv(cfg)
+    G = cfg.BH
+    qf = nab.reorder(q.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    kf = nab.reorder(k.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    res = gpu_ibcs(cfg, qf, kf, cfg.thr, cfg.sta)
+    qn = qf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)
+    kn = kf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)
+    n = check_clusters(res, qn, cfg.N, range(G))
+    ref_m, ref_A = oracle_mask(cfg, qn, kn, cfg.thr, cfg.sta)
+    mism, band = check_mask(res["mask"], ref_m, ref_A, cfg.thr)
+    say(f"  {n} blocks' centroids bit-identical; kept {res['mask'].mean():.3f}, mask mismatches {mism}, "
+        f"band {band}")
+    # the top block of every row is kept, as in NABLA
+    top = np.argmax(ref_A, axis=-1)
+    assert np.all(np.take_along_axis(res["mask"], top[..., None], axis=-1))
+
+
+def test_identical_queries_reduce_to_nabla():
+    """When all 64 queries of every block are equal, every query joins cluster 0 (all
+    distances tie), its centroid is the query and its weight 1, so the IBCS score row is
+    NABLA's pooled softmax row: the lists must equal nabla_build_mask's bit for bit."""
+    cfg = small("const_blocks", 3, 16, 24, 128, "bf16", 0.2, heads=2)
+    q, k, _ = make_qkv(cfg)
+    qf = nab.reorder(q.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    kf = nab.reorder(k.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    G, nb, N, d = cfg.BH, cfg.nb, cfg.N, cfg.d
+    qc = qf.reshape(G, nb, N, d)[:, :, :1, :].expand(G, nb, N, d).reshape(qf.shape).contiguous()
+    res = gpu_ibcs(cfg, qc, kf, cfg.thr)
+    assert np.all(res["w"][:, :, 0] == 1.0) and np.all(res["w"][:, :, 1:] == 0.0)
+    first = qc.float().cpu().numpy().reshape(G, nb, N, d)[:, :, 0, :]
+    assert np.array_equal(res["cent"][:, :, 0, :], first)
+    ref = nab.build_mask(qc, kf, cfg.T, cfg.H, cfg.W, cfg.P, N, cfg.thr, with_bitmap=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0].cpu(), res["cnt"].cpu())
+    assert np.array_equal(lists_to_mask(ref[0].cpu().numpy().reshape(G, nb), ref[1].cpu().numpy().reshape(G, nb, nb)),
+                          res["mask"])
+    say(f"IBCS on constant blocks equals the NABLA mask: kept {res['mask'].mean():.3f}")
+
+
+def test_ibcs_determinism_and_workspace_reuse():
+    """Two calls give identical lists; a dirty workspace (left by another call) changes
+    nothing."""
+    cfg = CASES[1]
+    q, k, _ = make_qkv(cfg)
+    qf = nab.reorder(q.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    kf = nab.reorder(k.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    nbytes = nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, cfg.N, ibcs=True)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device="cuda")
+    a = nab.build_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr, workspace=ws, ibcs=True)
+    b = nab.build_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr, ibcs=True)
+    torch.cuda.synchronize()
+    # only the first kv_count entries of a row are written
+    G, nb = cfg.BH, cfg.nb
+    assert torch.equal(a[0], b[0])
+    ma = lists_to_mask(a[0].cpu().numpy().reshape(G, nb), a[1].cpu().numpy().reshape(G, nb, nb))
+    mb = lists_to_mask(b[0].cpu().numpy().reshape(G, nb), b[1].cpu().numpy().reshape(G, nb, nb))
+    assert np.array_equal(ma, mb)
+
+
+def test_ibcs_full_size():
+    """The Wan-1.3B-like layer at full size: every head through the GPU; centroids of two
+    heads bit for bit and their masks against the oracle."""
+    cfg = CONFIGS[1]
+    say(f"IBCS full size {cfg.name}: {cfg.BH} heads nb {cfg.nb}")
+    q, k, _ = make_qkv(cfg)
+    G = cfg.BH
+    qf = nab.reorder(q.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    kf = nab.reorder(k.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    res = gpu_ibcs(cfg, qf, kf, cfg.thr)
+    say(f"  GPU mask built: kept {res['mask'].mean():.4f}")
+    heads = [0, G - 1]
+    qn = qf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)[heads]
+    kn = kf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)[heads]
+    sub = dict(cent=res["cent"][heads], w=res["w"][heads])
+    n = check_clusters(sub, qn, cfg.N, range(len(heads)))
+    say(f"  {n} blocks' centroids bit-identical")
+    ref_m, ref_A = oracle_mask(cfg, qn, kn, cfg.thr)
+    mism, band = check_mask(res["mask"][heads], ref_m, ref_A, cfg.thr)
+    say(f"  heads {heads}: mask mismatches {mism}, band {band}")
