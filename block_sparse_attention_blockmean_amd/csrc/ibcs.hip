@@ -44,21 +44,22 @@ __device__ inline void unpack16(const u32x4_t& v, float, float* out) {
     out[3] = __uint_as_float(v.w);
 }
 
-// One workgroup per query block (bh * nb + i).  LDS rows are padded to D + 1 floats so
-// that the 16 queries a wave reads at one coordinate fall in distinct banks.  Float
-// contraction is off in the whole kernel: each +, - and * rounds on its own, and the
-// division is the correctly rounded one (hipcc's default for float32 division).
+// One workgroup per query block (bh * nb + i).  LDS rows are padded by 16 bytes (d + 4
+// floats): row t starts 4 t banks further on, so the 16 queries a wave reads with one
+// 16-byte load fall in distinct bank groups.  Float contraction is off in the whole
+// kernel: each +, - and * rounds on its own, and the division is the correctly rounded
+// one (hipcc's default for float32 division).
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restrict__ q, float* __restrict__ cent,
                                                                 float* __restrict__ weight) {
 #pragma clang fp contract(off)
-    constexpr int LD = D + 1;
+    constexpr int LD = D + 4;
     constexpr int EPC = 16 / sizeof(T);                       // elements per 16-byte chunk
-    __shared__ float xq[kBlkQ * LD];
-    __shared__ float cen[kIbcsClusters * LD];
-    __shared__ float dist[kBlkQ * kPerQuery];
-    __shared__ int best[kBlkQ * kPerQuery];
-    __shared__ int assign[kBlkQ];
+    __shared__ __align__(16) float xq[kBlkQ * LD];
+    __shared__ __align__(16) float cen[kIbcsClusters * LD];
+    __shared__ float dist[kThreads];
+    __shared__ int best[kThreads];
+    __shared__ int members[kIbcsClusters * kBlkQ];           // each cluster's queries in row order
     __shared__ int counts[kIbcsClusters];
 
     const size_t blk = blockIdx.x;
@@ -69,7 +70,8 @@ __global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restr
         unpack16(__builtin_nontemporal_load(src + ch), T{}, v);
         const int row = ch / (D / EPC), col = (ch % (D / EPC)) * EPC;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) xq[row * LD + col + e] = v[e];
+        for (int e = 0; e < EPC; e += 4)
+            *reinterpret_cast<float4*>(xq + row * LD + col + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
     }
     __syncthreads();
     for (int e = tid; e < kIbcsClusters * D; e += kThreads) {
@@ -79,20 +81,32 @@ __global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restr
     __syncthreads();
 
     for (int it = 0; it < kIbcsIters; ++it) {
-        // assign, part 1: thread (query t, slot p) measures centroids kPerThread p + m
+        // assign, part 1: thread (query t, slot p) measures centroids kPerThread p + m,
+        // coordinates in index order
         {
             const int t = tid / kPerQuery, p = tid % kPerQuery;
-            const float* x = xq + t * LD;
-            const float* cp = cen + p * kPerThread * LD;
+            const float4* x4 = reinterpret_cast<const float4*>(xq + t * LD);
+            const float4* c4 = reinterpret_cast<const float4*>(cen + p * kPerThread * LD);
             float acc[kPerThread];
 #pragma unroll
             for (int m = 0; m < kPerThread; ++m) acc[m] = 0.f;
-            for (int e = 0; e < D; ++e) {
-                const float xe = x[e];
+#pragma unroll 4
+            for (int e4 = 0; e4 < D / 4; ++e4) {
+                const float4 xv = x4[e4];
 #pragma unroll
                 for (int m = 0; m < kPerThread; ++m) {
-                    const float df = xe - cp[m * LD + e];
-                    const float sq = df * df;
+                    const float4 cv = c4[m * (LD / 4) + e4];
+                    float df = xv.x - cv.x;
+                    float sq = df * df;
+                    acc[m] = acc[m] + sq;
+                    df = xv.y - cv.y;
+                    sq = df * df;
+                    acc[m] = acc[m] + sq;
+                    df = xv.z - cv.z;
+                    sq = df * df;
+                    acc[m] = acc[m] + sq;
+                    df = xv.w - cv.w;
+                    sq = df * df;
                     acc[m] = acc[m] + sq;
                 }
             }
@@ -109,8 +123,10 @@ __global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restr
             best[tid] = bc;
         }
         __syncthreads();
-        // assign, part 2: the slots hold increasing cluster ranges, so a strict compare
-        // in slot order keeps the lowest index among equal distances
+        // assign, part 2 (wave 0, lane = query): the slots hold increasing cluster
+        // ranges, so a strict compare in slot order keeps the lowest index among equal
+        // distances.  Each cluster's member list is then filled in row order by ballot
+        // ranks.
         if (tid < kBlkQ) {
             float bd = dist[tid * kPerQuery];
             int bc = best[tid * kPerQuery];
@@ -122,25 +138,29 @@ __global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restr
                     bc = best[tid * kPerQuery + p];
                 }
             }
-            assign[tid] = bc;
+            const uint64_t below = (1ull << tid) - 1ull;
+#pragma unroll
+            for (int c = 0; c < kIbcsClusters; ++c) {
+                const uint64_t in = __ballot(bc == c);
+                if (bc == c) members[c * kBlkQ + __popcll(in & below)] = tid;
+                if (tid == 0) counts[c] = __popcll(in);
+            }
         }
         __syncthreads();
         // update: thread (cluster c, part) owns coordinates part, part + kPerCluster, ...
+        // and sums them over the cluster's queries in row order
         {
             const int c = tid / kPerCluster, part = tid % kPerCluster;
             constexpr int NC = D / kPerCluster;
-            int cnt = 0;
+            const int cnt = counts[c];
             float acc[NC];
 #pragma unroll
             for (int m = 0; m < NC; ++m) acc[m] = 0.f;
-            for (int t = 0; t < kBlkQ; ++t) {
-                if (assign[t] == c) {
-                    ++cnt;
+            for (int n = 0; n < cnt; ++n) {
+                const float* x = xq + members[c * kBlkQ + n] * LD + part;
 #pragma unroll
-                    for (int m = 0; m < NC; ++m) acc[m] = acc[m] + xq[t * LD + part + m * kPerCluster];
-                }
+                for (int m = 0; m < NC; ++m) acc[m] = acc[m] + x[m * kPerCluster];
             }
-            if (part == 0) counts[c] = cnt;
             if (cnt > 0) {
                 const float fc = (float)cnt;
 #pragma unroll

@@ -5,8 +5,9 @@
 //                      the CDF cutoff found by bisection on float32 bit patterns, the
 //                      STA OR, and compaction of each row into an ascending kept list.
 // With IBCS block scores the rows of the map are the 8 cluster centroids of each query
-// block (ibcs.hip) instead of its mean, and a block's score row is the weighted sum of
-// its centroids' softmax rows; the cut and the lists are the same.
+// block (ibcs.hip) instead of its mean: ibcs_score_kernel forms each block's score row
+// as the weighted sum of its centroids' softmax rows, and map_select_kernel takes those
+// rows as given; the cut and the lists are the same.
 #include <math.h>
 
 #include "attn_tile.h"
@@ -260,130 +261,176 @@ __device__ void sip_row(float* arow, int nb, float inv_sum, int budget, const fl
     if (lane == 0) *out_count = base;
 }
 
-// `arows` holds the map's rows: n_arows = nb pooled queries per head, or with IBCS
-// (cw != null) n_arows = 8 nb centroids per head, cw their weights.
+// ---------------------------------------------------------------------------
+// Rows of the reduced map: S[r][j] = scale * X[row0 + r] . Kp_j for the workgroup's
+// kRows rows r (rows past n_rows use zero operands), parked in LDS rows of ld_s floats.
+// The NW waves take column tiles of 16 blocks in turn with v_mfma_f32_16x16x4_f32
+// (float32 operands and accumulation).  Lane (row l % 16, group g = l / 16) supplies
+// coordinate 16 v + 4 g + i of its row at MFMA step 4 v + i, in both operands: each
+// 16-byte load instruction then reads 64 contiguous bytes of each of 16 rows (16 cache
+// lines), where a contiguous quarter of d per lane would touch 64 lines per instruction
+// and leave the loads bound by the texture unit's per-line rate.
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__device__ inline void map_rows(const float* __restrict__ xh, int n_rows, int row0, const float* __restrict__ kh,
+                                int nb, int ld_s, float scale, float* s_lds, int wave, int lane) {
+    constexpr int KC = D / 4;          // k values per lane per MFMA chain
+    const int li = lane & 15;
+    const int kq = lane >> 4;
+    float a[KC];
+    const int qrow = row0 + li;
+    if (qrow < n_rows) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(xh + (size_t)qrow * D) + kq;
+#pragma unroll
+        for (int v = 0; v < KC / 4; ++v) {
+            f32x4 t = src[4 * v];
+            a[4 * v] = t[0]; a[4 * v + 1] = t[1]; a[4 * v + 2] = t[2]; a[4 * v + 3] = t[3];
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < KC; ++v) a[v] = 0.f;
+    }
+    const int n_ct = (nb + 15) / 16;
+    // K operand of column tile ct: rows 16 ct + lane % 16, coordinates as above
+    auto load_b = [&](int ct, float (&b)[KC]) {
+        const int j = ct * 16 + li;
+        if (j < nb) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(kh + (size_t)j * D) + kq;
+#pragma unroll
+            for (int v = 0; v < KC / 4; ++v) {
+                f32x4 t = src[4 * v];
+                b[4 * v] = t[0]; b[4 * v + 1] = t[1]; b[4 * v + 2] = t[2]; b[4 * v + 3] = t[3];
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < KC; ++v) b[v] = 0.f;
+        }
+    };
+    auto tile = [&](int ct, const float (&b)[KC]) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KC; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+        // lane holds S[4*(lane/16) + r][16*ct + lane%16]
+        const int j = ct * 16 + li;
+        if (j < nb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_lds[(4 * kq + r) * ld_s + j] = acc[r] * scale;
+        }
+    };
+    // the wave's column tiles ct = wave, wave + NW, ...: the next tile's operand is
+    // loaded while the current one multiplies
+    float b0[KC], b1[KC];
+    if (wave < n_ct) load_b(wave, b0);
+    for (int ct = wave; ct < n_ct; ct += 2 * NW) {
+        const bool has1 = ct + NW < n_ct;
+        if (has1) load_b(ct + NW, b1);
+        tile(ct, b0);
+        if (!has1) break;
+        if (ct + 2 * NW < n_ct) load_b(ct + 2 * NW, b0);
+        tile(ct + NW, b1);
+    }
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// IBCS scores.  A workgroup owns kRows centroid rows (kRows / 8 query blocks) of one
+// head: the centroid map by map_rows, each row turned into w_c softmax(row) by one
+// wave, then each query block's row A = sum of its 8 rows in cluster order, written to
+// A_out [BH, nb, nb] for the select kernel.  Rows sum to one.  Four waves per
+// workgroup: the map's operand registers (about 115 VGPRs at d = 128) allow four waves
+// per SIMD, so four such workgroups share a CU and one's loads overlap another's MFMAs.
+// ---------------------------------------------------------------------------
 static_assert(kRows % kIbcsClusters == 0, "a workgroup holds whole query blocks' centroids");
+constexpr int kScoreWaves = 4;
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
-    const float* __restrict__ arows, int n_arows, const float* __restrict__ cw, const float* __restrict__ kp,
-    int nb, int ld_s, float scale, float thr, int sta, int nH, int nW, int rt, int rh, int rw,
-    int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap,
-    int sip_budget, const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
-    extern __shared__ float s_lds[];   // [kRows][ld_s] rows, then [kWaves][kCap] candidates
-    constexpr int KC = D / 4;          // k values per lane per MFMA chain
+__global__ __launch_bounds__(kScoreWaves * 64) void ibcs_score_kernel(const float* __restrict__ cent,
+                                                                 const float* __restrict__ cw,
+                                                                 const float* __restrict__ kp, int nb, int ld_s,
+                                                                 float scale, float* __restrict__ A_out) {
+    extern __shared__ float s_lds[];   // [kRows][ld_s]
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kRows;
-    const bool ibcs = cw != nullptr;
-    const float* qh = arows + (size_t)bh * n_arows * D;
-    const float* kh = kp + (size_t)bh * nb * D;
-    constexpr float kLog2e = 1.4426950408889634f;
+    const int n_rows = nb * kIbcsClusters;
+    map_rows<D, kScoreWaves>(cent + (size_t)bh * n_rows * D, n_rows, row0, kp + (size_t)bh * nb * D, nb, ld_s,
+                             scale, s_lds, wave, lane);
+    __syncthreads();
+    for (int r = wave; r < kRows; r += kScoreWaves) {
+        const int crow = row0 + r;
+        if (crow >= n_rows) break;
+        float* srow = s_lds + r * ld_s;
+        float mx = -INFINITY;
+        for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, srow[j]);
+        const float mx2 = wave_max(mx) * kLog2e;
+        float sum = 0.f;
+        for (int j = lane; j < nb; j += 64) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(srow[j], kLog2e, -mx2));
+            srow[j] = e;
+            sum += e;
+        }
+        const float f = cw[(size_t)bh * n_rows + crow] / wave_sum(sum);
+        for (int j = lane; j < nb; j += 64) srow[j] *= f;
+    }
+    __syncthreads();
+    for (int r = 0; r < kRows / kIbcsClusters; ++r) {
+        const int row = row0 / kIbcsClusters + r;
+        if (row >= nb) break;
+        const float* grp = s_lds + r * kIbcsClusters * ld_s;
+        float* out = A_out + ((size_t)bh * nb + row) * nb;
+        for (int j = threadIdx.x; j < nb; j += kScoreWaves * 64) {
+            float a = grp[j];
+#pragma unroll
+            for (int c = 1; c < kIbcsClusters; ++c) a += grp[c * ld_s + j];
+            out[j] = a;
+        }
+    }
+}
 
-    // ---- phase 1: S tiles.  The MFMA's k index (lane / 16) selects a contiguous
-    // quarter of d in both operands, so operand loads are 16-byte vectors.
-    {
-        const int li = lane & 15;
-        const int kq = lane >> 4;
-        float a[KC];
-        const int qrow = row0 + li;
-        if (qrow < n_arows) {
-            const f32x4* src = reinterpret_cast<const f32x4*>(qh + (size_t)qrow * D + kq * KC);
-#pragma unroll
-            for (int v = 0; v < KC / 4; ++v) {
-                f32x4 t = src[v];
-                a[4 * v] = t[0]; a[4 * v + 1] = t[1]; a[4 * v + 2] = t[2]; a[4 * v + 3] = t[3];
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < KC; ++v) a[v] = 0.f;
+// ---------------------------------------------------------------------------
+// Map + select.  Rows are either NABLA's pooled map (qp given: map_rows, then a row
+// softmax) or block scores computed elsewhere (given_a [BH, nb, nb], rows summing to
+// one, loaded as they are).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
+    const float* __restrict__ qp, const float* __restrict__ given_a, const float* __restrict__ kp, int nb,
+    int ld_s, float scale, float thr, int sta, int nH, int nW, int rt, int rh, int rw,
+    int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap,
+    int sip_budget, const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
+    extern __shared__ float s_lds[];   // [kRows][ld_s] rows, then [kWaves][kCap] candidates
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.y;
+    const int row0 = blockIdx.x * kRows;
+    const bool given = given_a != nullptr;
+
+    // ---- phase 1: the workgroup's rows into LDS
+    if (given) {
+        for (int r = wave; r < kRows; r += kWaves) {
+            const int row = row0 + r;
+            if (row >= nb) break;
+            const float* src = given_a + ((size_t)bh * nb + row) * nb;
+            for (int j = lane; j < nb; j += 64) s_lds[r * ld_s + j] = src[j];
         }
-        const int n_ct = (nb + 15) / 16;
-        // K operand of column tile ct: rows 16 ct + lane % 16, quarter lane / 16 of d
-        auto load_b = [&](int ct, float (&b)[KC]) {
-            const int j = ct * 16 + li;
-            if (j < nb) {
-                const f32x4* src = reinterpret_cast<const f32x4*>(kh + (size_t)j * D + kq * KC);
-#pragma unroll
-                for (int v = 0; v < KC / 4; ++v) {
-                    f32x4 t = src[v];
-                    b[4 * v] = t[0]; b[4 * v + 1] = t[1]; b[4 * v + 2] = t[2]; b[4 * v + 3] = t[3];
-                }
-            } else {
-#pragma unroll
-                for (int v = 0; v < KC; ++v) b[v] = 0.f;
-            }
-        };
-        auto tile = [&](int ct, const float (&b)[KC]) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KC; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
-            // lane holds S[4*(lane/16) + r][16*ct + lane%16]
-            const int j = ct * 16 + li;
-            if (j < nb) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) s_lds[(4 * kq + r) * ld_s + j] = acc[r] * scale;
-            }
-        };
-        // the wave's column tiles ct = wave, wave + 8, ...: the next tile's operand is
-        // loaded while the current one multiplies
-        float b0[KC], b1[KC];
-        if (wave < n_ct) load_b(wave, b0);
-        for (int ct = wave; ct < n_ct; ct += 2 * kWaves) {
-            const bool has1 = ct + kWaves < n_ct;
-            if (has1) load_b(ct + kWaves, b1);
-            tile(ct, b0);
-            if (!has1) break;
-            if (ct + 2 * kWaves < n_ct) load_b(ct + 2 * kWaves, b0);
-            tile(ct + kWaves, b1);
-        }
+    } else {
+        map_rows<D, kWaves>(qp + (size_t)bh * nb * D, nb, row0, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds,
+                            wave, lane);
     }
     __syncthreads();
 
-    // ---- IBCS: each centroid row becomes w_c softmax(row), one row per wave
-    if (ibcs) {
-        for (int r = wave; r < kRows; r += kWaves) {
-            const int crow = row0 + r;
-            if (crow >= n_arows) break;
-            float* srow = s_lds + r * ld_s;
-            float mx = -INFINITY;
-            for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, srow[j]);
-            const float mx2 = wave_max(mx) * kLog2e;
-            float sum = 0.f;
-            for (int j = lane; j < nb; j += 64) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(srow[j], kLog2e, -mx2));
-                srow[j] = e;
-                sum += e;
-            }
-            const float f = cw[(size_t)bh * n_arows + crow] / wave_sum(sum);
-            for (int j = lane; j < nb; j += 64) srow[j] *= f;
-        }
-        __syncthreads();
-    }
-
-    // ---- phase 2: one row (query block) per wave at a time.
+    // ---- phase 2: one row per wave at a time.
     float* cand = s_lds + kRows * ld_s + wave * kCap;
     const int nwords = (nb + 31) >> 5;
-    const int out_rows = ibcs ? kRows / kIbcsClusters : kRows;
-    for (int r = wave; r < out_rows; r += kWaves) {
-        const int row = (ibcs ? row0 / kIbcsClusters : row0) + r;
+    for (int r = wave; r < kRows; r += kWaves) {
+        const int row = row0 + r;
         if (row >= nb) break;
-        float* arow;
-        float inv_sum;
-        if (ibcs) {
-            // A = sum over the block's clusters, in cluster order; rows already sum to one
-            arow = s_lds + r * kIbcsClusters * ld_s;
-            for (int j = lane; j < nb; j += 64) {
-                float a = arow[j];
-#pragma unroll
-                for (int c = 1; c < kIbcsClusters; ++c) a += arow[c * ld_s + j];
-                arow[j] = a;
-            }
-            inv_sum = 1.0f;
-        } else {
+        float* arow = s_lds + r * ld_s;
+        float inv_sum = 1.0f;
+        if (!given) {
             // softmax; the row is overwritten with the probabilities A
-            arow = s_lds + r * ld_s;
             float mx = -INFINITY;
             for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, arow[j]);
             mx = wave_max(mx);
@@ -593,11 +640,24 @@ hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
     const int max_lds = (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap) * (int)sizeof(float);
     hipError_t e = set_max_dynamic_lds((const void*)map_select_kernel<D>, max_lds, lds_set);
     if (e != hipSuccess) return e;
-    const int n_arows = a.ibcs ? a.nb * kIbcsClusters : a.nb;
-    dim3 grid((n_arows + kRows - 1) / kRows, a.BH);
-    hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.ibcs ? a.cent : a.qp, n_arows,
-                       a.ibcs ? a.cent_w : nullptr, a.kp, a.nb, ld_s, a.scale, a.thr, a.sta, a.nH, a.nW, a.rt,
-                       a.rh, a.rw, a.kv_count, a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
+    dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
+    hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.qp, a.ibcs ? a.ibcs_A : nullptr,
+                       a.kp, a.nb, ld_s, a.scale, a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count,
+                       a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_ibcs_score(const MaskArgs& a, hipStream_t s) {
+    const int ld_s = ((a.nb + 63) / 64) * 64 + 16;
+    const size_t lds = (size_t)kRows * ld_s * sizeof(float);
+    static std::atomic<uint64_t> lds_set{0};
+    const int max_lds = kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) * (int)sizeof(float);
+    hipError_t e = set_max_dynamic_lds((const void*)ibcs_score_kernel<D>, max_lds, lds_set);
+    if (e != hipSuccess) return e;
+    dim3 grid((a.nb * kIbcsClusters + kRows - 1) / kRows, a.BH);
+    hipLaunchKernelGGL((ibcs_score_kernel<D>), grid, dim3(kScoreWaves * 64), lds, s, a.cent, a.cent_w, a.kp, a.nb, ld_s,
+                       a.scale, a.ibcs_A);
     return hipGetLastError();
 }
 
@@ -611,7 +671,11 @@ hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
         e = (a.d == 128) ? launch_pool<float, 128>(a, s) : launch_pool<float, 64>(a, s);
     }
     if (e != hipSuccess) return e;
-    if (a.ibcs && (e = launch_ibcs_cluster(a, s)) != hipSuccess) return e;
+    if (a.ibcs) {
+        if ((e = launch_ibcs_cluster(a, s)) != hipSuccess) return e;
+        e = (a.d == 128) ? launch_ibcs_score<128>(a, s) : launch_ibcs_score<64>(a, s);
+        if (e != hipSuccess) return e;
+    }
     e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
     if (e != hipSuccess || !a.schedule) return e;
     // one wave per head; its bins fit the default LDS limit (NABLA_MAX_BLOCKS + 1 ints)

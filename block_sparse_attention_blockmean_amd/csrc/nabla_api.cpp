@@ -90,7 +90,8 @@ size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, 
     const size_t kp = (blocks * d * sizeof(float) + 255) & ~(size_t)255;
     const size_t cent = (blocks * nabla::kIbcsClusters * d * sizeof(float) + 255) & ~(size_t)255;
     const size_t cw = (blocks * nabla::kIbcsClusters * sizeof(float) + 255) & ~(size_t)255;
-    return kp + cent + cw;
+    const size_t scores = (blocks * (size_t)(L / N) * sizeof(float) + 255) & ~(size_t)255;
+    return kp + cent + cw + scores;
 }
 
 namespace {
@@ -218,7 +219,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     a.bitmap = bitmap;
     a.schedule = schedule;
     if (ibcs) {
-        // [Kp | centroids | weights], sections 256-byte aligned
+        // [Kp | centroids | weights | block scores], sections 256-byte aligned
         const size_t blocks = (size_t)a.BH * nb;
         char* base = (char*)workspace;
         a.qp = nullptr;
@@ -227,6 +228,8 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
         a.cent = (float*)base;
         base += (blocks * nabla::kIbcsClusters * d * sizeof(float) + 255) & ~(size_t)255;
         a.cent_w = (float*)base;
+        base += (blocks * nabla::kIbcsClusters * sizeof(float) + 255) & ~(size_t)255;
+        a.ibcs_A = (float*)base;
         a.ibcs = 1;
     } else {
         a.qp = (float*)workspace;

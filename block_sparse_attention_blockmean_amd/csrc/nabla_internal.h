@@ -89,6 +89,7 @@ struct MaskArgs {
     int ibcs;               // 1: rows of the map are IBCS centroids (Q is clustered, not pooled)
     float* cent;            // IBCS workspace [BH, nb * kIbcsClusters, d] centroids
     float* cent_w;          // IBCS workspace [BH, nb * kIbcsClusters] cluster weights
+    float* ibcs_A;          // IBCS workspace [BH, nb, nb] block scores (rows sum to one)
 };
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_ibcs_cluster(const MaskArgs& a, hipStream_t s);

@@ -219,9 +219,11 @@ nabla_status nabla_build_mask_sip(const void* q, const void* k, int batch, int h
 
 /*
  * nabla_build_mask_ibcs_workspace_size - bytes of device workspace nabla_build_mask_ibcs
- * needs (blocks = batch*heads*(L/N)): the pooled K (blocks*d floats), 8 centroids per
- * query block (8*blocks*d floats) and their weights (8*blocks floats), each section
- * rounded up to 256 bytes.  Returns 0 for non-positive sizes or L not a multiple of N.
+ * needs (blocks = batch*heads*(L/N)), four sections in this order, each rounded up to
+ * 256 bytes: the pooled K (blocks*d floats), 8 centroids per query block (8*blocks*d
+ * floats), their weights (8*blocks floats) and the block scores A (blocks*(L/N)
+ * floats).  After a call the sections hold those values, in float32, row-major
+ * [batch, heads, nb, ...].  Returns 0 for non-positive sizes or L not a multiple of N.
  */
 size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, int N);
 

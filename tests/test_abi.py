@@ -291,12 +291,13 @@ def test_attn_weighted_validation(lib):
 # ------------------------------------------------------------- IBCS entry points
 
 def test_ibcs_workspace_size(lib):
-    # pooled K, 8 centroids and 8 weights per query block, sections rounded up to 256
+    # pooled K, 8 centroids and 8 weights per query block, the nb x nb scores; sections
+    # rounded up to 256
     blocks = 12 * 504
-    want = blocks * 128 * 4 + blocks * 8 * 128 * 4 + blocks * 8 * 4
+    want = blocks * 128 * 4 + blocks * 8 * 128 * 4 + blocks * 8 * 4 + blocks * 504 * 4
     assert lib.nabla_build_mask_ibcs_workspace_size(1, 12, 32256, 128, 64) == want
-    # 3 blocks, d = 64: 768 B, 6144 B, 96 B -> 768 + 6144 + 256
-    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 192, 64, 64) == 768 + 6144 + 256
+    # 3 blocks, d = 64: 768 B, 6144 B, 96 B, 36 B -> 768 + 6144 + 256 + 256
+    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 192, 64, 64) == 768 + 6144 + 256 + 256
     assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 1000, 64, 64) == 0
     assert lib.nabla_build_mask_ibcs_workspace_size(1, -1, 1024, 64, 64) == 0
 

@@ -2,10 +2,11 @@
 against the oracle.
 
 The clustering is a fixed sequence of individually rounded float32 operations, so the
-centroids and weights the kernels leave in the workspace ([Kp | centroids | weights],
-sections 256-byte aligned) must equal the oracle's bit for bit.  The mask must equal the
-oracle's CDF cut of its float64 scores except at the cutoff (the band of the NABLA mask
-test: the GPU's scores are float32)."""
+centroids and weights the kernels leave in the workspace ([Kp | centroids | weights |
+scores], sections 256-byte aligned) must equal the oracle's bit for bit.  The scores are
+float32 on the GPU (MFMA map, exp2 softmax) and float64 in the oracle: within
+A_TOL relative to the row's largest score.  The mask must equal the oracle's CDF cut of
+its scores except at the cutoff (the band of the NABLA mask test)."""
 from __future__ import annotations
 
 import sys
@@ -22,6 +23,9 @@ from parity import bitmap_to_mask, check_mask, lists_to_mask
 pytestmark = pytest.mark.gpu
 
 K = O.IBCS_CLUSTERS
+# float32 logits of size ~10 carry ~1e-6 absolute error, a relative error of ~1e-6 in
+# each softmax value; the weighted sum of 8 keeps it there.  20x slack.
+A_TOL = 2e-5
 
 
 def say(*a):
@@ -49,12 +53,21 @@ def gpu_ibcs(cfg, qf, kf, thr, sta=None):
     torch.cuda.synchronize()
     o_cent = _up256(G * nb * d * 4)
     o_w = o_cent + _up256(G * nb * K * d * 4)
+    o_a = o_w + _up256(G * nb * K * 4)
+    assert o_a + _up256(G * nb * nb * 4) == nbytes
     host = ws.cpu()
     cent = host[o_cent:o_cent + G * nb * K * d * 4].view(torch.float32).numpy().reshape(G, nb, K, d)
     w = host[o_w:o_w + G * nb * K * 4].view(torch.float32).numpy().reshape(G, nb, K)
+    A = host[o_a:o_a + G * nb * nb * 4].view(torch.float32).numpy().reshape(G, nb, nb)
     m = lists_to_mask(cnt.cpu().numpy().reshape(G, nb), idx.cpu().numpy().reshape(G, nb, nb))
     assert np.array_equal(bitmap_to_mask(bm.cpu().numpy().reshape(G, nb, -1), nb), m)
-    return dict(cnt=cnt, idx=idx, mask=m, cent=cent, w=w)
+    return dict(cnt=cnt, idx=idx, mask=m, cent=cent, w=w, A=A)
+
+
+def score_err(gpu_A, ref_A):
+    """max over rows of max_j |gpu - oracle| / max_j oracle."""
+    ref = np.asarray(ref_A, dtype=np.float64)
+    return float(np.max(np.abs(gpu_A - ref).max(-1) / ref.max(-1)))
 
 
 def check_clusters(res, qf_np, N, heads, blocks=None):
@@ -101,9 +114,12 @@ def test_ibcs_parity(cfg):
     kn = kf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)
     n = check_clusters(res, qn, cfg.N, range(G))
     ref_m, ref_A = oracle_mask(cfg, qn, kn, cfg.thr, cfg.sta)
+    err = score_err(res["A"], ref_A)
+    assert err <= A_TOL, err
+    assert np.allclose(res["A"].sum(-1), 1.0, atol=1e-5)
     mism, band = check_mask(res["mask"], ref_m, ref_A, cfg.thr)
-    say(f"  {n} blocks' centroids bit-identical; kept {res['mask'].mean():.3f}, mask mismatches {mism}, "
-        f"band {band}")
+    say(f"  {n} blocks' centroids bit-identical; scores rel err {err:.2e}; kept {res['mask'].mean():.3f}, "
+        f"mask mismatches {mism}, band {band}")
     # the top block of every row is kept, as in NABLA
     top = np.argmax(ref_A, axis=-1)
     assert np.all(np.take_along_axis(res["mask"], top[..., None], axis=-1))
@@ -169,5 +185,7 @@ def test_ibcs_full_size():
     n = check_clusters(sub, qn, cfg.N, range(len(heads)))
     say(f"  {n} blocks' centroids bit-identical")
     ref_m, ref_A = oracle_mask(cfg, qn, kn, cfg.thr)
+    err = score_err(res["A"][heads], ref_A)
+    assert err <= A_TOL, err
     mism, band = check_mask(res["mask"][heads], ref_m, ref_A, cfg.thr)
-    say(f"  heads {heads}: mask mismatches {mism}, band {band}")
+    say(f"  heads {heads}: scores rel err {err:.2e}, mask mismatches {mism}, band {band}")
