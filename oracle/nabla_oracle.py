@@ -364,10 +364,11 @@ def _sq_dist_f32(x: np.ndarray, c: np.ndarray) -> np.ndarray:
 
 
 def ibcs_clusters(qblock: np.ndarray, n_clusters: int = IBCS_CLUSTERS, iters: int = IBCS_ITERS):
-    """k-means of one query block's N queries ([N, d]) into n_clusters clusters.
+    """k-means of one group of n queries ([n, d], one query block or several) into
+    n_clusters clusters.
 
     Readings (the page gives the cluster count, not the algorithm's steps): Lloyd's
-    algorithm; initial centroids are the queries at rows 0, N/k, 2N/k, ...; ``iters``
+    algorithm; initial centroids are the queries at rows 0, n/k, 2n/k, ...; ``iters``
     rounds of assign-then-update; a query joins its nearest centroid by squared
     Euclidean distance, ties to the lowest cluster index; a centroid becomes the mean of
     its queries (summed in row order in float32, then divided by their count), and an
@@ -390,34 +391,44 @@ def ibcs_clusters(qblock: np.ndarray, n_clusters: int = IBCS_CLUSTERS, iters: in
     return cent, weights
 
 
-def ibcs_scores(q: np.ndarray, k: np.ndarray, N: int, scale: Optional[float] = None) -> np.ndarray:
-    """IBCS block scores for [..., L, d] Q, K in fractal order: for query block i with
-    centroids mu_c and weights w_c, A_ij = sum_c w_c softmax_j(scale * mu_c . Kp_j),
-    Kp_j the mean key of block j - the weighted attention of the centroids to the mean
-    keys.  Rows sum to one like NABLA's pooled softmax, so the same CDF cut applies."""
+def ibcs_scores(q: np.ndarray, k: np.ndarray, N: int, scale: Optional[float] = None,
+                qn: Optional[int] = None) -> np.ndarray:
+    """IBCS block scores for [..., L, d] Q, K in fractal order.
+
+    The queries are taken in groups of qn consecutive tokens (default N; the page's
+    setting is 128) and each group is clustered (ibcs_clusters).  With centroids mu_c and
+    weights w_c of the group holding query block i,
+        A_ij = sum_c w_c softmax_j(scale * mu_c . Kp_j),
+    Kp_j the mean key of N-token block j: the weighted attention of the centroids to the
+    mean keys.  The qn / N blocks of a group share one row.  Rows sum to one like NABLA's
+    pooled softmax, so the same CDF cut applies."""
     d = q.shape[-1]
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     L = q.shape[-2]
+    qn = N if qn is None else qn
+    if qn % N or L % qn:
+        raise ValueError("qn must be a multiple of N that divides L")
     nb = L // N
+    per = qn // N
     lead = q.shape[:-2]
     qf = np.asarray(q, dtype=np.float32).reshape((-1, L, d))
     kp = block_mean(np.asarray(k).reshape((-1, L, d)), N, np.float64)
     A = np.zeros((qf.shape[0], nb, nb))
     for g in range(qf.shape[0]):
-        for i in range(nb):
-            cent, w = ibcs_clusters(qf[g, i * N:(i + 1) * N])
+        for gi in range(L // qn):
+            cent, w = ibcs_clusters(qf[g, gi * qn:(gi + 1) * qn])
             S = (cent.astype(np.float64) @ kp[g].T) * scale                      # [k, nb]
             P = np.exp(S - S.max(axis=1, keepdims=True))
             P /= P.sum(axis=1, keepdims=True)
-            A[g, i] = w @ P
+            A[g, gi * per:(gi + 1) * per] = w @ P
     return A.reshape(lead + (nb, nb))
 
 
 def ibcs_block_mask(q: np.ndarray, k: np.ndarray, N: int, thr: float,
-                    scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+                    scale: Optional[float] = None, qn: Optional[int] = None) -> Dict[str, np.ndarray]:
     """NABLA's CDF cut on the IBCS scores: keep block j of row i iff the mass of the
     blocks scoring at most A_ij exceeds thr.  Returns mask, F and A."""
-    A = ibcs_scores(q, k, N, scale)
+    A = ibcs_scores(q, k, N, scale, qn)
     A32 = A.astype(np.float32)
     F = cdf_values(A32)
     return {"mask": F > F.dtype.type(thr), "F": F, "A": A32}

@@ -567,6 +567,53 @@ def pin_ibcs_matches_library_kmeans():
         assert np.max(np.abs(cent - km.cluster_centers_)) <= 1e-5, trial
 
 
+def pin_ibcs_matches_library_kmeans_128():
+    """The page's 128-query groups: Lloyd's k-means of 128 queries from rows 0, 16, ...,
+    112, against scikit-learn's implementation."""
+    from sklearn.cluster import KMeans
+    rng = _rng(44)
+    for trial in range(3):
+        n, d = 128, 12
+        x = (rng.standard_normal((n, d)) + (rng.random((n, 1)) > 0.6) * 4).astype(np.float32)
+        cent, w = O.ibcs_clusters(x)
+        init = x[np.arange(8) * 16].astype(np.float64)
+        km = KMeans(n_clusters=8, init=init, n_init=1, max_iter=O.IBCS_ITERS, tol=0.0,
+                    algorithm="lloyd").fit(x.astype(np.float64))
+        # (scikit-learn's labels_ come from one more assignment against the final
+        # centres; the weights here are those of the assignment that made them, which
+        # the closed-form pin below checks)
+        assert np.max(np.abs(cent - km.cluster_centers_)) <= 1e-5, trial
+
+
+def pin_ibcs_group128_scores_closed_form():
+    """qn = 128: each group of two 64-token blocks holds 8 well-separated centres, 16
+    consecutive queries each (the initial rows 0, 16, ... fall one per centre), so the
+    clusters are the centres with weight 1/8 and both blocks of the group score
+    A_j = 1/8 sum_c softmax_j(scale c . Kp_j), computed here from the centres alone.
+    Clustering each 64-block on its own (4 centres, 2 initial rows each) gives other
+    rows."""
+    rng = _rng(45)
+    G, T, N, d, scale = 1, 4, 64, 8, 0.2
+    L = T * N * 2
+    nb = L // N
+    centers = rng.standard_normal((L // 128, 8, d)) * 10
+    q = np.repeat(centers, 16, axis=1).reshape(1, L, d)
+    q = (q + rng.standard_normal(q.shape) * 1e-3).astype(np.float32)
+    k = rng.standard_normal((G, L, d)).astype(np.float32)
+    A = O.ibcs_scores(q, k, N, scale, qn=128)
+    kp = k.astype(np.float64).reshape(nb, N, d).mean(axis=1)
+    for gi in range(L // 128):
+        mu = q[0, gi * 128:(gi + 1) * 128].astype(np.float64).reshape(8, 16, d).mean(axis=1)
+        S = mu @ kp.T * scale
+        P = np.exp(S - S.max(-1, keepdims=True))
+        P /= P.sum(-1, keepdims=True)
+        ref = P.mean(axis=0)
+        for b in (2 * gi, 2 * gi + 1):
+            assert np.max(np.abs(A[0, b] - ref)) <= 1e-5, (gi, b)
+    A64 = O.ibcs_scores(q, k, N, scale)
+    assert np.max(np.abs(A64 - A)) > 1e-3
+
+
 def pin_ibcs_rows_and_threshold():
     rng = _rng(43)
     G, L, N, d = 2, 384, 64, 8

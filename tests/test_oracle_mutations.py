@@ -176,6 +176,11 @@ def _ibcs_softmax_over_centroids(q, k, N, scale=None):
     return np.exp(A) / np.exp(A).sum(-1, keepdims=True)
 
 
+def _ibcs_group_ignored(q, k, N, scale=None, qn=None):
+    # every 64-token block clustered on its own, whatever the group size
+    return _orig_ibcs_scores(q, k, N, scale)
+
+
 MUTATIONS = [
     ("fractal_index", _fractal_colmajor),
     ("pooled_logits", _pooled_transposed),
@@ -200,6 +205,7 @@ MUTATIONS = [
     ("ibcs_clusters", _ibcs_uniform_weights),
     ("ibcs_clusters", _ibcs_first_rows_init),
     ("ibcs_scores", _ibcs_softmax_over_centroids),
+    ("ibcs_scores", _ibcs_group_ignored),
 ]
 
 
