@@ -238,22 +238,25 @@ def bench_sip(args, cfg, qd, kd, vd) -> int:
 
 def bench_ibcs(args, cfg, qd, kd, vd) -> int:
     """IBCS variant of the step on fractal-order tensors: nabla_build_mask_ibcs (K
-    pooling, 8 query clusters per block, centroid map, CDF cut, lists) and
-    block_sparse_attn_fwd on its lists, each bracketed by HIP events; the plain NABLA
-    mask on the same inputs is timed beside it."""
+    pooling, 8 clusters per group of 128 queries as on the AB-Attention page, centroid
+    map, CDF cut, lists) and block_sparse_attn_fwd on its lists, each bracketed by HIP
+    events; the IBCS mask with 64-query groups and the plain NABLA mask on the same
+    inputs are timed beside it."""
     T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
     qf, kf, vf = (nab.reorder(t, T, H, W, P) for t in (qd, kd, vd))
-    ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, N, ibcs=True),
+    ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, N, ibcs=True, ibcs_group=64),
                      dtype=torch.uint8, device="cuda")
     o = torch.empty_like(qf)
     state = {}
 
     def mask():
         state["lists"] = nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True,
-                                        workspace=ws, ibcs=True)
+                                        workspace=ws, ibcs=True, ibcs_group=128)
 
     def mask_nabla():
         nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws)
+        nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws, ibcs=True,
+                       ibcs_group=64)
 
     def attn():
         cnt, idx, sched = state["lists"]
@@ -264,7 +267,7 @@ def bench_ibcs(args, cfg, qd, kd, vd) -> int:
         attn()
         mask_nabla()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e in ev:
         e[0].record()
@@ -272,13 +275,17 @@ def bench_ibcs(args, cfg, qd, kd, vd) -> int:
         e[1].record()
         attn()
         e[2].record()
-        mask_nabla()
+        nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws)
         e[3].record()
+        nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws, ibcs=True,
+                       ibcs_group=64)
+        e[4].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_mask = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_nabla = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    ms_q64 = float(np.mean([e[3].elapsed_time(e[4]) for e in ev]))
     kept = int(state["lists"][0].sum().item())
     flops = kept * 4.0 * N * N * cfg.d
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -296,8 +303,9 @@ def bench_ibcs(args, cfg, qd, kd, vd) -> int:
         "dtype": cfg.dtype,
         "data": f"synthetic ({GENERATOR_VERSION})",
         "config": {"workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "L": cfg.L,
-                   "blocks_per_head": cfg.nb, "thr": cfg.thr, "sta": cfg.sta},
+                   "blocks_per_head": cfg.nb, "thr": cfg.thr, "sta": cfg.sta, "ibcs_query_group": 128},
         "ms_mask_ibcs": round(ms_mask, 4),
+        "ms_mask_ibcs_query_group_64": round(ms_q64, 4),
         "ms_mask_nabla_same_inputs": round(ms_nabla, 4),
         "ms_attn": round(ms_attn, 4),
         "kept_fraction": round(kept / (cfg.BH * cfg.nb * cfg.nb), 4),

@@ -69,9 +69,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_build_mask.restype = i
     lib.nabla_build_mask_raster.argtypes = lib.nabla_build_mask.argtypes
     lib.nabla_build_mask_raster.restype = i
-    lib.nabla_build_mask_ibcs.argtypes = lib.nabla_build_mask.argtypes
+    lib.nabla_build_mask_ibcs.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, f, ctypes.POINTER(StaWindow),
+                                          f, i, vp, vp, vp, vp, vp, sz, vp]
     lib.nabla_build_mask_ibcs.restype = i
-    lib.nabla_build_mask_ibcs_workspace_size.argtypes = [i, i, i, i, i]
+    lib.nabla_build_mask_ibcs_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.nabla_build_mask_ibcs_workspace_size.restype = sz
     lib.block_sparse_attn_fwd_raster.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, f, i, vp]
     lib.block_sparse_attn_fwd_raster.restype = i
@@ -141,10 +142,11 @@ def reorder(x: torch.Tensor, T: int, H: int, W: int, P: int, inverse: bool = Fal
 
 
 def build_mask_workspace_size(batch: int, heads: int, L: int, d: int, N: int = 64,
-                              ibcs: bool = False) -> int:
+                              ibcs: bool = False, ibcs_group: int = 128) -> int:
     lib = load_library()
-    fn = lib.nabla_build_mask_ibcs_workspace_size if ibcs else lib.nabla_build_mask_workspace_size
-    return int(fn(batch, heads, L, d, N))
+    if ibcs:
+        return int(lib.nabla_build_mask_ibcs_workspace_size(batch, heads, L, d, N, ibcs_group))
+    return int(lib.nabla_build_mask_workspace_size(batch, heads, L, d, N))
 
 
 def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int, N: int = 64,
@@ -153,10 +155,11 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
                with_schedule: bool = False, workspace: Optional[torch.Tensor] = None,
                kv_count: Optional[torch.Tensor] = None, kv_index: Optional[torch.Tensor] = None,
                schedule: Optional[torch.Tensor] = None, raster: bool = False,
-               ibcs: bool = False):
+               ibcs: bool = False, ibcs_group: int = 128):
     """NABLA block mask of fractal-ordered Q, K (``raster=True``: Q, K in raster order,
     the fractal flattening applied in the addressing; needs N == P*P; ``ibcs=True``: the
-    block scores come from 8 query clusters per block instead of the mean query).
+    block scores come from 8 clusters of each group of ``ibcs_group`` queries, 128 as on
+    the AB-Attention page or 64, instead of the mean query).
 
     Returns (kv_count, kv_index), plus the bitmap and/or the longest-first
     schedule when asked for (in that order)."""
@@ -177,11 +180,15 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
         schedule = torch.empty((B * NH * nb,), dtype=torch.int32, device=dev)
     if raster and ibcs:
         raise ValueError("IBCS scores are implemented for fractal-ordered inputs only")
-    ws_bytes = build_mask_workspace_size(B, NH, L, d, N, ibcs=ibcs)
+    ws_bytes = build_mask_workspace_size(B, NH, L, d, N, ibcs=ibcs, ibcs_group=ibcs_group)
     if workspace is None:
         workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
     win = None if sta is None else ctypes.byref(StaWindow(*sta))
-    entry = lib.nabla_build_mask_raster if raster else (lib.nabla_build_mask_ibcs if ibcs else lib.nabla_build_mask)
+    if ibcs:
+        entry = lambda q_, k_, B_, NH_, T_, H_, W_, d_, P_, N_, *rest: lib.nabla_build_mask_ibcs(
+            q_, k_, B_, NH_, T_, H_, W_, d_, P_, N_, int(ibcs_group), *rest)
+    else:
+        entry = lib.nabla_build_mask_raster if raster else lib.nabla_build_mask
     _check(entry(
         _dev(q, "q"), _dev(k, "k"), B, NH, T, H, W, d, P, N, float(thr), win,
         float(scale) if scale is not None else 0.0, _dtype_code(q),

@@ -1,10 +1,11 @@
 // IBCS query clustering (AB-Attention page, "Os três recursos do AB-Attention", first
-// feature): the 64 queries of each query block are grouped into 8 clusters, each with
-// a centroid and a weight equal to the fraction of the block's queries it holds.  The
-// block scores A_ij = sum_c w_c softmax_j(scale * mu_c . Kp_j) are then formed by the
-// map/select kernel, with the centroids as the rows of its reduced map.
+// feature): the queries of each group of QN consecutive tokens (one 64-token block, or
+// the page's 128-token blocks) are grouped into 8 clusters, each with a centroid and a
+// weight equal to the fraction of the group's queries it holds.  The block scores
+// A_ij = sum_c w_c softmax_j(scale * mu_c . Kp_j) are then formed in mask.hip, with the
+// centroids as the rows of the reduced map.
 //
-// Clustering is Lloyd's k-means: initial centroids the queries at rows 0, 8, ..., 56,
+// Clustering is Lloyd's k-means: initial centroids the queries at rows 0, QN/8, ...,
 // four rounds of assign-then-update, nearest centroid by squared Euclidean distance
 // with ties to the lowest index, a centroid the mean of its queries (an empty cluster
 // keeps its centroid).  Distances and means use individually rounded float32 operations
@@ -19,13 +20,11 @@
 namespace nabla {
 namespace {
 
-constexpr int kBlkQ = 64;       // queries per block
-constexpr int kThreads = 256;
-constexpr int kPerQuery = kThreads / kBlkQ;                 // threads per query in the assign step
-constexpr int kPerThread = kIbcsClusters / kPerQuery;       // centroids each of them measures
-constexpr int kPerCluster = kThreads / kIbcsClusters;       // threads per centroid in the update step
-static_assert(kIbcsClusters % kPerQuery == 0 && kThreads % kIbcsClusters == 0, "thread split");
-static_assert(kBlkQ % kIbcsClusters == 0, "initial centroids are every (64 / k)-th query");
+// Four threads per query: 256 for a 64-query group, 512 for 128.
+template <int QN>
+constexpr int cluster_threads() {
+    return 4 * QN;
+}
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -44,28 +43,46 @@ __device__ inline void unpack16(const u32x4_t& v, float, float* out) {
     out[3] = __uint_as_float(v.w);
 }
 
-// One workgroup per query block (bh * nb + i).  LDS rows are padded by 16 bytes (d + 4
-// floats): row t starts 4 t banks further on, so the 16 queries a wave reads with one
-// 16-byte load fall in distinct bank groups.  Float contraction is off in the whole
+// Dynamic LDS of one workgroup: queries, centroids, per-thread best distance and
+// cluster, member lists and counts.
+template <int D, int QN>
+constexpr size_t cluster_lds_bytes() {
+    constexpr int NT = cluster_threads<QN>();
+    return ((size_t)QN * (D + 4) + (size_t)kIbcsClusters * (D + 4) + NT) * sizeof(float) +
+           ((size_t)NT + (size_t)kIbcsClusters * QN + kIbcsClusters) * sizeof(int);
+}
+
+// One workgroup per query group (bh * groups + g).  LDS rows are padded by 16 bytes
+// (d + 4 floats): row t starts 4 t banks further on, so the 16 queries a wave reads with
+// one 16-byte load fall in distinct bank groups.  Float contraction is off in the whole
 // kernel: each +, - and * rounds on its own, and the division is the correctly rounded
 // one (hipcc's default for float32 division).
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restrict__ q, float* __restrict__ cent,
-                                                                float* __restrict__ weight) {
+template <typename T, int D, int QN>
+__global__ __launch_bounds__(cluster_threads<QN>()) void ibcs_cluster_kernel(const T* __restrict__ q,
+                                                                             float* __restrict__ cent,
+                                                                             float* __restrict__ weight) {
 #pragma clang fp contract(off)
+    constexpr int kThreads = cluster_threads<QN>();
+    constexpr int kPerCluster = kThreads / kIbcsClusters;     // threads per centroid in the update step
     constexpr int LD = D + 4;
     constexpr int EPC = 16 / sizeof(T);                       // elements per 16-byte chunk
-    __shared__ __align__(16) float xq[kBlkQ * LD];
-    __shared__ __align__(16) float cen[kIbcsClusters * LD];
-    __shared__ float dist[kThreads];
-    __shared__ int best[kThreads];
-    __shared__ int members[kIbcsClusters * kBlkQ];           // each cluster's queries in row order
-    __shared__ int counts[kIbcsClusters];
+    constexpr int PQ = kThreads / QN;                         // threads per query in the assign step
+    constexpr int PT = kIbcsClusters / PQ;                    // centroids each of them measures
+    static_assert(QN % 64 == 0 && kThreads % QN == 0 && kIbcsClusters % PQ == 0, "thread split");
+    static_assert(kThreads % kIbcsClusters == 0 && D % kPerCluster == 0, "update split");
+    static_assert(QN % kIbcsClusters == 0, "initial centroids are every (QN / k)-th query");
+    extern __shared__ __align__(16) float lds[];
+    float* xq = lds;                                          // [QN][LD]
+    float* cen = xq + QN * LD;                                // [k][LD]
+    float* dist = cen + kIbcsClusters * LD;                   // [kThreads]
+    int* best = reinterpret_cast<int*>(dist + kThreads);      // [kThreads]
+    int* members = best + kThreads;                           // [k][QN] each cluster's queries in row order
+    int* counts = members + kIbcsClusters * QN;               // [k]
 
-    const size_t blk = blockIdx.x;
+    const size_t grp = blockIdx.x;
     const int tid = threadIdx.x;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(q + blk * kBlkQ * D);
-    for (int ch = tid; ch < kBlkQ * D / EPC; ch += kThreads) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(q + grp * QN * D);
+    for (int ch = tid; ch < QN * D / EPC; ch += kThreads) {
         float v[EPC];
         unpack16(__builtin_nontemporal_load(src + ch), T{}, v);
         const int row = ch / (D / EPC), col = (ch % (D / EPC)) * EPC;
@@ -76,25 +93,25 @@ __global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restr
     __syncthreads();
     for (int e = tid; e < kIbcsClusters * D; e += kThreads) {
         const int c = e / D, col = e % D;
-        cen[c * LD + col] = xq[c * (kBlkQ / kIbcsClusters) * LD + col];
+        cen[c * LD + col] = xq[c * (QN / kIbcsClusters) * LD + col];
     }
     __syncthreads();
 
     for (int it = 0; it < kIbcsIters; ++it) {
-        // assign, part 1: thread (query t, slot p) measures centroids kPerThread p + m,
+        // assign, part 1: thread (query t, slot p) measures centroids PT p + m,
         // coordinates in index order
         {
-            const int t = tid / kPerQuery, p = tid % kPerQuery;
+            const int t = tid / PQ, p = tid % PQ;
             const float4* x4 = reinterpret_cast<const float4*>(xq + t * LD);
-            const float4* c4 = reinterpret_cast<const float4*>(cen + p * kPerThread * LD);
-            float acc[kPerThread];
+            const float4* c4 = reinterpret_cast<const float4*>(cen + p * PT * LD);
+            float acc[PT];
 #pragma unroll
-            for (int m = 0; m < kPerThread; ++m) acc[m] = 0.f;
+            for (int m = 0; m < PT; ++m) acc[m] = 0.f;
 #pragma unroll 4
             for (int e4 = 0; e4 < D / 4; ++e4) {
                 const float4 xv = x4[e4];
 #pragma unroll
-                for (int m = 0; m < kPerThread; ++m) {
+                for (int m = 0; m < PT; ++m) {
                     const float4 cv = c4[m * (LD / 4) + e4];
                     float df = xv.x - cv.x;
                     float sq = df * df;
@@ -111,39 +128,49 @@ __global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restr
                 }
             }
             float bd = acc[0];
-            int bc = p * kPerThread;
+            int bc = p * PT;
 #pragma unroll
-            for (int m = 1; m < kPerThread; ++m) {
+            for (int m = 1; m < PT; ++m) {
                 if (acc[m] < bd) {     // strict: a tie keeps the lower index
                     bd = acc[m];
-                    bc = p * kPerThread + m;
+                    bc = p * PT + m;
                 }
             }
             dist[tid] = bd;
             best[tid] = bc;
         }
         __syncthreads();
-        // assign, part 2 (wave 0, lane = query): the slots hold increasing cluster
-        // ranges, so a strict compare in slot order keeps the lowest index among equal
-        // distances.  Each cluster's member list is then filled in row order by ballot
-        // ranks.
-        if (tid < kBlkQ) {
-            float bd = dist[tid * kPerQuery];
-            int bc = best[tid * kPerQuery];
+        // assign, part 2 (wave 0, 64 queries at a time): the slots hold increasing
+        // cluster ranges, so a strict compare in slot order keeps the lowest index among
+        // equal distances.  Each cluster's member list is filled in row order by ballot
+        // ranks; base[c] is the same in every lane.
+        if (tid < 64) {
+            const uint64_t below = (1ull << tid) - 1ull;
+            int base[kIbcsClusters];
 #pragma unroll
-            for (int p = 1; p < kPerQuery; ++p) {
-                const float dd = dist[tid * kPerQuery + p];
-                if (dd < bd) {
-                    bd = dd;
-                    bc = best[tid * kPerQuery + p];
+            for (int c = 0; c < kIbcsClusters; ++c) base[c] = 0;
+            for (int ch = 0; ch < QN / 64; ++ch) {
+                const int t = ch * 64 + tid;
+                float bd = dist[t * PQ];
+                int bc = best[t * PQ];
+#pragma unroll
+                for (int p = 1; p < PQ; ++p) {
+                    const float dd = dist[t * PQ + p];
+                    if (dd < bd) {
+                        bd = dd;
+                        bc = best[t * PQ + p];
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < kIbcsClusters; ++c) {
+                    const uint64_t in = __ballot(bc == c);
+                    if (bc == c) members[c * QN + base[c] + __popcll(in & below)] = t;
+                    base[c] += __popcll(in);
                 }
             }
-            const uint64_t below = (1ull << tid) - 1ull;
+            if (tid == 0) {
 #pragma unroll
-            for (int c = 0; c < kIbcsClusters; ++c) {
-                const uint64_t in = __ballot(bc == c);
-                if (bc == c) members[c * kBlkQ + __popcll(in & below)] = tid;
-                if (tid == 0) counts[c] = __popcll(in);
+                for (int c = 0; c < kIbcsClusters; ++c) counts[c] = base[c];
             }
         }
         __syncthreads();
@@ -157,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restr
 #pragma unroll
             for (int m = 0; m < NC; ++m) acc[m] = 0.f;
             for (int n = 0; n < cnt; ++n) {
-                const float* x = xq + members[c * kBlkQ + n] * LD + part;
+                const float* x = xq + members[c * QN + n] * LD + part;
 #pragma unroll
                 for (int m = 0; m < NC; ++m) acc[m] = acc[m] + x[m * kPerCluster];
             }
@@ -170,23 +197,33 @@ __global__ __launch_bounds__(kThreads) void ibcs_cluster_kernel(const T* __restr
         __syncthreads();
     }
 
-    float* out = cent + blk * kIbcsClusters * D;
+    float* out = cent + grp * kIbcsClusters * D;
     for (int e = tid; e < kIbcsClusters * D; e += kThreads) out[e] = cen[(e / D) * LD + e % D];
-    if (tid < kIbcsClusters) weight[blk * kIbcsClusters + tid] = (float)counts[tid] / (float)kBlkQ;
+    if (tid < kIbcsClusters) weight[grp * kIbcsClusters + tid] = (float)counts[tid] / (float)QN;
 }
 
-template <typename T, int D>
+template <typename T, int D, int QN>
 hipError_t launch(const MaskArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((ibcs_cluster_kernel<T, D>), dim3(a.BH * a.nb), dim3(kThreads), 0, s, (const T*)a.q,
-                       a.cent, a.cent_w);
+    constexpr size_t lds = cluster_lds_bytes<D, QN>();
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = set_max_dynamic_lds((const void*)ibcs_cluster_kernel<T, D, QN>, (int)lds, lds_set);
+    if (e != hipSuccess) return e;
+    const int groups = a.nb / a.ibcs_group;
+    hipLaunchKernelGGL((ibcs_cluster_kernel<T, D, QN>), dim3(a.BH * groups), dim3(cluster_threads<QN>()), lds, s,
+                       (const T*)a.q, a.cent, a.cent_w);
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const MaskArgs& a, hipStream_t s) {
+    if (a.ibcs_group == 2) return a.d == 128 ? launch<T, 128, 128>(a, s) : launch<T, 64, 128>(a, s);
+    return a.d == 128 ? launch<T, 128, 64>(a, s) : launch<T, 64, 64>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_ibcs_cluster(const MaskArgs& a, hipStream_t s) {
-    if (a.bf16) return a.d == 128 ? launch<__bf16, 128>(a, s) : launch<__bf16, 64>(a, s);
-    return a.d == 128 ? launch<float, 128>(a, s) : launch<float, 64>(a, s);
+    return a.bf16 ? launch_t<__bf16>(a, s) : launch_t<float>(a, s);
 }
 
 }  // namespace nabla

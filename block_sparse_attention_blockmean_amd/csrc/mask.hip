@@ -334,10 +334,11 @@ __device__ inline void map_rows(const float* __restrict__ xh, int n_rows, int ro
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// IBCS scores.  A workgroup owns kRows centroid rows (kRows / 8 query blocks) of one
-// head: the centroid map by map_rows, each row turned into w_c softmax(row) by one
-// wave, then each query block's row A = sum of its 8 rows in cluster order, written to
-// A_out [BH, nb, nb] for the select kernel.  Rows sum to one.  Four waves per
+// IBCS scores.  A workgroup owns kRows centroid rows (kRows / 8 query groups) of one
+// head: the centroid map by map_rows; per row the maximum and the softmax normaliser
+// (one wave per row); then each group's row A = sum of its 8 rows' w_c softmax in
+// cluster order, the exponentials recomputed there rather than stored, written to
+// A_out [BH, groups, nb] for the select kernel.  Rows sum to one.  Four waves per
 // workgroup: the map's operand registers (about 115 VGPRs at d = 128) allow four waves
 // per SIMD, so four such workgroups share a CU and one's loads overlap another's MFMAs.
 // ---------------------------------------------------------------------------
@@ -347,43 +348,50 @@ constexpr int kScoreWaves = 4;
 template <int D>
 __global__ __launch_bounds__(kScoreWaves * 64) void ibcs_score_kernel(const float* __restrict__ cent,
                                                                  const float* __restrict__ cw,
-                                                                 const float* __restrict__ kp, int nb, int ld_s,
-                                                                 float scale, float* __restrict__ A_out) {
+                                                                 const float* __restrict__ kp, int nb, int groups,
+                                                                 int ld_s, float scale, float* __restrict__ A_out) {
     extern __shared__ float s_lds[];   // [kRows][ld_s]
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kRows;
-    const int n_rows = nb * kIbcsClusters;
+    const int n_rows = groups * kIbcsClusters;
     map_rows<D, kScoreWaves>(cent + (size_t)bh * n_rows * D, n_rows, row0, kp + (size_t)bh * nb * D, nb, ld_s,
                              scale, s_lds, wave, lane);
     __syncthreads();
+    // per centroid row: the maximum m_c and the factor w_c / sum_j exp(S_cj - m_c)
+    __shared__ float fac[kRows], mx2[kRows];
     for (int r = wave; r < kRows; r += kScoreWaves) {
         const int crow = row0 + r;
-        if (crow >= n_rows) break;
-        float* srow = s_lds + r * ld_s;
-        float mx = -INFINITY;
-        for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, srow[j]);
-        const float mx2 = wave_max(mx) * kLog2e;
-        float sum = 0.f;
-        for (int j = lane; j < nb; j += 64) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(srow[j], kLog2e, -mx2));
-            srow[j] = e;
-            sum += e;
+        float f = 0.f, m2 = 0.f;
+        if (crow < n_rows) {
+            const float* srow = s_lds + r * ld_s;
+            float mx = -INFINITY;
+            for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, srow[j]);
+            m2 = wave_max(mx) * kLog2e;
+            float sum = 0.f;
+            for (int j = lane; j < nb; j += 64) sum += __builtin_amdgcn_exp2f(fmaf(srow[j], kLog2e, -m2));
+            f = cw[(size_t)bh * n_rows + crow] / wave_sum(sum);
         }
-        const float f = cw[(size_t)bh * n_rows + crow] / wave_sum(sum);
-        for (int j = lane; j < nb; j += 64) srow[j] *= f;
+        if (lane == 0) {
+            fac[r] = f;
+            mx2[r] = m2;
+        }
     }
     __syncthreads();
+    // A_gj = sum over the group's clusters, in cluster order, of w_c softmax_j(S_c)
     for (int r = 0; r < kRows / kIbcsClusters; ++r) {
         const int row = row0 / kIbcsClusters + r;
-        if (row >= nb) break;
+        if (row >= groups) break;
         const float* grp = s_lds + r * kIbcsClusters * ld_s;
-        float* out = A_out + ((size_t)bh * nb + row) * nb;
+        float* out = A_out + ((size_t)bh * groups + row) * nb;
         for (int j = threadIdx.x; j < nb; j += kScoreWaves * 64) {
-            float a = grp[j];
+            float a = 0.f;
 #pragma unroll
-            for (int c = 1; c < kIbcsClusters; ++c) a += grp[c * ld_s + j];
+            for (int c = 0; c < kIbcsClusters; ++c) {
+                const int rc = r * kIbcsClusters + c;
+                a = fmaf(fac[rc], __builtin_amdgcn_exp2f(fmaf(grp[c * ld_s + j], kLog2e, -mx2[rc])), a);
+            }
             out[j] = a;
         }
     }
@@ -391,15 +399,15 @@ __global__ __launch_bounds__(kScoreWaves * 64) void ibcs_score_kernel(const floa
 
 // ---------------------------------------------------------------------------
 // Map + select.  Rows are either NABLA's pooled map (qp given: map_rows, then a row
-// softmax) or block scores computed elsewhere (given_a [BH, nb, nb], rows summing to
-// one, loaded as they are).
+// softmax) or block scores computed elsewhere (given_a [BH, nb / a_group, nb], rows
+// summing to one, row i / a_group for query block i, loaded as they are).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
     const float* __restrict__ qp, const float* __restrict__ given_a, const float* __restrict__ kp, int nb,
     int ld_s, float scale, float thr, int sta, int nH, int nW, int rt, int rh, int rw,
     int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap,
-    int sip_budget, const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
+    int sip_budget, const float* __restrict__ uniforms, float* __restrict__ kv_logw, int a_group) {
     extern __shared__ float s_lds[];   // [kRows][ld_s] rows, then [kWaves][kCap] candidates
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
         for (int r = wave; r < kRows; r += kWaves) {
             const int row = row0 + r;
             if (row >= nb) break;
-            const float* src = given_a + ((size_t)bh * nb + row) * nb;
+            const float* src = given_a + ((size_t)bh * (nb / a_group) + row / a_group) * nb;
             for (int j = lane; j < nb; j += 64) s_lds[r * ld_s + j] = src[j];
         }
     } else {
@@ -643,7 +651,7 @@ hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
     dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
     hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.qp, a.ibcs ? a.ibcs_A : nullptr,
                        a.kp, a.nb, ld_s, a.scale, a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count,
-                       a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
+                       a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw, a.ibcs ? a.ibcs_group : 1);
     return hipGetLastError();
 }
 
@@ -655,9 +663,10 @@ hipError_t launch_ibcs_score(const MaskArgs& a, hipStream_t s) {
     const int max_lds = kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) * (int)sizeof(float);
     hipError_t e = set_max_dynamic_lds((const void*)ibcs_score_kernel<D>, max_lds, lds_set);
     if (e != hipSuccess) return e;
-    dim3 grid((a.nb * kIbcsClusters + kRows - 1) / kRows, a.BH);
-    hipLaunchKernelGGL((ibcs_score_kernel<D>), grid, dim3(kScoreWaves * 64), lds, s, a.cent, a.cent_w, a.kp, a.nb, ld_s,
-                       a.scale, a.ibcs_A);
+    const int groups = a.nb / a.ibcs_group;
+    dim3 grid((groups * kIbcsClusters + kRows - 1) / kRows, a.BH);
+    hipLaunchKernelGGL((ibcs_score_kernel<D>), grid, dim3(kScoreWaves * 64), lds, s, a.cent, a.cent_w, a.kp, a.nb,
+                       groups, ld_s, a.scale, a.ibcs_A);
     return hipGetLastError();
 }
 

@@ -84,14 +84,28 @@ size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N
     return ((2 * one) + 255) & ~(size_t)255;
 }
 
-size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, int N) {
-    if (batch <= 0 || heads <= 0 || L <= 0 || d <= 0 || N <= 0 || L % N) return 0;
-    const size_t blocks = (size_t)batch * heads * (size_t)(L / N);
-    const size_t kp = (blocks * d * sizeof(float) + 255) & ~(size_t)255;
-    const size_t cent = (blocks * nabla::kIbcsClusters * d * sizeof(float) + 255) & ~(size_t)255;
-    const size_t cw = (blocks * nabla::kIbcsClusters * sizeof(float) + 255) & ~(size_t)255;
-    const size_t scores = (blocks * (size_t)(L / N) * sizeof(float) + 255) & ~(size_t)255;
-    return kp + cent + cw + scores;
+namespace {
+
+// Sections of the IBCS workspace, each a multiple of 256 bytes: pooled K, centroids,
+// weights, score rows.
+struct IbcsSections {
+    size_t kp, cent, cw, scores;
+    size_t total() const { return kp + cent + cw + scores; }
+};
+
+IbcsSections ibcs_sections(long long BH, long long nb, long long groups, int d) {
+    auto up = [](size_t n) { return (n + 255) & ~(size_t)255; };
+    return {up((size_t)BH * nb * d * sizeof(float)), up((size_t)BH * groups * nabla::kIbcsClusters * d * sizeof(float)),
+            up((size_t)BH * groups * nabla::kIbcsClusters * sizeof(float)), up((size_t)BH * groups * nb * sizeof(float))};
+}
+
+}  // namespace
+
+size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, int N, int q_group) {
+    if (batch <= 0 || heads <= 0 || L <= 0 || d <= 0 || N <= 0 || q_group <= 0 || L % N || q_group % N ||
+        L % q_group)
+        return 0;
+    return ibcs_sections((long long)batch * heads, L / N, L / q_group, d).total();
 }
 
 namespace {
@@ -102,7 +116,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                              int32_t* schedule, void* workspace, size_t workspace_bytes,
                              hipStream_t stream, int sip_budget = 0, const float* uniforms = nullptr,
-                             float* kv_logw = nullptr, int ibcs = 0);
+                             float* kv_logw = nullptr, int ibcs_q_group = 0);
 
 }  // namespace
 
@@ -132,14 +146,16 @@ nabla_status nabla_build_mask_sip(const void* q, const void* k, int batch, int h
 }
 
 nabla_status nabla_build_mask_ibcs(const void* q, const void* k, int batch, int heads, int T, int H,
-                                   int W, int d, int P, int N, float thr,
+                                   int W, int d, int P, int N, int q_group, float thr,
                                    const nabla_sta_window* sta, float scale, nabla_dtype dtype,
                                    int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                                    int32_t* schedule, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream) {
-    return build_mask_impl("nabla_build_mask_ibcs", 0, q, k, batch, heads, T, H, W, d, P, N, thr, sta, scale,
-                           dtype, kv_count, kv_index, bitmap, schedule, workspace, workspace_bytes, stream, 0,
-                           nullptr, nullptr, 1);
+    const char* who = "nabla_build_mask_ibcs";
+    if (q_group <= 0 || N <= 0 || q_group % N)
+        return fail(NABLA_E_INVAL, "%s: q_group=%d must be a positive multiple of N=%d", who, q_group, N);
+    return build_mask_impl(who, 0, q, k, batch, heads, T, H, W, d, P, N, thr, sta, scale, dtype, kv_count, kv_index,
+                           bitmap, schedule, workspace, workspace_bytes, stream, 0, nullptr, nullptr, q_group);
 }
 
 nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, int heads, int T, int H,
@@ -161,7 +177,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                              int32_t* schedule, void* workspace, size_t workspace_bytes,
                              hipStream_t stream, int sip_budget, const float* uniforms,
-                             float* kv_logw, int ibcs) {
+                             float* kv_logw, int ibcs_q_group) {
     if (!q || !k || !kv_count || !kv_index) return fail(NABLA_E_INVAL, "%s: null pointer", who);
     if (!aligned16(q) || !aligned16(k) || ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3) ||
         ((uintptr_t)bitmap & 3) || ((uintptr_t)schedule & 3))
@@ -185,14 +201,18 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
         return fail(NABLA_E_INVAL, "%s: raster order needs one P x P patch per block (N == P*P)", who);
     if (N != 64) return fail(NABLA_E_UNSUPPORTED, "%s: only N = 64 is implemented", who);
     if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "%s: d must be 64 or 128", who);
+    if (ibcs_q_group && L % ibcs_q_group)
+        return fail(NABLA_E_INVAL, "%s: L=%lld is not a multiple of q_group=%d", who, L, ibcs_q_group);
+    if (ibcs_q_group && ibcs_q_group != 64 && ibcs_q_group != 128)
+        return fail(NABLA_E_UNSUPPORTED, "%s: q_group must be 64 or 128", who);
     const long long nb = L / N;
     if (nb > NABLA_MAX_BLOCKS)
         return fail(NABLA_E_UNSUPPORTED, "%s: %lld blocks per head exceed %d", who, nb, NABLA_MAX_BLOCKS);
     // the launches cover up to 256 threads per block of every head with 32-bit thread ids
     if ((long long)batch * heads > 65535 || L * d >= kMaxHeadElems || (long long)batch * heads * nb >= (1ll << 24))
         return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
-    const size_t need = ibcs ? nabla_build_mask_ibcs_workspace_size(batch, heads, (int)L, d, N)
-                             : nabla_build_mask_workspace_size(batch, heads, (int)L, d, N);
+    const size_t need = ibcs_q_group ? nabla_build_mask_ibcs_workspace_size(batch, heads, (int)L, d, N, ibcs_q_group)
+                                     : nabla_build_mask_workspace_size(batch, heads, (int)L, d, N);
     if (!workspace || workspace_bytes < need)
         return fail(NABLA_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -218,19 +238,17 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     a.kv_index = kv_index;
     a.bitmap = bitmap;
     a.schedule = schedule;
-    if (ibcs) {
-        // [Kp | centroids | weights | block scores], sections 256-byte aligned
-        const size_t blocks = (size_t)a.BH * nb;
+    if (ibcs_q_group) {
+        // [Kp | centroids | weights | score rows], sections 256-byte aligned
+        const IbcsSections sec = ibcs_sections(a.BH, nb, L / ibcs_q_group, d);
         char* base = (char*)workspace;
         a.qp = nullptr;
         a.kp = (float*)base;
-        base += (blocks * d * sizeof(float) + 255) & ~(size_t)255;
-        a.cent = (float*)base;
-        base += (blocks * nabla::kIbcsClusters * d * sizeof(float) + 255) & ~(size_t)255;
-        a.cent_w = (float*)base;
-        base += (blocks * nabla::kIbcsClusters * sizeof(float) + 255) & ~(size_t)255;
-        a.ibcs_A = (float*)base;
+        a.cent = (float*)(base + sec.kp);
+        a.cent_w = (float*)(base + sec.kp + sec.cent);
+        a.ibcs_A = (float*)(base + sec.kp + sec.cent + sec.cw);
         a.ibcs = 1;
+        a.ibcs_group = ibcs_q_group / N;
     } else {
         a.qp = (float*)workspace;
         a.kp = a.qp + (size_t)a.BH * nb * d;

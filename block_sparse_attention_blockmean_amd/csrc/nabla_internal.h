@@ -87,9 +87,10 @@ struct MaskArgs {
     const float* uniforms;  // SIP draws [BH, nb, nb]
     float* kv_logw;         // SIP out: log(1 / pi) per list entry [BH, nb, nb]
     int ibcs;               // 1: rows of the map are IBCS centroids (Q is clustered, not pooled)
-    float* cent;            // IBCS workspace [BH, nb * kIbcsClusters, d] centroids
-    float* cent_w;          // IBCS workspace [BH, nb * kIbcsClusters] cluster weights
-    float* ibcs_A;          // IBCS workspace [BH, nb, nb] block scores (rows sum to one)
+    int ibcs_group;         // IBCS query blocks per cluster group (1: 64 queries, 2: 128)
+    float* cent;            // IBCS workspace [BH, groups * kIbcsClusters, d] centroids
+    float* cent_w;          // IBCS workspace [BH, groups * kIbcsClusters] cluster weights
+    float* ibcs_A;          // IBCS workspace [BH, groups, nb] block scores (rows sum to one)
 };
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_ibcs_cluster(const MaskArgs& a, hipStream_t s);

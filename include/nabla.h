@@ -219,37 +219,44 @@ nabla_status nabla_build_mask_sip(const void* q, const void* k, int batch, int h
 
 /*
  * nabla_build_mask_ibcs_workspace_size - bytes of device workspace nabla_build_mask_ibcs
- * needs (blocks = batch*heads*(L/N)), four sections in this order, each rounded up to
- * 256 bytes: the pooled K (blocks*d floats), 8 centroids per query block (8*blocks*d
- * floats), their weights (8*blocks floats) and the block scores A (blocks*(L/N)
- * floats).  After a call the sections hold those values, in float32, row-major
- * [batch, heads, nb, ...].  Returns 0 for non-positive sizes or L not a multiple of N.
+ * needs (BH = batch*heads, nb = L/N, groups = L/q_group), four sections in this order,
+ * each rounded up to 256 bytes: the pooled K (BH*nb*d floats), 8 centroids per query
+ * group (BH*groups*8*d floats), their weights (BH*groups*8 floats) and the score rows
+ * A (BH*groups*nb floats).  After a call the sections hold those values, float32,
+ * row-major [batch, heads, ...].  Returns 0 for non-positive sizes, L not a multiple of
+ * N or of q_group, or q_group not a multiple of N.
  */
-size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, int N);
+size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, int N, int q_group);
 
 /*
  * nabla_build_mask_ibcs - nabla_build_mask with IBCS block scores, the first feature of
- * the AB-Attention page ("Os três recursos do AB-Attention": the queries of a block are
- * clustered into 8 groups and the groups' centroids, weighted by group size, score the
- * KV blocks), in place of the mean query of NABLA's "Downsampling"; the keys are still
- * pooled, and the CDF cut, STA window, lists, bitmap and schedule are NABLA's.
- * For query block i (Q and K in fractal order):
- *   Lloyd's k-means of its N = 64 queries into k = 8 clusters: the first centroids are
- *   the queries at rows 0, 8, ..., 56; four rounds of assigning every query to its
- *   nearest centroid (squared Euclidean distance, ties to the lower index) and moving
- *   each centroid to the mean of its queries (an empty cluster keeps its centroid);
- *   mu_c the centroids, w_c = (queries in cluster c) / 64 under the last assignment;
- *   A_ij = sum_c w_c softmax_j(scale * mu_c . Kp_j),  Kp_j the mean key of block j;
- *   keep  = F_ij > thr with F the CDF of row A_i, as nabla_build_mask.
+ * the AB-Attention page ("Os três recursos do AB-Attention": the queries are taken in
+ * blocks of 128 tokens, each clustered into 8 groups, and the groups' centroids,
+ * weighted by group size, score the KV blocks) in place of the mean query of NABLA's
+ * "Downsampling"; the keys are still pooled over N-token blocks, and the CDF cut, STA
+ * window, lists, bitmap and schedule are NABLA's.  Q and K in fractal order.
+ * For each group of q_group consecutive queries (q_group = 128 as on the page, or 64 =
+ * one query block):
+ *   Lloyd's k-means of its queries into k = 8 clusters: the first centroids are the
+ *   queries at rows 0, q_group/8, 2 q_group/8, ...; four rounds of assigning every query
+ *   to its nearest centroid (squared Euclidean distance, ties to the lower index) and
+ *   moving each centroid to the mean of its queries (an empty cluster keeps its
+ *   centroid); mu_c the centroids, w_c = (queries in cluster c) / q_group under the last
+ *   assignment;
+ *   A_gj = sum_c w_c softmax_j(scale * mu_c . Kp_j),  Kp_j the mean key of block j;
+ * every query block i of group g = i / (q_group/N) takes row A_g, and
+ *   keep  = F_ij > thr with F the CDF of that row, as nabla_build_mask.
  * Distances and means are float32 with every operation rounded on its own, in a fixed
  * order (differences, squares and a running sum over d in index order; a running sum
  * over the cluster's queries in row order, then a division), so the clustering is
  * reproducible bit for bit by any implementation that follows the same order.
- * Arguments, outputs and errors as nabla_build_mask, with the workspace of
- * nabla_build_mask_ibcs_workspace_size().
+ * Arguments, outputs and errors as nabla_build_mask, plus q_group and the workspace of
+ * nabla_build_mask_ibcs_workspace_size(); NABLA_E_INVAL when q_group is not a positive
+ * multiple of N or does not divide L, NABLA_E_UNSUPPORTED when q_group is not 64 or
+ * 128.
  */
 nabla_status nabla_build_mask_ibcs(const void* q, const void* k, int batch, int heads, int T, int H,
-                                   int W, int d, int P, int N, float thr,
+                                   int W, int d, int P, int N, int q_group, float thr,
                                    const nabla_sta_window* sta, float scale, nabla_dtype dtype,
                                    int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                                    int32_t* schedule, void* workspace, size_t workspace_bytes,

@@ -291,32 +291,39 @@ def test_attn_weighted_validation(lib):
 # ------------------------------------------------------------- IBCS entry points
 
 def test_ibcs_workspace_size(lib):
-    # pooled K, 8 centroids and 8 weights per query block, the nb x nb scores; sections
-    # rounded up to 256
+    # pooled K per block; 8 centroids, 8 weights and one nb-long score row per query
+    # group; sections rounded up to 256
     blocks = 12 * 504
-    want = blocks * 128 * 4 + blocks * 8 * 128 * 4 + blocks * 8 * 4 + blocks * 504 * 4
-    assert lib.nabla_build_mask_ibcs_workspace_size(1, 12, 32256, 128, 64) == want
-    # 3 blocks, d = 64: 768 B, 6144 B, 96 B, 36 B -> 768 + 6144 + 256 + 256
-    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 192, 64, 64) == 768 + 6144 + 256 + 256
-    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 1000, 64, 64) == 0
-    assert lib.nabla_build_mask_ibcs_workspace_size(1, -1, 1024, 64, 64) == 0
+    for qg in (64, 128):
+        groups = blocks * 64 // qg
+        want = blocks * 128 * 4 + groups * 8 * 128 * 4 + groups * 8 * 4 + groups * 504 * 4
+        assert lib.nabla_build_mask_ibcs_workspace_size(1, 12, 32256, 128, 64, qg) == want
+    # 3 blocks, d = 64, one block per group: 768 B, 6144 B, 96 B, 36 B
+    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 192, 64, 64, 64) == 768 + 6144 + 256 + 256
+    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 192, 64, 64, 128) == 0     # 192 % 128
+    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 256, 64, 64, 96) == 0      # 96 % 64
+    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 1000, 64, 64, 64) == 0
+    assert lib.nabla_build_mask_ibcs_workspace_size(1, -1, 1024, 64, 64, 64) == 0
 
 
 def test_build_mask_ibcs_validation(lib):
     def call(**kw):
-        a = dict(q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, thr=0.1, sta=None, scale=0.0,
-                 dt=NABLA_BF16, cnt=C, idx=D_, ws=E, ws_bytes=1 << 30)
+        a = dict(q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, qg=128, thr=0.1, sta=None,
+                 scale=0.0, dt=NABLA_BF16, cnt=C, idx=D_, ws=E, ws_bytes=1 << 30)
         a.update(kw)
         win = None if a["sta"] is None else ctypes.byref(StaWindow(*a["sta"]))
         return lib.nabla_build_mask_ibcs(a["q"], a["k"], a["batch"], a["heads"], a["T"], a["H"], a["W"], a["d"],
-                                         a["P"], a["N"], a["thr"], win, a["scale"], a["dt"], a["cnt"], a["idx"],
-                                         None, None, a["ws"], a["ws_bytes"], None)
+                                         a["P"], a["N"], a["qg"], a["thr"], win, a["scale"], a["dt"], a["cnt"],
+                                         a["idx"], None, None, a["ws"], a["ws_bytes"], None)
     # the plain mask's workspace is too small for the centroids
     small_ws = lib.nabla_build_mask_workspace_size(1, 2, 1024, 64, 64)
     for kw, st in ((dict(q=None), NABLA_E_INVAL), (dict(thr=1.0), NABLA_E_INVAL), (dict(sta=(2, 3, 3)), NABLA_E_INVAL),
                    (dict(T=1, H=8, W=12, P=4), NABLA_E_INVAL), (dict(d=96), NABLA_E_UNSUPPORTED),
-                   (dict(N=32), NABLA_E_UNSUPPORTED), (dict(ws=None), NABLA_E_WORKSPACE),
-                   (dict(ws_bytes=small_ws), NABLA_E_WORKSPACE)):
+                   (dict(N=32, qg=64), NABLA_E_UNSUPPORTED), (dict(ws=None), NABLA_E_WORKSPACE),
+                   (dict(ws_bytes=small_ws), NABLA_E_WORKSPACE),
+                   (dict(qg=0), NABLA_E_INVAL), (dict(qg=96), NABLA_E_INVAL),
+                   (dict(T=3, H=8, W=8), NABLA_E_INVAL),          # 3 blocks: L = 192 not a multiple of 128
+                   (dict(qg=256), NABLA_E_UNSUPPORTED)):
         assert call(**kw) == st, kw
         assert lib.nabla_last_error().decode().startswith("nabla_build_mask_ibcs")
 

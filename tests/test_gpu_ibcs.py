@@ -42,23 +42,27 @@ def _up256(n):
     return (n + 255) // 256 * 256
 
 
-def gpu_ibcs(cfg, qf, kf, thr, sta=None):
-    """IBCS mask of fractal-ordered GPU tensors; returns lists, bitmap, and the
-    centroids [G, nb, 8, d] and weights [G, nb, 8] read back from the workspace."""
+def gpu_ibcs(cfg, qf, kf, thr, sta=None, qn=128):
+    """IBCS mask of fractal-ordered GPU tensors with query groups of qn tokens; returns
+    lists, bitmap, and the centroids [G, groups, 8, d], weights [G, groups, 8] and score
+    rows [G, groups, nb] read back from the workspace."""
     G, nb, d = cfg.BH, cfg.nb, cfg.d
-    nbytes = nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, d, cfg.N, ibcs=True)
+    ng = cfg.L // qn
+    nbytes = nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, d, cfg.N, ibcs=True, ibcs_group=qn)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=qf.device)
     cnt, idx, bm = nab.build_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, sta, with_bitmap=True,
-                                  workspace=ws, ibcs=True)
+                                  workspace=ws, ibcs=True, ibcs_group=qn)
     torch.cuda.synchronize()
     o_cent = _up256(G * nb * d * 4)
-    o_w = o_cent + _up256(G * nb * K * d * 4)
-    o_a = o_w + _up256(G * nb * K * 4)
-    assert o_a + _up256(G * nb * nb * 4) == nbytes
+    o_w = o_cent + _up256(G * ng * K * d * 4)
+    o_a = o_w + _up256(G * ng * K * 4)
+    assert o_a + _up256(G * ng * nb * 4) == nbytes
     host = ws.cpu()
-    cent = host[o_cent:o_cent + G * nb * K * d * 4].view(torch.float32).numpy().reshape(G, nb, K, d)
-    w = host[o_w:o_w + G * nb * K * 4].view(torch.float32).numpy().reshape(G, nb, K)
-    A = host[o_a:o_a + G * nb * nb * 4].view(torch.float32).numpy().reshape(G, nb, nb)
+    cent = host[o_cent:o_cent + G * ng * K * d * 4].view(torch.float32).numpy().reshape(G, ng, K, d)
+    w = host[o_w:o_w + G * ng * K * 4].view(torch.float32).numpy().reshape(G, ng, K)
+    A = host[o_a:o_a + G * ng * nb * 4].view(torch.float32).numpy().reshape(G, ng, nb)
+    # every query block takes its group's row
+    A = np.repeat(A, qn // cfg.N, axis=1)
     m = lists_to_mask(cnt.cpu().numpy().reshape(G, nb), idx.cpu().numpy().reshape(G, nb, nb))
     assert np.array_equal(bitmap_to_mask(bm.cpu().numpy().reshape(G, nb, -1), nb), m)
     return dict(cnt=cnt, idx=idx, mask=m, cent=cent, w=w, A=A)
@@ -70,13 +74,13 @@ def score_err(gpu_A, ref_A):
     return float(np.max(np.abs(gpu_A - ref).max(-1) / ref.max(-1)))
 
 
-def check_clusters(res, qf_np, N, heads, blocks=None):
-    """Centroids bit for bit, weights exactly, for the given heads (and blocks)."""
-    nb = res["cent"].shape[1]
+def check_clusters(res, qf_np, qn, heads):
+    """Centroids bit for bit, weights exactly, for every query group of the given heads."""
+    ng = res["cent"].shape[1]
     n = 0
     for g in heads:
-        for i in (range(nb) if blocks is None else blocks):
-            cent, w = O.ibcs_clusters(qf_np[g, i * N:(i + 1) * N])
+        for i in range(ng):
+            cent, w = O.ibcs_clusters(qf_np[g, i * qn:(i + 1) * qn])
             gc = res["cent"][g, i]
             assert np.array_equal(gc.view(np.uint32), cent.view(np.uint32)), (
                 f"head {g} block {i}: centroids differ, max-abs {np.max(np.abs(gc - cent)):.3e}")
@@ -85,8 +89,8 @@ def check_clusters(res, qf_np, N, heads, blocks=None):
     return n
 
 
-def oracle_mask(cfg, qf_np, kf_np, thr, sta=None):
-    ref = O.ibcs_block_mask(qf_np, kf_np, cfg.N, thr)
+def oracle_mask(cfg, qf_np, kf_np, thr, sta=None, qn=128):
+    ref = O.ibcs_block_mask(qf_np, kf_np, cfg.N, thr, qn=qn)
     mask = ref["mask"]
     if sta is not None:
         mask = mask | O.sta_mask(cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, sta)[None]
@@ -102,49 +106,56 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("qn", [128, 64])
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
-def test_ibcs_parity(cfg):
-    say(f"IBCS {cfg.name}: {cfg.B}x{cfg.heads} nb {cfg.nb} d{cfg.d} {cfg.dtype} thr {cfg.thr} sta {cfg.sta}")
+def test_ibcs_parity(cfg, qn):
+    if cfg.L % qn:
+        pytest.skip(f"nb = {cfg.nb} blocks do not split into {qn}-query groups (rejected by the entry point)")
+    say(f"IBCS {cfg.name} q_group {qn}: {cfg.B}x{cfg.heads} nb {cfg.nb} d{cfg.d} {cfg.dtype} thr {cfg.thr} "
+        f"sta {cfg.sta}")
     q, k, v = make_qkv(cfg)
     G = cfg.BH
     qf = nab.reorder(q.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
     kf = nab.reorder(k.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
-    res = gpu_ibcs(cfg, qf, kf, cfg.thr, cfg.sta)
-    qn = qf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)
-    kn = kf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)
-    n = check_clusters(res, qn, cfg.N, range(G))
-    ref_m, ref_A = oracle_mask(cfg, qn, kn, cfg.thr, cfg.sta)
+    res = gpu_ibcs(cfg, qf, kf, cfg.thr, cfg.sta, qn)
+    qnp = qf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)
+    knp = kf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)
+    n = check_clusters(res, qnp, qn, range(G))
+    ref_m, ref_A = oracle_mask(cfg, qnp, knp, cfg.thr, cfg.sta, qn)
     err = score_err(res["A"], ref_A)
     assert err <= A_TOL, err
     assert np.allclose(res["A"].sum(-1), 1.0, atol=1e-5)
     mism, band = check_mask(res["mask"], ref_m, ref_A, cfg.thr)
-    say(f"  {n} blocks' centroids bit-identical; scores rel err {err:.2e}; kept {res['mask'].mean():.3f}, "
+    say(f"  {n} groups' centroids bit-identical; scores rel err {err:.2e}; kept {res['mask'].mean():.3f}, "
         f"mask mismatches {mism}, band {band}")
     # the top block of every row is kept, as in NABLA
     top = np.argmax(ref_A, axis=-1)
     assert np.all(np.take_along_axis(res["mask"], top[..., None], axis=-1))
 
 
-def test_identical_queries_reduce_to_nabla():
-    """When all 64 queries of every block are equal, every query joins cluster 0 (all
-    distances tie), its centroid is the query and its weight 1, so the IBCS score row is
-    NABLA's pooled softmax row: the lists must equal nabla_build_mask's bit for bit."""
+@pytest.mark.parametrize("qn", [64, 128])
+def test_identical_queries_reduce_to_nabla(qn):
+    """When all queries of every group are equal, every query joins cluster 0 (all
+    distances tie), its centroid is the query (bf16 values: the running sum is exact)
+    and its weight 1, so the IBCS score row is NABLA's pooled softmax row: the lists must
+    equal nabla_build_mask's bit for bit."""
     cfg = small("const_blocks", 3, 16, 24, 128, "bf16", 0.2, heads=2)
     q, k, _ = make_qkv(cfg)
     qf = nab.reorder(q.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
     kf = nab.reorder(k.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
     G, nb, N, d = cfg.BH, cfg.nb, cfg.N, cfg.d
-    qc = qf.reshape(G, nb, N, d)[:, :, :1, :].expand(G, nb, N, d).reshape(qf.shape).contiguous()
-    res = gpu_ibcs(cfg, qc, kf, cfg.thr)
+    ng = cfg.L // qn
+    qc = qf.reshape(G, ng, qn, d)[:, :, :1, :].expand(G, ng, qn, d).reshape(qf.shape).contiguous()
+    res = gpu_ibcs(cfg, qc, kf, cfg.thr, qn=qn)
     assert np.all(res["w"][:, :, 0] == 1.0) and np.all(res["w"][:, :, 1:] == 0.0)
-    first = qc.float().cpu().numpy().reshape(G, nb, N, d)[:, :, 0, :]
+    first = qc.float().cpu().numpy().reshape(G, ng, qn, d)[:, :, 0, :]
     assert np.array_equal(res["cent"][:, :, 0, :], first)
     ref = nab.build_mask(qc, kf, cfg.T, cfg.H, cfg.W, cfg.P, N, cfg.thr, with_bitmap=True)
     torch.cuda.synchronize()
     assert torch.equal(ref[0].cpu(), res["cnt"].cpu())
     assert np.array_equal(lists_to_mask(ref[0].cpu().numpy().reshape(G, nb), ref[1].cpu().numpy().reshape(G, nb, nb)),
                           res["mask"])
-    say(f"IBCS on constant blocks equals the NABLA mask: kept {res['mask'].mean():.3f}")
+    say(f"IBCS on constant {qn}-query groups equals the NABLA mask: kept {res['mask'].mean():.3f}")
 
 
 def test_ibcs_determinism_and_workspace_reuse():
@@ -167,24 +178,25 @@ def test_ibcs_determinism_and_workspace_reuse():
     assert np.array_equal(ma, mb)
 
 
-def test_ibcs_full_size():
+@pytest.mark.parametrize("qn", [128, 64])
+def test_ibcs_full_size(qn):
     """The Wan-1.3B-like layer at full size: every head through the GPU; centroids of two
     heads bit for bit and their masks against the oracle."""
     cfg = CONFIGS[1]
-    say(f"IBCS full size {cfg.name}: {cfg.BH} heads nb {cfg.nb}")
+    say(f"IBCS full size {cfg.name} q_group {qn}: {cfg.BH} heads nb {cfg.nb}")
     q, k, _ = make_qkv(cfg)
     G = cfg.BH
     qf = nab.reorder(q.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
     kf = nab.reorder(k.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
-    res = gpu_ibcs(cfg, qf, kf, cfg.thr)
+    res = gpu_ibcs(cfg, qf, kf, cfg.thr, qn=qn)
     say(f"  GPU mask built: kept {res['mask'].mean():.4f}")
     heads = [0, G - 1]
-    qn = qf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)[heads]
-    kn = kf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)[heads]
+    qnp = qf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)[heads]
+    knp = kf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)[heads]
     sub = dict(cent=res["cent"][heads], w=res["w"][heads])
-    n = check_clusters(sub, qn, cfg.N, range(len(heads)))
-    say(f"  {n} blocks' centroids bit-identical")
-    ref_m, ref_A = oracle_mask(cfg, qn, kn, cfg.thr)
+    n = check_clusters(sub, qnp, qn, range(len(heads)))
+    say(f"  {n} groups' centroids bit-identical")
+    ref_m, ref_A = oracle_mask(cfg, qnp, knp, cfg.thr, qn=qn)
     err = score_err(res["A"][heads], ref_A)
     assert err <= A_TOL, err
     mism, band = check_mask(res["mask"][heads], ref_m, ref_A, cfg.thr)
