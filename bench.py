@@ -18,6 +18,7 @@ GB/s against HBM peak ride along, with the oracle timed on the host beside it.
     python bench.py --backward --no-cpu             # the gradient of the attention step
     python bench.py --sip 185 --no-cpu              # SIP selection + weighted attention
     python bench.py --ibcs --no-cpu                 # IBCS block scores + attention
+    python bench.py --mask-every 4 --no-cpu         # mask rebuilt every 4th step, reused between
 """
 from __future__ import annotations
 
@@ -315,6 +316,65 @@ def bench_ibcs(args, cfg, qd, kd, vd) -> int:
     return 0
 
 
+def bench_mask_reuse(args, cfg, qd, kd, vd) -> int:
+    """A run of denoising steps in which the mask is rebuilt only every `mask_every`-th
+    step and its lists are reused by the steps in between (the AB-Attention page
+    recomputes its plan every 4 steps): raster-order entry points, the step's attention
+    every step.  Reports the amortised step time; inputs stay the same from step to
+    step, which changes no kernel's work."""
+    T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
+    K = args.mask_every
+    nb = cfg.nb
+    cnt = torch.empty((cfg.B, cfg.heads, nb), dtype=torch.int32, device="cuda")
+    idx = torch.empty((cfg.B, cfg.heads, nb, nb), dtype=torch.int32, device="cuda")
+    sched = torch.empty((cfg.BH * nb,), dtype=torch.int32, device="cuda")
+    ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, N), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(qd)
+
+    def step(i):
+        if i % K == 0:
+            nab.build_mask(qd, kd, T, H, W, P, N, cfg.thr, cfg.sta, workspace=ws, kv_count=cnt, kv_index=idx,
+                           schedule=sched, raster=True)
+        nab.attn_fwd_raster(qd, kd, vd, cnt, idx, T, H, W, P, N, out=o, schedule=sched)
+
+    steps = max(K, (args.steps // K) * K)          # whole mask periods
+    for i in range(max(args.warmup, 1) * K):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = e0.elapsed_time(e1) / steps
+    kept = int(cnt.sum().item())
+    flops = kept * 4.0 * N * N * cfg.d
+    rec = {
+        "metric": "NABLA step with the mask reused: kept-tile TFLOP/s over the amortised step",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(args.warmup, 1) * K,
+        "ms_per_step": round(ms, 4),
+        "wall_ms_per_step": round((t1 - t0) * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": f"synthetic ({GENERATOR_VERSION})",
+        "config": {"workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "L": cfg.L,
+                   "blocks_per_head": nb, "thr": cfg.thr, "sta": cfg.sta, "mask_every": K},
+        "kept_fraction": round(kept / (cfg.BH * nb * nb), 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +397,9 @@ def main(argv=None):
     ap.add_argument("--ibcs", action="store_true",
                     help="time the IBCS variant instead: block scores from 8 query clusters per block, "
                          "NABLA's CDF cut, attention on the kept tiles; prints its own JSON line")
+    ap.add_argument("--mask-every", type=int, default=0, metavar="K",
+                    help="time a run of steps that rebuilds the mask only every K-th step and reuses "
+                         "its lists in between; prints its own JSON line")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="time only a dense 8192^3 bf16 GEMM of the vendor library (torch.matmul) "
                          "for --loop-seconds (default 10): the rate a plain GEMM sustains on this "
@@ -454,6 +517,8 @@ def main(argv=None):
         return bench_sip(args, cfg, qd, kd, vd)
     if args.ibcs:
         return bench_ibcs(args, cfg, qd, kd, vd)
+    if args.mask_every > 0:
+        return bench_mask_reuse(args, cfg, qd, kd, vd)
 
     for _ in range(args.warmup):
         step()

@@ -201,3 +201,25 @@ def test_ibcs_full_size(qn):
     assert err <= A_TOL, err
     mism, band = check_mask(res["mask"][heads], ref_m, ref_A, cfg.thr)
     say(f"  heads {heads}: scores rel err {err:.2e}, mask mismatches {mism}, band {band}")
+
+
+@pytest.mark.parametrize("qn", [128, 64])
+def test_ibcs_max_blocks_per_head(qn):
+    """The largest mask the library accepts, 2048 blocks per head (16 frames of 8 x 16
+    patches): the score kernel then holds 16 centroid rows of 2048 logits in LDS."""
+    cfg = small("nb2048", 16, 64, 128, 64, "bf16", 0.2, heads=1)
+    assert cfg.nb == 2048
+    say(f"IBCS max blocks per head q_group {qn}: nb {cfg.nb}, L {cfg.L}")
+    q, k, _ = make_qkv(cfg)
+    qf = nab.reorder(q.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    kf = nab.reorder(k.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+    res = gpu_ibcs(cfg, qf, kf, cfg.thr, qn=qn)
+    qnp = qf.float().cpu().numpy().reshape(1, cfg.L, cfg.d)
+    knp = kf.float().cpu().numpy().reshape(1, cfg.L, cfg.d)
+    n = check_clusters(res, qnp, qn, [0])
+    ref_m, ref_A = oracle_mask(cfg, qnp, knp, cfg.thr, qn=qn)
+    err = score_err(res["A"], ref_A)
+    assert err <= A_TOL, err
+    mism, band = check_mask(res["mask"], ref_m, ref_A, cfg.thr)
+    say(f"  {n} groups' centroids bit-identical; scores rel err {err:.2e}; kept {res['mask'].mean():.4f}, "
+        f"mask mismatches {mism}, band {band}")
