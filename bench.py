@@ -18,6 +18,7 @@ GB/s against HBM peak ride along, with the oracle timed on the host beside it.
     python bench.py --backward --no-cpu             # the gradient of the attention step
     python bench.py --sip 185 --no-cpu              # SIP selection + weighted attention
     python bench.py --ibcs --no-cpu                 # IBCS block scores + attention
+    python bench.py --ibcs --sip 185 --no-cpu       # SIP sampling from IBCS scores
     python bench.py --mask-every 4 --no-cpu         # mask rebuilt every 4th step, reused between
 """
 from __future__ import annotations
@@ -176,19 +177,21 @@ def bench_backward(args, cfg, qd, kd, vd) -> int:
 
 def bench_sip(args, cfg, qd, kd, vd) -> int:
     """SIP variant of the step on fractal-order tensors: nabla_build_mask_sip (pooling,
-    pooled map, inclusion probabilities, sampling against seeded draws) and
-    block_sparse_attn_fwd_weighted, each bracketed by HIP events."""
+    pooled map, inclusion probabilities, sampling against seeded draws) - or with --ibcs
+    nabla_build_mask_ibcs_sip (IBCS scores of 128-query clusters, then the same
+    sampling) - and block_sparse_attn_fwd_weighted, each bracketed by HIP events."""
     T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
     qf, kf, vf = (nab.reorder(t, T, H, W, P) for t in (qd, kd, vd))
     g = torch.Generator(device="cuda").manual_seed(4321)
     u = torch.rand((cfg.B, cfg.heads, cfg.nb, cfg.nb), device="cuda", generator=g)
-    ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, N), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, N, ibcs=args.ibcs),
+                     dtype=torch.uint8, device="cuda")
     o = torch.empty_like(qf)
     state = {}
 
     def mask():
-        state["lists"] = nab.build_mask_sip(qf, kf, T, H, W, P, args.sip, u, N, with_schedule=True, workspace=ws)
+        state["lists"] = nab.build_mask_sip(qf, kf, T, H, W, P, args.sip, u, N, with_schedule=True, workspace=ws,
+                                            ibcs=args.ibcs)
 
     def attn():
         cnt, idx, logw, sched = state["lists"]
@@ -214,7 +217,7 @@ def bench_sip(args, cfg, qd, kd, vd) -> int:
     flops = kept * 4.0 * N * N * cfg.d
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     rec = {
-        "metric": "SIP block-sparse attn: kept-tile TFLOP/s (weighted attention), ms/layer",
+        "metric": ("IBCS+SIP" if args.ibcs else "SIP") + " block-sparse attn: kept-tile TFLOP/s (weighted attention), ms/layer",
         "value": round(flops / (ms_attn * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -227,7 +230,7 @@ def bench_sip(args, cfg, qd, kd, vd) -> int:
         "dtype": cfg.dtype,
         "data": f"synthetic ({GENERATOR_VERSION}), draws U[0,1) seeded",
         "config": {"workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "L": cfg.L,
-                   "blocks_per_head": cfg.nb, "budget": args.sip},
+                   "blocks_per_head": cfg.nb, "budget": args.sip, "scores": "ibcs_q128" if args.ibcs else "pooled"},
         "ms_mask_sip": round(ms_mask, 4),
         "ms_attn_weighted": round(ms_attn, 4),
         "mean_kept_per_row": round(kept / (cfg.BH * cfg.nb), 2),
@@ -514,7 +517,7 @@ def main(argv=None):
     if args.backward:
         return bench_backward(args, cfg, qd, kd, vd)
     if args.sip > 0:
-        return bench_sip(args, cfg, qd, kd, vd)
+        return bench_sip(args, cfg, qd, kd, vd)   # --ibcs picks the IBCS scores
     if args.ibcs:
         return bench_ibcs(args, cfg, qd, kd, vd)
     if args.mask_every > 0:

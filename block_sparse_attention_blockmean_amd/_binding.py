@@ -27,6 +27,7 @@ EXPORTS = (
     "nabla_build_mask_sip",
     "nabla_build_mask_ibcs_workspace_size",
     "nabla_build_mask_ibcs",
+    "nabla_build_mask_ibcs_sip",
     "block_sparse_attn_fwd_weighted",
     "block_sparse_attn_fwd",
     "block_sparse_attn_fwd_raster",
@@ -73,6 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                           f, i, vp, vp, vp, vp, vp, sz, vp]
     lib.nabla_build_mask_ibcs.restype = i
     lib.nabla_build_mask_ibcs_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.nabla_build_mask_ibcs_sip.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, i, vp, f, i, vp, vp, vp, vp, vp, vp,
+                                              sz, vp]
+    lib.nabla_build_mask_ibcs_sip.restype = i
     lib.nabla_build_mask_ibcs_workspace_size.restype = sz
     lib.block_sparse_attn_fwd_raster.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, f, i, vp]
     lib.block_sparse_attn_fwd_raster.restype = i
@@ -267,10 +271,11 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.
 def build_mask_sip(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int, budget: int,
                    uniforms: torch.Tensor, N: int = 64, scale: Optional[float] = None,
                    with_bitmap: bool = False, with_schedule: bool = False,
-                   workspace: Optional[torch.Tensor] = None):
+                   workspace: Optional[torch.Tensor] = None, ibcs: bool = False, ibcs_group: int = 128):
     """SIP block selection of fractal-ordered Q, K: returns (kv_count, kv_index, kv_logw),
     plus the bitmap and/or schedule when asked for.  ``uniforms`` is a float32
-    [B, heads, nb, nb] tensor of draws in [0, 1)."""
+    [B, heads, nb, nb] tensor of draws in [0, 1).  The scores sampled from are NABLA's
+    pooled map, or with ``ibcs=True`` the IBCS scores of ``ibcs_group``-query clusters."""
     lib = load_library()
     B, NH, L, d = q.shape
     if k.shape != q.shape or k.dtype != q.dtype:
@@ -284,10 +289,15 @@ def build_mask_sip(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: 
     kv_logw = torch.empty((B, NH, nb, nb), dtype=torch.float32, device=dev)
     bitmap = torch.empty((B, NH, nb, (nb + 31) // 32), dtype=torch.int32, device=dev) if with_bitmap else None
     schedule = torch.empty((B * NH * nb,), dtype=torch.int32, device=dev) if with_schedule else None
-    ws_bytes = lib.nabla_build_mask_workspace_size(B, NH, L, d, N)
+    ws_bytes = build_mask_workspace_size(B, NH, L, d, N, ibcs=ibcs, ibcs_group=ibcs_group)
     if workspace is None:
         workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
-    _check(lib.nabla_build_mask_sip(
+    if ibcs:
+        entry = lambda q_, k_, B_, NH_, T_, H_, W_, d_, P_, N_, *rest: lib.nabla_build_mask_ibcs_sip(
+            q_, k_, B_, NH_, T_, H_, W_, d_, P_, N_, int(ibcs_group), *rest)
+    else:
+        entry = lib.nabla_build_mask_sip
+    _check(entry(
         _dev(q, "q"), _dev(k, "k"), B, NH, T, H, W, d, P, N, int(budget), _dev(uniforms, "uniforms"),
         float(scale) if scale is not None else 0.0, _dtype_code(q), _dev(kv_count, "kv_count"),
         _dev(kv_index, "kv_index"), _dev(kv_logw, "kv_logw"),

@@ -158,6 +158,23 @@ nabla_status nabla_build_mask_ibcs(const void* q, const void* k, int batch, int 
                            bitmap, schedule, workspace, workspace_bytes, stream, 0, nullptr, nullptr, q_group);
 }
 
+nabla_status nabla_build_mask_ibcs_sip(const void* q, const void* k, int batch, int heads, int T, int H, int W,
+                                       int d, int P, int N, int q_group, int budget, const float* uniforms,
+                                       float scale, nabla_dtype dtype, int32_t* kv_count, int32_t* kv_index,
+                                       float* kv_logw, uint32_t* bitmap, int32_t* schedule, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    const char* who = "nabla_build_mask_ibcs_sip";
+    if (!uniforms || !kv_logw) return fail(NABLA_E_INVAL, "%s: null pointer", who);
+    if (((uintptr_t)uniforms & 3) || ((uintptr_t)kv_logw & 3))
+        return fail(NABLA_E_INVAL, "%s: misaligned pointer", who);
+    if (budget < 1) return fail(NABLA_E_INVAL, "%s: budget must be at least 1", who);
+    if (q_group <= 0 || N <= 0 || q_group % N)
+        return fail(NABLA_E_INVAL, "%s: q_group=%d must be a positive multiple of N=%d", who, q_group, N);
+    return build_mask_impl(who, 0, q, k, batch, heads, T, H, W, d, P, N, 0.0f, nullptr, scale, dtype, kv_count,
+                           kv_index, bitmap, schedule, workspace, workspace_bytes, stream, budget, uniforms, kv_logw,
+                           q_group);
+}
+
 nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, int heads, int T, int H,
                                      int W, int d, int P, int N, float thr,
                                      const nabla_sta_window* sta, float scale, nabla_dtype dtype,

@@ -263,6 +263,24 @@ nabla_status nabla_build_mask_ibcs(const void* q, const void* k, int batch, int 
                                    hipStream_t stream);
 
 /*
+ * nabla_build_mask_ibcs_sip - the AB-Attention page's two selectors together: IBCS
+ * block scores (as nabla_build_mask_ibcs: q_group-query clusters, weighted centroid
+ * attention to the mean keys) sampled by SIP (as nabla_build_mask_sip: inclusion
+ * probabilities pi_j = min(1, c A_j) with the row's top block certain and an expected
+ * `budget` blocks per row, block j kept iff uniforms[b,h,i,j] < pi_j, list entries
+ * carrying kv_logw = log(1 / pi_j) for block_sparse_attn_fwd_weighted).  Block i
+ * samples from its group's score row with its own draws.
+ * Arguments and outputs as nabla_build_mask_sip, plus q_group; the workspace of
+ * nabla_build_mask_ibcs_workspace_size().  Errors: as nabla_build_mask_sip and
+ * nabla_build_mask_ibcs.
+ */
+nabla_status nabla_build_mask_ibcs_sip(const void* q, const void* k, int batch, int heads, int T, int H, int W,
+                                       int d, int P, int N, int q_group, int budget, const float* uniforms,
+                                       float scale, nabla_dtype dtype, int32_t* kv_count, int32_t* kv_index,
+                                       float* kv_logw, uint32_t* bitmap, int32_t* schedule, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
  * block_sparse_attn_fwd_weighted - block_sparse_attn_fwd with an additive logit shift
  * per kept tile: the logits of the tokens of list entry e of row i are
  * scale * q . k + kv_logw[b,h,i,e] (the SIP weights of nabla_build_mask_sip; the

@@ -328,6 +328,23 @@ def test_build_mask_ibcs_validation(lib):
         assert lib.nabla_last_error().decode().startswith("nabla_build_mask_ibcs")
 
 
+def test_build_mask_ibcs_sip_validation(lib):
+    def call(**kw):
+        a = dict(q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, qg=128, budget=4, u=G, scale=0.0,
+                 dt=NABLA_BF16, cnt=C, idx=D_, logw=E, ws=F_, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.nabla_build_mask_ibcs_sip(a["q"], a["k"], a["batch"], a["heads"], a["T"], a["H"], a["W"],
+                                             a["d"], a["P"], a["N"], a["qg"], a["budget"], a["u"], a["scale"],
+                                             a["dt"], a["cnt"], a["idx"], a["logw"], None, None, a["ws"],
+                                             a["ws_bytes"], None)
+    small_ws = lib.nabla_build_mask_workspace_size(1, 2, 1024, 64, 64)
+    for kw, st in ((dict(u=None), NABLA_E_INVAL), (dict(logw=None), NABLA_E_INVAL), (dict(budget=0), NABLA_E_INVAL),
+                   (dict(qg=96), NABLA_E_INVAL), (dict(T=3, H=8, W=8), NABLA_E_INVAL), (dict(qg=256), NABLA_E_UNSUPPORTED),
+                   (dict(d=96), NABLA_E_UNSUPPORTED), (dict(ws_bytes=small_ws), NABLA_E_WORKSPACE)):
+        assert call(**kw) == st, kw
+        assert lib.nabla_last_error().decode().startswith("nabla_build_mask_ibcs_sip")
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 1024, 64)

@@ -134,3 +134,44 @@ def test_sip_full_size():
         sub = dict(mask=res["mask"][sl], u=res["u"][sl], dense_w=res["dense_w"][sl], cnt=res["cnt"].reshape(G, nb)[sl])
         mism, err_w = check_sip(sub, ref_m, ref_w, ref_pi, budget)
         say(f"  head {g}: band mismatches {mism}, logw err {err_w:.2e}")
+
+
+@pytest.mark.parametrize("qn", [128, 64])
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2]], ids=lambda c: c.name)
+def test_ibcs_sip_parity(cfg, qn):
+    """The AB-Attention page's selectors together: SIP sampling from IBCS scores
+    (q_group-query clusters).  Decisions against the oracle's sip_mask of its
+    ibcs_scores, within the draw band; log-weights; weighted attention on the GPU's
+    lists."""
+    q, k, v = make_qkv(cfg)
+    G, nb = cfg.BH, cfg.nb
+    qd, kd = q.cuda(), k.cuda()
+    qf, kf = (nab.reorder(t, cfg.T, cfg.H, cfg.W, cfg.P) for t in (qd, kd))
+    qnp, knp = (t.float().cpu().numpy().reshape(G, cfg.L, cfg.d) for t in (qf, kf))
+    A = O.ibcs_scores(qnp, knp, cfg.N, qn=qn)
+    for budget in (1, max(2, nb // 6), nb // 2, nb):
+        u = torch.rand((cfg.B, cfg.heads, nb, nb), generator=torch.Generator().manual_seed(budget + 100))
+        cnt, idx, logw, bm = nab.build_mask_sip(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, budget, u.cuda(), cfg.N,
+                                                with_bitmap=True, ibcs=True, ibcs_group=qn)
+        torch.cuda.synchronize()
+        cn = cnt.cpu().numpy().reshape(G, nb)
+        ix = idx.cpu().numpy().reshape(G, nb, nb)
+        lw = logw.cpu().numpy().reshape(G, nb, nb)
+        m = lists_to_mask(cn, ix)
+        dense_w = np.zeros((G, nb, nb))
+        for g in range(G):
+            for i in range(nb):
+                dense_w[g, i, ix[g, i, :cn[g, i]]] = lw[g, i, :cn[g, i]]
+        res = dict(mask=m, u=u.numpy().reshape(G, nb, nb), dense_w=dense_w, cnt=cnt)
+        ref_m, ref_w, ref_pi = O.sip_mask(A, budget, res["u"])
+        mism, err_w = check_sip(res, ref_m, ref_w, ref_pi, budget)
+        say(f"IBCS+SIP {cfg.name} q_group {qn} budget {budget}: mean kept {m.sum(-1).mean():.2f}, "
+            f"band mismatches {mism}, logw err {err_w:.2e}")
+        vf = nab.reorder(v.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)
+        o = nab.attn_fwd_weighted(qf, kf, vf, cnt, idx, logw, cfg.N)
+        torch.cuda.synchronize()
+        args = [t.float().cpu().numpy().reshape(G, cfg.L, cfg.d) for t in (qf, kf, vf)]
+        ref_o = O.weighted_block_attention(*args, m, dense_w, cfg.N)
+        err = max_abs(o.float().cpu().numpy().reshape(G, cfg.L, cfg.d), ref_o)
+        tol = TOL_BF16 if cfg.dtype == "bf16" else TOL_F32
+        assert err <= tol, err
