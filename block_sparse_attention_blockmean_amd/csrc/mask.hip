@@ -2,12 +2,13 @@
 // STA union of item 3):
 //   pool_kernel        block means of Q and K (one HBM pass over both, float32 sums)
 //   map_select_kernel  reduced map S = Qp Kp^T * scale on float32 MFMA, row softmax,
-//                      the CDF cutoff found by bisection on float32 bit patterns, the
-//                      STA OR, and compaction of each row into an ascending kept list.
+//                      then per row (select_row) the CDF cutoff found by bisection on
+//                      float32 bit patterns (or SIP sampling), the STA OR, and
+//                      compaction into an ascending kept list
 // With IBCS block scores the rows of the map are the 8 cluster centroids of each query
-// block (ibcs.hip) instead of its mean: ibcs_score_kernel forms each block's score row
-// as the weighted sum of its centroids' softmax rows, and map_select_kernel takes those
-// rows as given; the cut and the lists are the same.
+// group (ibcs.hip) instead of its mean: ibcs_score_kernel writes each group's score row,
+// the weighted sum of its centroids' softmax rows, and select_kernel applies select_row
+// to those rows; the cut and the lists are the same.
 #include <math.h>
 
 #include "attn_tile.h"
@@ -109,22 +110,20 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// Reduced map + softmax + CDF cutoff + STA + lists.
-// A workgroup (16 waves) owns 16 query blocks (rows) of one head.
-// Phase 1: the waves compute 16x16 tiles of S with v_mfma_f32_16x16x4_f32 (float32
-//   operands and accumulation) and park the 16 rows in LDS.
-// Phase 2: each wave takes whole rows.  Keeping block j iff F_j > thr is the same as
-//   keeping every block whose probability is at least v*, the smallest row value
-//   with g(v*) > thr, where g(u) = sum of the row values <= u.  g only grows with u,
-//   and non-negative floats order like their bit patterns, so v* is found by
-//   bisection over bit patterns.  The search starts at u0 = thr / nb (g(u0) <= nb u0
-//   = thr) and keeps only the values still inside the bracket (compacted into a
-//   per-wave LDS buffer), so each step touches fewer values and the search stops
-//   once a single candidate is left.  All sums run in a fixed order, so the result
-//   is deterministic.
+// Reduced map, then the cut.
+// The map kernels hold kRows = 16 rows of S per workgroup (the M of the 16x16 float32
+//   MFMA).
+// The cut (select_row) takes one row in one wave.  Keeping block j iff F_j > thr is the
+//   same as keeping every block whose probability is at least v*, the smallest row
+//   value with g(v*) > thr, where g(u) = sum of the row values <= u.  g only grows with
+//   u, and non-negative floats order like their bit patterns, so v* is found by
+//   bisection over bit patterns.  The search starts at u0 = thr / nb (g(u0) <= nb u0 =
+//   thr) and keeps only the values still inside the bracket (compacted into a per-wave
+//   LDS buffer), so each step touches fewer values and the search stops once a single
+//   candidate is left.  All sums run in a fixed order, so the result is deterministic.
 // ---------------------------------------------------------------------------
 constexpr int kRows = 16;
-constexpr int kWaves = 16;
+constexpr int kScoreWaves = 4;   // waves of an IBCS score workgroup
 constexpr int kCap = 256;   // candidates per wave held in LDS
 
 // Wave-wide reductions on DPP: shifts of 1, 2, 4, 8 lanes inside each 16-lane row, then
@@ -343,7 +342,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // per SIMD, so four such workgroups share a CU and one's loads overlap another's MFMAs.
 // ---------------------------------------------------------------------------
 static_assert(kRows % kIbcsClusters == 0, "a workgroup holds whole query blocks' centroids");
-constexpr int kScoreWaves = 4;
 
 template <int D>
 __global__ __launch_bounds__(kScoreWaves * 64) void ibcs_score_kernel(const float* __restrict__ cent,
@@ -398,184 +396,207 @@ __global__ __launch_bounds__(kScoreWaves * 64) void ibcs_score_kernel(const floa
 }
 
 // ---------------------------------------------------------------------------
-// Map + select.  Rows are either NABLA's pooled map (qp given: map_rows, then a row
-// softmax) or block scores computed elsewhere (given_a [BH, nb / a_group, nb], rows
-// summing to one, row i / a_group for query block i, loaded as they are).
+// The cut of one row, in one wave: `arow` (LDS) holds the row's values, inv_sum times
+// which are its probabilities A (summing to one; the product is written back on the
+// first pass), `cand` is the wave's candidate buffer.  SIP sampling when
+// sip_budget > 0, else the CDF cut; then the STA OR and the ascending list, count and
+// bitmap of query block `row` of head bh.
 // ---------------------------------------------------------------------------
+__device__ void select_row(float* arow, float inv_sum, float* cand, int nb, int bh, int row, float thr, int sta,
+                           int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
+                           int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int sip_budget,
+                           const float* __restrict__ uniforms, float* __restrict__ kv_logw, int lane) {
+    const int nwords = (nb + 31) >> 5;
+    if (sip_budget > 0) {
+        sip_row(arow, nb, inv_sum, sip_budget, uniforms + ((size_t)bh * nb + row) * nb,
+                kv_index + ((size_t)bh * nb + row) * nb, kv_logw + ((size_t)bh * nb + row) * nb,
+                bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr, nwords,
+                kv_count + (size_t)bh * nb + row, lane);
+        return;
+    }
+    // start of the bracket: u0 = thr / nb, nudged down so rounding cannot push
+    // g(u0) above thr; it is verified below and dropped to 0 if it fails
+    uint32_t lo = __float_as_uint(thr / ((float)nb * 1.0001f));
+    float g_lo = 0.f;
+    int n_in = 0;
+    uint32_t maxb = 0;
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+        const int j = j0 + lane;
+        bool in = false;
+        if (j < nb) {
+            const float p = arow[j] * inv_sum;
+            arow[j] = p;
+            const uint32_t b = __float_as_uint(p);
+            maxb = max(maxb, b);
+            if (b <= lo) g_lo += p; else in = true;
+        }
+        n_in += __popcll(__ballot(in));
+    }
+    g_lo = wave_sum(g_lo);
+    maxb = wave_max_u(maxb);
+    if (g_lo > thr) {   // cannot happen in exact arithmetic; fall back to g(0) = 0
+        lo = 0;
+        g_lo = 0.f;
+        n_in = 0;
+        for (int j0 = 0; j0 < nb; j0 += 64) {
+            const int j = j0 + lane;
+            n_in += __popcll(__ballot(j < nb && __float_as_uint(arow[j]) > 0u));
+        }
+    }
+    uint32_t hi = maxb;
+    // bracket (lo, hi]: g(lo) = g_lo <= thr and, unless the whole row sums to at
+    // most thr, g(hi) > thr; n_in values lie inside it (always >= 1: the maximum)
+    const float* src = arow;
+    int len = nb;
+    if (n_in <= kCap) {
+        len = compact(arow, nb, lo, hi, cand, lane);
+        src = cand;
+    }
+    // bisection until at most 64 values are left in the bracket
+    while (hi - lo > 1 && n_in > 64) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        float s_ = 0.f;
+        int c = 0;
+        for (int j0 = 0; j0 < len; j0 += 64) {
+            const int j = j0 + lane;
+            const float x = (j < len) ? src[j] : 0.f;
+            const uint32_t b = __float_as_uint(x);
+            const bool in = (j < len) && b > lo && b <= mid;
+            if (in) s_ += x;
+            c += __popcll(__ballot(in));
+        }
+        s_ = wave_sum(s_);
+        if (g_lo + s_ > thr) {
+            hi = mid;
+            n_in = c;
+        } else {
+            lo = mid;
+            g_lo += s_;
+            n_in -= c;
+        }
+        if (n_in <= kCap && 2 * n_in <= len) {
+            len = compact(src, len, lo, hi, cand, lane);
+            src = cand;
+        }
+    }
+    uint32_t cut = hi;
+    if (n_in <= 64) {
+        // one candidate per lane: F(x) = g_lo + (sum of the candidates <= x), tied
+        // values together; the cut is the smallest candidate with F(x) > thr
+        len = compact(src, len, lo, hi, cand, lane);
+        const float x = lane < len ? cand[lane] : 0.f;
+        const uint32_t bx = __float_as_uint(x);
+        float below = 0.f;
+        for (int m = 0; m < len; ++m) {
+            const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), m));
+            if (__float_as_uint(y) <= bx) below += y;
+        }
+        const bool crosses = lane < len && g_lo + below > thr;
+        const uint32_t pick = crosses ? bx : 0xffffffffu;
+        const uint32_t best = ~wave_max_u(~pick);   // smallest pattern among the crossing ones
+        if (best != 0xffffffffu) cut = best;
+    }
+
+    int qt = 0, qh_ = 0, qw = 0;
+    const int pf = nH * nW;
+    if (sta) {
+        qt = row / pf;
+        const int rem = row - qt * pf;
+        qh_ = rem / nW;
+        qw = rem - qh_ * nW;
+    }
+    int32_t* out_idx = kv_index + ((size_t)bh * nb + row) * nb;
+    uint32_t* out_bits = bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr;
+    int base = 0;
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+        const int j = j0 + lane;
+        bool keep = false;
+        if (j < nb) {
+            keep = __float_as_uint(arow[j]) >= cut;
+            if (sta && !keep) {
+                const int kt = j / pf;
+                const int rem = j - kt * pf;
+                const int kh_ = rem / nW;
+                const int kw = rem - kh_ * nW;
+                keep = abs(kt - qt) <= rt && abs(kh_ - qh_) <= rh && abs(kw - qw) <= rw;
+            }
+        }
+        const uint64_t ballot = __ballot(keep);
+        if (keep) out_idx[base + __popcll(ballot & ((1ull << lane) - 1ull))] = j;
+        base += __popcll(ballot);
+        if (out_bits) {
+            const int w = j0 >> 5;
+            if (lane == 0 && w < nwords) out_bits[w] = (uint32_t)ballot;
+            if (lane == 1 && w + 1 < nwords) out_bits[w + 1] = (uint32_t)(ballot >> 32);
+        }
+    }
+    if (lane == 0) kv_count[(size_t)bh * nb + row] = base;
+}
+
+// ---------------------------------------------------------------------------
+// NABLA's reduced map and cut in one kernel.  A workgroup (16 waves) owns kRows pooled
+// query rows of one head: the map by map_rows, then per row (one wave) the softmax
+// A = exp(S - max) / sum in place and select_row.  The rows never leave LDS, which at
+// large nb (nb^2 floats per head) saves an HBM round trip.
+// ---------------------------------------------------------------------------
+constexpr int kWaves = 16;
+
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
-    const float* __restrict__ qp, const float* __restrict__ given_a, const float* __restrict__ kp, int nb,
-    int ld_s, float scale, float thr, int sta, int nH, int nW, int rt, int rh, int rw,
-    int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap,
-    int sip_budget, const float* __restrict__ uniforms, float* __restrict__ kv_logw, int a_group) {
+    const float* __restrict__ qp, const float* __restrict__ kp, int nb, int ld_s, float scale, float thr, int sta,
+    int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
+    uint32_t* __restrict__ bitmap, int sip_budget, const float* __restrict__ uniforms,
+    float* __restrict__ kv_logw) {
     extern __shared__ float s_lds[];   // [kRows][ld_s] rows, then [kWaves][kCap] candidates
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kRows;
-    const bool given = given_a != nullptr;
-
-    // ---- phase 1: the workgroup's rows into LDS
-    if (given) {
-        for (int r = wave; r < kRows; r += kWaves) {
-            const int row = row0 + r;
-            if (row >= nb) break;
-            const float* src = given_a + ((size_t)bh * (nb / a_group) + row / a_group) * nb;
-            for (int j = lane; j < nb; j += 64) s_lds[r * ld_s + j] = src[j];
-        }
-    } else {
-        map_rows<D, kWaves>(qp + (size_t)bh * nb * D, nb, row0, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds,
-                            wave, lane);
-    }
+    map_rows<D, kWaves>(qp + (size_t)bh * nb * D, nb, row0, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds, wave,
+                        lane);
     __syncthreads();
-
-    // ---- phase 2: one row per wave at a time.
     float* cand = s_lds + kRows * ld_s + wave * kCap;
-    const int nwords = (nb + 31) >> 5;
     for (int r = wave; r < kRows; r += kWaves) {
         const int row = row0 + r;
         if (row >= nb) break;
         float* arow = s_lds + r * ld_s;
-        float inv_sum = 1.0f;
-        if (!given) {
-            // softmax; the row is overwritten with the probabilities A
-            float mx = -INFINITY;
-            for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, arow[j]);
-            mx = wave_max(mx);
-            const float mx2 = mx * kLog2e;
-            float sum = 0.f;
-            for (int j = lane; j < nb; j += 64) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(arow[j], kLog2e, -mx2));
-                arow[j] = e;
-                sum += e;
-            }
-            inv_sum = 1.0f / wave_sum(sum);
+        float mx = -INFINITY;
+        for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, arow[j]);
+        const float mx2 = wave_max(mx) * kLog2e;
+        float sum = 0.f;
+        for (int j = lane; j < nb; j += 64) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(arow[j], kLog2e, -mx2));
+            arow[j] = e;
+            sum += e;
         }
-        if (sip_budget > 0) {
-            sip_row(arow, nb, inv_sum, sip_budget, uniforms + ((size_t)bh * nb + row) * nb,
-                    kv_index + ((size_t)bh * nb + row) * nb, kv_logw + ((size_t)bh * nb + row) * nb,
-                    bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr, nwords,
-                    kv_count + (size_t)bh * nb + row, lane);
-            continue;
-        }
-        // start of the bracket: u0 = thr / nb, nudged down so rounding cannot push
-        // g(u0) above thr; it is verified below and dropped to 0 if it fails
-        uint32_t lo = __float_as_uint(thr / ((float)nb * 1.0001f));
-        float g_lo = 0.f;
-        int n_in = 0;
-        uint32_t maxb = 0;
-        for (int j0 = 0; j0 < nb; j0 += 64) {
-            const int j = j0 + lane;
-            bool in = false;
-            if (j < nb) {
-                const float p = arow[j] * inv_sum;
-                arow[j] = p;
-                const uint32_t b = __float_as_uint(p);
-                maxb = max(maxb, b);
-                if (b <= lo) g_lo += p; else in = true;
-            }
-            n_in += __popcll(__ballot(in));
-        }
-        g_lo = wave_sum(g_lo);
-        maxb = wave_max_u(maxb);
-        if (g_lo > thr) {   // cannot happen in exact arithmetic; fall back to g(0) = 0
-            lo = 0;
-            g_lo = 0.f;
-            n_in = 0;
-            for (int j0 = 0; j0 < nb; j0 += 64) {
-                const int j = j0 + lane;
-                n_in += __popcll(__ballot(j < nb && __float_as_uint(arow[j]) > 0u));
-            }
-        }
-        uint32_t hi = maxb;
-        // bracket (lo, hi]: g(lo) = g_lo <= thr and, unless the whole row sums to at
-        // most thr, g(hi) > thr; n_in values lie inside it (always >= 1: the maximum)
-        const float* src = arow;
-        int len = nb;
-        if (n_in <= kCap) {
-            len = compact(arow, nb, lo, hi, cand, lane);
-            src = cand;
-        }
-        // bisection until at most 64 values are left in the bracket
-        while (hi - lo > 1 && n_in > 64) {
-            const uint32_t mid = lo + ((hi - lo) >> 1);
-            float s_ = 0.f;
-            int c = 0;
-            for (int j0 = 0; j0 < len; j0 += 64) {
-                const int j = j0 + lane;
-                const float x = (j < len) ? src[j] : 0.f;
-                const uint32_t b = __float_as_uint(x);
-                const bool in = (j < len) && b > lo && b <= mid;
-                if (in) s_ += x;
-                c += __popcll(__ballot(in));
-            }
-            s_ = wave_sum(s_);
-            if (g_lo + s_ > thr) {
-                hi = mid;
-                n_in = c;
-            } else {
-                lo = mid;
-                g_lo += s_;
-                n_in -= c;
-            }
-            if (n_in <= kCap && 2 * n_in <= len) {
-                len = compact(src, len, lo, hi, cand, lane);
-                src = cand;
-            }
-        }
-        uint32_t cut = hi;
-        if (n_in <= 64) {
-            // one candidate per lane: F(x) = g_lo + (sum of the candidates <= x), tied
-            // values together; the cut is the smallest candidate with F(x) > thr
-            len = compact(src, len, lo, hi, cand, lane);
-            const float x = lane < len ? cand[lane] : 0.f;
-            const uint32_t bx = __float_as_uint(x);
-            float below = 0.f;
-            for (int m = 0; m < len; ++m) {
-                const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), m));
-                if (__float_as_uint(y) <= bx) below += y;
-            }
-            const bool crosses = lane < len && g_lo + below > thr;
-            const uint32_t pick = crosses ? bx : 0xffffffffu;
-            const uint32_t best = ~wave_max_u(~pick);   // smallest pattern among the crossing ones
-            if (best != 0xffffffffu) cut = best;
-        }
-
-        int qt = 0, qh_ = 0, qw = 0;
-        const int pf = nH * nW;
-        if (sta) {
-            qt = row / pf;
-            const int rem = row - qt * pf;
-            qh_ = rem / nW;
-            qw = rem - qh_ * nW;
-        }
-        int32_t* out_idx = kv_index + ((size_t)bh * nb + row) * nb;
-        uint32_t* out_bits = bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr;
-        int base = 0;
-        for (int j0 = 0; j0 < nb; j0 += 64) {
-            const int j = j0 + lane;
-            bool keep = false;
-            if (j < nb) {
-                keep = __float_as_uint(arow[j]) >= cut;
-                if (sta && !keep) {
-                    const int kt = j / pf;
-                    const int rem = j - kt * pf;
-                    const int kh_ = rem / nW;
-                    const int kw = rem - kh_ * nW;
-                    keep = abs(kt - qt) <= rt && abs(kh_ - qh_) <= rh && abs(kw - qw) <= rw;
-                }
-            }
-            const uint64_t ballot = __ballot(keep);
-            if (keep) out_idx[base + __popcll(ballot & ((1ull << lane) - 1ull))] = j;
-            base += __popcll(ballot);
-            if (out_bits) {
-                const int w = j0 >> 5;
-                if (lane == 0 && w < nwords) out_bits[w] = (uint32_t)ballot;
-                if (lane == 1 && w + 1 < nwords) out_bits[w + 1] = (uint32_t)(ballot >> 32);
-            }
-        }
-        if (lane == 0) kv_count[(size_t)bh * nb + row] = base;
+        const float inv_sum = 1.0f / wave_sum(sum);
+        select_row(arow, inv_sum, cand, nb, bh, row, thr, sta, nH, nW, rt, rh, rw, kv_count, kv_index, bitmap,
+                   sip_budget, uniforms, kv_logw, lane);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Cut of score rows computed elsewhere (IBCS): one wave per query block, its row
+// (row i / a_group of A [BH, nb / a_group, nb], summing to one) copied into the wave's
+// LDS row, then select_row.  Waves share nothing, so the workgroup never synchronises.
+// ---------------------------------------------------------------------------
+constexpr int kSelWaves = 4;
+
+__global__ __launch_bounds__(kSelWaves * 64) void select_kernel(
+    const float* __restrict__ A, int a_group, int nb, int ld_s, float thr, int sta, int nH, int nW, int rt, int rh,
+    int rw, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap,
+    int sip_budget, const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
+    extern __shared__ float s_lds[];   // [kSelWaves][ld_s] rows, then [kSelWaves][kCap] candidates
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.y;
+    const int row = blockIdx.x * kSelWaves + wave;
+    if (row >= nb) return;
+    float* arow = s_lds + wave * ld_s;
+    const float* src = A + ((size_t)bh * (nb / a_group) + row / a_group) * nb;
+    for (int j = lane; j < nb; j += 64) arow[j] = src[j];
+    select_row(arow, 1.0f, s_lds + kSelWaves * ld_s + wave * kCap, nb, bh, row, thr, sta, nH, nW, rt, rh, rw,
+               kv_count, kv_index, bitmap, sip_budget, uniforms, kv_logw, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -649,9 +670,23 @@ hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
     hipError_t e = set_max_dynamic_lds((const void*)map_select_kernel<D>, max_lds, lds_set);
     if (e != hipSuccess) return e;
     dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
-    hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.qp, a.ibcs ? a.ibcs_A : nullptr,
-                       a.kp, a.nb, ld_s, a.scale, a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count,
-                       a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw, a.ibcs ? a.ibcs_group : 1);
+    hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.qp, a.kp, a.nb, ld_s, a.scale,
+                       a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count, a.kv_index, a.bitmap, a.sip_budget,
+                       a.uniforms, a.kv_logw);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const MaskArgs& a, hipStream_t s) {
+    const int ld_s = ((a.nb + 63) / 64) * 64 + 16;
+    const size_t lds = ((size_t)kSelWaves * ld_s + (size_t)kSelWaves * kCap) * sizeof(float);
+    static std::atomic<uint64_t> lds_set{0};
+    const int max_lds = (kSelWaves * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kSelWaves * kCap) * (int)sizeof(float);
+    hipError_t e = set_max_dynamic_lds((const void*)select_kernel, max_lds, lds_set);
+    if (e != hipSuccess) return e;
+    dim3 grid((a.nb + kSelWaves - 1) / kSelWaves, a.BH);
+    hipLaunchKernelGGL(select_kernel, grid, dim3(kSelWaves * 64), lds, s, a.scores, a.ibcs_group, a.nb,
+                       ld_s, a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count, a.kv_index, a.bitmap,
+                       a.sip_budget, a.uniforms, a.kv_logw);
     return hipGetLastError();
 }
 
@@ -666,7 +701,7 @@ hipError_t launch_ibcs_score(const MaskArgs& a, hipStream_t s) {
     const int groups = a.nb / a.ibcs_group;
     dim3 grid((groups * kIbcsClusters + kRows - 1) / kRows, a.BH);
     hipLaunchKernelGGL((ibcs_score_kernel<D>), grid, dim3(kScoreWaves * 64), lds, s, a.cent, a.cent_w, a.kp, a.nb,
-                       groups, ld_s, a.scale, a.ibcs_A);
+                       groups, ld_s, a.scale, a.scores);
     return hipGetLastError();
 }
 
@@ -683,9 +718,10 @@ hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
     if (a.ibcs) {
         if ((e = launch_ibcs_cluster(a, s)) != hipSuccess) return e;
         e = (a.d == 128) ? launch_ibcs_score<128>(a, s) : launch_ibcs_score<64>(a, s);
-        if (e != hipSuccess) return e;
+        if (e == hipSuccess) e = launch_select(a, s);
+    } else {
+        e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
     }
-    e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
     if (e != hipSuccess || !a.schedule) return e;
     // one wave per head; its bins fit the default LDS limit (NABLA_MAX_BLOCKS + 1 ints)
     return launch_schedule(a.kv_count, a.BH, a.nb, a.schedule, s);

@@ -78,10 +78,25 @@ nabla_status nabla_reorder(const void* src, void* dst, int batch, int heads, int
     return hip_status(nabla::launch_reorder(a, stream), "nabla_reorder");
 }
 
+namespace {
+
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Sections of the NABLA workspace: pooled Q, pooled K.
+struct NablaSections {
+    size_t qp, kp;
+    size_t total() const { return qp + kp; }
+};
+
+NablaSections nabla_sections(long long BH, long long nb, int d) {
+    return {up256((size_t)BH * nb * d * sizeof(float)), up256((size_t)BH * nb * d * sizeof(float))};
+}
+
+}  // namespace
+
 size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N) {
     if (batch <= 0 || heads <= 0 || L <= 0 || d <= 0 || N <= 0 || L % N) return 0;
-    const size_t one = (size_t)batch * heads * (size_t)(L / N) * d * sizeof(float);
-    return ((2 * one) + 255) & ~(size_t)255;
+    return nabla_sections((long long)batch * heads, L / N, d).total();
 }
 
 namespace {
@@ -94,9 +109,10 @@ struct IbcsSections {
 };
 
 IbcsSections ibcs_sections(long long BH, long long nb, long long groups, int d) {
-    auto up = [](size_t n) { return (n + 255) & ~(size_t)255; };
-    return {up((size_t)BH * nb * d * sizeof(float)), up((size_t)BH * groups * nabla::kIbcsClusters * d * sizeof(float)),
-            up((size_t)BH * groups * nabla::kIbcsClusters * sizeof(float)), up((size_t)BH * groups * nb * sizeof(float))};
+    return {up256((size_t)BH * nb * d * sizeof(float)),
+            up256((size_t)BH * groups * nabla::kIbcsClusters * d * sizeof(float)),
+            up256((size_t)BH * groups * nabla::kIbcsClusters * sizeof(float)),
+            up256((size_t)BH * groups * nb * sizeof(float))};
 }
 
 }  // namespace
@@ -263,12 +279,15 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
         a.kp = (float*)base;
         a.cent = (float*)(base + sec.kp);
         a.cent_w = (float*)(base + sec.kp + sec.cent);
-        a.ibcs_A = (float*)(base + sec.kp + sec.cent + sec.cw);
+        a.scores = (float*)(base + sec.kp + sec.cent + sec.cw);
         a.ibcs = 1;
         a.ibcs_group = ibcs_q_group / N;
     } else {
-        a.qp = (float*)workspace;
-        a.kp = a.qp + (size_t)a.BH * nb * d;
+        // [Qp | Kp], sections 256-byte aligned
+        const NablaSections sec = nabla_sections(a.BH, nb, d);
+        char* base = (char*)workspace;
+        a.qp = (float*)base;
+        a.kp = (float*)(base + sec.qp);
     }
     a.bf16 = dtype == NABLA_BF16;
     a.raster = raster;

@@ -80,6 +80,7 @@ struct MaskArgs {
     int32_t* schedule;      // may be null
     float* qp;              // workspace [BH, nb, d]
     float* kp;              // workspace [BH, nb, d]
+    float* scores;          // IBCS workspace [BH, groups, nb] score rows (rows sum to one)
     int bf16;
     int raster;             // 0: q, k in fractal order; 1: raster order, 8 x 8 patches per block
     int H, W;               // token grid, for the raster order
@@ -90,7 +91,6 @@ struct MaskArgs {
     int ibcs_group;         // IBCS query blocks per cluster group (1: 64 queries, 2: 128)
     float* cent;            // IBCS workspace [BH, groups * kIbcsClusters, d] centroids
     float* cent_w;          // IBCS workspace [BH, groups * kIbcsClusters] cluster weights
-    float* ibcs_A;          // IBCS workspace [BH, groups, nb] block scores (rows sum to one)
 };
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_ibcs_cluster(const MaskArgs& a, hipStream_t s);

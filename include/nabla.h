@@ -76,9 +76,11 @@ nabla_status nabla_reorder(const void* src, void* dst, int batch, int heads, int
                            hipStream_t stream);
 
 /*
- * nabla_build_mask_workspace_size - bytes of device workspace nabla_build_mask needs:
- * the pooled Q and K in float32, 2 * batch*heads*(L/N)*d*4 bytes, rounded up to 256.
- * Returns 0 for non-positive sizes or L not a multiple of N.
+ * nabla_build_mask_workspace_size - bytes of device workspace nabla_build_mask (and its
+ * raster and SIP forms) needs (BH = batch*heads, nb = L/N): the pooled Q and the pooled
+ * K, BH*nb*d floats each, each section rounded up to 256 bytes.  After a call they hold
+ * those means, float32, row-major.  Returns 0 for non-positive sizes or L not a
+ * multiple of N.
  */
 size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N);
 

@@ -53,9 +53,11 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    # 2 * B*H*nb*d*4 bytes, rounded up to 256
+    # pooled Q and pooled K, B*H*nb*d floats each, each rounded up to 256
     assert lib.nabla_build_mask_workspace_size(1, 12, 32256, 128, 64) == 2 * 12 * 504 * 128 * 4
     assert lib.nabla_build_mask_workspace_size(1, 2, 1024, 64, 64) == 2 * 2 * 16 * 64 * 4
+    # 3 blocks, d = 16: 192 B each, rounded up to 256
+    assert lib.nabla_build_mask_workspace_size(1, 1, 192, 16, 64) == 256 + 256
     assert lib.nabla_build_mask_workspace_size(1, 1, 1000, 64, 64) == 0
     assert lib.nabla_build_mask_workspace_size(0, 1, 1024, 64, 64) == 0
 
