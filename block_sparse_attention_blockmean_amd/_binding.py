@@ -188,13 +188,11 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
     if workspace is None:
         workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
     win = None if sta is None else ctypes.byref(StaWindow(*sta))
-    if ibcs:
-        entry = lambda q_, k_, B_, NH_, T_, H_, W_, d_, P_, N_, *rest: lib.nabla_build_mask_ibcs(
-            q_, k_, B_, NH_, T_, H_, W_, d_, P_, N_, int(ibcs_group), *rest)
-    else:
-        entry = lib.nabla_build_mask_raster if raster else lib.nabla_build_mask
+    # the IBCS entry takes the query-group size right after N
+    shape = (B, NH, T, H, W, d, P, N) + ((int(ibcs_group),) if ibcs else ())
+    entry = lib.nabla_build_mask_ibcs if ibcs else (lib.nabla_build_mask_raster if raster else lib.nabla_build_mask)
     _check(entry(
-        _dev(q, "q"), _dev(k, "k"), B, NH, T, H, W, d, P, N, float(thr), win,
+        _dev(q, "q"), _dev(k, "k"), *shape, float(thr), win,
         float(scale) if scale is not None else 0.0, _dtype_code(q),
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
         _dev(bitmap, "bitmap") if bitmap is not None else None,
@@ -292,13 +290,11 @@ def build_mask_sip(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: 
     ws_bytes = build_mask_workspace_size(B, NH, L, d, N, ibcs=ibcs, ibcs_group=ibcs_group)
     if workspace is None:
         workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
-    if ibcs:
-        entry = lambda q_, k_, B_, NH_, T_, H_, W_, d_, P_, N_, *rest: lib.nabla_build_mask_ibcs_sip(
-            q_, k_, B_, NH_, T_, H_, W_, d_, P_, N_, int(ibcs_group), *rest)
-    else:
-        entry = lib.nabla_build_mask_sip
+    # the IBCS entry takes the query-group size right after N
+    shape = (B, NH, T, H, W, d, P, N) + ((int(ibcs_group),) if ibcs else ())
+    entry = lib.nabla_build_mask_ibcs_sip if ibcs else lib.nabla_build_mask_sip
     _check(entry(
-        _dev(q, "q"), _dev(k, "k"), B, NH, T, H, W, d, P, N, int(budget), _dev(uniforms, "uniforms"),
+        _dev(q, "q"), _dev(k, "k"), *shape, int(budget), _dev(uniforms, "uniforms"),
         float(scale) if scale is not None else 0.0, _dtype_code(q), _dev(kv_count, "kv_count"),
         _dev(kv_index, "kv_index"), _dev(kv_logw, "kv_logw"),
         _dev(bitmap, "bitmap") if bitmap is not None else None,

@@ -32,9 +32,20 @@ struct Tile {
     static constexpr int kRowsPerLine = 256 / kRowBytes;  // rows per 256-byte LDS bank line
     static constexpr int kBytes = kBlk * kRowBytes;
     static constexpr int kCopiesPerWave = kBytes / 1024 / kWaves;  // 1 KiB per copy
-    // K is read 16 bytes per lane from 16 consecutive rows at one chunk: spread the
-    // rows over all chunk slots of a bank line.
-    __device__ static inline int k_swz(int row) { return (row / kRowsPerLine) & (kChunks - 1); }
+    static_assert(kChunks == 16 || kChunks == 8, "d = 128 or 64");
+    // Tiles read as rows (16 bytes per lane, 16 consecutive rows at one chunk) and, in
+    // the gradient kernels, also through the transposing read (8 bytes per lane; each
+    // 32 lanes cover 4 consecutive rows, aligned to 4, times 4 consecutive chunks from a
+    // multiple of 4).  The swizzle is an XOR with a bijection f of the row's position in
+    // 16 bank lines: row reads need f one-to-one there; the transposing read needs the
+    // rows sharing a bank line to differ in f's top bits, so that their 4-chunk groups
+    // land apart.  d = 128 (one row per bank line): f = rows' bits 1:0 above bits 3:2.
+    // d = 64 (two rows per line, 8 chunks): f = line bit 0 above line bits 2:1.
+    __device__ static inline int k_swz(int row) {
+        const int line = row / kRowsPerLine;
+        if constexpr (kChunks == 16) return ((line & 3) << 2) | ((line >> 2) & 3);
+        else return ((line & 1) << 2) | ((line >> 1) & 3);
+    }
     // V is read 8 bytes per lane, 4 rows x 64 bytes per 16 lanes: spread groups of
     // 4 chunks over the bank line.
     __device__ static inline int v_swz(int row) { return 4 * ((row / kRowsPerLine) & (kChunks / 4 - 1)); }
