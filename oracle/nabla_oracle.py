@@ -354,40 +354,87 @@ IBCS_CLUSTERS = 8
 IBCS_ITERS = 4
 
 
+def fma_f32(a: np.ndarray, b: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """Correctly rounded float32 a*b + c with a single rounding (a fused multiply-add).
+
+    a*b of two float32 values is exact in float64 (24 + 24 significand bits).  hi, the
+    float64 sum of it and c, and lo, the exact error of that sum (TwoSum), give the
+    exact result hi + lo.  Rounding hi to float32 rounds hi + lo correctly except when
+    hi lies exactly halfway between two float32 values and lo != 0: a float32 midpoint
+    is a float64 number, and |lo| is below half the float64 spacing at hi, so any other
+    midpoint is on the same side of hi and hi + lo.  In that case the result is the
+    float32 neighbour on lo's side.  In the float32 normal range hi is a midpoint iff
+    its 29 mantissa bits below float32 precision are 1 followed by zeros; only those
+    elements, and nonzero ones below the normal range, are examined."""
+    a64 = np.asarray(a, dtype=np.float32).astype(np.float64)
+    b64 = np.asarray(b, dtype=np.float32).astype(np.float64)
+    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
+    p = a64 * b64
+    hi = p + c64
+    r = hi.astype(np.float32)
+    low = hi.view(np.uint64) & np.uint64(0x1FFFFFFF)
+    tiny = (np.abs(hi) < 2.0 ** -126) & (hi != 0)
+    cand = np.flatnonzero((low == np.uint64(0x10000000)) | tiny)
+    if cand.size:
+        pf, cf, hf, rf = p.flat[cand], c64.flat[cand], hi.flat[cand], r.flat[cand]
+        z = hf - pf
+        lf = (pf - (hf - z)) + (cf - z)
+        rf64 = rf.astype(np.float64)
+        other = np.nextafter(rf, np.where(rf64 > hf, np.float32(-np.inf), np.float32(np.inf)).astype(np.float32))
+        tie = (hf == (rf64 + other.astype(np.float64)) * 0.5) & (lf != 0)
+        side = np.where(lf > 0, np.maximum(rf, other), np.minimum(rf, other))
+        r.flat[cand] = np.where(tie, side, rf)
+    return r
+
+
 def _sq_dist_f32(x: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """Squared Euclidean distances [n, k] in float32: per coordinate, difference, then
-    square, each rounded to float32, summed over d in index order (no fused
-    multiply-add, no pairwise summation)."""
-    diff = (x[:, None, :].astype(np.float32) - c[None, :, :].astype(np.float32)).astype(np.float32)
-    sq = (diff * diff).astype(np.float32)
-    return np.add.accumulate(sq, axis=-1, dtype=np.float32)[..., -1]
+    """Squared Euclidean distances [G, n, k] between the rows of x [G, n, d] and of c
+    [G, k, d] in float32: per coordinate, in index order, the difference rounded to
+    float32, then its square added to the running sum by one fused multiply-add."""
+    G, n, d = x.shape
+    k = c.shape[1]
+    acc = np.zeros((G, n, k), dtype=np.float32)
+    for e in range(d):
+        diff = (x[:, :, None, e] - c[:, None, :, e]).astype(np.float32)
+        acc = fma_f32(diff, diff, acc)
+    return acc
 
 
-def ibcs_clusters(qblock: np.ndarray, n_clusters: int = IBCS_CLUSTERS, iters: int = IBCS_ITERS):
-    """k-means of one group of n queries ([n, d], one query block or several) into
-    n_clusters clusters.
+def ibcs_clusters(qgroup: np.ndarray, n_clusters: int = IBCS_CLUSTERS, iters: int = IBCS_ITERS):
+    """k-means of one group of n queries ([n, d]), or of a batch of groups ([G, n, d]),
+    into n_clusters clusters each.
 
     Readings (the page gives the cluster count, not the algorithm's steps): Lloyd's
     algorithm; initial centroids are the queries at rows 0, n/k, 2n/k, ...; ``iters``
     rounds of assign-then-update; a query joins its nearest centroid by squared
-    Euclidean distance, ties to the lowest cluster index; a centroid becomes the mean of
-    its queries (summed in row order in float32, then divided by their count), and an
-    empty cluster keeps its centroid.  Returns (centroids [k, d] float32, weights [k] =
-    fraction of the block's queries in each cluster under the last assignment)."""
-    x = np.asarray(qblock, dtype=np.float32)
-    n = x.shape[0]
-    step = n // n_clusters
-    cent = x[np.arange(n_clusters) * step].copy()
-    assign = np.zeros(n, dtype=np.int64)
+    Euclidean distance (_sq_dist_f32), ties to the lowest cluster index; a centroid
+    becomes the mean of its queries (a float32 running sum from 0 over its queries in
+    row order, then one division by their count), and an empty cluster keeps its
+    centroid.  Returns (centroids [..., k, d] float32, weights [..., k] = fraction of the
+    group's queries in each cluster under the last assignment)."""
+    x = np.asarray(qgroup, dtype=np.float32)
+    single = x.ndim == 2
+    if single:
+        x = x[None]
+    G, n, d = x.shape
+    k = n_clusters
+    cent = x[:, np.arange(k) * (n // k)].copy()
+    assign = np.zeros((G, n), dtype=np.int64)
+    zero_row = np.zeros((G, 1, d), dtype=np.float32)
     for _ in range(iters):
-        dist = _sq_dist_f32(x, cent)
-        assign = np.argmin(dist, axis=1)          # first minimum: lowest index on ties
-        for c in range(n_clusters):
-            rows = x[assign == c]
-            if len(rows):
-                total = np.add.accumulate(rows, axis=0, dtype=np.float32)[-1]
-                cent[c] = (total / np.float32(len(rows))).astype(np.float32)
-    weights = np.bincount(assign, minlength=n_clusters).astype(np.float64) / n
+        assign = np.argmin(_sq_dist_f32(x, cent), axis=2)      # first minimum: lowest index on ties
+        for c in range(k):
+            member = assign == c
+            count = member.sum(axis=1)
+            # 0, then the members in row order; rows of other clusters add +0, which
+            # leaves a float32 sum started at +0 unchanged
+            rows = np.concatenate([zero_row, np.where(member[..., None], x, np.float32(0))], axis=1)
+            total = np.add.accumulate(rows, axis=1, dtype=np.float32)[:, -1]
+            has = count > 0
+            cent[has, c] = (total[has] / count[has].astype(np.float32)[:, None]).astype(np.float32)
+    weights = np.stack([np.bincount(a, minlength=k) for a in assign]).astype(np.float64) / n
+    if single:
+        return cent[0], weights[0]
     return cent, weights
 
 
@@ -415,12 +462,12 @@ def ibcs_scores(q: np.ndarray, k: np.ndarray, N: int, scale: Optional[float] = N
     kp = block_mean(np.asarray(k).reshape((-1, L, d)), N, np.float64)
     A = np.zeros((qf.shape[0], nb, nb))
     for g in range(qf.shape[0]):
+        cents, ws = ibcs_clusters(qf[g].reshape(L // qn, qn, d))              # every group of the head
         for gi in range(L // qn):
-            cent, w = ibcs_clusters(qf[g, gi * qn:(gi + 1) * qn])
-            S = (cent.astype(np.float64) @ kp[g].T) * scale                      # [k, nb]
+            S = (cents[gi].astype(np.float64) @ kp[g].T) * scale                 # [k, nb]
             P = np.exp(S - S.max(axis=1, keepdims=True))
             P /= P.sum(axis=1, keepdims=True)
-            A[g, gi * per:(gi + 1) * per] = w @ P
+            A[g, gi * per:(gi + 1) * per] = ws[gi] @ P
     return A.reshape(lead + (nb, nb))
 
 

@@ -515,6 +515,55 @@ def pin_sip_full_budget_is_plain_attention():
 
 # ---------------------------------------------------------------- IBCS (intra-block clustering)
 
+def _round_f32_exact(v):
+    """Nearest float32 to the rational v, ties to the even significand (from the
+    definition, by exact comparison of the candidates)."""
+    from fractions import Fraction
+    f = np.float32(float(v))
+    best = None
+    for c in (f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))):
+        key = (abs(Fraction(float(c)) - v), int(np.array(c).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def pin_fma_f32_is_correctly_rounded():
+    """fma_f32 against exact rational arithmetic: random products (squares among them)
+    and sums over a wide range of exponents, and constructed cases where the float64 sum
+    lands exactly on a float32 midpoint that the exact sum is not on (where rounding
+    twice goes wrong)."""
+    from fractions import Fraction
+    rng = _rng(46)
+    n = 3000
+    a = (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n))).astype(np.float32)
+    b = np.where(rng.random(n) < 0.5, a, (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n)))).astype(np.float32)
+    c = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32)
+    got = O.fma_f32(a, b, c)
+    for i in range(n):
+        v = Fraction(float(a[i])) * Fraction(float(b[i])) + Fraction(float(c[i]))
+        assert got[i] == _round_f32_exact(v), (a[i], b[i], c[i])
+    # ties: c + X with X an odd multiple of half c's float32 spacing, a b = X + (tiny)
+    ties = []
+    for _ in range(400000):
+        c1 = np.float32(np.ldexp(1.0 + rng.integers(0, 2 ** 23) / 2 ** 23, int(rng.integers(-10, 10))))
+        X = (2 * int(rng.integers(0, 2 ** 10)) + 1) * np.float64(np.spacing(c1)) / 2
+        a1 = np.float32(np.sqrt(X) * (1 + rng.standard_normal() * 1e-3))
+        b1 = np.float32(X / np.float64(a1))
+        exact = Fraction(float(a1)) * Fraction(float(b1)) + Fraction(float(c1))
+        if np.float64(a1) * np.float64(b1) + np.float64(c1) == np.float64(c1) + X and exact != Fraction(float(c1) + X):
+            ties.append((a1, b1, c1, exact))
+            if len(ties) == 12:
+                break
+    assert len(ties) == 12
+    ta, tb, tc = (np.array([t[i] for t in ties], dtype=np.float32) for i in range(3))
+    got = O.fma_f32(ta, tb, tc)
+    twice = (ta.astype(np.float64) * tb + tc).astype(np.float32)
+    want = [_round_f32_exact(t[3]) for t in ties]
+    assert all(g == w for g, w in zip(got, want))
+    assert any(t != w for t, w in zip(twice, want)), "the constructed cases must separate the two roundings"
+
+
 def pin_ibcs_identical_queries_is_block_mean():
     """A block whose queries are all equal forms one cluster whose centroid is the block
     mean: IBCS's row is then exactly NABLA's pooled softmax row."""

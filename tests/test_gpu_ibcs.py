@@ -75,17 +75,20 @@ def score_err(gpu_A, ref_A):
 
 
 def check_clusters(res, qf_np, qn, heads):
-    """Centroids bit for bit, weights exactly, for every query group of the given heads."""
+    """Centroids bit for bit, weights exactly, for every query group of the given heads
+    (the oracle clusters all groups of a head at once)."""
     ng = res["cent"].shape[1]
+    d = qf_np.shape[-1]
     n = 0
     for g in heads:
-        for i in range(ng):
-            cent, w = O.ibcs_clusters(qf_np[g, i * qn:(i + 1) * qn])
-            gc = res["cent"][g, i]
-            assert np.array_equal(gc.view(np.uint32), cent.view(np.uint32)), (
-                f"head {g} block {i}: centroids differ, max-abs {np.max(np.abs(gc - cent)):.3e}")
-            assert np.array_equal(res["w"][g, i].astype(np.float64), w), (g, i, res["w"][g, i], w)
-            n += 1
+        cent, w = O.ibcs_clusters(qf_np[g, :ng * qn].reshape(ng, qn, d))
+        gc = res["cent"][g]
+        same = np.all(gc.view(np.uint32) == cent.view(np.uint32), axis=(1, 2))
+        assert same.all(), (
+            f"head {g}: centroids of {int((~same).sum())} groups differ, first {int(np.argmin(same))}, "
+            f"max-abs {np.max(np.abs(gc - cent)):.3e}")
+        assert np.array_equal(res["w"][g].astype(np.float64), w), g
+        n += ng
     return n
 
 

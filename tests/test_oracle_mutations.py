@@ -176,6 +176,11 @@ def _ibcs_softmax_over_centroids(q, k, N, scale=None):
     return np.exp(A) / np.exp(A).sum(-1, keepdims=True)
 
 
+def _fma_rounded_twice(a, b, c):
+    # float64 sum rounded to float32: two roundings instead of one
+    return (np.asarray(a, np.float64) * np.asarray(b, np.float64) + np.asarray(c, np.float64)).astype(np.float32)
+
+
 def _ibcs_group_ignored(q, k, N, scale=None, qn=None):
     # every 64-token block clustered on its own, whatever the group size
     return _orig_ibcs_scores(q, k, N, scale)
@@ -206,6 +211,7 @@ MUTATIONS = [
     ("ibcs_clusters", _ibcs_first_rows_init),
     ("ibcs_scores", _ibcs_softmax_over_centroids),
     ("ibcs_scores", _ibcs_group_ignored),
+    ("fma_f32", _fma_rounded_twice),
 ]
 
 
