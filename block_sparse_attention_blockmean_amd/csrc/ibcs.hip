@@ -8,11 +8,11 @@
 // Clustering is Lloyd's k-means: initial centroids the queries at rows 0, QN/8, ...,
 // four rounds of assign-then-update, nearest centroid by squared Euclidean distance
 // with ties to the lowest index, a centroid the mean of its queries (an empty cluster
-// keeps its centroid).  Distances and means use individually rounded float32 operations
-// in a fixed order - per coordinate the difference, its square, a running sum over d in
-// index order; a running sum over the cluster's queries in row order, then one division
-// - so the assignment is a function of the inputs alone, the same on any machine that
-// performs those operations in that order.
+// keeps its centroid).  Distances and means use float32 operations in a fixed order -
+// per coordinate in index order the rounded difference, then its square added to the
+// running sum by one fused multiply-add; a running sum over the cluster's queries in row
+// order, then one division - so the assignment is a function of the inputs alone, the
+// same on any machine that performs those operations in that order.
 #include <math.h>
 
 #include "nabla_internal.h"
@@ -55,8 +55,9 @@ constexpr size_t cluster_lds_bytes() {
 // One workgroup per query group (bh * groups + g).  LDS rows are padded by 16 bytes
 // (d + 4 floats): row t starts 4 t banks further on, so the 16 queries a wave reads with
 // one 16-byte load fall in distinct bank groups.  Float contraction is off in the whole
-// kernel: each +, - and * rounds on its own, and the division is the correctly rounded
-// one (hipcc's default for float32 division).
+// kernel, so the only fused operations are the explicit fmaf of the distances; every
+// other +, - and * rounds on its own, and the division is the correctly rounded one
+// (hipcc's default for float32 division).
 template <typename T, int D, int QN>
 __global__ __launch_bounds__(cluster_threads<QN>()) void ibcs_cluster_kernel(const T* __restrict__ q,
                                                                              float* __restrict__ cent,
@@ -114,17 +115,13 @@ __global__ __launch_bounds__(cluster_threads<QN>()) void ibcs_cluster_kernel(con
                 for (int m = 0; m < PT; ++m) {
                     const float4 cv = c4[m * (LD / 4) + e4];
                     float df = xv.x - cv.x;
-                    float sq = df * df;
-                    acc[m] = acc[m] + sq;
+                    acc[m] = fmaf(df, df, acc[m]);
                     df = xv.y - cv.y;
-                    sq = df * df;
-                    acc[m] = acc[m] + sq;
+                    acc[m] = fmaf(df, df, acc[m]);
                     df = xv.z - cv.z;
-                    sq = df * df;
-                    acc[m] = acc[m] + sq;
+                    acc[m] = fmaf(df, df, acc[m]);
                     df = xv.w - cv.w;
-                    sq = df * df;
-                    acc[m] = acc[m] + sq;
+                    acc[m] = fmaf(df, df, acc[m]);
                 }
             }
             float bd = acc[0];

@@ -248,10 +248,11 @@ size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, 
  *   A_gj = sum_c w_c softmax_j(scale * mu_c . Kp_j),  Kp_j the mean key of block j;
  * every query block i of group g = i / (q_group/N) takes row A_g, and
  *   keep  = F_ij > thr with F the CDF of that row, as nabla_build_mask.
- * Distances and means are float32 with every operation rounded on its own, in a fixed
- * order (differences, squares and a running sum over d in index order; a running sum
- * over the cluster's queries in row order, then a division), so the clustering is
- * reproducible bit for bit by any implementation that follows the same order.
+ * Distances and means are float32 in a fixed order (per coordinate, in index order,
+ * the rounded difference, then its square added to the running sum by one fused
+ * multiply-add; a running sum over the cluster's queries in row order, then one
+ * division), so the clustering is reproducible bit for bit by any implementation that
+ * follows the same order.
  * Arguments, outputs and errors as nabla_build_mask, plus q_group and the workspace of
  * nabla_build_mask_ibcs_workspace_size(); NABLA_E_INVAL when q_group is not a positive
  * multiple of N or does not divide L, NABLA_E_UNSUPPORTED when q_group is not 64 or
