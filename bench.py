@@ -241,13 +241,14 @@ def bench_sip(args, cfg, qd, kd, vd) -> int:
 
 
 def bench_ibcs(args, cfg, qd, kd, vd) -> int:
-    """IBCS variant of the step on fractal-order tensors: nabla_build_mask_ibcs (K
-    pooling, 8 clusters per group of 128 queries as on the AB-Attention page, centroid
-    map, CDF cut, lists) and block_sparse_attn_fwd on its lists, each bracketed by HIP
+    """IBCS variant of the step on raster-order tensors, the fractal flattening applied
+    in the addressing as in the default step: nabla_build_mask_ibcs_raster (K pooling,
+    8 clusters per group of 128 queries as on the AB-Attention page, centroid map, CDF
+    cut, lists) and block_sparse_attn_fwd_raster on its lists, each bracketed by HIP
     events; the IBCS mask with 64-query groups and the plain NABLA mask on the same
     inputs are timed beside it."""
     T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
-    qf, kf, vf = (nab.reorder(t, T, H, W, P) for t in (qd, kd, vd))
+    qf, kf, vf = qd, kd, vd      # raster order
     ws = torch.empty(nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, N, ibcs=True, ibcs_group=64),
                      dtype=torch.uint8, device="cuda")
     o = torch.empty_like(qf)
@@ -255,16 +256,16 @@ def bench_ibcs(args, cfg, qd, kd, vd) -> int:
 
     def mask():
         state["lists"] = nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True,
-                                        workspace=ws, ibcs=True, ibcs_group=128)
+                                        workspace=ws, ibcs=True, ibcs_group=128, raster=True)
 
     def mask_nabla():
-        nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws)
+        nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws, raster=True)
         nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws, ibcs=True,
-                       ibcs_group=64)
+                       ibcs_group=64, raster=True)
 
     def attn():
         cnt, idx, sched = state["lists"]
-        nab.attn_fwd(qf, kf, vf, cnt, idx, N, out=o, schedule=sched)
+        nab.attn_fwd_raster(qf, kf, vf, cnt, idx, T, H, W, P, N, out=o, schedule=sched)
 
     for _ in range(args.warmup):
         mask()
@@ -279,10 +280,10 @@ def bench_ibcs(args, cfg, qd, kd, vd) -> int:
         e[1].record()
         attn()
         e[2].record()
-        nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws)
+        nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws, raster=True)
         e[3].record()
         nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, workspace=ws, ibcs=True,
-                       ibcs_group=64)
+                       ibcs_group=64, raster=True)
         e[4].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -307,7 +308,8 @@ def bench_ibcs(args, cfg, qd, kd, vd) -> int:
         "dtype": cfg.dtype,
         "data": f"synthetic ({GENERATOR_VERSION})",
         "config": {"workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "L": cfg.L,
-                   "blocks_per_head": cfg.nb, "thr": cfg.thr, "sta": cfg.sta, "ibcs_query_group": 128},
+                   "blocks_per_head": cfg.nb, "thr": cfg.thr, "sta": cfg.sta, "ibcs_query_group": 128,
+                   "order": "raster, flattening in the addressing"},
         "ms_mask_ibcs": round(ms_mask, 4),
         "ms_mask_ibcs_query_group_64": round(ms_q64, 4),
         "ms_mask_nabla_same_inputs": round(ms_nabla, 4),

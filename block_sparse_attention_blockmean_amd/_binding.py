@@ -27,6 +27,7 @@ EXPORTS = (
     "nabla_build_mask_sip",
     "nabla_build_mask_ibcs_workspace_size",
     "nabla_build_mask_ibcs",
+    "nabla_build_mask_ibcs_raster",
     "nabla_build_mask_ibcs_sip",
     "block_sparse_attn_fwd_weighted",
     "block_sparse_attn_fwd",
@@ -73,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_build_mask_ibcs.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, f, ctypes.POINTER(StaWindow),
                                           f, i, vp, vp, vp, vp, vp, sz, vp]
     lib.nabla_build_mask_ibcs.restype = i
+    lib.nabla_build_mask_ibcs_raster.argtypes = lib.nabla_build_mask_ibcs.argtypes
+    lib.nabla_build_mask_ibcs_raster.restype = i
     lib.nabla_build_mask_ibcs_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.nabla_build_mask_ibcs_sip.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, i, vp, f, i, vp, vp, vp, vp, vp, vp,
                                               sz, vp]
@@ -182,15 +185,16 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
         bitmap = torch.empty((B, NH, nb, (nb + 31) // 32), dtype=torch.int32, device=dev)
     if with_schedule and schedule is None:
         schedule = torch.empty((B * NH * nb,), dtype=torch.int32, device=dev)
-    if raster and ibcs:
-        raise ValueError("IBCS scores are implemented for fractal-ordered inputs only")
     ws_bytes = build_mask_workspace_size(B, NH, L, d, N, ibcs=ibcs, ibcs_group=ibcs_group)
     if workspace is None:
         workspace = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=dev)
     win = None if sta is None else ctypes.byref(StaWindow(*sta))
     # the IBCS entry takes the query-group size right after N
     shape = (B, NH, T, H, W, d, P, N) + ((int(ibcs_group),) if ibcs else ())
-    entry = lib.nabla_build_mask_ibcs if ibcs else (lib.nabla_build_mask_raster if raster else lib.nabla_build_mask)
+    if ibcs:
+        entry = lib.nabla_build_mask_ibcs_raster if raster else lib.nabla_build_mask_ibcs
+    else:
+        entry = lib.nabla_build_mask_raster if raster else lib.nabla_build_mask
     _check(entry(
         _dev(q, "q"), _dev(k, "k"), *shape, float(thr), win,
         float(scale) if scale is not None else 0.0, _dtype_code(q),

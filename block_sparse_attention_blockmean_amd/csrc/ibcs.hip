@@ -15,6 +15,7 @@
 // same on any machine that performs those operations in that order.
 #include <math.h>
 
+#include "attn_tile.h"
 #include "nabla_internal.h"
 
 namespace nabla {
@@ -52,16 +53,19 @@ constexpr size_t cluster_lds_bytes() {
            ((size_t)NT + (size_t)kIbcsClusters * QN + kIbcsClusters) * sizeof(int);
 }
 
-// One workgroup per query group (bh * groups + g).  LDS rows are padded by 16 bytes
+// One workgroup per query group (bh * groups + g).  In fractal order the group is QN
+// consecutive rows; in raster order (RASTER) its 64-token blocks are the 8 x 8 patches
+// that fractal order numbers g * QN / 64, ..., read through the patch addressing.  LDS rows are padded by 16 bytes
 // (d + 4 floats): row t starts 4 t banks further on, so the 16 queries a wave reads with
 // one 16-byte load fall in distinct bank groups.  Float contraction is off in the whole
 // kernel, so the only fused operations are the explicit fmaf of the distances; every
 // other +, - and * rounds on its own, and the division is the correctly rounded one
 // (hipcc's default for float32 division).
-template <typename T, int D, int QN>
+template <typename T, int D, int QN, bool RASTER>
 __global__ __launch_bounds__(cluster_threads<QN>()) void ibcs_cluster_kernel(const T* __restrict__ q,
                                                                              float* __restrict__ cent,
-                                                                             float* __restrict__ weight) {
+                                                                             float* __restrict__ weight, int groups,
+                                                                             int L, attn::RasterGrid grid) {
 #pragma clang fp contract(off)
     constexpr int kThreads = cluster_threads<QN>();
     constexpr int kPerCluster = kThreads / kIbcsClusters;     // threads per centroid in the update step
@@ -82,11 +86,18 @@ __global__ __launch_bounds__(cluster_threads<QN>()) void ibcs_cluster_kernel(con
 
     const size_t grp = blockIdx.x;
     const int tid = threadIdx.x;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(q + grp * QN * D);
     for (int ch = tid; ch < QN * D / EPC; ch += kThreads) {
         float v[EPC];
-        unpack16(__builtin_nontemporal_load(src + ch), T{}, v);
         const int row = ch / (D / EPC), col = (ch % (D / EPC)) * EPC;
+        size_t token;
+        if (RASTER) {
+            const size_t bh = grp / groups;
+            const uint32_t blk = (uint32_t)(grp - bh * groups) * (QN / 64) + row / 64;
+            token = bh * L + attn::block_row<true>(grid, blk) + attn::row_in_block<true>(grid, row % 64);
+        } else {
+            token = grp * QN + row;
+        }
+        unpack16(__builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(q + token * D + col)), T{}, v);
 #pragma unroll
         for (int e = 0; e < EPC; e += 4)
             *reinterpret_cast<float4*>(xq + row * LD + col + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
@@ -199,22 +210,34 @@ __global__ __launch_bounds__(cluster_threads<QN>()) void ibcs_cluster_kernel(con
     if (tid < kIbcsClusters) weight[grp * kIbcsClusters + tid] = (float)counts[tid] / (float)QN;
 }
 
-template <typename T, int D, int QN>
+template <typename T, int D, int QN, bool RASTER>
 hipError_t launch(const MaskArgs& a, hipStream_t s) {
     constexpr size_t lds = cluster_lds_bytes<D, QN>();
     static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = set_max_dynamic_lds((const void*)ibcs_cluster_kernel<T, D, QN>, (int)lds, lds_set);
+    hipError_t e = set_max_dynamic_lds((const void*)ibcs_cluster_kernel<T, D, QN, RASTER>, (int)lds, lds_set);
     if (e != hipSuccess) return e;
     const int groups = a.nb / a.ibcs_group;
-    hipLaunchKernelGGL((ibcs_cluster_kernel<T, D, QN>), dim3(a.BH * groups), dim3(cluster_threads<QN>()), lds, s,
-                       (const T*)a.q, a.cent, a.cent_w);
+    attn::RasterGrid grid{};
+    if (RASTER) {
+        grid.W = (uint32_t)a.W;
+        grid.HW = (uint32_t)(a.H * a.W);
+        grid.nHW = FastDiv((uint32_t)(a.nH * a.nW));
+        grid.nW = FastDiv((uint32_t)a.nW);
+    }
+    hipLaunchKernelGGL((ibcs_cluster_kernel<T, D, QN, RASTER>), dim3(a.BH * groups), dim3(cluster_threads<QN>()), lds,
+                       s, (const T*)a.q, a.cent, a.cent_w, groups, a.nb * 64, grid);
     return hipGetLastError();
+}
+
+template <typename T, int D, int QN>
+hipError_t launch_r(const MaskArgs& a, hipStream_t s) {
+    return a.raster ? launch<T, D, QN, true>(a, s) : launch<T, D, QN, false>(a, s);
 }
 
 template <typename T>
 hipError_t launch_t(const MaskArgs& a, hipStream_t s) {
-    if (a.ibcs_group == 2) return a.d == 128 ? launch<T, 128, 128>(a, s) : launch<T, 64, 128>(a, s);
-    return a.d == 128 ? launch<T, 128, 64>(a, s) : launch<T, 64, 64>(a, s);
+    if (a.ibcs_group == 2) return a.d == 128 ? launch_r<T, 128, 128>(a, s) : launch_r<T, 64, 128>(a, s);
+    return a.d == 128 ? launch_r<T, 128, 64>(a, s) : launch_r<T, 64, 64>(a, s);
 }
 
 }  // namespace

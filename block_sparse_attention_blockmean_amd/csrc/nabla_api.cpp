@@ -174,6 +174,19 @@ nabla_status nabla_build_mask_ibcs(const void* q, const void* k, int batch, int 
                            bitmap, schedule, workspace, workspace_bytes, stream, 0, nullptr, nullptr, q_group);
 }
 
+nabla_status nabla_build_mask_ibcs_raster(const void* q, const void* k, int batch, int heads, int T, int H,
+                                          int W, int d, int P, int N, int q_group, float thr,
+                                          const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                                          int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                                          int32_t* schedule, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+    const char* who = "nabla_build_mask_ibcs_raster";
+    if (q_group <= 0 || N <= 0 || q_group % N)
+        return fail(NABLA_E_INVAL, "%s: q_group=%d must be a positive multiple of N=%d", who, q_group, N);
+    return build_mask_impl(who, 1, q, k, batch, heads, T, H, W, d, P, N, thr, sta, scale, dtype, kv_count, kv_index,
+                           bitmap, schedule, workspace, workspace_bytes, stream, 0, nullptr, nullptr, q_group);
+}
+
 nabla_status nabla_build_mask_ibcs_sip(const void* q, const void* k, int batch, int heads, int T, int H, int W,
                                        int d, int P, int N, int q_group, int budget, const float* uniforms,
                                        float scale, nabla_dtype dtype, int32_t* kv_count, int32_t* kv_index,

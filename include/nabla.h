@@ -266,6 +266,22 @@ nabla_status nabla_build_mask_ibcs(const void* q, const void* k, int batch, int 
                                    hipStream_t stream);
 
 /*
+ * nabla_build_mask_ibcs_raster - nabla_build_mask_ibcs for Q and K in raster order (the
+ * fractal flattening, "Metodologia: NABLA" item 1, applied in the addressing as in
+ * nabla_build_mask_raster: query block b is the P x P patch fractal order places at
+ * rows [N b, N b + N), read as P runs of P tokens; a query group is q_group / N such
+ * blocks).  Results, including the workspace's centroids and scores, are identical to
+ * nabla_reorder followed by nabla_build_mask_ibcs.  Arguments and errors as
+ * nabla_build_mask_ibcs, plus NABLA_E_INVAL when N != P*P.
+ */
+nabla_status nabla_build_mask_ibcs_raster(const void* q, const void* k, int batch, int heads, int T, int H,
+                                          int W, int d, int P, int N, int q_group, float thr,
+                                          const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                                          int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                                          int32_t* schedule, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+/*
  * nabla_build_mask_ibcs_sip - the AB-Attention page's two selectors together: IBCS
  * block scores (as nabla_build_mask_ibcs: q_group-query clusters, weighted centroid
  * attention to the mean keys) sampled by SIP (as nabla_build_mask_sip: inclusion

@@ -330,6 +330,20 @@ def test_build_mask_ibcs_validation(lib):
         assert lib.nabla_last_error().decode().startswith("nabla_build_mask_ibcs")
 
 
+def test_build_mask_ibcs_raster_validation(lib):
+    def call(**kw):
+        a = dict(q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, qg=128, thr=0.1, dt=NABLA_BF16,
+                 ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.nabla_build_mask_ibcs_raster(a["q"], a["k"], a["batch"], a["heads"], a["T"], a["H"], a["W"],
+                                                a["d"], a["P"], a["N"], a["qg"], a["thr"], None, 0.0, a["dt"], C, D_,
+                                                None, None, E, a["ws_bytes"], None)
+    for kw, st in ((dict(q=None), NABLA_E_INVAL), (dict(P=4, H=16, W=16), NABLA_E_INVAL),   # N != P*P
+                   (dict(qg=96), NABLA_E_INVAL), (dict(qg=256), NABLA_E_UNSUPPORTED), (dict(ws_bytes=64), NABLA_E_WORKSPACE)):
+        assert call(**kw) == st, kw
+        assert lib.nabla_last_error().decode().startswith("nabla_build_mask_ibcs_raster")
+
+
 def test_build_mask_ibcs_sip_validation(lib):
     def call(**kw):
         a = dict(q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, qg=128, budget=4, u=G, scale=0.0,

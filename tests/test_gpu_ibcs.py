@@ -226,3 +226,30 @@ def test_ibcs_max_blocks_per_head(qn):
     mism, band = check_mask(res["mask"], ref_m, ref_A, cfg.thr)
     say(f"  {n} groups' centroids bit-identical; scores rel err {err:.2e}; kept {res['mask'].mean():.4f}, "
         f"mask mismatches {mism}, band {band}")
+
+
+@pytest.mark.parametrize("qn", [128, 64])
+@pytest.mark.parametrize("cfg", [CASES[2], CASES[3]], ids=lambda c: c.name)
+def test_ibcs_raster_equals_explicit_reorder(cfg, qn):
+    """nabla_build_mask_ibcs_raster on raster-order Q, K gives the lists, bitmap and
+    workspace (pooled K, centroids, weights, scores) of nabla_reorder followed by
+    nabla_build_mask_ibcs, bit for bit."""
+    q, k, _ = make_qkv(cfg)
+    qd, kd = q.cuda(), k.cuda()
+    qf = nab.reorder(qd, cfg.T, cfg.H, cfg.W, cfg.P)
+    kf = nab.reorder(kd, cfg.T, cfg.H, cfg.W, cfg.P)
+    nbytes = nab.build_mask_workspace_size(cfg.B, cfg.heads, cfg.L, cfg.d, cfg.N, ibcs=True, ibcs_group=qn)
+    ws_a = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    ws_b = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    a = nab.build_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr, cfg.sta, with_bitmap=True,
+                       with_schedule=True, workspace=ws_a, ibcs=True, ibcs_group=qn)
+    b = nab.build_mask(qd, kd, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr, cfg.sta, with_bitmap=True,
+                       with_schedule=True, workspace=ws_b, ibcs=True, ibcs_group=qn, raster=True)
+    torch.cuda.synchronize()
+    G, nb = cfg.BH, cfg.nb
+    assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2]) and torch.equal(a[3], b[3])
+    ma = lists_to_mask(a[0].cpu().numpy().reshape(G, nb), a[1].cpu().numpy().reshape(G, nb, nb))
+    mb = lists_to_mask(b[0].cpu().numpy().reshape(G, nb), b[1].cpu().numpy().reshape(G, nb, nb))
+    assert np.array_equal(ma, mb)
+    assert torch.equal(ws_a, ws_b), "workspace sections differ"
+    say(f"IBCS raster == explicit reorder, {cfg.name} q_group {qn}: kept {ma.mean():.3f}")
