@@ -330,6 +330,50 @@ __device__ inline void map_rows(const float* __restrict__ xh, int n_rows, int ro
     }
 }
 
+// The same map for workgroups of many waves.  The kRows X rows sit in LDS (x_lds, rows of
+// D + 4 floats: row r starts 4 r banks on, so the 16 rows of one 16-byte read fall in
+// distinct banks), staged once by the whole workgroup, and are read per MFMA step; each
+// wave holds half a column tile's K operand at a time.  About 35 VGPRs rather than 115,
+// so two 16-wave workgroups share a CU: one's loads and barrier wait overlap the other's
+// select phase, and a launch of 1.5 workgroups per CU runs in one round, not two.
+template <int D>
+constexpr int kXld = D + 4;
+
+template <int D, int NW>
+__device__ inline void map_rows_xl(const float* __restrict__ x_lds, const float* __restrict__ kh, int nb, int ld_s,
+                                   float scale, float* s_lds, int wave, int lane) {
+    constexpr int KC = D / 4;
+    const int li = lane & 15;
+    const int kq = lane >> 4;
+    const f32x4* xa = reinterpret_cast<const f32x4*>(x_lds + li * kXld<D>) + kq;
+    const int n_ct = (nb + 15) / 16;
+    for (int ct = wave; ct < n_ct; ct += NW) {
+        const int j = ct * 16 + li;
+        const f32x4* src = reinterpret_cast<const f32x4*>(kh + (size_t)min(j, nb - 1) * D) + kq;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // the K operand in two halves of d (16 values per lane each)
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+            f32x4 b[KC / 8];
+#pragma unroll
+            for (int v = 0; v < KC / 8; ++v) {
+                b[v] = src[4 * (h * (KC / 8) + v)];
+                if (j >= nb) b[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int v = 0; v < KC / 8; ++v) {
+                const f32x4 a = xa[4 * (h * (KC / 8) + v)];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[v][i], acc, 0, 0, 0);
+            }
+        }
+        if (j < nb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_lds[(4 * kq + r) * ld_s + j] = acc[r] * scale;
+        }
+    }
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
@@ -535,25 +579,33 @@ __device__ void select_row(float* arow, float inv_sum, float* cand, int nb, int 
 
 // ---------------------------------------------------------------------------
 // NABLA's reduced map and cut in one kernel.  A workgroup (16 waves) owns kRows pooled
-// query rows of one head: the map by map_rows, then per row (one wave) the softmax
+// query rows of one head: the map by map_rows_xl, then per row (one wave) the softmax
 // A = exp(S - max) / sum in place and select_row.  The rows never leave LDS, which at
 // large nb (nb^2 floats per head) saves an HBM round trip.
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 16;
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) void map_select_kernel(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(8, 8))) void map_select_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp, int nb, int ld_s, float scale, float thr, int sta,
     int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
     uint32_t* __restrict__ bitmap, int sip_budget, const float* __restrict__ uniforms,
     float* __restrict__ kv_logw) {
-    extern __shared__ float s_lds[];   // [kRows][ld_s] rows, then [kWaves][kCap] candidates
+    // [kRows][ld_s] rows, then [kWaves][kCap] candidates, then [kRows][kXld] pooled queries
+    extern __shared__ __align__(16) float s_lds[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kRows;
-    map_rows<D, kWaves>(qp + (size_t)bh * nb * D, nb, row0, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds, wave,
-                        lane);
+    float* x_lds = s_lds + kRows * ld_s + kWaves * kCap;
+    for (int e = threadIdx.x; e < kRows * D / 4; e += kWaves * 64) {
+        const int r = e / (D / 4), c4 = e % (D / 4);
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (row0 + r < nb) v = reinterpret_cast<const f32x4*>(qp + ((size_t)bh * nb + row0 + r) * D)[c4];
+        *reinterpret_cast<f32x4*>(x_lds + r * kXld<D> + 4 * c4) = v;
+    }
+    __syncthreads();
+    map_rows_xl<D, kWaves>(x_lds, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds, wave, lane);
     __syncthreads();
     float* cand = s_lds + kRows * ld_s + wave * kCap;
     for (int r = wave; r < kRows; r += kWaves) {
@@ -664,9 +716,13 @@ hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
     const int ld_s = ((a.nb + 63) / 64) * 64 + 16;
-    const size_t lds = ((size_t)kRows * ld_s + (size_t)kWaves * kCap) * sizeof(float);
+    const size_t lds = ((size_t)kRows * ld_s + (size_t)kWaves * kCap + (size_t)kRows * kXld<D>) * sizeof(float);
     static std::atomic<uint64_t> lds_set{0};
-    const int max_lds = (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap) * (int)sizeof(float);
+    const int max_lds =
+        (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap + kRows * kXld<D>) * (int)sizeof(float);
+    static_assert((kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap + kRows * kXld<128>) *
+                          sizeof(float) <= 160 * 1024,
+                  "map/select LDS at the largest nb");
     hipError_t e = set_max_dynamic_lds((const void*)map_select_kernel<D>, max_lds, lds_set);
     if (e != hipSuccess) return e;
     dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
