@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle as O
-from synth import CONFIGS, Config, make_qkv
+from synth import Config, get_config, make_qkv
 import block_sparse_attention_blockmean_amd as nab
 from parity import lists_to_mask, max_abs
 
@@ -144,7 +144,7 @@ def test_backward_full_size():
     sampled query blocks and dK, dV of sampled KV blocks against the oracle, and the
     closed-form sums over every head (dK sums to zero over the keys, dV to the dO of the
     rows that keep something)."""
-    cfg = CONFIGS[1]
+    cfg = get_config("wan1.3b_480p")
     say(f"backward full size {cfg.name}: {cfg.BH} heads L{cfg.L} nb{cfg.nb}")
     q, k, v = make_qkv(cfg)
     G, nb, L, d, N = cfg.BH, cfg.nb, cfg.L, cfg.d, cfg.N

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle as O
-from synth import CONFIGS, Config, make_qkv
+from synth import Config, get_config, make_qkv
 import block_sparse_attention_blockmean_amd as nab
 from parity import bitmap_to_mask, check_mask, lists_to_mask
 
@@ -185,7 +185,7 @@ def test_ibcs_determinism_and_workspace_reuse():
 def test_ibcs_full_size(qn):
     """The Wan-1.3B-like layer at full size: every head through the GPU; centroids of two
     heads bit for bit and their masks against the oracle."""
-    cfg = CONFIGS[1]
+    cfg = get_config("wan1.3b_480p")
     say(f"IBCS full size {cfg.name} q_group {qn}: {cfg.BH} heads nb {cfg.nb}")
     q, k, _ = make_qkv(cfg)
     G = cfg.BH

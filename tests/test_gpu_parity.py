@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle as O
-from synth import CONFIGS, Config, make_head, make_qkv
+from synth import CONFIGS, Config, get_config, make_head, make_qkv
 import block_sparse_attention_blockmean_amd as nab
 from parity import (TOL_BF16, TOL_F32, bitmap_to_mask, check_mask, lists_to_mask, max_abs)
 
@@ -40,9 +40,9 @@ def small(name, T, H, W, P, d, dtype, thr, sta=None, heads=2, B=1, seed_index=7)
 
 
 SMALL = [
-    CONFIGS[0],
-    dataclasses.replace(CONFIGS[0], name="tiny_thr0", thr=0.0),
-    dataclasses.replace(CONFIGS[0], name="tiny_thr05", thr=0.5),
+    get_config("tiny"),
+    dataclasses.replace(get_config("tiny"), name="tiny_thr0", thr=0.0),
+    dataclasses.replace(get_config("tiny"), name="tiny_thr05", thr=0.5),
     small("bf16_d128_ragged", 5, 24, 40, 8, 128, "bf16", 0.2),
     small("bf16_d128_ragged_sta", 5, 24, 40, 8, 128, "bf16", 0.2, sta=(3, 3, 3)),
     small("bf16_d64", 3, 32, 32, 8, 64, "bf16", 0.05, heads=3),
@@ -123,7 +123,7 @@ def test_small_grid_parity(cfg):
 
 def test_thr0_is_full_attention():
     """thr = 0 keeps every block, so the path is dense attention in raster order."""
-    cfg = dataclasses.replace(CONFIGS[0], thr=0.0)
+    cfg = dataclasses.replace(get_config("tiny"), thr=0.0)
     q, k, v = make_qkv(cfg)
     res = run_gpu_path(cfg, q, k, v)
     assert torch.all(res["cnt"] == cfg.nb)
@@ -257,7 +257,7 @@ def test_max_blocks_per_head():
     assert worst <= TOL_BF16
 
 
-@pytest.mark.parametrize("cfg", CONFIGS[1:], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [c for c in CONFIGS if c.name != "tiny"], ids=lambda c: c.name)
 def test_full_config_parity(cfg):
     """Full mask parity on every head; attention on a seeded sample of query blocks
     (rows are independent given the mask, so sampled rows are exact checks)."""

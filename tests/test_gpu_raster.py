@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle as O
-from synth import CONFIGS, Config, make_qkv
+from synth import Config, get_config, make_qkv
 import block_sparse_attention_blockmean_amd as nab
 from parity import TOL_BF16, TOL_F32, max_abs
 
@@ -85,7 +85,7 @@ def test_raster_equals_explicit_reorder(cfg):
 def test_raster_full_size_bitwise():
     """The Wan-1.3B-like layer at full size: the raster path gives the explicit path's
     lists and output bit for bit."""
-    cfg = CONFIGS[1]
+    cfg = get_config("wan1.3b_480p")
     say(f"raster path full size {cfg.name}")
     q, k, v = make_qkv(cfg)
     ref, o_ref, ras, o_ras = both_paths(cfg, q, k, v)

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle as O
-from synth import CONFIGS, Config, make_qkv
+from synth import Config, get_config, make_qkv
 import block_sparse_attention_blockmean_amd as nab
 from parity import TOL_BF16, TOL_F32, lists_to_mask, max_abs
 
@@ -115,7 +115,7 @@ def test_sip_parity(cfg):
 def test_sip_full_size():
     """The Wan-1.3B-like layer with the NABLA run's average kept count as the budget:
     decisions and weights of two heads against the oracle, and the expected budget."""
-    cfg = CONFIGS[1]
+    cfg = get_config("wan1.3b_480p")
     q, k, v = make_qkv(cfg)
     budget = 185
     res = gpu_sip(cfg, q, k, budget, seed=99)
