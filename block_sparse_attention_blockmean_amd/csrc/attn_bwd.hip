@@ -306,9 +306,14 @@ void bwd_dq_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 //     dK^T += Q^T dS   A = Q^T through the transposing LDS read, B = dS (VGPRs)
 // K and V stay in LDS for the whole sweep.  Q is double-buffered (the next query
 // block's Q is copied at the top of an iteration); dO has one buffer, refilled once
-// every wave has formed its dV.  16 + 16 + 2 x 16 + 16 KiB = 80 KiB of LDS at d = 128:
-// two workgroups fill a CU's 160 KiB.  The two query halves are summed through LDS at
-// the end.
+// every wave has formed its dP.  16 + 16 + 2 x 16 + 16 KiB = 80 KiB of LDS at d = 128:
+// two workgroups fill a CU's 160 KiB, with no room for a buffer of the row statistics,
+// which are loaded into registers.  Vector-memory waits count in issue order, so the
+// order of issue decides what each wait covers: per query block the statistics loads
+// go out first, then the next Q copy, and the next dO copy last.  A wait for the
+// statistics then never waits for a copy, the block's dO copy has S and P to land
+// behind, and the next Q copy has the whole block.  The two query halves are summed
+// through LDS at the end.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -321,6 +326,11 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     constexpr int KS = D / 16;
     constexpr int DT = D / 32;
     constexpr uint32_t kTileBytes = kBlk * D * 2;
+    // vector-memory operations a wave issues per query block, in issue order: the row
+    // statistics (two groups of four 16-byte loads), the next Q copy, the next dO copy
+    constexpr int kStatLoads = 8;
+    constexpr int kQCopies = G::kCopiesPerWave;
+    constexpr int kDoCopies = G::kCopiesPerWave;
     __shared__ __attribute__((aligned(1024))) char k_t[G::kBytes];
     __shared__ __attribute__((aligned(1024))) char v_t[G::kBytes];
     __shared__ __attribute__((aligned(1024))) char q_t0[G::kBytes];
@@ -398,19 +408,27 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         const char* qbuf = PAR ? q_t1 : q_t0;
         char* q_next = PAR ? q_t0 : q_t1;
         const int qblk = list[i];
-        // Q and dO of query block qblk have landed; every wave is done with the previous
-        // block, so the other Q buffer takes the next block's Q now
-        wait_vmcnt<0>();
+        // Q of query block qblk has landed (only its dO copy, the last one issued, may
+        // still be in flight), and every wave is done with the previous block
+        wait_vmcnt<kDoCopies>();
         lds_barrier();
-        const bool more = i + 1 < count;
-        const uint32_t nxt = more ? list[i + 1] * kTileBytes : 0u;
-        if (more) copy_tile<D>(q_rsrc, nxt, q_next, wave, lane_copy);
-        float4 ls[4];
+        // the row statistics first, then the next block's Q into the other buffer: a
+        // wait for the statistics never waits for that copy.  The copy is unconditional
+        // (the last block copies its own Q again into a buffer nothing reads), so the
+        // compiler's waits stay exact.
+        float4 ls[4], dr[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             ls[g] = *reinterpret_cast<const float4*>(lse + stat_off + (size_t)qblk * kBlk + 8 * g);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            dr[g] = *reinterpret_cast<const float4*>(drow + stat_off + (size_t)qblk * kBlk + 8 * g);
+        const uint32_t nxt = list[min(i + 1, count - 1)] * kTileBytes;
+        __builtin_amdgcn_sched_barrier(0);
+        copy_tile<D>(q_rsrc, nxt, q_next, wave, lane_copy);
+        __builtin_amdgcn_sched_barrier(0);
 
-        // S, then P (the log-sum-exp and S die here), then dV, then dP and dS
+        // S, then P (the log-sum-exp and S die here)
         f32x16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
@@ -420,6 +438,9 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
             const bf16x8 b = *reinterpret_cast<const bf16x8*>(k_t + b_shift + a_off[s]);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, sacc, 0, 0, 0);
         }
+        // the products are issued before the wait for the statistics (and, behind them
+        // in issue order, this block's dO copy)
+        __builtin_amdgcn_sched_barrier(0);
         float p[16];
         bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -428,6 +449,12 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
             p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2e, -l2));
             pb[r / 8][r % 8] = (__bf16)p[r];
         }
+        // dO of qblk: this wave's share landed (only the statistics loads and the Q
+        // copy were issued after it), then every wave's
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kStatLoads + kQCopies>();
+        lds_barrier();
+        // dV, then dP and dS
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -449,14 +476,13 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
             dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dpacc, 0, 0, 0);
         }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 dr = *reinterpret_cast<const float4*>(drow + stat_off + (size_t)qblk * kBlk + 8 * g);
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) dsb[g / 2][4 * (g % 2) + c] = (__bf16)(p[4 * g + c] * (dpacc[4 * g + c] - dr[c]));
-        }
+            for (int c = 0; c < 4; ++c)
+                dsb[g / 2][4 * (g % 2) + c] = (__bf16)(p[4 * g + c] * (dpacc[4 * g + c] - dr[g][c]));
         // every wave has read this dO: its buffer takes the next block's dO
         lds_barrier();
-        if (more) copy_tile<D>(do_rsrc, nxt, do_t, wave, lane_copy);
+        copy_tile<D>(do_rsrc, nxt, do_t, wave, lane_copy);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
