@@ -123,7 +123,6 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
 //   candidate is left.  All sums run in a fixed order, so the result is deterministic.
 // ---------------------------------------------------------------------------
 constexpr int kRows = 16;
-constexpr int kScoreWaves = 4;   // waves of an IBCS score workgroup
 constexpr int kCap = 256;   // candidates per wave held in LDS
 
 // Wave-wide reductions on DPP: shifts of 1, 2, 4, 8 lanes inside each 16-lane row, then
@@ -261,86 +260,35 @@ __device__ void sip_row(float* arow, int nb, float inv_sum, int budget, const fl
 }
 
 // ---------------------------------------------------------------------------
-// Rows of the reduced map: S[r][j] = scale * X[row0 + r] . Kp_j for the workgroup's
-// kRows rows r (rows past n_rows use zero operands), parked in LDS rows of ld_s floats.
+// Rows of the reduced map: S[r][j] = scale * X[r] . Kp_j for the workgroup's kRows rows
+// r, parked in LDS rows of ld_s floats.  The kRows X rows sit in LDS (x_lds, rows of
+// d + 4 floats: row r starts 4 r banks on, so the 16 rows of one 16-byte read fall in
+// distinct banks), staged once by the whole workgroup (rows past the last are zeros).
 // The NW waves take column tiles of 16 blocks in turn with v_mfma_f32_16x16x4_f32
 // (float32 operands and accumulation).  Lane (row l % 16, group g = l / 16) supplies
 // coordinate 16 v + 4 g + i of its row at MFMA step 4 v + i, in both operands: each
 // 16-byte load instruction then reads 64 contiguous bytes of each of 16 rows (16 cache
 // lines), where a contiguous quarter of d per lane would touch 64 lines per instruction
-// and leave the loads bound by the texture unit's per-line rate.
+// and leave the loads bound by the texture unit's per-line rate.  A wave holds half a
+// column tile's Kp operand at a time: about 35 VGPRs, so 16-wave workgroups run two to
+// a CU, and one's loads and barrier waits overlap the other's work.
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-__device__ inline void map_rows(const float* __restrict__ xh, int n_rows, int row0, const float* __restrict__ kh,
-                                int nb, int ld_s, float scale, float* s_lds, int wave, int lane) {
-    constexpr int KC = D / 4;          // k values per lane per MFMA chain
-    const int li = lane & 15;
-    const int kq = lane >> 4;
-    float a[KC];
-    const int qrow = row0 + li;
-    if (qrow < n_rows) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(xh + (size_t)qrow * D) + kq;
-#pragma unroll
-        for (int v = 0; v < KC / 4; ++v) {
-            f32x4 t = src[4 * v];
-            a[4 * v] = t[0]; a[4 * v + 1] = t[1]; a[4 * v + 2] = t[2]; a[4 * v + 3] = t[3];
-        }
-    } else {
-#pragma unroll
-        for (int v = 0; v < KC; ++v) a[v] = 0.f;
-    }
-    const int n_ct = (nb + 15) / 16;
-    // K operand of column tile ct: rows 16 ct + lane % 16, coordinates as above
-    auto load_b = [&](int ct, float (&b)[KC]) {
-        const int j = ct * 16 + li;
-        if (j < nb) {
-            const f32x4* src = reinterpret_cast<const f32x4*>(kh + (size_t)j * D) + kq;
-#pragma unroll
-            for (int v = 0; v < KC / 4; ++v) {
-                f32x4 t = src[4 * v];
-                b[4 * v] = t[0]; b[4 * v + 1] = t[1]; b[4 * v + 2] = t[2]; b[4 * v + 3] = t[3];
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < KC; ++v) b[v] = 0.f;
-        }
-    };
-    auto tile = [&](int ct, const float (&b)[KC]) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KC; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
-        // lane holds S[4*(lane/16) + r][16*ct + lane%16]
-        const int j = ct * 16 + li;
-        if (j < nb) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s_lds[(4 * kq + r) * ld_s + j] = acc[r] * scale;
-        }
-    };
-    // the wave's column tiles ct = wave, wave + NW, ...: the next tile's operand is
-    // loaded while the current one multiplies
-    float b0[KC], b1[KC];
-    if (wave < n_ct) load_b(wave, b0);
-    for (int ct = wave; ct < n_ct; ct += 2 * NW) {
-        const bool has1 = ct + NW < n_ct;
-        if (has1) load_b(ct + NW, b1);
-        tile(ct, b0);
-        if (!has1) break;
-        if (ct + 2 * NW < n_ct) load_b(ct + 2 * NW, b0);
-        tile(ct + NW, b1);
-    }
-}
-
-// The same map for workgroups of many waves.  The kRows X rows sit in LDS (x_lds, rows of
-// D + 4 floats: row r starts 4 r banks on, so the 16 rows of one 16-byte read fall in
-// distinct banks), staged once by the whole workgroup, and are read per MFMA step; each
-// wave holds half a column tile's K operand at a time.  About 35 VGPRs rather than 115,
-// so two 16-wave workgroups share a CU: one's loads and barrier wait overlap the other's
-// select phase, and a launch of 1.5 workgroups per CU runs in one round, not two.
 template <int D>
 constexpr int kXld = D + 4;
 
+// Stages rows row0 .. row0 + kRows - 1 of X [n_rows, D] (zeros past the last) into x_lds.
+template <int D, int NT>
+__device__ inline void stage_rows(const float* __restrict__ xh, int n_rows, int row0, float* x_lds) {
+    for (int e = threadIdx.x; e < kRows * D / 4; e += NT) {
+        const int r = e / (D / 4), c4 = e % (D / 4);
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (row0 + r < n_rows) v = reinterpret_cast<const f32x4*>(xh + (size_t)(row0 + r) * D)[c4];
+        *reinterpret_cast<f32x4*>(x_lds + r * kXld<D> + 4 * c4) = v;
+    }
+}
+
 template <int D, int NW>
-__device__ inline void map_rows_xl(const float* __restrict__ x_lds, const float* __restrict__ kh, int nb, int ld_s,
+__device__ inline void map_rows(const float* __restrict__ x_lds, const float* __restrict__ kh, int nb, int ld_s,
                                    float scale, float* s_lds, int wave, int lane) {
     constexpr int KC = D / 4;
     const int li = lane & 15;
@@ -378,28 +326,30 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
 // IBCS scores.  A workgroup owns kRows centroid rows (kRows / 8 query groups) of one
-// head: the centroid map by map_rows; per row the maximum and the softmax normaliser
-// (one wave per row); then each group's row A = sum of its 8 rows' w_c softmax in
-// cluster order, the exponentials recomputed there rather than stored, written to
-// A_out [BH, groups, nb] for the select kernel.  Rows sum to one.  Four waves per
-// workgroup: the map's operand registers (about 115 VGPRs at d = 128) allow four waves
-// per SIMD, so four such workgroups share a CU and one's loads overlap another's MFMAs.
+// head: the centroid rows staged in LDS and the map by map_rows; per row the maximum
+// and the softmax normaliser (one wave per row); then each group's row A = sum of its 8
+// rows' w_c softmax in cluster order, the exponentials recomputed there rather than
+// stored, written to A_out [BH, groups, nb] for the select kernel.  Rows sum to one.
+// Sixteen waves and the LDS-staged operand (35 VGPRs) let two workgroups share a CU.
 // ---------------------------------------------------------------------------
 static_assert(kRows % kIbcsClusters == 0, "a workgroup holds whole query blocks' centroids");
+constexpr int kScoreWaves = 16;
 
 template <int D>
-__global__ __launch_bounds__(kScoreWaves * 64) void ibcs_score_kernel(const float* __restrict__ cent,
-                                                                 const float* __restrict__ cw,
-                                                                 const float* __restrict__ kp, int nb, int groups,
-                                                                 int ld_s, float scale, float* __restrict__ A_out) {
-    extern __shared__ float s_lds[];   // [kRows][ld_s]
+__global__ __launch_bounds__(kScoreWaves * 64) __attribute__((amdgpu_waves_per_eu(8, 8))) void ibcs_score_kernel(
+    const float* __restrict__ cent, const float* __restrict__ cw, const float* __restrict__ kp, int nb, int groups,
+    int ld_s, float scale, float* __restrict__ A_out) {
+    // [kRows][ld_s] rows, then [kRows][kXld] centroid rows
+    extern __shared__ __align__(16) float s_lds[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kRows;
     const int n_rows = groups * kIbcsClusters;
-    map_rows<D, kScoreWaves>(cent + (size_t)bh * n_rows * D, n_rows, row0, kp + (size_t)bh * nb * D, nb, ld_s,
-                             scale, s_lds, wave, lane);
+    float* x_lds = s_lds + kRows * ld_s;
+    stage_rows<D, kScoreWaves * 64>(cent + (size_t)bh * n_rows * D, n_rows, row0, x_lds);
+    __syncthreads();
+    map_rows<D, kScoreWaves>(x_lds, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds, wave, lane);
     __syncthreads();
     // per centroid row: the maximum m_c and the factor w_c / sum_j exp(S_cj - m_c)
     __shared__ float fac[kRows], mx2[kRows];
@@ -579,7 +529,7 @@ __device__ void select_row(float* arow, float inv_sum, float* cand, int nb, int 
 
 // ---------------------------------------------------------------------------
 // NABLA's reduced map and cut in one kernel.  A workgroup (16 waves) owns kRows pooled
-// query rows of one head: the map by map_rows_xl, then per row (one wave) the softmax
+// query rows of one head: the map by map_rows, then per row (one wave) the softmax
 // A = exp(S - max) / sum in place and select_row.  The rows never leave LDS, which at
 // large nb (nb^2 floats per head) saves an HBM round trip.
 // ---------------------------------------------------------------------------
@@ -598,14 +548,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(8, 
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kRows;
     float* x_lds = s_lds + kRows * ld_s + kWaves * kCap;
-    for (int e = threadIdx.x; e < kRows * D / 4; e += kWaves * 64) {
-        const int r = e / (D / 4), c4 = e % (D / 4);
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (row0 + r < nb) v = reinterpret_cast<const f32x4*>(qp + ((size_t)bh * nb + row0 + r) * D)[c4];
-        *reinterpret_cast<f32x4*>(x_lds + r * kXld<D> + 4 * c4) = v;
-    }
+    stage_rows<D, kWaves * 64>(qp + (size_t)bh * nb * D, nb, row0, x_lds);
     __syncthreads();
-    map_rows_xl<D, kWaves>(x_lds, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds, wave, lane);
+    map_rows<D, kWaves>(x_lds, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds, wave, lane);
     __syncthreads();
     float* cand = s_lds + kRows * ld_s + wave * kCap;
     for (int r = wave; r < kRows; r += kWaves) {
@@ -749,9 +694,9 @@ hipError_t launch_select(const MaskArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_ibcs_score(const MaskArgs& a, hipStream_t s) {
     const int ld_s = ((a.nb + 63) / 64) * 64 + 16;
-    const size_t lds = (size_t)kRows * ld_s * sizeof(float);
+    const size_t lds = ((size_t)kRows * ld_s + (size_t)kRows * kXld<D>) * sizeof(float);
     static std::atomic<uint64_t> lds_set{0};
-    const int max_lds = kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) * (int)sizeof(float);
+    const int max_lds = (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kRows * kXld<D>) * (int)sizeof(float);
     hipError_t e = set_max_dynamic_lds((const void*)ibcs_score_kernel<D>, max_lds, lds_set);
     if (e != hipSuccess) return e;
     const int groups = a.nb / a.ibcs_group;
