@@ -1,0 +1,31 @@
+"""bench.py's command-line contract on a machine without a GPU: more than one GPU is
+refused with exit status 2 and a message naming the reason, and a run with no GPU fails
+loudly rather than falling back to the CPU."""
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                          capture_output=True, text=True, timeout=300)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+    assert r.stdout == ""          # no JSON line
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the behaviour without a GPU")
+def test_no_gpu_fails_loudly():
+    r = _bench("--steps", "1", "--warmup", "0", "--no-cpu")
+    assert r.returncode != 0
+    assert "GPU" in r.stderr
+    assert r.stdout == ""
