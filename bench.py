@@ -58,9 +58,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
+def read_traffic(workload: str, kernel: str):
     """HBM bytes per attention launch from the committed --pmc summary, valid only
-    if it was taken on the current kernel source."""
+    if it was taken on the current kernel source, for this workload and this kernel."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -69,6 +69,8 @@ def read_traffic():
             key, val = ln.split(":", 1)
             kv[key.strip()] = val.strip()
     if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if kv.get("workload") != workload or kv.get("kernel") != kernel:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -574,7 +576,8 @@ def main(argv=None):
     mask_bytes = 2 * tensor_bytes + 4 * (kept + cfg.BH * nb)
     attn_tflops = kept_flops / (ms_attn * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = read_traffic()
+    kernel = f"attn_fwd_{'bf16' if cfg.dtype == 'bf16' else 'f32'}_kernel<{cfg.d}, {'raster' if raster else 'fractal'}>"
+    traffic = read_traffic(cfg.name, kernel)
 
     rec = {
         "metric": METRIC,
@@ -615,7 +618,8 @@ def main(argv=None):
         "mask_frac_of_hbm": round(mask_bytes / (ms_mask * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "reorder_GBps": round(3 * 2 * tensor_bytes / (ms_reorder_in * 1e-3) / 1e9, 1),
         "roofline": {
-            "bound": "mfma",
+            # the float32 path computes on plain float32 FMAs (the vector unit)
+            "bound": "mfma" if cfg.dtype == "bf16" else "alu",
             "achieved": round(attn_tflops, 2),
             "peak": peak,
             "unit": "TFLOP/s",

@@ -29,3 +29,15 @@ def test_no_gpu_fails_loudly():
     assert r.returncode != 0
     assert "GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_traffic_figure_only_for_its_workload_and_kernel():
+    """The committed counter figure belongs to one kernel on one workload: any other
+    bench line reports its traffic as unknown rather than borrowing it."""
+    sys.path.insert(0, ROOT)
+    import bench
+    t = bench.read_traffic("wan1.3b_480p", "attn_fwd_bf16_kernel<128, raster>")
+    assert t is None or t > 0
+    assert bench.read_traffic("tiny", "attn_fwd_f32_kernel<64, raster>") is None
+    assert bench.read_traffic("wan1.3b_480p", "attn_fwd_bf16_kernel<128, fractal>") is None
+    assert bench.read_traffic("hunyuan_720p_sta", "attn_fwd_bf16_kernel<128, raster>") is None
