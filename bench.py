@@ -7,19 +7,24 @@ flattening of O.  The timed step runs the raster-order entry points, which apply
 flattening in the kernels' addressing; the same step with explicit reorder passes
 (nabla_reorder before and after) is timed in the same run and reported beside it.
 
+The default workload is the largest one that fits one GPU: the Wan2.1-14B-like 720p
+layer with its classifier-free-guidance batch (B 2, 40 heads, 21 x 48 x 80 latent grid);
+the Wan2.1-1.3B-like 480p layer is measured in the same run and reported under
+``extra_workloads``.
+
 Prints one JSON line.  ``value`` is kept-tile TFLOP/s over the whole step
 (4 N^2 d FLOP per kept 64 x 64 tile / step time); the sub-phase times, the
 attention kernel's own TFLOP/s against the bf16 MFMA peak and the mask phase's
 GB/s against HBM peak ride along, with the oracle timed on the host beside it.
 
-    python bench.py [--steps K] [--warmup W] [--config 1] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu] [--no-extra]
     python bench.py --no-cpu --loop-seconds 12      # steady load for power / clock readings
     python bench.py --gemm-reference                # dense bf16 GEMM of the vendor library
-    python bench.py --backward --no-cpu             # the gradient of the attention step
-    python bench.py --sip 185 --no-cpu              # SIP selection + weighted attention
-    python bench.py --ibcs --no-cpu                 # IBCS block scores + attention
-    python bench.py --ibcs --sip 185 --no-cpu       # SIP sampling from IBCS scores
-    python bench.py --mask-every 4 --no-cpu         # mask rebuilt every 4th step, reused between
+    python bench.py --config 1 --backward --no-cpu  # the gradient of the attention step
+    python bench.py --config 1 --sip 185 --no-cpu   # SIP selection + weighted attention
+    python bench.py --config 1 --ibcs --no-cpu      # IBCS block scores + attention
+    python bench.py --config 1 --ibcs --sip 185 --no-cpu   # SIP sampling from IBCS scores
+    python bench.py --config 1 --mask-every 4 --no-cpu     # mask rebuilt every 4th step
 """
 from __future__ import annotations
 
@@ -78,41 +83,57 @@ def read_traffic(workload: str, kernel: str):
         return None
 
 
-def cpu_baseline(cfg, q, k, v, kept_flops_total, budget_s=15.0):
-    """The oracle (untuned) on a bounded sample of the same workload, extrapolated to
-    one whole step: whole heads (reorder of Q, K, V, the float32 mask, float64 attention
-    over every kept tile), one after another until the budget is spent, scaled by the
-    head count."""
+def cpu_baseline(cfg, q, k, v, kept_flops_total, budget_s=20.0, blocks_per_head=48):
+    """The oracle (untuned) on a bounded sample of the same workload, extrapolated to one
+    whole step.  Heads are taken in a seeded order (first, last, then the rest shuffled);
+    for each, the oracle's reorder of Q, K, V and its float32 mask, then float64 attention
+    of a seeded sample of the head's query blocks over their kept tiles, until the budget
+    is spent.  Mask time is scaled by the head count, attention time by the kept-tile
+    count of the whole step."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    G = cfg.BH
+    G, nb = cfg.BH, cfg.nb
     scale = 1.0 / np.sqrt(cfg.d)
-    t0 = time.perf_counter()
-    heads = 0
-    for g in range(G):
+    rng = np.random.default_rng(1000 + cfg.index)
+    order = [0] + ([G - 1] if G > 1 else []) + [int(x) for x in rng.permutation(np.arange(1, G - 1))]
+    t_mask = t_attn = 0.0
+    heads = blocks = tiles = 0
+    t_start = time.perf_counter()
+    for g in order:
         b, h = divmod(g, cfg.heads)
+        t0 = time.perf_counter()
         qn, kn, vn = (t[b, h].float().numpy() for t in (q, k, v))
         qf, kf, vf = (O.reorder(a, cfg.T, cfg.H, cfg.W, cfg.P) for a in (qn, kn, vn))
         mk = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.thr, cfg.sta)
-        for i in range(cfg.nb):
-            O.attention_block(qf, kf, vf, mk["mask"][i], int(i), cfg.N, scale)
+        t_mask += time.perf_counter() - t0
         heads += 1
-        if time.perf_counter() - t0 > budget_s:
+        for i in rng.choice(nb, size=min(nb, blocks_per_head), replace=False):
+            t0 = time.perf_counter()
+            O.attention_block(qf, kf, vf, mk["mask"][i], int(i), cfg.N, scale)
+            t_attn += time.perf_counter() - t0
+            blocks += 1
+            tiles += int(mk["mask"][i].sum())
+            if time.perf_counter() - t_start > budget_s:
+                break
+        if time.perf_counter() - t_start > budget_s:
             break
-    elapsed = time.perf_counter() - t0
-    t_step = elapsed * G / heads
+    kept_total = kept_flops_total / (4.0 * cfg.N * cfg.N * cfg.d)
+    t_step = t_mask * G / heads + t_attn * kept_total / max(tiles, 1)
+    whole = heads == G and blocks == G * nb
     return {
         "value": kept_flops_total / t_step / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{heads} of {G} (batch, head) slices, each whole: reorder of Q,K,V, the float32 "
-                   f"mask and float64 attention over all its kept tiles; {elapsed:.1f} s measured, "
-                   f"scaled by {G}/{heads} to est. {t_step:.0f} s per step"),
+        "extrapolated": not whole,
+        "sample": (f"oracle reorder + float32 mask on {heads} of {G} (batch, head) slices ({t_mask:.1f} s), "
+                   f"float64 attention of {blocks} seeded query blocks over their {tiles} kept tiles "
+                   f"({t_attn:.1f} s); scaled by head count and by kept tiles ({kept_total:.0f} in the step) "
+                   f"to est. {t_step:.0f} s per step"),
         "est_s_per_step": t_step,
     }
 
@@ -387,7 +408,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="1", help="workload index or name")
+    ap.add_argument("--config", default="4", help="workload index or name (default: the Wan-14B-like "
+                    "720p layer with its CFG batch, the largest single-GPU workload)")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="skip the Wan-1.3B-like 480p workload that the default run reports as an extra key")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only an identity reorder (P=1, a plain copy) of 1 GiB, for counter scaling")
@@ -462,12 +486,137 @@ def main(argv=None):
         return 0
 
     cfg = get_config(int(args.config) if args.config.isdigit() else args.config)
-    print(f"# workload {cfg.name}: B{cfg.B} heads{cfg.heads} d{cfg.d} {cfg.dtype} "
-          f"{cfg.T}x{cfg.H}x{cfg.W} P{cfg.P} N{cfg.N} thr{cfg.thr} sta{cfg.sta}", file=sys.stderr,
-          flush=True)
+    say(f"# workload {cfg.name}: B{cfg.B} heads{cfg.heads} d{cfg.d} {cfg.dtype} "
+        f"{cfg.T}x{cfg.H}x{cfg.W} P{cfg.P} N{cfg.N} thr{cfg.thr} sta{cfg.sta}")
     q, k, v = make_qkv(cfg)
+    say("# inputs generated")
     dev = torch.device("cuda:0")
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
+
+    if args.backward:
+        return bench_backward(args, cfg, qd, kd, vd)
+    if args.sip > 0:
+        return bench_sip(args, cfg, qd, kd, vd)   # --ibcs picks the IBCS scores
+    if args.ibcs:
+        return bench_ibcs(args, cfg, qd, kd, vd)
+    if args.mask_every > 0:
+        return bench_mask_reuse(args, cfg, qd, kd, vd)
+    if args.loop_seconds > 0:
+        return loop_step(args, cfg, qd, kd, vd)
+
+    m = measure_step(args, cfg, qd, kd, vd)
+    kept, kept_flops = m["kept"], m["kept_flops"]
+    ms_step, ms_mask, ms_attn = m["ms_step"], m["ms_mask"], m["ms_attn"]
+    nb = cfg.nb
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    attn_tflops = kept_flops / (ms_attn * 1e-3) / 1e12
+    kernel = f"attn_fwd_{'bf16' if cfg.dtype == 'bf16' else 'f32'}_kernel<{cfg.d}, {'raster' if m['raster'] else 'fractal'}>"
+    traffic = read_traffic(cfg.name, kernel)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(kept_flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": f"synthetic ({GENERATOR_VERSION}: smooth 3D cosine field + N(0,0.5^2) noise, seeded)",
+        "config": workload_config(cfg),
+        "path": ("raster order in and out, fractal flattening applied in the mask and attention "
+                 "kernels' addressing" if m["raster"] else "explicit reorder passes"),
+    }
+    rec.update(phase_summary(cfg, m))
+    rec["roofline"] = {
+        # the float32 path computes on plain float32 FMAs (the vector unit)
+        "bound": "mfma" if cfg.dtype == "bf16" else "alu",
+        "achieved": round(attn_tflops, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(attn_tflops / peak, 4),
+        "traffic": traffic,
+    }
+    rec["device"] = torch.cuda.get_device_name(0)
+    rec["cus"] = torch.cuda.get_device_properties(0).multi_processor_count
+
+    # the other large workload as an extra key (same step, same counts of steps)
+    if args.extra and args.config in ("4", "wan14b_720p_cfg"):
+        del qd, kd, vd
+        torch.cuda.empty_cache()
+        ecfg = get_config("wan1.3b_480p")
+        say(f"# extra workload {ecfg.name}")
+        eq, ek, ev = (t.to(dev) for t in make_qkv(ecfg))
+        em = measure_step(args, ecfg, eq, ek, ev)
+        e_attn = em["kept_flops"] / (em["ms_attn"] * 1e-3) / 1e12
+        extra = {"config": workload_config(ecfg), "ms_per_step": round(em["ms_step"], 4),
+                 "value": round(em["kept_flops"] / (em["ms_step"] * 1e-3) / 1e12, 3)}
+        extra.update(phase_summary(ecfg, em))
+        extra["attn_frac_of_peak"] = round(e_attn / PEAK_BF16_TFLOPS, 4)
+        rec["extra_workloads"] = {ecfg.name: extra}
+        del eq, ek, ev
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        say("# timing the oracle on the host (bounded sample)")
+        cb = cpu_baseline(cfg, q, k, v, kept_flops)
+        cb["value"] = float(f"{cb['value']:.3g}")
+        rec["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample", "extrapolated")}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def say(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def workload_config(cfg) -> dict:
+    return {"workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "T": cfg.T, "H": cfg.H,
+            "W": cfg.W, "P": cfg.P, "N": cfg.N, "thr": cfg.thr, "sta": list(cfg.sta) if cfg.sta else None,
+            "L": cfg.L, "blocks_per_head": cfg.nb}
+
+
+def phase_summary(cfg, m) -> dict:
+    """Per-phase times and rates of one measured step (see measure_step)."""
+    esize = 2 if cfg.dtype == "bf16" else 4
+    tensor_bytes = cfg.BH * cfg.L * cfg.d * esize
+    mask_bytes = 2 * tensor_bytes + 4 * (m["kept"] + cfg.BH * cfg.nb)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    attn_tflops = m["kept_flops"] / (m["ms_attn"] * 1e-3) / 1e12
+    out = {
+        "ms_layer": round(float(m["ms_mask"] + m["ms_attn"]), 4),
+        "ms_attn": round(float(m["ms_attn"]), 4),
+        "ms_mask": round(float(m["ms_mask"]), 4),
+        "gpu_ms_per_step": round(float(m["gpu_ms"]), 4),
+        "kept_fraction": round(m["kept"] / (cfg.BH * cfg.nb * cfg.nb), 5),
+        "kept_tiles": int(m["kept"]),
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_frac_of_peak": round(attn_tflops / peak, 4),
+        "mask_GBps": round(mask_bytes / (m["ms_mask"] * 1e-3) / 1e9, 1),
+        "mask_frac_of_hbm": round(mask_bytes / (m["ms_mask"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+    }
+    if "ms_step_x" in m:
+        out["explicit_reorder_path"] = {
+            "ms_per_step": round(m["ms_step_x"], 4),
+            "value": round(m["kept_flops"] / (m["ms_step_x"] * 1e-3) / 1e12, 3),
+            "ms_reorder_qkv": round(m["ms_reorder_in"], 4),
+            "ms_mask": round(m["ms_mask_x"], 4),
+            "ms_attn": round(m["ms_attn_x"], 4),
+            "ms_reorder_o": round(m["ms_reorder_out"], 4),
+        }
+        out["reorder_GBps"] = round(3 * 2 * tensor_bytes / (m["ms_reorder_in"] * 1e-3) / 1e9, 1)
+    return out
+
+
+def make_steps(cfg, qd, kd, vd):
+    """The timed step (raster-order entry points when N == P*P) and the same path with
+    explicit reorder passes, on shared output buffers.  Each takes an optional list of
+    events, recorded on torch's current stream, which is the stream every library call
+    launches on."""
+    dev = qd.device
     qf, kf, vf, of, od = (torch.empty_like(qd) for _ in range(5))
     nb = cfg.nb
     cnt = torch.empty((cfg.B, cfg.heads, nb), dtype=torch.int32, device=dev)
@@ -476,9 +625,6 @@ def main(argv=None):
                      dtype=torch.uint8, device=dev)
     sched = torch.empty((cfg.BH * nb,), dtype=torch.int32, device=dev)
     T, H, W, P = cfg.T, cfg.H, cfg.W, cfg.P
-    # five events per timed step, all on torch's current stream, which is the stream
-    # every library call launches on
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
 
     def step(ev=None):
         if ev:
@@ -501,9 +647,6 @@ def main(argv=None):
 
     # The same path with the fractal flattening folded into the kernels' addressing
     # (raster-order entry points, N == P*P): no reorder pass, bit-identical output.
-    raster = cfg.N == P * P
-    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-
     def step_raster(ev=None):
         if ev:
             ev[0].record()
@@ -515,39 +658,24 @@ def main(argv=None):
         if ev:
             ev[2].record()
 
-    main_step = step_raster if raster else step
+    raster = cfg.N == P * P
+    return step, (step_raster if raster else None), cnt
 
-    if args.backward:
-        return bench_backward(args, cfg, qd, kd, vd)
-    if args.sip > 0:
-        return bench_sip(args, cfg, qd, kd, vd)   # --ibcs picks the IBCS scores
-    if args.ibcs:
-        return bench_ibcs(args, cfg, qd, kd, vd)
-    if args.mask_every > 0:
-        return bench_mask_reuse(args, cfg, qd, kd, vd)
 
+def measure_step(args, cfg, qd, kd, vd) -> dict:
+    """Warm-up, then args.steps timed steps of each form of the step (wall clock between
+    synchronisations; per-phase times from HIP events on the launch stream)."""
+    step, step_raster, cnt = make_steps(cfg, qd, kd, vd)
+    raster = step_raster is not None
     for _ in range(args.warmup):
         step()
         if raster:
             step_raster()
     torch.cuda.synchronize()
-    if args.loop_seconds > 0:
-        t0 = time.perf_counter()
-        n, last = 0, t0
-        while time.perf_counter() - t0 < args.loop_seconds:
-            for _ in range(50):
-                main_step()
-            torch.cuda.synchronize()
-            n += 50
-            now = time.perf_counter()
-            if now - last >= 1.0:
-                print(f"# t={now - t0:.1f}s steps={n} ms/step={(now - t0) * 1e3 / n:.3f}", file=sys.stderr,
-                      flush=True)
-                last = now
-        return 0
     kept = int(cnt.sum().item())
-    kept_flops = kept * 4.0 * cfg.N * cfg.N * cfg.d
+    m = {"kept": kept, "kept_flops": kept * 4.0 * cfg.N * cfg.N * cfg.d, "raster": raster}
 
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -555,9 +683,10 @@ def main(argv=None):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     phase = np.mean([[ev[i].elapsed_time(ev[i + 1]) for i in range(4)] for ev in events], axis=0)
-    ms_reorder_in, ms_mask_x, ms_attn_x, ms_reorder_out = (float(x) for x in phase)
-    ms_step_x = (t1 - t0) * 1e3 / args.steps
+    m["ms_reorder_in"], m["ms_mask_x"], m["ms_attn_x"], m["ms_reorder_out"] = (float(x) for x in phase)
+    m["ms_step_x"] = (t1 - t0) * 1e3 / args.steps
     if raster:
+        rev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(args.steps):
@@ -565,76 +694,34 @@ def main(argv=None):
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         rphase = np.mean([[ev[i].elapsed_time(ev[i + 1]) for i in range(2)] for ev in rev], axis=0)
-        ms_mask, ms_attn = (float(x) for x in rphase)
-        ms_step = (t1 - t0) * 1e3 / args.steps
-        gpu_ms = float(rphase.sum())
+        m["ms_mask"], m["ms_attn"] = (float(x) for x in rphase)
+        m["ms_step"] = (t1 - t0) * 1e3 / args.steps
+        m["gpu_ms"] = float(rphase.sum())
     else:
-        ms_mask, ms_attn, ms_step, gpu_ms = ms_mask_x, ms_attn_x, ms_step_x, float(phase.sum())
+        m["ms_mask"], m["ms_attn"], m["ms_step"] = m["ms_mask_x"], m["ms_attn_x"], m["ms_step_x"]
+        m["gpu_ms"] = float(phase.sum())
+    return m
 
-    esize = 2 if cfg.dtype == "bf16" else 4
-    tensor_bytes = cfg.BH * cfg.L * cfg.d * esize
-    mask_bytes = 2 * tensor_bytes + 4 * (kept + cfg.BH * nb)
-    attn_tflops = kept_flops / (ms_attn * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    kernel = f"attn_fwd_{'bf16' if cfg.dtype == 'bf16' else 'f32'}_kernel<{cfg.d}, {'raster' if raster else 'fractal'}>"
-    traffic = read_traffic(cfg.name, kernel)
 
-    rec = {
-        "metric": METRIC,
-        "value": round(kept_flops / (ms_step * 1e-3) / 1e12, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": f"synthetic ({GENERATOR_VERSION}: smooth 3D cosine field + N(0,0.5^2) noise, seeded)",
-        "config": {
-            "workload": cfg.name, "B": cfg.B, "heads": cfg.heads, "d": cfg.d, "T": cfg.T,
-            "H": cfg.H, "W": cfg.W, "P": cfg.P, "N": cfg.N, "thr": cfg.thr,
-            "sta": list(cfg.sta) if cfg.sta else None, "L": cfg.L, "blocks_per_head": nb,
-        },
-        "path": ("raster order in and out, fractal flattening applied in the mask and attention "
-                 "kernels' addressing" if raster else "explicit reorder passes"),
-        "ms_layer": round(float(ms_mask + ms_attn), 4),
-        "ms_attn": round(float(ms_attn), 4),
-        "ms_mask": round(float(ms_mask), 4),
-        "gpu_ms_per_step": round(gpu_ms, 4),
-        "explicit_reorder_path": {
-            "ms_per_step": round(ms_step_x, 4),
-            "value": round(kept_flops / (ms_step_x * 1e-3) / 1e12, 3),
-            "ms_reorder_qkv": round(ms_reorder_in, 4),
-            "ms_mask": round(ms_mask_x, 4),
-            "ms_attn": round(ms_attn_x, 4),
-            "ms_reorder_o": round(ms_reorder_out, 4),
-        },
-        "kept_fraction": round(kept / (cfg.BH * nb * nb), 5),
-        "attn_tflops": round(attn_tflops, 2),
-        "attn_frac_of_peak": round(attn_tflops / peak, 4),
-        "mask_GBps": round(mask_bytes / (ms_mask * 1e-3) / 1e9, 1),
-        "mask_frac_of_hbm": round(mask_bytes / (ms_mask * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "reorder_GBps": round(3 * 2 * tensor_bytes / (ms_reorder_in * 1e-3) / 1e9, 1),
-        "roofline": {
-            # the float32 path computes on plain float32 FMAs (the vector unit)
-            "bound": "mfma" if cfg.dtype == "bf16" else "alu",
-            "achieved": round(attn_tflops, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(attn_tflops / peak, 4),
-            "traffic": traffic,
-        },
-        "device": torch.cuda.get_device_name(0),
-        "cus": torch.cuda.get_device_properties(0).multi_processor_count,
-    }
-    if not args.no_cpu:
-        print("# timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        cb = cpu_baseline(cfg, q, k, v, kept_flops)
-        cb["value"] = float(f"{cb['value']:.3g}")
-        rec["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
-    print(json.dumps(rec), flush=True)
+def loop_step(args, cfg, qd, kd, vd) -> int:
+    """The step back to back for args.loop_seconds, a progress line per second (no JSON
+    line): a steady load for power and clock readings."""
+    step, step_raster, _ = make_steps(cfg, qd, kd, vd)
+    main_step = step_raster or step
+    for _ in range(max(args.warmup, 1)):
+        main_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n, last = 0, t0
+    while time.perf_counter() - t0 < args.loop_seconds:
+        for _ in range(5):
+            main_step()
+        torch.cuda.synchronize()
+        n += 5
+        now = time.perf_counter()
+        if now - last >= 1.0:
+            say(f"# t={now - t0:.1f}s steps={n} ms/step={(now - t0) * 1e3 / n:.3f}")
+            last = now
     return 0
 
 

@@ -171,10 +171,12 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
     Returns (kv_count, kv_index), plus the bitmap and/or the longest-first
     schedule when asked for (in that order)."""
     lib = load_library()
+    _check_mask_inputs(q, k, T, H, W, N)
     B, NH, L, d = q.shape
-    if k.shape != q.shape or k.dtype != q.dtype:
-        raise ValueError("q and k must have the same shape and dtype")
     nb = L // N
+    _check_int32(kv_count, "kv_count", B * NH * nb)
+    _check_int32(kv_index, "kv_index", B * NH * nb * nb)
+    _check_int32(schedule, "schedule", B * NH * nb)
     dev = q.device
     if kv_count is None:
         kv_count = torch.empty((B, NH, nb), dtype=torch.int32, device=dev)
@@ -210,6 +212,30 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
     return tuple(out)
 
 
+def _check_mask_inputs(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, N: int) -> None:
+    """Shape checks shared by the mask entry points, before any pointer is taken: the
+    library sizes its outputs from T*H*W, so q's token count must equal it."""
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, L, d]")
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must have the same shape and dtype")
+    L = q.shape[2]
+    if L != T * H * W:
+        raise ValueError(f"L={L} does not match T*H*W={T * H * W}")
+    if N <= 0 or L % N:
+        raise ValueError(f"L={L} is not a multiple of N={N}")
+
+
+def _check_int32(t: Optional[torch.Tensor], name: str, numel: int) -> None:
+    """A caller-supplied int32 output or list must hold exactly ``numel`` entries."""
+    if t is None:
+        return
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    if t.numel() != numel:
+        raise ValueError(f"{name} holds {t.numel()} entries, {numel} needed")
+
+
 def _check_lists(q: torch.Tensor, kv_count: torch.Tensor, kv_index: torch.Tensor, N: int) -> None:
     B, NH, L, d = q.shape
     nb = L // N
@@ -217,6 +243,8 @@ def _check_lists(q: torch.Tensor, kv_count: torch.Tensor, kv_index: torch.Tensor
         raise TypeError("kv_count and kv_index must be int32")
     if kv_count.numel() != B * NH * nb or kv_index.numel() != B * NH * nb * nb:
         raise ValueError("kv_count / kv_index sizes do not match q")
+    if L % N:
+        raise ValueError(f"L={L} is not a multiple of N={N}")
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.Tensor,
@@ -279,9 +307,8 @@ def build_mask_sip(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: 
     [B, heads, nb, nb] tensor of draws in [0, 1).  The scores sampled from are NABLA's
     pooled map, or with ``ibcs=True`` the IBCS scores of ``ibcs_group``-query clusters."""
     lib = load_library()
+    _check_mask_inputs(q, k, T, H, W, N)
     B, NH, L, d = q.shape
-    if k.shape != q.shape or k.dtype != q.dtype:
-        raise ValueError("q and k must have the same shape and dtype")
     nb = L // N
     if uniforms.dtype != torch.float32 or uniforms.numel() != B * NH * nb * nb:
         raise ValueError("uniforms must hold batch*heads*nb*nb float32 values")

@@ -32,6 +32,9 @@ bool valid_dtype(nabla_dtype dt) { return dt == NABLA_F32 || dt == NABLA_BF16; }
 
 // Tokens per head times d must stay addressable with 32-bit chunk indices.
 constexpr long long kMaxHeadElems = 1ll << 33;
+// The attention kernels address a head's K and V through buffer resources with 32-bit
+// byte offsets (signed in the tile arithmetic), so a head must stay below 2^31 bytes.
+constexpr long long kMaxHeadBytes = 1ll << 31;
 
 }  // namespace
 
@@ -410,8 +413,9 @@ nabla_status block_sparse_attn_bwd(const void* q, const void* k, const void* v, 
     if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "%s: d must be 64 or 128", who);
     if (L / N > NABLA_MAX_BLOCKS)
         return fail(NABLA_E_UNSUPPORTED, "%s: %d blocks per head exceed %d", who, L / N, NABLA_MAX_BLOCKS);
-    if ((long long)L * d >= kMaxHeadElems || (long long)batch * heads * (L / N) >= (1ll << 31))
-        return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
+    if ((long long)L * d * (long long)elem_size(dtype) >= kMaxHeadBytes ||
+        (long long)batch * heads * (L / N) >= (1ll << 31))
+        return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large (a head must stay below 2^31 bytes)", who);
     const size_t need = nabla_attn_bwd_workspace_size(batch, heads, L, N);
     if (!workspace || workspace_bytes < need)
         return fail(NABLA_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
@@ -472,8 +476,9 @@ nabla_status attn_fwd_impl(const char* who, const void* q, const void* k, const 
     if (!valid_dtype(dtype)) return fail(NABLA_E_INVAL, "%s: unknown dtype %d", who, (int)dtype);
     if (N != 64) return fail(NABLA_E_UNSUPPORTED, "%s: only N = 64 is implemented", who);
     if (d != 64 && d != 128) return fail(NABLA_E_UNSUPPORTED, "%s: d must be 64 or 128", who);
-    if ((long long)L * d >= kMaxHeadElems || (long long)batch * heads * (L / N) >= (1ll << 31))
-        return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
+    if ((long long)L * d * (long long)elem_size(dtype) >= kMaxHeadBytes ||
+        (long long)batch * heads * (L / N) >= (1ll << 31))
+        return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large (a head must stay below 2^31 bytes)", who);
     nabla::AttnArgs a{};
     a.q = q;
     a.k = k;

@@ -9,7 +9,7 @@ from .nabla_oracle import (
     block_tiles, sta_mask, block_mask, kv_lists, mask_from_lists, attention_block,
     masked_attention, forward, block_lse, masked_attention_lse, masked_attention_backward,
     sip_probabilities, sip_mask, weighted_block_attention, ibcs_clusters, ibcs_scores,
-    ibcs_block_mask, IBCS_CLUSTERS, IBCS_ITERS, fma_f32,
+    ibcs_block_mask, IBCS_CLUSTERS, IBCS_ITERS, IBCS_TIE_EPS,
 )
 
 __all__ = [
@@ -17,5 +17,5 @@ __all__ = [
     "cdf_keep", "block_tiles", "sta_mask", "block_mask", "kv_lists", "mask_from_lists",
     "attention_block", "masked_attention", "forward", "block_lse", "masked_attention_lse",
     "masked_attention_backward", "sip_probabilities", "sip_mask", "weighted_block_attention",
-    "ibcs_clusters", "ibcs_scores", "ibcs_block_mask", "IBCS_CLUSTERS", "IBCS_ITERS", "fma_f32",
+    "ibcs_clusters", "ibcs_scores", "ibcs_block_mask", "IBCS_CLUSTERS", "IBCS_ITERS", "IBCS_TIE_EPS",
 ]

@@ -354,93 +354,57 @@ IBCS_CLUSTERS = 8
 IBCS_ITERS = 4
 
 
-def fma_f32(a: np.ndarray, b: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """Correctly rounded float32 a*b + c with a single rounding (a fused multiply-add).
-
-    a*b of two float32 values is exact in float64 (24 + 24 significand bits).  hi, the
-    float64 sum of it and c, and lo, the exact error of that sum (TwoSum), give the
-    exact result hi + lo.  Rounding hi to float32 rounds hi + lo correctly except when
-    hi lies exactly halfway between two float32 values and lo != 0: a float32 midpoint
-    is a float64 number, and |lo| is below half the float64 spacing at hi, so any other
-    midpoint is on the same side of hi and hi + lo.  In that case the result is the
-    float32 neighbour on lo's side.  In the float32 normal range hi is a midpoint iff
-    its 29 mantissa bits below float32 precision are 1 followed by zeros; only those
-    elements, and nonzero ones below the normal range, are examined."""
-    a64 = np.asarray(a, dtype=np.float32).astype(np.float64)
-    b64 = np.asarray(b, dtype=np.float32).astype(np.float64)
-    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
-    p = a64 * b64
-    hi = p + c64
-    r = hi.astype(np.float32)
-    low = hi.view(np.uint64) & np.uint64(0x1FFFFFFF)
-    tiny = (np.abs(hi) < 2.0 ** -126) & (hi != 0)
-    cand = np.flatnonzero((low == np.uint64(0x10000000)) | tiny)
-    if cand.size:
-        pf, cf, hf, rf = p.flat[cand], c64.flat[cand], hi.flat[cand], r.flat[cand]
-        z = hf - pf
-        lf = (pf - (hf - z)) + (cf - z)
-        rf64 = rf.astype(np.float64)
-        other = np.nextafter(rf, np.where(rf64 > hf, np.float32(-np.inf), np.float32(np.inf)).astype(np.float32))
-        tie = (hf == (rf64 + other.astype(np.float64)) * 0.5) & (lf != 0)
-        side = np.where(lf > 0, np.maximum(rf, other), np.minimum(rf, other))
-        r.flat[cand] = np.where(tie, side, rf)
-    return r
+IBCS_TIE_EPS = 1e-5
 
 
-def _sq_dist_f32(x: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """Squared Euclidean distances [G, n, k] between the rows of x [G, n, d] and of c
-    [G, k, d] in float32: per coordinate, in index order, the difference rounded to
-    float32, then its square added to the running sum by one fused multiply-add."""
-    G, n, d = x.shape
-    k = c.shape[1]
-    acc = np.zeros((G, n, k), dtype=np.float32)
-    for e in range(d):
-        diff = (x[:, :, None, e] - c[:, None, :, e]).astype(np.float32)
-        acc = fma_f32(diff, diff, acc)
-    return acc
+def ibcs_clusters(qgroup: np.ndarray, n_clusters: int = IBCS_CLUSTERS, iters: int = IBCS_ITERS,
+                  return_gap: bool = False):
+    """Lloyd's k-means of one group of n queries ([n, d]), or of a batch of groups
+    ([G, n, d]), into n_clusters clusters each, in float64.
 
+    Readings (the page gives the cluster count, not the algorithm's steps): the initial
+    centroids are the queries at rows 0, n/k, 2n/k, ...; ``iters`` rounds of
+    assign-then-update; a query joins the centroid at the smallest squared Euclidean
+    distance (ties to the lowest cluster index); a centroid moves to the mean of its
+    queries, and an empty cluster keeps its centroid.  Returns (centroids [..., k, d],
+    weights [..., k] = fraction of the group's queries in each cluster under the last
+    assignment).
 
-def ibcs_clusters(qgroup: np.ndarray, n_clusters: int = IBCS_CLUSTERS, iters: int = IBCS_ITERS):
-    """k-means of one group of n queries ([n, d]), or of a batch of groups ([G, n, d]),
-    into n_clusters clusters each.
-
-    Readings (the page gives the cluster count, not the algorithm's steps): Lloyd's
-    algorithm; initial centroids are the queries at rows 0, n/k, 2n/k, ...; ``iters``
-    rounds of assign-then-update; a query joins its nearest centroid by squared
-    Euclidean distance (_sq_dist_f32), ties to the lowest cluster index; a centroid
-    becomes the mean of its queries (a float32 running sum from 0 over its queries in
-    row order, then one division by their count), and an empty cluster keeps its
-    centroid.  Returns (centroids [..., k, d] float32, weights [..., k] = fraction of the
-    group's queries in each cluster under the last assignment)."""
-    x = np.asarray(qgroup, dtype=np.float32)
+    With ``return_gap`` a third value gives, per group, the smallest relative margin
+    (second-smallest minus smallest squared distance, over the second-smallest) of any
+    query in any round.  An assignment whose margin is below a few float32 rounding
+    errors of a d-term sum can come out either way in float32 arithmetic."""
+    x = np.asarray(qgroup, dtype=np.float64)
     single = x.ndim == 2
     if single:
         x = x[None]
     G, n, d = x.shape
     k = n_clusters
     cent = x[:, np.arange(k) * (n // k)].copy()
+    gap = np.full(G, np.inf)
     assign = np.zeros((G, n), dtype=np.int64)
-    zero_row = np.zeros((G, 1, d), dtype=np.float32)
     for _ in range(iters):
-        assign = np.argmin(_sq_dist_f32(x, cent), axis=2)      # first minimum: lowest index on ties
+        dist = np.stack([np.sum((x - cent[:, c:c + 1, :]) ** 2, axis=-1) for c in range(k)], axis=-1)
+        assign = np.argmin(dist, axis=-1)                    # first minimum: lowest index on ties
+        two = np.sort(dist, axis=-1)[..., :2]
+        margin = (two[..., 1] - two[..., 0]) / np.maximum(two[..., 1], np.finfo(np.float64).tiny)
+        gap = np.minimum(gap, margin.min(axis=-1))
         for c in range(k):
             member = assign == c
             count = member.sum(axis=1)
-            # 0, then the members in row order; rows of other clusters add +0, which
-            # leaves a float32 sum started at +0 unchanged
-            rows = np.concatenate([zero_row, np.where(member[..., None], x, np.float32(0))], axis=1)
-            total = np.add.accumulate(rows, axis=1, dtype=np.float32)[:, -1]
+            total = np.where(member[..., None], x, 0.0).sum(axis=1)
             has = count > 0
-            cent[has, c] = (total[has] / count[has].astype(np.float32)[:, None]).astype(np.float32)
+            cent[has, c] = total[has] / count[has][:, None]
     weights = np.stack([np.bincount(a, minlength=k) for a in assign]).astype(np.float64) / n
+    out = (cent, weights, gap)
     if single:
-        return cent[0], weights[0]
-    return cent, weights
+        out = (cent[0], weights[0], gap[0])
+    return out if return_gap else out[:2]
 
 
 def ibcs_scores(q: np.ndarray, k: np.ndarray, N: int, scale: Optional[float] = None,
-                qn: Optional[int] = None) -> np.ndarray:
-    """IBCS block scores for [..., L, d] Q, K in fractal order.
+                qn: Optional[int] = None, return_gap: bool = False):
+    """IBCS block scores for [..., L, d] Q, K in fractal order, in float64.
 
     The queries are taken in groups of qn consecutive tokens (default N; the page's
     setting is 128) and each group is clustered (ibcs_clusters).  With centroids mu_c and
@@ -448,7 +412,8 @@ def ibcs_scores(q: np.ndarray, k: np.ndarray, N: int, scale: Optional[float] = N
         A_ij = sum_c w_c softmax_j(scale * mu_c . Kp_j),
     Kp_j the mean key of N-token block j: the weighted attention of the centroids to the
     mean keys.  The qn / N blocks of a group share one row.  Rows sum to one like NABLA's
-    pooled softmax, so the same CDF cut applies."""
+    pooled softmax, so the same CDF cut applies.  With ``return_gap`` also the clustering
+    margin of each row's group ([..., nb], see ibcs_clusters)."""
     d = q.shape[-1]
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     L = q.shape[-2]
@@ -458,27 +423,31 @@ def ibcs_scores(q: np.ndarray, k: np.ndarray, N: int, scale: Optional[float] = N
     nb = L // N
     per = qn // N
     lead = q.shape[:-2]
-    qf = np.asarray(q, dtype=np.float32).reshape((-1, L, d))
+    qf = np.asarray(q, dtype=np.float64).reshape((-1, L, d))
     kp = block_mean(np.asarray(k).reshape((-1, L, d)), N, np.float64)
     A = np.zeros((qf.shape[0], nb, nb))
+    gap = np.zeros((qf.shape[0], nb))
     for g in range(qf.shape[0]):
-        cents, ws = ibcs_clusters(qf[g].reshape(L // qn, qn, d))              # every group of the head
+        cents, ws, gg = ibcs_clusters(qf[g].reshape(L // qn, qn, d), return_gap=True)   # every group of the head
+        gap[g] = np.repeat(gg, per)
         for gi in range(L // qn):
-            S = (cents[gi].astype(np.float64) @ kp[g].T) * scale                 # [k, nb]
+            S = (cents[gi] @ kp[g].T) * scale                                    # [k, nb]
             P = np.exp(S - S.max(axis=1, keepdims=True))
             P /= P.sum(axis=1, keepdims=True)
             A[g, gi * per:(gi + 1) * per] = ws[gi] @ P
-    return A.reshape(lead + (nb, nb))
+    A = A.reshape(lead + (nb, nb))
+    return (A, gap.reshape(lead + (nb,))) if return_gap else A
 
 
 def ibcs_block_mask(q: np.ndarray, k: np.ndarray, N: int, thr: float,
                     scale: Optional[float] = None, qn: Optional[int] = None) -> Dict[str, np.ndarray]:
     """NABLA's CDF cut on the IBCS scores: keep block j of row i iff the mass of the
-    blocks scoring at most A_ij exceeds thr.  Returns mask, F and A."""
-    A = ibcs_scores(q, k, N, scale, qn)
+    blocks scoring at most A_ij exceeds thr.  Returns mask, F, A (the scores rounded to
+    float32, where the cut is taken) and gap (each row's clustering margin)."""
+    A, gap = ibcs_scores(q, k, N, scale, qn, return_gap=True)
     A32 = A.astype(np.float32)
     F = cdf_values(A32)
-    return {"mask": F > F.dtype.type(thr), "F": F, "A": A32}
+    return {"mask": F > F.dtype.type(thr), "F": F, "A": A32, "gap": gap}
 
 
 # ---------------------------------------------------------------------------

@@ -203,6 +203,34 @@ def pin_sta_brute():
     assert np.array_equal(M, ref)
 
 
+def pin_sta_union():
+    """M = M_nabla OR M_STA: the mask with a window is the CDF mask with every block of
+    the window added, so it contains each part, and on a grid where each part holds
+    blocks the other lacks it is strictly larger than both.  The window part is
+    enumerated here from tile coordinates (block i = (t*nH + h)*nW + w, its 1 x P x P
+    tile), independently of sta_mask."""
+    rng = _rng(12)
+    T, H, W, P, N, d = 3, 16, 24, 8, 64, 16
+    nH, nW = H // P, W // P
+    L = T * H * W
+    base = rng.standard_normal((1, L, d)).astype(np.float32)
+    q = (base + 0.3 * rng.standard_normal((1, L, d))).astype(np.float32)
+    k = (base + 0.3 * rng.standard_normal((1, L, d))).astype(np.float32)
+    win = (1, 3, 1)
+    plain = O.block_mask(q, k, T, H, W, P, N, 0.3)
+    both = O.block_mask(q, k, T, H, W, P, N, 0.3, sta=win)
+    nb = T * nH * nW
+    ref = np.zeros((nb, nb), dtype=bool)
+    for (t1, h1, w1), (t2, h2, w2) in itertools.product(
+            itertools.product(range(T), range(nH), range(nW)), repeat=2):
+        ref[(t1 * nH + h1) * nW + w1, (t2 * nH + h2) * nW + w2] = t1 == t2 and abs(h1 - h2) <= 1 and w1 == w2
+    m_cdf = plain["mask"][0]
+    assert np.array_equal(both["mask_nabla"][0], m_cdf)
+    assert np.array_equal(both["mask"][0], m_cdf | ref)
+    assert np.all(both["mask"][0] >= m_cdf) and np.all(both["mask"][0] >= ref)
+    assert (ref & ~m_cdf).any() and (m_cdf & ~ref).any(), "each part must add blocks the other lacks"
+
+
 # ---------------------------------------------------------------- lists
 
 def pin_kv_lists():
@@ -515,55 +543,6 @@ def pin_sip_full_budget_is_plain_attention():
 
 # ---------------------------------------------------------------- IBCS (intra-block clustering)
 
-def _round_f32_exact(v):
-    """Nearest float32 to the rational v, ties to the even significand (from the
-    definition, by exact comparison of the candidates)."""
-    from fractions import Fraction
-    f = np.float32(float(v))
-    best = None
-    for c in (f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))):
-        key = (abs(Fraction(float(c)) - v), int(np.array(c).view(np.uint32)) & 1)
-        if best is None or key < best[0]:
-            best = (key, c)
-    return best[1]
-
-
-def pin_fma_f32_is_correctly_rounded():
-    """fma_f32 against exact rational arithmetic: random products (squares among them)
-    and sums over a wide range of exponents, and constructed cases where the float64 sum
-    lands exactly on a float32 midpoint that the exact sum is not on (where rounding
-    twice goes wrong)."""
-    from fractions import Fraction
-    rng = _rng(46)
-    n = 3000
-    a = (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n))).astype(np.float32)
-    b = np.where(rng.random(n) < 0.5, a, (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n)))).astype(np.float32)
-    c = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32)
-    got = O.fma_f32(a, b, c)
-    for i in range(n):
-        v = Fraction(float(a[i])) * Fraction(float(b[i])) + Fraction(float(c[i]))
-        assert got[i] == _round_f32_exact(v), (a[i], b[i], c[i])
-    # ties: c + X with X an odd multiple of half c's float32 spacing, a b = X + (tiny)
-    ties = []
-    for _ in range(400000):
-        c1 = np.float32(np.ldexp(1.0 + rng.integers(0, 2 ** 23) / 2 ** 23, int(rng.integers(-10, 10))))
-        X = (2 * int(rng.integers(0, 2 ** 10)) + 1) * np.float64(np.spacing(c1)) / 2
-        a1 = np.float32(np.sqrt(X) * (1 + rng.standard_normal() * 1e-3))
-        b1 = np.float32(X / np.float64(a1))
-        exact = Fraction(float(a1)) * Fraction(float(b1)) + Fraction(float(c1))
-        if np.float64(a1) * np.float64(b1) + np.float64(c1) == np.float64(c1) + X and exact != Fraction(float(c1) + X):
-            ties.append((a1, b1, c1, exact))
-            if len(ties) == 12:
-                break
-    assert len(ties) == 12
-    ta, tb, tc = (np.array([t[i] for t in ties], dtype=np.float32) for i in range(3))
-    got = O.fma_f32(ta, tb, tc)
-    twice = (ta.astype(np.float64) * tb + tc).astype(np.float32)
-    want = [_round_f32_exact(t[3]) for t in ties]
-    assert all(g == w for g, w in zip(got, want))
-    assert any(t != w for t, w in zip(twice, want)), "the constructed cases must separate the two roundings"
-
-
 def pin_ibcs_identical_queries_is_block_mean():
     """A block whose queries are all equal forms one cluster whose centroid is the block
     mean: IBCS's row is then exactly NABLA's pooled softmax row."""
@@ -578,14 +557,12 @@ def pin_ibcs_identical_queries_is_block_mean():
     S = qp @ kp.transpose(0, 2, 1) * 0.3
     ref = np.exp(S - S.max(-1, keepdims=True))
     ref /= ref.sum(-1, keepdims=True)
-    # the centroid is a float32 running sum of 64 equal queries over 64, which may round
-    # away from the query by a few float32 ulps
-    assert np.max(np.abs(A - ref)) <= 1e-6
+    assert np.max(np.abs(A - ref)) <= 1e-12
     for i in range(nb):
-        _, w = O.ibcs_clusters(q[0, i * N:(i + 1) * N])
-        # one cluster holds the whole block (which one depends on float32 rounding of the
-        # running mean: a query ties at distance 0 with the untouched initial centroids)
-        assert np.count_nonzero(w) == 1 and w.max() == 1.0
+        cent, w = O.ibcs_clusters(q[0, i * N:(i + 1) * N])
+        # every distance ties at 0, so every query joins cluster 0, whose mean is the query
+        assert w[0] == 1.0 and np.all(w[1:] == 0.0)
+        assert np.array_equal(cent[0], q[0, i * N].astype(np.float64))
 
 
 def pin_ibcs_separated_groups():
@@ -613,7 +590,12 @@ def pin_ibcs_matches_library_kmeans():
         init = x[np.arange(8) * 8].astype(np.float64)
         km = KMeans(n_clusters=8, init=init, n_init=1, max_iter=O.IBCS_ITERS, tol=0.0,
                     algorithm="lloyd").fit(x.astype(np.float64))
-        assert np.max(np.abs(cent - km.cluster_centers_)) <= 1e-5, trial
+        assert np.max(np.abs(cent - km.cluster_centers_)) <= 1e-10, trial
+        # the weights come from the last assignment, the one made against the centroids of
+        # the previous round: scikit-learn's final labels after one round fewer
+        km3 = KMeans(n_clusters=8, init=init, n_init=1, max_iter=O.IBCS_ITERS - 1, tol=0.0,
+                     algorithm="lloyd").fit(x.astype(np.float64))
+        assert np.array_equal(w, np.bincount(km3.labels_, minlength=8) / N), trial
 
 
 def pin_ibcs_matches_library_kmeans_128():
@@ -631,7 +613,7 @@ def pin_ibcs_matches_library_kmeans_128():
         # (scikit-learn's labels_ come from one more assignment against the final
         # centres; the weights here are those of the assignment that made them, which
         # the closed-form pin below checks)
-        assert np.max(np.abs(cent - km.cluster_centers_)) <= 1e-5, trial
+        assert np.max(np.abs(cent - km.cluster_centers_)) <= 1e-10, trial
 
 
 def pin_ibcs_group128_scores_closed_form():
@@ -661,6 +643,35 @@ def pin_ibcs_group128_scores_closed_form():
             assert np.max(np.abs(A[0, b] - ref)) <= 1e-5, (gi, b)
     A64 = O.ibcs_scores(q, k, N, scale)
     assert np.max(np.abs(A64 - A)) > 1e-3
+
+
+def pin_ibcs_margin_closed_form():
+    """The clustering margin of a group (second-smallest minus smallest squared distance,
+    over the second-smallest, minimised over queries and rounds) in closed form: eight
+    distinct queries that are themselves the eight initial centroids each sit at distance
+    0 from their own centroid, so every margin is exactly 1 and each cluster keeps one
+    query; a query repeated at rows 0 and 1 ties at distance 0 between clusters 0 and 1,
+    so the margin is 0, both copies join cluster 0 (lowest index on ties) and cluster 1
+    stays empty."""
+    rng = _rng(47)
+    x = rng.standard_normal((8, 5)) * 3
+    cent, w, gap = O.ibcs_clusters(x, return_gap=True)
+    assert gap == 1.0 and np.all(w == 1.0 / 8)
+    assert np.array_equal(cent, x)
+    y = x.copy()
+    y[1] = y[0]
+    cent, w, gap = O.ibcs_clusters(y, return_gap=True)
+    assert gap == 0.0
+    assert w[0] == 2.0 / 8 and w[1] == 0.0 and np.all(w[2:] == 1.0 / 8)
+    # batched form, per group, and per row of ibcs_scores (both query blocks of a group)
+    cents, ws, gaps = O.ibcs_clusters(np.stack([x, y]), return_gap=True)
+    assert np.array_equal(gaps, [1.0, 0.0])
+    q = np.concatenate([np.repeat(x, 8, axis=0), np.repeat(y, 8, axis=0)])[None]     # 2 groups of 64
+    k = rng.standard_normal((1, 128, 5))
+    A, g = O.ibcs_scores(q, k, 64, qn=64, return_gap=True)
+    # each group of 64 holds 8 copies of each of its rows: rows 0, 8, ..., 56 are the
+    # initial centroids, all distinct in the first group (margin 1) and tied in the second
+    assert np.array_equal(g[0], [1.0, 0.0])
 
 
 def pin_ibcs_rows_and_threshold():

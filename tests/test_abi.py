@@ -151,6 +151,8 @@ def attn(lib, q=A, k=B_, v=C, o=D_, batch=1, heads=2, L=1024, d=64, N=64, cnt=E,
     (dict(dt=3), NABLA_E_INVAL),
     (dict(N=128), NABLA_E_UNSUPPORTED),
     (dict(d=256), NABLA_E_UNSUPPORTED),
+    (dict(L=1 << 23, d=128), NABLA_E_UNSUPPORTED),       # one head = 2^31 bytes of bf16
+    (dict(L=1 << 22, d=128, dt=NABLA_F32), NABLA_E_UNSUPPORTED),
 ])
 def test_attn_validation(lib, kw, status):
     assert attn(lib, **kw) == status
@@ -217,6 +219,7 @@ def attn_bwd(lib, **kw):
     (dict(N=32), NABLA_E_UNSUPPORTED),
     (dict(d=32), NABLA_E_UNSUPPORTED),
     (dict(L=64 * 2049), NABLA_E_UNSUPPORTED),
+    (dict(L=1 << 23, d=128), NABLA_E_UNSUPPORTED),
     (dict(ws=None), NABLA_E_WORKSPACE),
     (dict(ws_bytes=1000), NABLA_E_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x100010)), NABLA_E_INVAL),
@@ -366,3 +369,26 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 1024, 64)
     with pytest.raises(ValueError):
         nb_lib.reorder(x, 4, 16, 16, 8)
+
+
+def test_binding_checks_mask_shapes_before_pointers():
+    """The mask wrappers check the token count against T*H*W and the caller's output
+    buffers (dtype, size) before taking any pointer: the library sizes its lists from
+    T*H*W, so a mismatch would write lists with another stride into q-sized buffers."""
+    import torch
+    q = torch.zeros(1, 2, 1024, 64)
+    with pytest.raises(ValueError, match="does not match T\\*H\\*W"):
+        nb_lib.build_mask(q, q, 4, 16, 8, 8)                       # T*H*W = 512
+    with pytest.raises(ValueError, match="does not match T\\*H\\*W"):
+        nb_lib.build_mask_sip(q, q, 2, 16, 16, 8, 4, torch.zeros(1, 2, 16, 16))
+    with pytest.raises(ValueError, match="same shape"):
+        nb_lib.build_mask(q, torch.zeros(1, 2, 1024, 32), 4, 16, 16, 8)
+    with pytest.raises(TypeError, match="kv_count must be int32"):
+        nb_lib.build_mask(q, q, 4, 16, 16, 8, kv_count=torch.zeros(1, 2, 16, dtype=torch.int64))
+    with pytest.raises(ValueError, match="kv_index holds"):
+        nb_lib.build_mask(q, q, 4, 16, 16, 8, kv_index=torch.zeros(1, 2, 16, 15, dtype=torch.int32))
+    with pytest.raises(ValueError, match="schedule holds"):
+        nb_lib.build_mask(q, q, 4, 16, 16, 8, schedule=torch.zeros(31, dtype=torch.int32))
+    with pytest.raises(ValueError, match="sizes do not match"):
+        nb_lib.attn_fwd_raster(q, q, q, torch.zeros(1, 2, 16, dtype=torch.int32),
+                               torch.zeros(1, 2, 16, 16, dtype=torch.int32)[..., :8].contiguous(), 4, 16, 16, 8)

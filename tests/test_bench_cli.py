@@ -36,8 +36,31 @@ def test_traffic_figure_only_for_its_workload_and_kernel():
     bench line reports its traffic as unknown rather than borrowing it."""
     sys.path.insert(0, ROOT)
     import bench
-    t = bench.read_traffic("wan1.3b_480p", "attn_fwd_bf16_kernel<128, raster>")
+    kv = {}
+    for ln in open(bench.TRAFFIC_FILE):
+        if ":" in ln and not ln.lstrip().startswith("#"):
+            key, val = ln.split(":", 1)
+            kv[key.strip()] = val.strip()
+    own = (kv["workload"], kv["kernel"])
+    t = bench.read_traffic(*own)
     assert t is None or t > 0
-    assert bench.read_traffic("tiny", "attn_fwd_f32_kernel<64, raster>") is None
-    assert bench.read_traffic("wan1.3b_480p", "attn_fwd_bf16_kernel<128, fractal>") is None
-    assert bench.read_traffic("hunyuan_720p_sta", "attn_fwd_bf16_kernel<128, raster>") is None
+    for other in [("tiny", "attn_fwd_f32_kernel<64, raster>"), ("wan14b_720p_cfg", "attn_fwd_bf16_kernel<128, fractal>"),
+                  ("hunyuan_720p_sta", "attn_fwd_bf16_kernel<128, raster>"), ("wan1.3b_480p", "attn_fwd_bf16_kernel<128, fractal>"),
+                  ("wan14b_720p_cfg", "attn_fwd_bf16_kernel<128, raster>"), ("wan1.3b_480p", "attn_fwd_bf16_kernel<128, raster>")]:
+        if other != own:
+            assert bench.read_traffic(*other) is None, other
+
+
+def test_cpu_baseline_is_bounded_and_extrapolated():
+    """The oracle baseline on a tiny budget: a sample of heads and query blocks, scaled
+    to the whole step and flagged as extrapolated."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from synth import get_config, make_qkv
+    cfg = get_config("wan1.3b_480p")
+    q, k, v = make_qkv(cfg, pairs=[(0, 0), (0, cfg.heads - 1)])
+    cb = bench.cpu_baseline(cfg, q, k, v, kept_flops_total=1.0e6 * 4 * 64 * 64 * 128, budget_s=0.5,
+                            blocks_per_head=4)
+    assert cb["extrapolated"] is True and cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s"
+    assert cb["value"] > 0 and cb["cores"] >= 1
+    assert "of 12 (batch, head) slices" in cb["sample"]

@@ -1,12 +1,16 @@
 """GPU parity of the IBCS block scores (8 query clusters per block scoring the mean keys)
 against the oracle.
 
-The clustering is a fixed sequence of individually rounded float32 operations, so the
-centroids and weights the kernels leave in the workspace ([Kp | centroids | weights |
-scores], sections 256-byte aligned) must equal the oracle's bit for bit.  The scores are
-float32 on the GPU (MFMA map, exp2 softmax) and float64 in the oracle: within
-A_TOL relative to the row's largest score.  The mask must equal the oracle's CDF cut of
-its scores except at the cutoff (the band of the NABLA mask test)."""
+The oracle clusters in float64 (plain Lloyd's k-means); the kernels cluster in float32.
+An assignment whose two nearest centroids are closer than float32 can resolve may go
+either way, after which the two clusterings part.  So per query group: where the oracle's
+clustering margin (relative gap between the nearest and second-nearest squared distance,
+smallest over queries and rounds) is below IBCS_TIE_EPS the group is a near tie, counted
+and capped at 2% of groups (at least 2) and left out of the comparison; every other group
+must carry the oracle's weights exactly and its centroids within CENT_RTOL.  The scores
+are float32 on the GPU (MFMA map, exp2 softmax) and float64 in the oracle: within A_TOL
+relative to the row's largest score.  The mask must equal the oracle's CDF cut of its
+scores except at the cutoff (the band of the NABLA mask test)."""
 from __future__ import annotations
 
 import sys
@@ -26,6 +30,9 @@ K = O.IBCS_CLUSTERS
 # float32 logits of size ~10 carry ~1e-6 absolute error, a relative error of ~1e-6 in
 # each softmax value; the weighted sum of 8 keeps it there.  20x slack.
 A_TOL = 2e-5
+# a float32 mean of at most 128 queries, the sum rounded once per query: below
+# 128 * 2^-24 ~ 7.6e-6 of the largest coordinate in the worst case (measured ~5e-8)
+CENT_RTOL = 8e-6
 
 
 def say(*a):
@@ -75,21 +82,29 @@ def score_err(gpu_A, ref_A):
 
 
 def check_clusters(res, qf_np, qn, heads):
-    """Centroids bit for bit, weights exactly, for every query group of the given heads
-    (the oracle clusters all groups of a head at once)."""
+    """Per query group of the given heads (the oracle clusters all groups of a head at
+    once): near-tie groups counted, every other group's weights exactly and centroids
+    within CENT_RTOL.  Returns (groups, near-tie groups, per head a [nb] bool of the query
+    blocks whose group is a near tie)."""
     ng = res["cent"].shape[1]
     d = qf_np.shape[-1]
-    n = 0
+    per = qn // 64
+    n = n_tie = 0
+    tie_rows = []
     for g in heads:
-        cent, w = O.ibcs_clusters(qf_np[g, :ng * qn].reshape(ng, qn, d))
-        gc = res["cent"][g]
-        same = np.all(gc.view(np.uint32) == cent.view(np.uint32), axis=(1, 2))
-        assert same.all(), (
-            f"head {g}: centroids of {int((~same).sum())} groups differ, first {int(np.argmin(same))}, "
-            f"max-abs {np.max(np.abs(gc - cent)):.3e}")
-        assert np.array_equal(res["w"][g].astype(np.float64), w), g
+        cent, w, gap = O.ibcs_clusters(qf_np[g, :ng * qn].reshape(ng, qn, d), return_gap=True)
+        tie = gap < O.IBCS_TIE_EPS
+        ok = ~tie
+        gc = res["cent"][g].astype(np.float64)
+        assert np.array_equal(res["w"][g][ok].astype(np.float64), w[ok]), (
+            f"head {g}: weights of {int((res['w'][g][ok] != w[ok]).any(-1).sum())} groups differ")
+        rel = np.max(np.abs(gc - cent), axis=(1, 2)) / np.max(np.abs(cent), axis=(1, 2))
+        assert np.all(rel[ok] <= CENT_RTOL), f"head {g}: centroid rel err {rel[ok].max():.3e}"
         n += ng
-    return n
+        n_tie += int(tie.sum())
+        tie_rows.append(np.repeat(tie, per))
+    assert n_tie <= max(2, int(np.ceil(0.02 * n))), f"{n_tie} of {n} groups are near ties"
+    return n, n_tie, np.stack(tie_rows)
 
 
 def oracle_mask(cfg, qf_np, kf_np, thr, sta=None, qn=128):
@@ -98,6 +113,16 @@ def oracle_mask(cfg, qf_np, kf_np, thr, sta=None, qn=128):
     if sta is not None:
         mask = mask | O.sta_mask(cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, sta)[None]
     return mask, ref["A"]
+
+
+def compare_rows(res_A, res_mask, ref_A, ref_m, tie_rows, thr):
+    """Scores within A_TOL and the mask by the band rule on the rows whose group is not a
+    near tie; returns (score error, mask mismatches, band population)."""
+    keep = ~tie_rows
+    err = score_err(res_A[keep], ref_A[keep])
+    assert err <= A_TOL, err
+    mism, band = check_mask(res_mask[keep], ref_m[keep], ref_A[keep], thr)
+    return err, mism, band
 
 
 CASES = [
@@ -123,13 +148,11 @@ def test_ibcs_parity(cfg, qn):
     res = gpu_ibcs(cfg, qf, kf, cfg.thr, cfg.sta, qn)
     qnp = qf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)
     knp = kf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)
-    n = check_clusters(res, qnp, qn, range(G))
+    n, n_tie, tie_rows = check_clusters(res, qnp, qn, range(G))
     ref_m, ref_A = oracle_mask(cfg, qnp, knp, cfg.thr, cfg.sta, qn)
-    err = score_err(res["A"], ref_A)
-    assert err <= A_TOL, err
+    err, mism, band = compare_rows(res["A"], res["mask"], ref_A, ref_m, tie_rows, cfg.thr)
     assert np.allclose(res["A"].sum(-1), 1.0, atol=1e-5)
-    mism, band = check_mask(res["mask"], ref_m, ref_A, cfg.thr)
-    say(f"  {n} groups' centroids bit-identical; scores rel err {err:.2e}; kept {res['mask'].mean():.3f}, "
+    say(f"  {n} groups ({n_tie} near ties); scores rel err {err:.2e}; kept {res['mask'].mean():.3f}, "
         f"mask mismatches {mism}, band {band}")
     # the top block of every row is kept, as in NABLA
     top = np.argmax(ref_A, axis=-1)
@@ -197,13 +220,11 @@ def test_ibcs_full_size(qn):
     qnp = qf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)[heads]
     knp = kf.float().cpu().numpy().reshape(G, cfg.L, cfg.d)[heads]
     sub = dict(cent=res["cent"][heads], w=res["w"][heads])
-    n = check_clusters(sub, qnp, qn, range(len(heads)))
-    say(f"  {n} groups' centroids bit-identical")
+    n, n_tie, tie_rows = check_clusters(sub, qnp, qn, range(len(heads)))
     ref_m, ref_A = oracle_mask(cfg, qnp, knp, cfg.thr, qn=qn)
-    err = score_err(res["A"][heads], ref_A)
-    assert err <= A_TOL, err
-    mism, band = check_mask(res["mask"][heads], ref_m, ref_A, cfg.thr)
-    say(f"  heads {heads}: scores rel err {err:.2e}, mask mismatches {mism}, band {band}")
+    err, mism, band = compare_rows(res["A"][heads], res["mask"][heads], ref_A, ref_m, tie_rows, cfg.thr)
+    say(f"  heads {heads}: {n} groups ({n_tie} near ties), scores rel err {err:.2e}, mask mismatches {mism}, "
+        f"band {band}")
 
 
 @pytest.mark.parametrize("qn", [128, 64])
@@ -219,12 +240,10 @@ def test_ibcs_max_blocks_per_head(qn):
     res = gpu_ibcs(cfg, qf, kf, cfg.thr, qn=qn)
     qnp = qf.float().cpu().numpy().reshape(1, cfg.L, cfg.d)
     knp = kf.float().cpu().numpy().reshape(1, cfg.L, cfg.d)
-    n = check_clusters(res, qnp, qn, [0])
+    n, n_tie, tie_rows = check_clusters(res, qnp, qn, [0])
     ref_m, ref_A = oracle_mask(cfg, qnp, knp, cfg.thr, qn=qn)
-    err = score_err(res["A"], ref_A)
-    assert err <= A_TOL, err
-    mism, band = check_mask(res["mask"], ref_m, ref_A, cfg.thr)
-    say(f"  {n} groups' centroids bit-identical; scores rel err {err:.2e}; kept {res['mask'].mean():.4f}, "
+    err, mism, band = compare_rows(res["A"], res["mask"], ref_A, ref_m, tie_rows, cfg.thr)
+    say(f"  {n} groups ({n_tie} near ties); scores rel err {err:.2e}; kept {res['mask'].mean():.4f}, "
         f"mask mismatches {mism}, band {band}")
 
 

@@ -148,7 +148,11 @@ def test_ibcs_sip_parity(cfg, qn):
     qd, kd = q.cuda(), k.cuda()
     qf, kf = (nab.reorder(t, cfg.T, cfg.H, cfg.W, cfg.P) for t in (qd, kd))
     qnp, knp = (t.float().cpu().numpy().reshape(G, cfg.L, cfg.d) for t in (qf, kf))
-    A = O.ibcs_scores(qnp, knp, cfg.N, qn=qn)
+    A, gap = O.ibcs_scores(qnp, knp, cfg.N, qn=qn, return_gap=True)
+    # rows whose query group is a float32 near tie of the clustering are left out (see
+    # test_gpu_ibcs.py); at most 2% of groups, at least 2
+    keep = gap >= O.IBCS_TIE_EPS
+    assert (~keep).sum() <= max(2, int(np.ceil(0.02 * keep.size))) * (qn // cfg.N)
     for budget in (1, max(2, nb // 6), nb // 2, nb):
         u = torch.rand((cfg.B, cfg.heads, nb, nb), generator=torch.Generator().manual_seed(budget + 100))
         cnt, idx, logw, bm = nab.build_mask_sip(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, budget, u.cuda(), cfg.N,
@@ -162,9 +166,10 @@ def test_ibcs_sip_parity(cfg, qn):
         for g in range(G):
             for i in range(nb):
                 dense_w[g, i, ix[g, i, :cn[g, i]]] = lw[g, i, :cn[g, i]]
-        res = dict(mask=m, u=u.numpy().reshape(G, nb, nb), dense_w=dense_w, cnt=cnt)
-        ref_m, ref_w, ref_pi = O.sip_mask(A, budget, res["u"])
-        mism, err_w = check_sip(res, ref_m, ref_w, ref_pi, budget)
+        un = u.numpy().reshape(G, nb, nb)
+        ref_m, ref_w, ref_pi = O.sip_mask(A, budget, un)
+        res = dict(mask=m[keep], u=un[keep], dense_w=dense_w[keep], cnt=cnt.reshape(G, nb)[torch.from_numpy(keep).cuda()])
+        mism, err_w = check_sip(res, ref_m[keep], ref_w[keep], ref_pi[keep], budget)
         say(f"IBCS+SIP {cfg.name} q_group {qn} budget {budget}: mean kept {m.sum(-1).mean():.2f}, "
             f"band mismatches {mism}, logw err {err_w:.2e}")
         vf = nab.reorder(v.cuda(), cfg.T, cfg.H, cfg.W, cfg.P)

@@ -176,14 +176,37 @@ def _ibcs_softmax_over_centroids(q, k, N, scale=None):
     return np.exp(A) / np.exp(A).sum(-1, keepdims=True)
 
 
-def _fma_rounded_twice(a, b, c):
-    # float64 sum rounded to float32: two roundings instead of one
-    return (np.asarray(a, np.float64) * np.asarray(b, np.float64) + np.asarray(c, np.float64)).astype(np.float32)
-
-
 def _ibcs_group_ignored(q, k, N, scale=None, qn=None):
     # every 64-token block clustered on its own, whatever the group size
     return _orig_ibcs_scores(q, k, N, scale)
+
+
+_orig_block_mask = O.block_mask
+
+
+def _block_mask_and(q, k, T, H, W, P, N, thr, sta=None, scale=None, dtype=np.float32):
+    # the window intersected with the CDF mask instead of joined to it
+    res = _orig_block_mask(q, k, T, H, W, P, N, thr, None, scale, dtype)
+    if sta is not None:
+        res["mask"] = res["mask_nabla"] & O.sta_mask(T, H, W, P, N, sta)
+    return res
+
+
+def _ibcs_gap_unscaled(qgroup, n_clusters=8, iters=4, return_gap=False):
+    # the margin taken as an absolute difference, not relative to the distance
+    out = _orig_ibcs_clusters(qgroup, n_clusters, iters, return_gap=True)
+    if not return_gap:
+        return out[:2]
+    x = np.asarray(qgroup, dtype=np.float64)
+    return out[0], out[1], out[2] * float(np.sum(x[..., :1, :] ** 2) + 1.0)
+
+
+def _ibcs_last_round_weights_off(qgroup, n_clusters=8, iters=4, return_gap=False):
+    # weights from the assignment one round earlier than the centroids' last update
+    out = _orig_ibcs_clusters(qgroup, n_clusters, max(iters - 1, 1), return_gap=True)
+    cent = _orig_ibcs_clusters(qgroup, n_clusters, iters)[0]
+    res = (cent, out[1], out[2])
+    return res if return_gap else res[:2]
 
 
 MUTATIONS = [
@@ -211,7 +234,9 @@ MUTATIONS = [
     ("ibcs_clusters", _ibcs_first_rows_init),
     ("ibcs_scores", _ibcs_softmax_over_centroids),
     ("ibcs_scores", _ibcs_group_ignored),
-    ("fma_f32", _fma_rounded_twice),
+    ("block_mask", _block_mask_and),
+    ("ibcs_clusters", _ibcs_gap_unscaled),
+    ("ibcs_clusters", _ibcs_last_round_weights_off),
 ]
 
 
