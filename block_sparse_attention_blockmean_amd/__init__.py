@@ -8,12 +8,14 @@ device tensors, pass their pointers and the current HIP stream to the C ABI in
 """
 from ._binding import (
     EXPORTS, LIB_PATH, NablaError, StaWindow, attn_bwd, attn_bwd_workspace_size, attn_fwd,
-    attn_fwd_raster, attn_fwd_weighted, build_mask, build_mask_sip, build_mask_workspace_size,
+    attn_fwd_raster, attn_fwd_weighted, build_mask, build_mask_raster_noalloc, build_mask_sip,
+    build_mask_workspace_size,
     load_library, reorder,
 )
 
 __all__ = [
     "EXPORTS", "LIB_PATH", "NablaError", "StaWindow", "attn_bwd", "attn_bwd_workspace_size",
-    "attn_fwd", "attn_fwd_raster", "attn_fwd_weighted", "build_mask", "build_mask_sip",
+    "attn_fwd", "attn_fwd_raster", "attn_fwd_weighted", "build_mask", "build_mask_raster_noalloc",
+    "build_mask_sip",
     "build_mask_workspace_size", "load_library", "reorder",
 ]

@@ -24,6 +24,7 @@ EXPORTS = (
     "nabla_build_mask_workspace_size",
     "nabla_build_mask",
     "nabla_build_mask_raster",
+    "nabla_build_mask_raster_noalloc",
     "nabla_build_mask_sip",
     "nabla_build_mask_ibcs_workspace_size",
     "nabla_build_mask_ibcs",
@@ -71,6 +72,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_build_mask.restype = i
     lib.nabla_build_mask_raster.argtypes = lib.nabla_build_mask.argtypes
     lib.nabla_build_mask_raster.restype = i
+    lib.nabla_build_mask_raster_noalloc.argtypes = [vp, vp, i, i, i, i, i, i, i, i, f, ctypes.POINTER(StaWindow),
+                                                    f, i, vp, vp, vp, vp, vp]
+    lib.nabla_build_mask_raster_noalloc.restype = i
     lib.nabla_build_mask_ibcs.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, f, ctypes.POINTER(StaWindow),
                                           f, i, vp, vp, vp, vp, vp, sz, vp]
     lib.nabla_build_mask_ibcs.restype = i
@@ -210,6 +214,32 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
     if with_schedule or schedule is not None:
         out.append(schedule)
     return tuple(out)
+
+
+def build_mask_raster_noalloc(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, P: int,
+                              kv_count: torch.Tensor, kv_index: torch.Tensor, N: int = 64, thr: float = 0.1,
+                              sta: Optional[Tuple[int, int, int]] = None, scale: Optional[float] = None,
+                              bitmap: Optional[torch.Tensor] = None, schedule: Optional[torch.Tensor] = None):
+    """The NABLA mask of raster-order Q, K through the entry point that allocates nothing:
+    the caller passes every output (int32 kv_count [B, heads, nb], kv_index
+    [B, heads, nb, nb], optional int32 bitmap [B, heads, nb, ceil(nb/32)] and schedule
+    [B*heads*nb]); the pooled means live in the library's own device array.  Calls that
+    overlap on one GPU race on that array."""
+    lib = load_library()
+    _check_mask_inputs(q, k, T, H, W, N)
+    B, NH, L, d = q.shape
+    nb = L // N
+    _check_int32(kv_count, "kv_count", B * NH * nb)
+    _check_int32(kv_index, "kv_index", B * NH * nb * nb)
+    _check_int32(bitmap, "bitmap", B * NH * nb * ((nb + 31) // 32))
+    _check_int32(schedule, "schedule", B * NH * nb)
+    win = None if sta is None else ctypes.byref(StaWindow(*sta))
+    _check(lib.nabla_build_mask_raster_noalloc(
+        _dev(q, "q"), _dev(k, "k"), B, NH, T, H, W, d, P, N, float(thr), win,
+        float(scale) if scale is not None else 0.0, _dtype_code(q),
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+        _dev(bitmap, "bitmap") if bitmap is not None else None,
+        _dev(schedule, "schedule") if schedule is not None else None, _stream()), lib)
 
 
 def _check_mask_inputs(q: torch.Tensor, k: torch.Tensor, T: int, H: int, W: int, N: int) -> None:

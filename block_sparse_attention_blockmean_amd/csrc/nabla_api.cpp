@@ -135,7 +135,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                              int32_t* schedule, void* workspace, size_t workspace_bytes,
                              hipStream_t stream, int sip_budget = 0, const float* uniforms = nullptr,
-                             float* kv_logw = nullptr, int ibcs_q_group = 0);
+                             float* kv_logw = nullptr, int ibcs_q_group = 0, int use_scratch = 0);
 
 }  // namespace
 
@@ -218,6 +218,15 @@ nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, in
                            stream);
 }
 
+nabla_status nabla_build_mask_raster_noalloc(const void* q, const void* k, int batch, int heads, int T, int H,
+                                             int W, int d, int P, int N, float thr, const nabla_sta_window* sta,
+                                             float scale, nabla_dtype dtype, int32_t* kv_count, int32_t* kv_index,
+                                             uint32_t* bitmap, int32_t* schedule, hipStream_t stream) {
+    return build_mask_impl("nabla_build_mask_raster_noalloc", 1, q, k, batch, heads, T, H, W, d, P, N, thr, sta,
+                           scale, dtype, kv_count, kv_index, bitmap, schedule, nullptr, 0, stream, 0, nullptr,
+                           nullptr, 0, 1);
+}
+
 namespace {
 
 nabla_status build_mask_impl(const char* who, int raster, const void* q, const void* k, int batch,
@@ -226,7 +235,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
                              int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                              int32_t* schedule, void* workspace, size_t workspace_bytes,
                              hipStream_t stream, int sip_budget, const float* uniforms,
-                             float* kv_logw, int ibcs_q_group) {
+                             float* kv_logw, int ibcs_q_group, int use_scratch) {
     if (!q || !k || !kv_count || !kv_index) return fail(NABLA_E_INVAL, "%s: null pointer", who);
     if (!aligned16(q) || !aligned16(k) || ((uintptr_t)kv_count & 3) || ((uintptr_t)kv_index & 3) ||
         ((uintptr_t)bitmap & 3) || ((uintptr_t)schedule & 3))
@@ -260,9 +269,20 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     // the launches cover up to 256 threads per block of every head with 32-bit thread ids
     if ((long long)batch * heads > 65535 || L * d >= kMaxHeadElems || (long long)batch * heads * nb >= (1ll << 24))
         return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
+    // pooled Q and K of one head (each section a multiple of 256 bytes for d = 64, 128)
+    const size_t head_pool_bytes = 2 * (size_t)nb * d * sizeof(float);
+    if (use_scratch && head_pool_bytes > nabla::kScratchBytes)
+        return fail(NABLA_E_UNSUPPORTED, "%s: one head's pooled Q and K need %zu bytes, the scratch holds %zu", who,
+                    head_pool_bytes, nabla::kScratchBytes);
     const size_t need = ibcs_q_group ? nabla_build_mask_ibcs_workspace_size(batch, heads, (int)L, d, N, ibcs_q_group)
                                      : nabla_build_mask_workspace_size(batch, heads, (int)L, d, N);
-    if (!workspace || workspace_bytes < need)
+    if (use_scratch) {
+        // the library's own device array stands in for the workspace
+        size_t bytes = 0;
+        nabla_status st = hip_status(nabla::device_scratch(&workspace, &bytes), who);
+        if (st != NABLA_OK) return st;
+        workspace_bytes = bytes;
+    } else if (!workspace || workspace_bytes < need)
         return fail(NABLA_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
                     workspace ? workspace_bytes : (size_t)0);
     if (((uintptr_t)workspace & 15)) return fail(NABLA_E_INVAL, "%s: misaligned workspace", who);
@@ -312,7 +332,29 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     a.sip_budget = sip_budget;
     a.uniforms = uniforms;
     a.kv_logw = kv_logw;
-    return hip_status(nabla::launch_build_mask(a, stream), who);
+    if (!use_scratch) return hip_status(nabla::launch_build_mask(a, stream), who);
+
+    // Heads in chunks whose pooled Q and K fit the scratch, each chunk's launches reusing
+    // it in stream order; the start order, which reads only the counts, runs once at the end.
+    const int per_chunk = (int)(workspace_bytes / head_pool_bytes);
+    const size_t head_bytes = (size_t)L * d * elem_size(dtype);
+    const size_t words = (size_t)(nb + 31) / 32;
+    for (int h0 = 0; h0 < a.BH; h0 += per_chunk) {
+        nabla::MaskArgs c = a;
+        c.BH = a.BH - h0 < per_chunk ? a.BH - h0 : per_chunk;
+        c.q = (const char*)q + (size_t)h0 * head_bytes;
+        c.k = (const char*)k + (size_t)h0 * head_bytes;
+        c.kv_count = kv_count + (size_t)h0 * nb;
+        c.kv_index = kv_index + (size_t)h0 * nb * nb;
+        c.bitmap = bitmap ? bitmap + (size_t)h0 * nb * words : nullptr;
+        c.schedule = nullptr;
+        c.qp = (float*)workspace;
+        c.kp = (float*)((char*)workspace + (size_t)c.BH * nb * d * sizeof(float));
+        nabla_status st = hip_status(nabla::launch_build_mask(c, stream), who);
+        if (st != NABLA_OK) return st;
+    }
+    if (!schedule) return NABLA_OK;
+    return hip_status(nabla::launch_schedule(kv_count, a.BH, (int)nb, schedule, stream), who);
 }
 
 }  // namespace

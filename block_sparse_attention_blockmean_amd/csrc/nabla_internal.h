@@ -93,6 +93,12 @@ struct MaskArgs {
     float* cent_w;          // IBCS workspace [BH, groups * kIbcsClusters] cluster weights
 };
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
+
+// The allocation-free mask entry's scratch: a device array of kScratchBytes per GPU
+// (scratch.hip).  device_scratch returns its address on the current device, resolved once
+// per device.
+constexpr size_t kScratchBytes = NABLA_NOALLOC_SCRATCH_BYTES;
+hipError_t device_scratch(void** ptr, size_t* bytes);
 hipError_t launch_ibcs_cluster(const MaskArgs& a, hipStream_t s);
 
 struct AttnArgs {

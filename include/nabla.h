@@ -16,7 +16,9 @@
  *   - Tensors are dense, row-major [batch, heads, L, d] (d innermost), in device
  *     memory, 16-byte aligned.  Q, K, V, O of one call share one dtype.
  *   - The caller owns every buffer, including the workspace; the library allocates
- *     no device memory and keeps no per-call state.
+ *     no device memory and keeps no per-call state.  The one exception is the device
+ *     array behind nabla_build_mask_raster_noalloc, a fixed NABLA_NOALLOC_SCRATCH_BYTES
+ *     per GPU that exists from the library's load on.
  *   - Every call is asynchronous on `stream` (0 = the null stream) and never
  *     synchronises the host.  Calls on distinct streams may run concurrently as long
  *     as they do not write the same buffers.
@@ -174,6 +176,29 @@ nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, in
                                      int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
                                      int32_t* schedule, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
+
+/*
+ * nabla_build_mask_raster_noalloc - nabla_build_mask_raster for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): no workspace argument, and no allocation of any kind.  The
+ * pooled Q and K live in a device array of the library, NABLA_NOALLOC_SCRATCH_BYTES per
+ * GPU, held from the library's load until the process ends; heads are processed in
+ * chunks whose pooled Q and K fit in it (2 * nb * d * 4 bytes per head), one launch
+ * sequence per chunk on `stream`.  Results (counts, lists, bitmap, schedule) are those of
+ * nabla_build_mask_raster on the same arguments.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and give undefined
+ * lists.  Nothing in the array needs clearing between calls: each chunk writes its pooled
+ * means before reading them.
+ * Errors: as nabla_build_mask_raster (without the workspace errors), plus
+ * NABLA_E_UNSUPPORTED when one head's pooled Q and K exceed the array.
+ */
+#define NABLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+nabla_status nabla_build_mask_raster_noalloc(const void* q, const void* k, int batch, int heads, int T,
+                                             int H, int W, int d, int P, int N, float thr,
+                                             const nabla_sta_window* sta, float scale, nabla_dtype dtype,
+                                             int32_t* kv_count, int32_t* kv_index, uint32_t* bitmap,
+                                             int32_t* schedule, hipStream_t stream);
 
 /*
  * block_sparse_attn_fwd_raster - block_sparse_attn_fwd for Q, K, V and O in raster order,

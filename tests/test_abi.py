@@ -392,3 +392,22 @@ def test_binding_checks_mask_shapes_before_pointers():
     with pytest.raises(ValueError, match="sizes do not match"):
         nb_lib.attn_fwd_raster(q, q, q, torch.zeros(1, 2, 16, dtype=torch.int32),
                                torch.zeros(1, 2, 16, 16, dtype=torch.int32)[..., :8].contiguous(), 4, 16, 16, 8)
+
+
+def test_build_mask_raster_noalloc_validation(lib):
+    """The allocation-free entry validates like nabla_build_mask_raster (it has no
+    workspace) before any HIP call."""
+    win = None
+
+    def call(**kw):
+        a = dict(q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, thr=0.1, scale=0.0,
+                 dt=NABLA_F32, cnt=C, idx=D_)
+        a.update(kw)
+        return lib.nabla_build_mask_raster_noalloc(a["q"], a["k"], a["batch"], a["heads"], a["T"], a["H"], a["W"],
+                                                   a["d"], a["P"], a["N"], a["thr"], win, a["scale"], a["dt"],
+                                                   a["cnt"], a["idx"], None, None, None)
+    for kw, st in ((dict(q=None), NABLA_E_INVAL), (dict(idx=None), NABLA_E_INVAL), (dict(thr=1.5), NABLA_E_INVAL),
+                   (dict(P=4, H=16, W=16), NABLA_E_INVAL), (dict(H=20), NABLA_E_INVAL),
+                   (dict(d=96), NABLA_E_UNSUPPORTED), (dict(T=129, H=32, W=32), NABLA_E_UNSUPPORTED)):
+        assert call(**kw) == st, kw
+        assert lib.nabla_last_error().decode().startswith("nabla_build_mask_raster_noalloc")
