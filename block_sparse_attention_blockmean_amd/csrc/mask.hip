@@ -638,6 +638,80 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Start order for the attention launch, which computes two query blocks per workgroup
+// (schedule entries 2j and 2j+1) and copies each KV tile the two keep once.  Blocks of
+// neighbouring frames at the same patch position keep largely the same KV blocks, so
+// block i of frame t is paired with block i of frame t + 1 (t even); with an odd number
+// of frames the last frame's blocks pair side by side, and with an odd number of blocks
+// per frame as well one block per head is left single.  Inside a head the pairs run by
+// decreasing combined kept count (counting sort, one wave per head), heads in order, so
+// consecutive workgroups - dealt round-robin to the 8 XCDs - keep the whole GPU on one
+// or two heads at a time and each head's short lists run last.  The single blocks of all
+// heads go at the very end, so that every head's pairs stay aligned to even positions.
+// `fpf` is the number of blocks per frame (1 when frames do not hold whole blocks, which
+// pairs blocks 2j and 2j + 1).
+// ---------------------------------------------------------------------------
+__device__ inline void pair_members(int j, int fpf, int tpairs, int& a, int& b) {
+    if (j < tpairs * fpf) {
+        const int t = 2 * (j / fpf), p = j - (j / fpf) * fpf;
+        a = t * fpf + p;
+        b = a + fpf;
+    } else {
+        a = 2 * tpairs * fpf + 2 * (j - tpairs * fpf);
+        b = a + 1;
+    }
+}
+
+__global__ __launch_bounds__(64) void pair_schedule_kernel(const int32_t* __restrict__ kv_count, int nb, int fpf,
+                                                           int BH, int32_t* __restrict__ schedule) {
+    extern __shared__ int bins[];   // 2 nb + 1 counters
+    const int h = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int32_t* cnt = kv_count + (size_t)h * nb;
+    const int frames = nb / fpf;
+    const int tpairs = frames / 2;                    // frame pairs (t, t + 1), t even
+    const int single = (frames & 1) & (fpf & 1);      // a block left without a partner
+    const int npairs = (nb - single) / 2;
+    const int nbins = 2 * nb + 1;
+    for (int b = lane; b < nbins; b += 64) bins[b] = 0;
+    __syncthreads();
+    auto key = [&](int j) {
+        int a, b;
+        pair_members(j, fpf, tpairs, a, b);
+        return 2 * nb - (min(max(cnt[a], 0), nb) + min(max(cnt[b], 0), nb));
+    };
+    for (int j = lane; j < npairs; j += 64) atomicAdd(&bins[key(j)], 1);
+    __syncthreads();
+    // exclusive prefix sum over the bins: one contiguous chunk per lane
+    const int per = (nbins + 63) / 64;
+    const int b0 = lane * per, b1 = min(b0 + per, nbins);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += bins[b];
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    int run = incl - local;
+    for (int b = b0; b < b1; ++b) {
+        const int n = bins[b];
+        bins[b] = run;
+        run += n;
+    }
+    __syncthreads();
+    int32_t* out = schedule + (size_t)h * (nb - single);
+    for (int j = lane; j < npairs; j += 64) {
+        int a, b;
+        pair_members(j, fpf, tpairs, a, b);
+        const int pos = atomicAdd(&bins[key(j)], 1);
+        out[2 * pos] = h * nb + a;
+        out[2 * pos + 1] = h * nb + b;
+    }
+    if (single && lane == 0) schedule[(size_t)BH * (nb - 1) + h] = h * nb + nb - 1;
+}
+
 template <typename T, int D>
 hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
     const int total = a.BH * a.nb;
@@ -724,8 +798,17 @@ hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
         e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
     }
     if (e != hipSuccess || !a.schedule) return e;
-    // one wave per head; its bins fit the default LDS limit (NABLA_MAX_BLOCKS + 1 ints)
-    return launch_schedule(a.kv_count, a.BH, a.nb, a.schedule, s);
+    return launch_pair_schedule(a, a.kv_count, a.schedule, s);
+}
+
+hipError_t launch_pair_schedule(const MaskArgs& a, const int32_t* counts, int32_t* schedule, hipStream_t s) {
+    // blocks per frame when frames hold whole N-token blocks, else 1 (blocks 2j, 2j + 1)
+    const long long hw = (long long)a.H * a.W;
+    const int fpf = (hw % a.N == 0 && a.nb % (int)(hw / a.N) == 0) ? (int)(hw / a.N) : 1;
+    // one wave per head; its 2 nb + 1 bins fit the default LDS limit
+    hipLaunchKernelGGL(pair_schedule_kernel, dim3(a.BH), dim3(64), (size_t)(2 * a.nb + 1) * sizeof(int), s, counts,
+                       a.nb, fpf, a.BH, schedule);
+    return hipGetLastError();
 }
 
 hipError_t launch_schedule(const int32_t* counts, int BH, int nb, int32_t* schedule, hipStream_t s) {

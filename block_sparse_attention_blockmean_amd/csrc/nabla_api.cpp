@@ -354,7 +354,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
         if (st != NABLA_OK) return st;
     }
     if (!schedule) return NABLA_OK;
-    return hip_status(nabla::launch_schedule(kv_count, a.BH, (int)nb, schedule, stream), who);
+    return hip_status(nabla::launch_pair_schedule(a, kv_count, schedule, stream), who);
 }
 
 }  // namespace

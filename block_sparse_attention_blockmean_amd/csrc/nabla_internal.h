@@ -119,6 +119,10 @@ struct AttnArgs {
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
+// Start order of the mask step's schedule output: pairs of query blocks of neighbouring
+// frames, heads in turn, each head's pairs by decreasing combined count (mask.hip).
+hipError_t launch_pair_schedule(const MaskArgs& a, const int32_t* counts, int32_t* schedule, hipStream_t s);
+
 // Start order of BH*nb items, heads in turn, each head's items by decreasing count.
 hipError_t launch_schedule(const int32_t* counts, int BH, int nb, int32_t* schedule, hipStream_t s);
 

@@ -112,11 +112,17 @@ size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N
  *             bits of the last word are zero.
  * schedule    optional out (NULL to skip), int32 [batch*heads*nb]: every query block
  *             (b*heads + h)*nb + i exactly once, as a start order for
- *             block_sparse_attn_fwd: heads in order, each head's blocks by decreasing
- *             kv_count (order among equal counts unspecified).  Consecutive workgroups
- *             spread over all XCDs, so the whole GPU works on one or two heads at a
- *             time (their K/V stay in the last-level cache) and each head's short lists
- *             run last.  It never changes results.
+ *             block_sparse_attn_fwd, which computes entries 2j and 2j+1 in one
+ *             workgroup.  Entries 2j, 2j+1 are a pair of blocks at the same patch
+ *             position in neighbouring frames t, t+1 (t even; with an odd frame count
+ *             the last frame's blocks pair side by side; frames that do not hold whole
+ *             blocks pair blocks 2i, 2i+1), whose kept lists largely coincide.  Heads in
+ *             order, each head's pairs by decreasing combined kv_count (order among equal
+ *             counts unspecified); the one block per head left without a partner (odd
+ *             frame count and odd blocks per frame) goes after all heads' pairs.
+ *             Consecutive workgroups spread over all XCDs, so the whole GPU works on one
+ *             or two heads at a time (their K/V stay in the last-level cache) and each
+ *             head's short lists run last.  It never changes results.
  * workspace   device buffer of at least nabla_build_mask_workspace_size() bytes.
  * Errors: NABLA_E_INVAL (null pointers, L != T*H*W, H or W not a multiple of P,
  * L not a multiple of N, thr outside [0,1) or NaN, a window size even or < 1, a window
@@ -147,7 +153,11 @@ nabla_status nabla_build_mask(const void* q, const void* k, int batch, int heads
  *             kv_count 0 gets zero output.
  * schedule    optional (NULL for natural order): a permutation of the batch*heads*nb
  *             query blocks giving the order in which they are started, e.g. the one
- *             nabla_build_mask writes.  Results do not depend on it.
+ *             nabla_build_mask writes.  With bf16 the kernel computes two query blocks
+ *             per workgroup, entries 2j and 2j+1 (natural order: blocks 2j, 2j+1), and
+ *             copies each KV tile that both keep once; pairing blocks whose lists
+ *             overlap saves copies.  Results depend on neither the order nor the
+ *             pairing.
  * scale       <= 0 selects 1/sqrt(d).
  * bf16: scores and the running softmax in float32, P rounded to bf16 for the P V
  * product, float32 accumulation, output rounded to nearest-even bf16.

@@ -183,27 +183,50 @@ def test_exact_ties_grouped(dtype):
         assert np.all(np.abs(ref["F"][mism] - thr) <= 1e-4), thr
 
 
+def check_pair_schedule(cfg, sched, cnt):
+    """The mask step's start order: a permutation of the query blocks in which entries 2j
+    and 2j + 1 form a pair - block i of frame t with block i of frame t + 1 (t even), the
+    last frame's blocks side by side when the frame count is odd - heads in order, each
+    head's pairs by non-increasing combined kept count, and the one block per head left
+    without a partner (odd frame count and odd blocks per frame) at the very end."""
+    G, nb = cfg.BH, cfg.nb
+    assert np.array_equal(np.sort(sched), np.arange(G * nb))
+    fpf = cfg.H * cfg.W // cfg.N if (cfg.H * cfg.W) % cfg.N == 0 else 1
+    frames = nb // fpf
+    single = (frames % 2) * (fpf % 2)
+    for g in range(G):
+        part = sched[g * (nb - single):(g + 1) * (nb - single)]
+        assert np.all(part // nb == g), "a head's pairs stay in its region"
+        a, b = part[0::2] - g * nb, part[1::2] - g * nb
+        temporal = (b == a + fpf) & ((a // fpf) % 2 == 0)
+        last = (a // fpf == frames - 1) & (b == a + 1) & ((a % fpf) % 2 == 0)
+        assert np.all(temporal | (last & (frames % 2 == 1))), "pairs are neighbours in time"
+        sums = cnt[g * nb + a] + cnt[g * nb + b]
+        assert np.all(np.diff(sums) <= 0), "pairs by non-increasing combined count"
+    if single:
+        assert np.array_equal(sched[G * (nb - 1):], np.arange(G) * nb + nb - 1)
+
+
 @pytest.mark.parametrize("cfg", [SMALL[0], SMALL[3], SMALL[8]], ids=lambda c: c.name)
 def test_schedule(cfg):
-    """The schedule lists every query block once, head by head, longest kept list first
-    inside a head, and the attention output does not depend on the start order."""
+    """The start order pairs neighbouring frames' blocks, and the attention output does not
+    depend on the order or the pairing: reversed, shuffled (pairs across heads) and no
+    order at all give the same bits."""
     q, k, v = make_qkv(cfg)
     res = run_gpu_path(cfg, q, k, v)
     sched = res["sched"].cpu().numpy()
     cnt = res["cnt"].cpu().numpy().reshape(-1)
-    assert np.array_equal(np.sort(sched), np.arange(cfg.BH * cfg.nb))
-    # heads in order, inside a head the blocks by non-increasing kept count
-    for g in range(cfg.BH):
-        part = sched[g * cfg.nb:(g + 1) * cfg.nb]
-        assert np.array_equal(np.sort(part), np.arange(g * cfg.nb, (g + 1) * cfg.nb))
-        assert np.all(np.diff(cnt[part]) <= 0)
+    check_pair_schedule(cfg, sched, cnt)
     plain = nab.attn_fwd(res["qf"], res["kf"], res["vf"], res["cnt"], res["idx"], cfg.N)
     rev = torch.flip(res["sched"], [0]).contiguous()
     backwards = nab.attn_fwd(res["qf"], res["kf"], res["vf"], res["cnt"], res["idx"], cfg.N,
                              schedule=rev)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(cfg.BH * cfg.nb).astype(np.int32)).cuda()
+    shuffled = nab.attn_fwd(res["qf"], res["kf"], res["vf"], res["cnt"], res["idx"], cfg.N, schedule=perm)
     torch.cuda.synchronize()
     assert torch.equal(plain, res["of"])
     assert torch.equal(backwards, res["of"])
+    assert torch.equal(shuffled, res["of"])
 
 
 def test_determinism():
