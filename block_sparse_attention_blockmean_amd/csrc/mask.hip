@@ -528,47 +528,335 @@ __device__ void select_row(float* arow, float inv_sum, float* cand, int nb, int 
 }
 
 // ---------------------------------------------------------------------------
-// NABLA's reduced map and cut in one kernel.  A workgroup (16 waves) owns kRows pooled
-// query rows of one head: the map by map_rows, then per row (one wave) the softmax
-// A = exp(S - max) / sum in place and select_row.  The rows never leave LDS, which at
-// large nb (nb^2 floats per head) saves an HBM round trip.
+// SIP on one row held in registers (v[i] = A_j of block j = lane + 64 i, probabilities):
+// the same rule and order of arithmetic as sip_row.
+// ---------------------------------------------------------------------------
+template <int NREG>
+__device__ void sip_row_regs(const float (&v)[NREG], int nb, int budget, const float* u, int32_t* out_idx,
+                             float* out_logw, uint32_t* out_bits, int nwords, int32_t* out_count, int lane) {
+    float best = -1.f;
+    int bj = nb;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+        const int j = lane + 64 * i;
+        if (j < nb && v[i] > best) {
+            best = v[i];
+            bj = j;
+        }
+    }
+    const float amax = wave_max(best);
+    const int top = (int)~wave_max_u(~(uint32_t)(best == amax ? bj : nb));
+    const int kp = budget - 1;
+    const bool all = budget >= nb;
+    // water level over the blocks other than the top one
+    float c = 0.f, c_cert = 0.f;
+    if (!all && kp > 0) {
+        float rest = 0.f;
+#pragma unroll
+        for (int i = 0; i < NREG; ++i) {
+            const int j = lane + 64 * i;
+            if (j < nb && j != top) rest += v[i];
+        }
+        rest = wave_sum(rest);
+        c = rest > 0.f ? (float)kp / rest : 0.f;
+        c_cert = c;
+        int m = 0;
+        for (int it = 0; it < 64; ++it) {
+            float unc = 0.f;   // mass of the blocks still below 1
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < NREG; ++i) {
+                const int j = lane + 64 * i;
+                const bool other = j < nb && j != top;
+                const bool cert = other && c * v[i] >= 1.f;
+                if (other && !cert) unc += v[i];
+                cnt += __popcll(__ballot(cert));
+            }
+            unc = wave_sum(unc);
+            if (cnt == m) {
+                c_cert = c;
+                break;
+            }
+            m = cnt;
+            c_cert = c;
+            if (m >= kp || !(unc > 0.f)) {
+                c = 0.f;
+                break;
+            }
+            c = (float)(kp - m) / unc;
+        }
+    }
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+        const int j = lane + 64 * i;
+        bool keep = false;
+        float pi = 0.f;
+        if (j < nb) {
+            pi = (all || j == top || c_cert * v[i] >= 1.f) ? 1.f : c * v[i];
+            keep = u[j] < pi;
+        }
+        const uint64_t ballot = __ballot(keep);
+        if (keep) {
+            const int pos = base + __popcll(ballot & ((1ull << lane) - 1ull));
+            out_idx[pos] = j;
+            out_logw[pos] = -logf(pi);
+        }
+        base += __popcll(ballot);
+        if (out_bits) {
+            const int w = 2 * i;
+            if (lane == 0 && w < nwords) out_bits[w] = (uint32_t)ballot;
+            if (lane == 1 && w + 1 < nwords) out_bits[w + 1] = (uint32_t)(ballot >> 32);
+        }
+    }
+    if (lane == 0) *out_count = base;
+}
+
+// ---------------------------------------------------------------------------
+// The CDF cut of one row held in registers, in one wave: v[i] = A_j of block
+// j = lane + 64 i (probabilities summing to one; entries past nb must be +0, which no
+// bracket (lo, hi] holds and no sum notices).  The
+// same cut as select_row (bisection over bit patterns from u0 = thr / nb, an exact
+// finish over at most 64 candidates), with every pass over the row running on
+// registers instead of LDS reads; `cand` (one wave's kCap floats of LDS) takes the
+// final candidates.  Then the STA OR, the ascending list, the count and the bitmap.
+// ---------------------------------------------------------------------------
+template <int NREG>
+__device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int bh, int row, float thr, int sta,
+                                int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
+                                int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int lane) {
+    const int nwords = (nb + 31) >> 5;
+    // start of the bracket: u0 = thr / nb, nudged down so rounding cannot push g(u0)
+    // above thr; verified below and dropped to 0 if it fails
+    uint32_t lo = __float_as_uint(thr / ((float)nb * 1.0001f));
+    float g_lo = 0.f;
+    int n_in = 0;
+    uint32_t maxb = 0;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+        const uint32_t b = __float_as_uint(v[i]);
+        maxb = max(maxb, b);
+        const bool in = b > lo;
+        if (!in) g_lo += v[i];
+        n_in += __popcll(__ballot(in));
+    }
+    g_lo = wave_sum(g_lo);
+    maxb = wave_max_u(maxb);
+    if (g_lo > thr) {   // cannot happen in exact arithmetic; fall back to g(0) = 0
+        lo = 0;
+        g_lo = 0.f;
+        n_in = 0;
+#pragma unroll
+        for (int i = 0; i < NREG; ++i) n_in += __popcll(__ballot(__float_as_uint(v[i]) > 0u));
+    }
+    uint32_t hi = maxb;
+    // bisection until at most 64 values are left in the bracket (lo, hi]
+    while (hi - lo > 1 && n_in > 64) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        float s_ = 0.f;
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < NREG; ++i) {
+            const uint32_t b = __float_as_uint(v[i]);
+            const bool in = b > lo && b <= mid;
+            if (in) s_ += v[i];
+            c += __popcll(__ballot(in));
+        }
+        s_ = wave_sum(s_);
+        if (g_lo + s_ > thr) {
+            hi = mid;
+            n_in = c;
+        } else {
+            lo = mid;
+            g_lo += s_;
+            n_in -= c;
+        }
+    }
+    uint32_t cut = hi;
+    if (n_in <= 64) {
+        // one candidate per lane: F(x) = g_lo + (sum of the candidates <= x), tied
+        // values together; the cut is the smallest candidate with F(x) > thr
+        int len = 0;
+#pragma unroll
+        for (int i = 0; i < NREG; ++i) {
+            const uint32_t b = __float_as_uint(v[i]);
+            const bool in = b > lo && b <= hi;
+            const uint64_t ballot = __ballot(in);
+            if (in) cand[len + __popcll(ballot & ((1ull << lane) - 1ull))] = v[i];
+            len += __popcll(ballot);
+        }
+        const float x = lane < len ? cand[lane] : 0.f;
+        const uint32_t bx = __float_as_uint(x);
+        float below = 0.f;
+        for (int m = 0; m < len; ++m) {
+            const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), m));
+            if (__float_as_uint(y) <= bx) below += y;
+        }
+        const bool crosses = lane < len && g_lo + below > thr;
+        const uint32_t pick = crosses ? bx : 0xffffffffu;
+        const uint32_t best = ~wave_max_u(~pick);   // smallest pattern among the crossing ones
+        if (best != 0xffffffffu) cut = best;
+    }
+
+    int qt = 0, qh_ = 0, qw = 0;
+    const int pf = nH * nW;
+    if (sta) {
+        qt = row / pf;
+        const int rem = row - qt * pf;
+        qh_ = rem / nW;
+        qw = rem - qh_ * nW;
+    }
+    int32_t* out_idx = kv_index + ((size_t)bh * nb + row) * nb;
+    uint32_t* out_bits = bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+        const int j = lane + 64 * i;
+        bool keep = false;
+        if (j < nb) {
+            keep = __float_as_uint(v[i]) >= cut;
+            if (sta && !keep) {
+                const int kt = j / pf;
+                const int rem = j - kt * pf;
+                const int kh_ = rem / nW;
+                const int kw = rem - kh_ * nW;
+                keep = abs(kt - qt) <= rt && abs(kh_ - qh_) <= rh && abs(kw - qw) <= rw;
+            }
+        }
+        const uint64_t ballot = __ballot(keep);
+        if (keep) out_idx[base + __popcll(ballot & ((1ull << lane) - 1ull))] = j;
+        base += __popcll(ballot);
+        if (out_bits) {
+            const int w = 2 * i;
+            if (lane == 0 && w < nwords) out_bits[w] = (uint32_t)ballot;
+            if (lane == 1 && w + 1 < nwords) out_bits[w + 1] = (uint32_t)(ballot >> 32);
+        }
+    }
+    if (lane == 0) kv_count[(size_t)bh * nb + row] = base;
+}
+
+// ---------------------------------------------------------------------------
+// NABLA's reduced map and cut in one kernel.  A workgroup (16 waves) owns kRows = 16
+// pooled query rows of one head, and wave r owns row r: the row ends up in the wave's
+// registers (v[i] = S_j of block j = lane + 64 i), so the softmax and the cut run without
+// touching LDS.  The map runs in chunks of 256 columns: each wave computes one 16 x 16
+// tile of the chunk on the float32 MFMA (map_tile) into an LDS chunk buffer, and after
+// one barrier every wave copies its row's 256 values into registers.  Two chunk buffers
+// alternate, so one barrier per chunk suffices (a wave writes chunk c + 2 only after the
+// barrier of chunk c + 1, which every wave reaches after reading chunk c).  LDS per
+// workgroup is then ~46 KiB whatever nb, and two workgroups share a CU: one's loads and
+// barriers overlap the other's cut.
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 16;
+constexpr int kChunkCols = 16 * kWaves;     // one 16-column tile per wave
+constexpr int kChunkLd = kChunkCols + 4;    // padded row: the 16 x 16 tile stores hit distinct banks
+constexpr int kFinalCand = 64;              // candidates of a row's exact finish
 
+// One 16 x 16 tile of X Kp^T (unscaled): the kRows X rows staged in x_lds, columns
+// j0 .. j0 + 15 of the head's Kp [nb, D] (columns past nb read as zeros).  Lane (row/col
+// l % 16, group g = l / 16) supplies coordinate 16 m + 4 g + i at MFMA step 4 m + i in
+// both operands, so each 16-byte load reads 64 contiguous bytes of 16 rows.  The Kp
+// operand is loaded two 16-byte chunks at a time (8 VGPRs), leaving the registers to the
+// wave's row.
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(8, 8))) void map_select_kernel(
-    const float* __restrict__ qp, const float* __restrict__ kp, int nb, int ld_s, float scale, float thr, int sta,
-    int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
-    uint32_t* __restrict__ bitmap, int sip_budget, const float* __restrict__ uniforms,
-    float* __restrict__ kv_logw) {
-    // [kRows][ld_s] rows, then [kWaves][kCap] candidates, then [kRows][kXld] pooled queries
+__device__ inline f32x4 map_tile(const float* __restrict__ x_lds, const float* __restrict__ kh, int nb, int j0,
+                                 int lane) {
+    constexpr int KC = D / 4;   // 16-byte chunks per row
+    const int li = lane & 15;
+    const int kq = lane >> 4;
+    const int j = j0 + li;
+    const f32x4* xa = reinterpret_cast<const f32x4*>(x_lds + li * kXld<D>) + kq;
+    const f32x4* src = reinterpret_cast<const f32x4*>(kh + (size_t)min(j, nb - 1) * D) + kq;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int m = 0; m < KC / 4; m += 2) {
+        f32x4 b0 = src[4 * m];
+        f32x4 b1 = src[4 * m + 4];
+        if (j >= nb) b0 = b1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 a0 = xa[4 * m];
+        const f32x4 a1 = xa[4 * m + 4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[i], b0[i], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[i], b1[i], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Rows of up to 20 register blocks (1280 KV blocks) run eight waves per SIMD (two
+// workgroups per CU) within 64 VGPRs; longer rows four waves per SIMD with 128.
+template <int NREG>
+constexpr int kMapSelectWaves = NREG > 20 ? 4 : 8;
+
+template <int D, int NREG>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMapSelectWaves<NREG>,
+                                                                             kMapSelectWaves<NREG>))) void
+map_select_kernel(const float* __restrict__ qp, const float* __restrict__ kp, int nb, float scale, float thr, int sta,
+                  int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
+                  int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int sip_budget,
+                  const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
+    // [2][kRows][kChunkLd] chunk buffers, [kWaves][kFinalCand] candidates, [kRows][kXld] pooled queries
     extern __shared__ __align__(16) float s_lds[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kRows;
-    float* x_lds = s_lds + kRows * ld_s + kWaves * kCap;
+    const int row = row0 + wave;
+    float* cand = s_lds + 2 * kRows * kChunkLd + wave * kFinalCand;
+    float* x_lds = s_lds + 2 * kRows * kChunkLd + kWaves * kFinalCand;
+    const float* kh = kp + (size_t)bh * nb * D;
     stage_rows<D, kWaves * 64>(qp + (size_t)bh * nb * D, nb, row0, x_lds);
     __syncthreads();
-    map_rows<D, kWaves>(x_lds, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds, wave, lane);
-    __syncthreads();
-    float* cand = s_lds + kRows * ld_s + wave * kCap;
-    for (int r = wave; r < kRows; r += kWaves) {
-        const int row = row0 + r;
-        if (row >= nb) break;
-        float* arow = s_lds + r * ld_s;
-        float mx = -INFINITY;
-        for (int j = lane; j < nb; j += 64) mx = fmaxf(mx, arow[j]);
-        const float mx2 = wave_max(mx) * kLog2e;
-        float sum = 0.f;
-        for (int j = lane; j < nb; j += 64) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(arow[j], kLog2e, -mx2));
-            arow[j] = e;
-            sum += e;
+
+    float v[NREG];
+    const int li = lane & 15;
+    const int kq = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < NREG / 4; ++c) {
+        if (c * kChunkCols < nb) {              // uniform over the workgroup
+            float* buf = s_lds + (c & 1) * kRows * kChunkLd;
+            const int j0 = c * kChunkCols + 16 * wave;
+            if (j0 < nb) {
+                const f32x4 acc = map_tile<D>(x_lds, kh, nb, j0, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) buf[(4 * kq + r) * kChunkLd + 16 * wave + li] = acc[r] * scale;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int j = c * kChunkCols + lane + 64 * m;
+                v[4 * c + m] = j < nb ? buf[wave * kChunkLd + lane + 64 * m] : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) v[4 * c + m] = -INFINITY;
         }
-        const float inv_sum = 1.0f / wave_sum(sum);
-        select_row(arow, inv_sum, cand, nb, bh, row, thr, sta, nH, nW, rt, rh, rw, kv_count, kv_index, bitmap,
-                   sip_budget, uniforms, kv_logw, lane);
+    }
+    if (row >= nb) return;
+
+    // softmax in place: A = exp2((S - max) log2 e) / sum, the sum in block order per lane
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) mx = fmaxf(mx, v[i]);
+    const float mx2 = wave_max(mx) * kLog2e;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(v[i], kLog2e, -mx2));   // -inf past nb: +0
+        v[i] = e;
+        sum += e;
+    }
+    const float inv_sum = 1.0f / wave_sum(sum);
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) v[i] *= inv_sum;
+    if (sip_budget > 0) {
+        const int nwords = (nb + 31) >> 5;
+        sip_row_regs<NREG>(v, nb, sip_budget, uniforms + ((size_t)bh * nb + row) * nb,
+                           kv_index + ((size_t)bh * nb + row) * nb, kv_logw + ((size_t)bh * nb + row) * nb,
+                           bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr, nwords,
+                           kv_count + (size_t)bh * nb + row, lane);
+    } else {
+        select_row_regs<NREG>(v, cand, nb, bh, row, thr, sta, nH, nW, rt, rh, rw, kv_count, kv_index, bitmap, lane);
     }
 }
 
@@ -732,23 +1020,35 @@ hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int NREG>
 hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
-    const int ld_s = ((a.nb + 63) / 64) * 64 + 16;
-    const size_t lds = ((size_t)kRows * ld_s + (size_t)kWaves * kCap + (size_t)kRows * kXld<D>) * sizeof(float);
-    static std::atomic<uint64_t> lds_set{0};
-    const int max_lds =
-        (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap + kRows * kXld<D>) * (int)sizeof(float);
-    static_assert((kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kWaves * kCap + kRows * kXld<128>) *
-                          sizeof(float) <= 160 * 1024,
-                  "map/select LDS at the largest nb");
-    hipError_t e = set_max_dynamic_lds((const void*)map_select_kernel<D>, max_lds, lds_set);
-    if (e != hipSuccess) return e;
+    const size_t lds = ((size_t)2 * kRows * kChunkLd + (size_t)kWaves * kFinalCand + (size_t)kRows * kXld<D>) *
+                       sizeof(float);
+    static_assert((2 * kRows * kChunkLd + kWaves * kFinalCand + kRows * kXld<128>) * sizeof(float) <= 64 * 1024,
+                  "map/select LDS within the default dynamic limit");
     dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
-    hipLaunchKernelGGL((map_select_kernel<D>), grid, dim3(kWaves * 64), lds, s, a.qp, a.kp, a.nb, ld_s, a.scale,
+    hipLaunchKernelGGL((map_select_kernel<D, NREG>), grid, dim3(kWaves * 64), lds, s, a.qp, a.kp, a.nb, a.scale,
                        a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count, a.kv_index, a.bitmap, a.sip_budget,
                        a.uniforms, a.kv_logw);
     return hipGetLastError();
+}
+
+// registers per lane for a row of nb values: a multiple of 4 (one 256-column chunk)
+// covering nb / 64
+template <int D>
+hipError_t launch_map_select_nreg(const MaskArgs& a, hipStream_t s) {
+    static_assert(NABLA_MAX_BLOCKS <= 32 * 64, "rows of at most 32 registers per lane");
+    if (a.nb <= 4 * 64) return launch_map_select<D, 4>(a, s);
+    if (a.nb <= 8 * 64) return launch_map_select<D, 8>(a, s);
+    if (a.nb <= 12 * 64) return launch_map_select<D, 12>(a, s);
+    if (a.nb <= 16 * 64) return launch_map_select<D, 16>(a, s);
+    if (a.nb <= 20 * 64) return launch_map_select<D, 20>(a, s);
+    if (a.nb <= 24 * 64) return launch_map_select<D, 24>(a, s);
+    return launch_map_select<D, 32>(a, s);
+}
+
+hipError_t launch_map_select_for(const MaskArgs& a, hipStream_t s) {
+    return a.d == 128 ? launch_map_select_nreg<128>(a, s) : launch_map_select_nreg<64>(a, s);
 }
 
 hipError_t launch_select(const MaskArgs& a, hipStream_t s) {
@@ -795,7 +1095,7 @@ hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
         e = (a.d == 128) ? launch_ibcs_score<128>(a, s) : launch_ibcs_score<64>(a, s);
         if (e == hipSuccess) e = launch_select(a, s);
     } else {
-        e = (a.d == 128) ? launch_map_select<128>(a, s) : launch_map_select<64>(a, s);
+        e = launch_map_select_for(a, s);
     }
     if (e != hipSuccess || !a.schedule) return e;
     return launch_pair_schedule(a, a.kv_count, a.schedule, s);
