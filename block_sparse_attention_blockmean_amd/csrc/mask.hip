@@ -50,6 +50,78 @@ struct Elem<float> {
     }
 };
 
+// Sum of one N-token block in one wave: lane l reads 16-byte chunk c = l % CHUNKS of
+// tokens g = l / CHUNKS, g + G, ... (`row(r)` gives the head row of the block's r-th
+// token), sums them in token order, and a fixed butterfly adds the G partial sums.  The
+// lanes with l < CHUNKS end with the block's sums of elements c*EPC .. c*EPC + EPC - 1.
+// BATCH loads are in flight at a time (all of them, ITERS, in the HBM-bound pool kernel;
+// fewer where registers are scarce); the sums run in token order either way.
+template <typename T, int D, int N, int BATCH, typename RowOf>
+__device__ inline void block_sum_wave(const T* __restrict__ head, RowOf row, int lane, float (&acc)[Elem<T>::kPerChunk]) {
+    constexpr int EPC = Elem<T>::kPerChunk;
+    constexpr int CHUNKS = D / EPC;          // 16-byte chunks per token
+    constexpr int G = 64 / CHUNKS;           // tokens per load instruction
+    constexpr int ITERS = N / G;
+    constexpr int NB = BATCH < ITERS ? BATCH : ITERS;
+    static_assert(ITERS % NB == 0, "whole batches");
+    const int c = lane % CHUNKS;
+    const int g = lane / CHUNKS;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int r0 = 0; r0 < ITERS; r0 += NB) {
+        u32x4 raw[NB];
+#pragma unroll
+        for (int r = 0; r < NB; ++r)
+            raw[r] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(head + (size_t)row((r0 + r) * G + g) * D) + c);
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            float v[EPC];
+            Elem<T>::unpack(raw[r], v);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[e] += v[e];
+        }
+    }
+#pragma unroll
+    for (int off = CHUNKS; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], off);
+    }
+}
+
+// The head row of token r of block b: fractal order, runs of N rows; raster order, one
+// 8 x 8 patch (attn::block_row / row_in_block).
+template <bool RASTER, int N>
+struct BlockRows {
+    uint32_t base;
+    attn::RasterGrid grid;
+    __device__ BlockRows(const attn::RasterGrid& g, uint32_t b)
+        : base(RASTER ? attn::block_row<true>(g, b) : b * N), grid(g) {}
+    __device__ uint32_t operator()(int r) const { return base + attn::row_in_block<RASTER>(grid, r); }
+};
+
+// Mean of query block b of one head (one wave) into the LDS row xr (float32, the same
+// arithmetic as pool_kernel, so the pooled rows do not depend on which kernel forms them).
+template <typename T, int D>
+__device__ inline void pool_row(const T* __restrict__ head, const attn::RasterGrid& grid, bool raster, uint32_t b,
+                                int lane, float* xr) {
+    constexpr int EPC = Elem<T>::kPerChunk;
+    constexpr int CHUNKS = D / EPC;
+    float acc[EPC];
+    if (raster) block_sum_wave<T, D, 64, 2>(head, BlockRows<true, 64>(grid, b), lane, acc);
+    else block_sum_wave<T, D, 64, 2>(head, BlockRows<false, 64>(grid, b), lane, acc);
+    if (lane < CHUNKS) {
+        constexpr float inv = 1.0f / 64;
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4)
+            *reinterpret_cast<f32x4*>(xr + lane * EPC + e) =
+                f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+    }
+}
+
+// Block means of K (and of Q for callers that want them stored): one wave per (tensor,
+// head, block), float32 means stored as [block][D].
 template <typename T, int D, int N, bool RASTER>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
                                                     const T* __restrict__ k,
@@ -57,50 +129,19 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
                                                     float* __restrict__ kp, int total_blocks, int nb,
                                                     int L, attn::RasterGrid grid, int first_wave) {
     constexpr int EPC = Elem<T>::kPerChunk;
-    constexpr int CHUNKS = D / EPC;          // 16-byte chunks per token
-    constexpr int G = 64 / CHUNKS;           // tokens per load instruction
-    constexpr int ITERS = N / G;
+    constexpr int CHUNKS = D / EPC;
     const int wave = first_wave + ((blockIdx.x * 256 + threadIdx.x) >> 6);
     const int lane = threadIdx.x & 63;
     if (wave >= 2 * total_blocks) return;
     const bool is_k = wave >= total_blocks;
     const int blk = is_k ? wave - total_blocks : wave;
-    // the block's first row: fractal order, runs of N rows; raster order, one 8 x 8 patch
-    const T* src;
-    if (RASTER) {
-        const int bh = blk / nb;
-        src = (is_k ? k : q) + ((size_t)bh * L + attn::block_row<true>(grid, blk - bh * nb)) * D;
-    } else {
-        src = (is_k ? k : q) + (size_t)blk * N * D;
-    }
-    float* dst = (is_k ? kp : qp) + (size_t)blk * D;
-    const int c = lane % CHUNKS;
-    const int g = lane / CHUNKS;
-
-    u32x4 raw[ITERS];
-#pragma unroll
-    for (int r = 0; r < ITERS; ++r) {
-        raw[r] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(src + (size_t)attn::row_in_block<RASTER>(grid, r * G + g) * D) + c);
-    }
+    const int bh = blk / nb;
+    const T* head = (is_k ? k : q) + (size_t)bh * L * D;
     float acc[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int r = 0; r < ITERS; ++r) {
-        float v[EPC];
-        Elem<T>::unpack(raw[r], v);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += v[e];
-    }
-#pragma unroll
-    for (int off = CHUNKS; off < 64; off <<= 1) {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], off);
-    }
-    if (g == 0) {
+    block_sum_wave<T, D, N, 64>(head, BlockRows<RASTER, N>(grid, blk - bh * nb), lane, acc);
+    if (lane < CHUNKS) {
         constexpr float inv = 1.0f / N;      // N is a power of two: exact
-        float* o = dst + c * EPC;
+        float* o = (is_k ? kp : qp) + (size_t)blk * D + lane * EPC;
 #pragma unroll
         for (int e = 0; e < EPC; e += 4) {
             *reinterpret_cast<f32x4*>(o + e) =
@@ -615,16 +656,63 @@ __device__ void sip_row_regs(const float (&v)[NREG], int nb, int budget, const f
 // ---------------------------------------------------------------------------
 // The CDF cut of one row held in registers, in one wave: v[i] = A_j of block
 // j = lane + 64 i (probabilities summing to one; entries past nb must be +0, which no
-// bracket (lo, hi] holds and no sum notices).  The
-// same cut as select_row (bisection over bit patterns from u0 = thr / nb, an exact
-// finish over at most 64 candidates), with every pass over the row running on
-// registers instead of LDS reads; `cand` (one wave's kCap floats of LDS) takes the
-// final candidates.  Then the STA OR, the ascending list, the count and the bitmap.
+// bracket (lo, hi] holds and no sum notices).  The same cut as select_row: bisection over
+// bit patterns from u0 = thr / nb.  The first steps pass over the whole row in
+// registers; once at most kCap values are left in the bracket they are compacted, in
+// block order, through the wave's LDS buffer `cand` into four registers per lane, where
+// the steps continue until at most kFinish remain; those take the exact finish, one per
+// lane.  Then the STA OR (tile coordinates by multiply-high division), the ascending
+// list, the count and the bitmap.
 // ---------------------------------------------------------------------------
+constexpr int kFinish = 16;
+
+// Writes the values of v (NV registers per lane, lane-major) whose bit pattern lies in
+// (lo, hi] to cand in order and returns their number.
+template <int NV>
+__device__ inline int compact_regs(const float (&v)[NV], uint32_t lo, uint32_t hi, float* cand, int lane) {
+    int len = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const uint32_t b = __float_as_uint(v[i]);
+        const bool in = b > lo && b <= hi;
+        const uint64_t ballot = __ballot(in);
+        if (in) cand[len + __popcll(ballot & ((1ull << lane) - 1ull))] = v[i];
+        len += __popcll(ballot);
+    }
+    return len;
+}
+
+// One bisection step over the values in registers: narrows (lo, hi] to the half that
+// holds the cut, keeping g_lo (mass of the values <= lo) and n_in (values in the bracket).
+template <int NV>
+__device__ inline void bisect_step(const float (&v)[NV], uint32_t& lo, uint32_t& hi, float& g_lo, int& n_in,
+                                   float thr) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    float s_ = 0.f;
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const uint32_t b = __float_as_uint(v[i]);
+        const bool in = b > lo && b <= mid;
+        if (in) s_ += v[i];
+        c += __popcll(__ballot(in));
+    }
+    s_ = wave_sum(s_);
+    if (g_lo + s_ > thr) {
+        hi = mid;
+        n_in = c;
+    } else {
+        lo = mid;
+        g_lo += s_;
+        n_in -= c;
+    }
+}
+
 template <int NREG>
 __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int bh, int row, float thr, int sta,
-                                int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
-                                int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int lane) {
+                                FastDiv fd_pf, FastDiv fd_nw, int rt, int rh, int rw,
+                                int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
+                                uint32_t* __restrict__ bitmap, int lane) {
     const int nwords = (nb + 31) >> 5;
     // start of the bracket: u0 = thr / nb, nudged down so rounding cannot push g(u0)
     // above thr; verified below and dropped to 0 if it fails
@@ -650,61 +738,42 @@ __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int
         for (int i = 0; i < NREG; ++i) n_in += __popcll(__ballot(__float_as_uint(v[i]) > 0u));
     }
     uint32_t hi = maxb;
-    // bisection until at most 64 values are left in the bracket (lo, hi]
-    while (hi - lo > 1 && n_in > 64) {
-        const uint32_t mid = lo + ((hi - lo) >> 1);
-        float s_ = 0.f;
-        int c = 0;
-#pragma unroll
-        for (int i = 0; i < NREG; ++i) {
-            const uint32_t b = __float_as_uint(v[i]);
-            const bool in = b > lo && b <= mid;
-            if (in) s_ += v[i];
-            c += __popcll(__ballot(in));
-        }
-        s_ = wave_sum(s_);
-        if (g_lo + s_ > thr) {
-            hi = mid;
-            n_in = c;
-        } else {
-            lo = mid;
-            g_lo += s_;
-            n_in -= c;
-        }
-    }
+    // bracket (lo, hi]: g(lo) = g_lo <= thr and, unless the whole row sums to at most
+    // thr, g(hi) > thr; n_in values lie inside it (always >= 1: the maximum)
+    while (hi - lo > 1 && n_in > kCap) bisect_step(v, lo, hi, g_lo, n_in, thr);
     uint32_t cut = hi;
-    if (n_in <= 64) {
-        // one candidate per lane: F(x) = g_lo + (sum of the candidates <= x), tied
-        // values together; the cut is the smallest candidate with F(x) > thr
-        int len = 0;
+    if (n_in <= kCap) {
+        float c4[kCap / 64];
+        const int len = compact_regs(v, lo, hi, cand, lane);
 #pragma unroll
-        for (int i = 0; i < NREG; ++i) {
-            const uint32_t b = __float_as_uint(v[i]);
-            const bool in = b > lo && b <= hi;
-            const uint64_t ballot = __ballot(in);
-            if (in) cand[len + __popcll(ballot & ((1ull << lane) - 1ull))] = v[i];
-            len += __popcll(ballot);
+        for (int k = 0; k < kCap / 64; ++k) c4[k] = lane + 64 * k < len ? cand[lane + 64 * k] : 0.f;
+        while (hi - lo > 1 && n_in > kFinish) bisect_step(c4, lo, hi, g_lo, n_in, thr);
+        if (n_in <= kFinish) {
+            // one candidate per lane: F(x) = g_lo + (sum of the candidates <= x), tied
+            // values together; the cut is the smallest candidate with F(x) > thr
+            const int m_len = compact_regs(c4, lo, hi, cand, lane);
+            const float x = lane < m_len ? cand[lane] : 0.f;
+            const uint32_t bx = __float_as_uint(x);
+            float below = 0.f;
+            for (int m = 0; m < m_len; ++m) {
+                const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), m));
+                if (__float_as_uint(y) <= bx) below += y;
+            }
+            const bool crosses = lane < m_len && g_lo + below > thr;
+            const uint32_t pick = crosses ? bx : 0xffffffffu;
+            const uint32_t best = ~wave_max_u(~pick);   // smallest pattern among the crossing ones
+            if (best != 0xffffffffu) cut = best;
         }
-        const float x = lane < len ? cand[lane] : 0.f;
-        const uint32_t bx = __float_as_uint(x);
-        float below = 0.f;
-        for (int m = 0; m < len; ++m) {
-            const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), m));
-            if (__float_as_uint(y) <= bx) below += y;
-        }
-        const bool crosses = lane < len && g_lo + below > thr;
-        const uint32_t pick = crosses ? bx : 0xffffffffu;
-        const uint32_t best = ~wave_max_u(~pick);   // smallest pattern among the crossing ones
-        if (best != 0xffffffffu) cut = best;
     }
 
     int qt = 0, qh_ = 0, qw = 0;
-    const int pf = nH * nW;
     if (sta) {
-        qt = row / pf;
-        const int rem = row - qt * pf;
-        qh_ = rem / nW;
-        qw = rem - qh_ * nW;
+        uint32_t t_, rem_, h_, w_;
+        fd_pf.divmod((uint32_t)row, t_, rem_);
+        fd_nw.divmod(rem_, h_, w_);
+        qt = (int)t_;
+        qh_ = (int)h_;
+        qw = (int)w_;
     }
     int32_t* out_idx = kv_index + ((size_t)bh * nb + row) * nb;
     uint32_t* out_bits = bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr;
@@ -716,11 +785,10 @@ __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int
         if (j < nb) {
             keep = __float_as_uint(v[i]) >= cut;
             if (sta && !keep) {
-                const int kt = j / pf;
-                const int rem = j - kt * pf;
-                const int kh_ = rem / nW;
-                const int kw = rem - kh_ * nW;
-                keep = abs(kt - qt) <= rt && abs(kh_ - qh_) <= rh && abs(kw - qw) <= rw;
+                uint32_t kt, rem, kh_, kw;
+                fd_pf.divmod((uint32_t)j, kt, rem);
+                fd_nw.divmod(rem, kh_, kw);
+                keep = abs((int)kt - qt) <= rt && abs((int)kh_ - qh_) <= rh && abs((int)kw - qw) <= rw;
             }
         }
         const uint64_t ballot = __ballot(keep);
@@ -737,7 +805,8 @@ __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int
 
 // ---------------------------------------------------------------------------
 // NABLA's reduced map and cut in one kernel.  A workgroup (16 waves) owns kRows = 16
-// pooled query rows of one head, and wave r owns row r: the row ends up in the wave's
+// query blocks of one head; wave r pools block r from Q (block_sum_wave, as pool_kernel
+// does for K) and owns row r of the map: the row ends up in the wave's
 // registers (v[i] = S_j of block j = lane + 64 i), so the softmax and the cut run without
 // touching LDS.  The map runs in chunks of 256 columns: each wave computes one 16 x 16
 // tile of the chunk on the float32 MFMA (map_tile) into an LDS chunk buffer, and after
@@ -750,14 +819,14 @@ __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int
 constexpr int kWaves = 16;
 constexpr int kChunkCols = 16 * kWaves;     // one 16-column tile per wave
 constexpr int kChunkLd = kChunkCols + 4;    // padded row: the 16 x 16 tile stores hit distinct banks
-constexpr int kFinalCand = 64;              // candidates of a row's exact finish
+constexpr int kRowCand = kCap;              // a wave's compacted candidates
 
 // One 16 x 16 tile of X Kp^T (unscaled): the kRows X rows staged in x_lds, columns
 // j0 .. j0 + 15 of the head's Kp [nb, D] (columns past nb read as zeros).  Lane (row/col
 // l % 16, group g = l / 16) supplies coordinate 16 m + 4 g + i at MFMA step 4 m + i in
 // both operands, so each 16-byte load reads 64 contiguous bytes of 16 rows.  The Kp
-// operand is loaded two 16-byte chunks at a time (8 VGPRs), leaving the registers to the
-// wave's row.
+// operand is loaded in two halves of d (two load round trips per tile, 16 VGPRs at
+// d = 128), leaving the registers to the wave's row.
 template <int D>
 __device__ inline f32x4 map_tile(const float* __restrict__ x_lds, const float* __restrict__ kh, int nb, int j0,
                                  int lane) {
@@ -768,17 +837,21 @@ __device__ inline f32x4 map_tile(const float* __restrict__ x_lds, const float* _
     const f32x4* xa = reinterpret_cast<const f32x4*>(x_lds + li * kXld<D>) + kq;
     const f32x4* src = reinterpret_cast<const f32x4*>(kh + (size_t)min(j, nb - 1) * D) + kq;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    constexpr int H = KC / 8;   // chunks per half: two load round trips per tile
 #pragma unroll 1
-    for (int m = 0; m < KC / 4; m += 2) {
-        f32x4 b0 = src[4 * m];
-        f32x4 b1 = src[4 * m + 4];
-        if (j >= nb) b0 = b1 = f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 a0 = xa[4 * m];
-        const f32x4 a1 = xa[4 * m + 4];
+    for (int h = 0; h < 2; ++h) {
+        f32x4 b[H];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[i], b0[i], acc, 0, 0, 0);
+        for (int m = 0; m < H; ++m) {
+            b[m] = src[4 * (h * H + m)];
+            if (j >= nb) b[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[i], b1[i], acc, 0, 0, 0);
+        for (int m = 0; m < H; ++m) {
+            const f32x4 a = xa[4 * (h * H + m)];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[m][i], acc, 0, 0, 0);
+        }
     }
     return acc;
 }
@@ -788,24 +861,35 @@ __device__ inline f32x4 map_tile(const float* __restrict__ x_lds, const float* _
 template <int NREG>
 constexpr int kMapSelectWaves = NREG > 20 ? 4 : 8;
 
-template <int D, int NREG>
+template <int D, int NREG, bool SIP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMapSelectWaves<NREG>,
                                                                              kMapSelectWaves<NREG>))) void
-map_select_kernel(const float* __restrict__ qp, const float* __restrict__ kp, int nb, float scale, float thr, int sta,
-                  int nH, int nW, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
+map_select_kernel(const void* __restrict__ q, int bf16, int raster, attn::RasterGrid grid, int L,
+                  const float* __restrict__ kp, int nb, float scale, float thr, int sta,
+                  FastDiv fd_pf, FastDiv fd_nw, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
                   int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int sip_budget,
                   const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
-    // [2][kRows][kChunkLd] chunk buffers, [kWaves][kFinalCand] candidates, [kRows][kXld] pooled queries
+    // [2][kRows][kChunkLd] chunk buffers, [kWaves][kRowCand] candidates, [kRows][kXld] pooled queries
     extern __shared__ __align__(16) float s_lds[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kRows;
     const int row = row0 + wave;
-    float* cand = s_lds + 2 * kRows * kChunkLd + wave * kFinalCand;
-    float* x_lds = s_lds + 2 * kRows * kChunkLd + kWaves * kFinalCand;
+    float* cand = s_lds + 2 * kRows * kChunkLd + wave * kRowCand;
+    float* x_lds = s_lds + 2 * kRows * kChunkLd + kWaves * kRowCand;
     const float* kh = kp + (size_t)bh * nb * D;
-    stage_rows<D, kWaves * 64>(qp + (size_t)bh * nb * D, nb, row0, x_lds);
+    // the workgroup's pooled query rows: wave w forms the mean of query block row0 + w
+    // from Q itself (zeros past nb), so Q is read once, here, beside other workgroups' work
+    {
+        float* xr = x_lds + wave * kXld<D>;
+        if (row < nb) {
+            if (bf16) pool_row<__bf16, D>((const __bf16*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row, lane, xr);
+            else pool_row<float, D>((const float*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row, lane, xr);
+        } else {
+            for (int e = lane; e < D; e += 64) xr[e] = 0.f;
+        }
+    }
     __syncthreads();
 
     float v[NREG];
@@ -849,14 +933,15 @@ map_select_kernel(const float* __restrict__ qp, const float* __restrict__ kp, in
     const float inv_sum = 1.0f / wave_sum(sum);
 #pragma unroll
     for (int i = 0; i < NREG; ++i) v[i] *= inv_sum;
-    if (sip_budget > 0) {
+    if constexpr (SIP) {
         const int nwords = (nb + 31) >> 5;
         sip_row_regs<NREG>(v, nb, sip_budget, uniforms + ((size_t)bh * nb + row) * nb,
                            kv_index + ((size_t)bh * nb + row) * nb, kv_logw + ((size_t)bh * nb + row) * nb,
                            bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr, nwords,
                            kv_count + (size_t)bh * nb + row, lane);
     } else {
-        select_row_regs<NREG>(v, cand, nb, bh, row, thr, sta, nH, nW, rt, rh, rw, kv_count, kv_index, bitmap, lane);
+        select_row_regs<NREG>(v, cand, nb, bh, row, thr, sta, fd_pf, fd_nw, rt, rh, rw, kv_count, kv_index, bitmap,
+                              lane);
     }
 }
 
@@ -1004,7 +1089,7 @@ template <typename T, int D>
 hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
     const int total = a.BH * a.nb;
     const int waves = 2 * total;
-    const int first = a.ibcs ? total : 0;   // IBCS clusters Q instead of pooling it
+    const int first = total;   // K only: NABLA's map pools Q itself, IBCS clusters Q
     attn::RasterGrid grid{};
     if (a.raster) {
         grid.W = (uint32_t)a.W;
@@ -1022,14 +1107,28 @@ hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
 
 template <int D, int NREG>
 hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
-    const size_t lds = ((size_t)2 * kRows * kChunkLd + (size_t)kWaves * kFinalCand + (size_t)kRows * kXld<D>) *
+    const size_t lds = ((size_t)2 * kRows * kChunkLd + (size_t)kWaves * kRowCand + (size_t)kRows * kXld<D>) *
                        sizeof(float);
-    static_assert((2 * kRows * kChunkLd + kWaves * kFinalCand + kRows * kXld<128>) * sizeof(float) <= 64 * 1024,
-                  "map/select LDS within the default dynamic limit");
+    static_assert((2 * kRows * kChunkLd + kWaves * kRowCand + kRows * kXld<128>) * sizeof(float) <= 64 * 1024,
+                  "map/select LDS within the default dynamic limit, two workgroups per CU");
     dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
-    hipLaunchKernelGGL((map_select_kernel<D, NREG>), grid, dim3(kWaves * 64), lds, s, a.qp, a.kp, a.nb, a.scale,
-                       a.thr, a.sta, a.nH, a.nW, a.rt, a.rh, a.rw, a.kv_count, a.kv_index, a.bitmap, a.sip_budget,
-                       a.uniforms, a.kv_logw);
+    const FastDiv fd_pf((uint32_t)(a.nH * a.nW)), fd_nw((uint32_t)a.nW);   // block -> (frame, patch row, column)
+    attn::RasterGrid rg{};
+    if (a.raster) {
+        rg.W = (uint32_t)a.W;
+        rg.HW = (uint32_t)(a.H * a.W);
+        rg.nHW = FastDiv((uint32_t)(a.nH * a.nW));
+        rg.nW = FastDiv((uint32_t)a.nW);
+    }
+    if (a.sip_budget > 0) {
+        hipLaunchKernelGGL((map_select_kernel<D, NREG, true>), grid, dim3(kWaves * 64), lds, s, a.q, a.bf16, a.raster,
+                           rg, a.nb * 64, a.kp, a.nb, a.scale, a.thr, a.sta, fd_pf, fd_nw, a.rt, a.rh, a.rw,
+                           a.kv_count, a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
+    } else {
+        hipLaunchKernelGGL((map_select_kernel<D, NREG, false>), grid, dim3(kWaves * 64), lds, s, a.q, a.bf16,
+                           a.raster, rg, a.nb * 64, a.kp, a.nb, a.scale, a.thr, a.sta, fd_pf, fd_nw, a.rt, a.rh,
+                           a.rw, a.kv_count, a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
+    }
     return hipGetLastError();
 }
 

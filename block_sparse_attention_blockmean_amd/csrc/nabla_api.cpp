@@ -85,14 +85,14 @@ namespace {
 
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Sections of the NABLA workspace: pooled Q, pooled K.
+// The NABLA workspace: the pooled K (the map kernel pools Q itself).
 struct NablaSections {
-    size_t qp, kp;
-    size_t total() const { return qp + kp; }
+    size_t kp;
+    size_t total() const { return kp; }
 };
 
 NablaSections nabla_sections(long long BH, long long nb, int d) {
-    return {up256((size_t)BH * nb * d * sizeof(float)), up256((size_t)BH * nb * d * sizeof(float))};
+    return {up256((size_t)BH * nb * d * sizeof(float))};
 }
 
 }  // namespace
@@ -269,10 +269,10 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     // the launches cover up to 256 threads per block of every head with 32-bit thread ids
     if ((long long)batch * heads > 65535 || L * d >= kMaxHeadElems || (long long)batch * heads * nb >= (1ll << 24))
         return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
-    // pooled Q and K of one head (each section a multiple of 256 bytes for d = 64, 128)
-    const size_t head_pool_bytes = 2 * (size_t)nb * d * sizeof(float);
+    // pooled K of one head (a multiple of 256 bytes for d = 64, 128)
+    const size_t head_pool_bytes = (size_t)nb * d * sizeof(float);
     if (use_scratch && head_pool_bytes > nabla::kScratchBytes)
-        return fail(NABLA_E_UNSUPPORTED, "%s: one head's pooled Q and K need %zu bytes, the scratch holds %zu", who,
+        return fail(NABLA_E_UNSUPPORTED, "%s: one head's pooled K needs %zu bytes, the scratch holds %zu", who,
                     head_pool_bytes, nabla::kScratchBytes);
     const size_t need = ibcs_q_group ? nabla_build_mask_ibcs_workspace_size(batch, heads, (int)L, d, N, ibcs_q_group)
                                      : nabla_build_mask_workspace_size(batch, heads, (int)L, d, N);
@@ -319,11 +319,9 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
         a.ibcs = 1;
         a.ibcs_group = ibcs_q_group / N;
     } else {
-        // [Qp | Kp], sections 256-byte aligned
-        const NablaSections sec = nabla_sections(a.BH, nb, d);
-        char* base = (char*)workspace;
-        a.qp = (float*)base;
-        a.kp = (float*)(base + sec.qp);
+        // [Kp]
+        a.qp = nullptr;
+        a.kp = (float*)workspace;
     }
     a.bf16 = dtype == NABLA_BF16;
     a.raster = raster;
@@ -334,7 +332,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     a.kv_logw = kv_logw;
     if (!use_scratch) return hip_status(nabla::launch_build_mask(a, stream), who);
 
-    // Heads in chunks whose pooled Q and K fit the scratch, each chunk's launches reusing
+    // Heads in chunks whose pooled K fits the scratch, each chunk's launches reusing
     // it in stream order; the start order, which reads only the counts, runs once at the end.
     const int per_chunk = (int)(workspace_bytes / head_pool_bytes);
     const size_t head_bytes = (size_t)L * d * elem_size(dtype);
@@ -348,8 +346,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
         c.kv_index = kv_index + (size_t)h0 * nb * nb;
         c.bitmap = bitmap ? bitmap + (size_t)h0 * nb * words : nullptr;
         c.schedule = nullptr;
-        c.qp = (float*)workspace;
-        c.kp = (float*)((char*)workspace + (size_t)c.BH * nb * d * sizeof(float));
+        c.kp = (float*)workspace;
         nabla_status st = hip_status(nabla::launch_build_mask(c, stream), who);
         if (st != NABLA_OK) return st;
     }

@@ -79,10 +79,10 @@ nabla_status nabla_reorder(const void* src, void* dst, int batch, int heads, int
 
 /*
  * nabla_build_mask_workspace_size - bytes of device workspace nabla_build_mask (and its
- * raster and SIP forms) needs (BH = batch*heads, nb = L/N): the pooled Q and the pooled
- * K, BH*nb*d floats each, each section rounded up to 256 bytes.  After a call they hold
- * those means, float32, row-major.  Returns 0 for non-positive sizes or L not a
- * multiple of N.
+ * raster and SIP forms) needs (BH = batch*heads, nb = L/N): the pooled K, BH*nb*d floats,
+ * rounded up to 256 bytes.  After a call it holds those means, float32, row-major (the
+ * pooled Q is formed inside the map kernel and not stored).  Returns 0 for non-positive
+ * sizes or L not a multiple of N.
  */
 size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N);
 
@@ -191,9 +191,9 @@ nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, in
  * nabla_build_mask_raster_noalloc - nabla_build_mask_raster for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): no workspace argument, and no allocation of any kind.  The
- * pooled Q and K live in a device array of the library, NABLA_NOALLOC_SCRATCH_BYTES per
+ * pooled K lives in a device array of the library, NABLA_NOALLOC_SCRATCH_BYTES per
  * GPU, held from the library's load until the process ends; heads are processed in
- * chunks whose pooled Q and K fit in it (2 * nb * d * 4 bytes per head), one launch
+ * chunks whose pooled K fits in it (nb * d * 4 bytes per head), one launch
  * sequence per chunk on `stream`.  Results (counts, lists, bitmap, schedule) are those of
  * nabla_build_mask_raster on the same arguments.
  * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
@@ -201,7 +201,7 @@ nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, in
  * lists.  Nothing in the array needs clearing between calls: each chunk writes its pooled
  * means before reading them.
  * Errors: as nabla_build_mask_raster (without the workspace errors), plus
- * NABLA_E_UNSUPPORTED when one head's pooled Q and K exceed the array.
+ * NABLA_E_UNSUPPORTED when one head's pooled K exceeds the array.
  */
 #define NABLA_NOALLOC_SCRATCH_BYTES (32u << 20)
 nabla_status nabla_build_mask_raster_noalloc(const void* q, const void* k, int batch, int heads, int T,
