@@ -856,14 +856,16 @@ __device__ inline f32x4 map_tile(const float* __restrict__ x_lds, const float* _
     return acc;
 }
 
-// Rows of up to 20 register blocks (1280 KV blocks) run eight waves per SIMD (two
-// workgroups per CU) within 64 VGPRs; longer rows four waves per SIMD with 128.
-template <int NREG>
-constexpr int kMapSelectWaves = NREG > 20 ? 4 : 8;
+// Rows of up to 24 register blocks (1536 KV blocks) run eight waves per SIMD (two
+// workgroups per CU) within 64 VGPRs; longer rows four waves per SIMD with 128, and so
+// does the SIP form from rows of 12 registers on (it keeps more values live across its
+// water-level loop).
+template <int NREG, bool SIP>
+constexpr int kMapSelectWaves = (NREG > 24 || (SIP && NREG >= 12)) ? 4 : 8;
 
 template <int D, int NREG, bool SIP>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMapSelectWaves<NREG>,
-                                                                             kMapSelectWaves<NREG>))) void
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMapSelectWaves<NREG, SIP>,
+                                                                             kMapSelectWaves<NREG, SIP>))) void
 map_select_kernel(const void* __restrict__ q, int bf16, int raster, attn::RasterGrid grid, int L,
                   const float* __restrict__ kp, int nb, float scale, float thr, int sta,
                   FastDiv fd_pf, FastDiv fd_nw, int rt, int rh, int rw, int32_t* __restrict__ kv_count,

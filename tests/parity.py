@@ -61,9 +61,15 @@ def cutoff_ambiguity(A: np.ndarray, thr: float, eps: float = TIE_EPS) -> np.ndar
     return amb.reshape(A.shape)
 
 
-def check_mask(gpu_mask: np.ndarray, oracle_mask: np.ndarray, oracle_A: np.ndarray, thr: float):
+def check_mask(gpu_mask: np.ndarray, oracle_mask: np.ndarray, oracle_A: np.ndarray, thr: float,
+               oracle_F: np.ndarray = None, counts: dict = None):
     """Bit-exact except blocks at the cutoff (see cutoff_ambiguity), and those at most
-    MAX_BAND_FRAC of all blocks.  Returns (mismatches, band population)."""
+    MAX_BAND_FRAC of all blocks.  Returns (mismatches, band population).
+
+    With the oracle's F, the mismatches are also split into those the plain band
+    |F - thr| <= BAND admits and those only the near-tie extension admits; the plain
+    ones must stay within MAX_BAND_FRAC on their own.  ``counts`` (a dict) accumulates
+    blocks, mismatches, plain, tie_only and band."""
     assert gpu_mask.shape == oracle_mask.shape
     mism = gpu_mask != oracle_mask
     in_band = cutoff_ambiguity(oracle_A, thr)
@@ -72,6 +78,16 @@ def check_mask(gpu_mask: np.ndarray, oracle_mask: np.ndarray, oracle_A: np.ndarr
         f"{int(outside.sum())} mask disagreements outside the band, e.g. at "
         f"{np.argwhere(outside)[:5].tolist()}")
     assert mism.sum() <= MAX_BAND_FRAC * mism.size, f"{int(mism.sum())} band disagreements"
+    if oracle_F is not None:
+        plain = mism & (np.abs(np.asarray(oracle_F, dtype=np.float64) - thr) <= BAND)
+        assert plain.sum() <= MAX_BAND_FRAC * mism.size, f"{int(plain.sum())} plain-band disagreements"
+        if counts is not None:
+            counts["plain"] = counts.get("plain", 0) + int(plain.sum())
+            counts["tie_only"] = counts.get("tie_only", 0) + int((mism & ~plain).sum())
+    if counts is not None:
+        counts["blocks"] = counts.get("blocks", 0) + int(mism.size)
+        counts["mismatches"] = counts.get("mismatches", 0) + int(mism.sum())
+        counts["band"] = counts.get("band", 0) + int(in_band.sum())
     return int(mism.sum()), int(in_band.sum())
 
 

@@ -280,21 +280,70 @@ def test_max_blocks_per_head():
     assert worst <= TOL_BF16
 
 
+def _full_sample(G, nb, cnt, rng, frac=0.01):
+    """Every query block of the first and the last (batch, head), plus a seeded fraction
+    of the blocks of every other head (at least one per head), plus the longest and the
+    shortest list."""
+    pairs = {(g, i) for g in {0, G - 1} for i in range(nb)}
+    per = max(1, int(round(frac * nb)))
+    for g in range(1, G - 1):
+        for i in rng.choice(nb, size=per, replace=False):
+            pairs.add((g, int(i)))
+    flat = cnt.reshape(-1)
+    for f in (int(np.argmax(flat)), int(np.argmin(flat))):
+        pairs.add((f // nb, f % nb))
+    return sorted(pairs)
+
+
+def _raster_path(cfg, qd, kd, vd, thr, sta):
+    T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
+    cnt, idx, bm, sched = nab.build_mask(qd, kd, T, H, W, P, N, thr, sta, with_bitmap=True, with_schedule=True,
+                                         raster=True)
+    o = nab.attn_fwd_raster(qd, kd, vd, cnt, idx, T, H, W, P, N, schedule=sched)
+    torch.cuda.synchronize()
+    return cnt, idx, bm, sched, o
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [c for c in CONFIGS if c.name != "tiny"], ids=lambda c: c.name)
 def test_full_config_parity(cfg):
-    """Full mask parity on every head; attention on a seeded sample of query blocks
-    (rows are independent given the mask, so sampled rows are exact checks)."""
+    """At full size, for every threshold of the workload: the raster-order entry points
+    (the path the bench times) give the explicit path's counts, lists, bitmap, start order
+    and output bit for bit; the mask matches the oracle on every head by the band rule,
+    with its mismatches split into plain-band and near-tie-only ones; with a window, the
+    window-free mask (STA off) matches the oracle's CDF part on its own, and the kept
+    fractions of the CDF part, the window and their union are reported; attention matches
+    the oracle (evaluated with the GPU's mask, float32) on every query block of the first
+    and last (batch, head) and a seeded 1% of the others' (rows are independent given the
+    mask, so each is an exact check)."""
     say(f"full config {cfg.name}: {cfg.B}x{cfg.heads} L{cfg.L} nb{cfg.nb}")
     q, k, v = make_qkv(cfg)
     say("  inputs generated")
-    G = cfg.BH
+    G, nb = cfg.BH, cfg.nb
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    sta_part = None
+    if cfg.sta is not None:
+        sta_part = O.sta_mask(cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, cfg.sta)
     for thr in (cfg.thr_list or (cfg.thr,)):
         res = run_gpu_path(cfg, q, k, v, thr=thr)
-        cnt = res["cnt"].cpu().numpy().reshape(G, cfg.nb)
-        idx = res["idx"].cpu().numpy().reshape(G, cfg.nb, cfg.nb)
+        ras = _raster_path(cfg, qd, kd, vd, thr, cfg.sta)
+        assert torch.equal(res["cnt"], ras[0]) and torch.equal(res["bitmap"], ras[2])
+        assert torch.equal(res["sched"], ras[3])
+        assert torch.equal(res["o"].view(torch.int16), ras[4].view(torch.int16)), "raster output differs"
+        cnt = res["cnt"].cpu().numpy().reshape(G, nb)
+        idx = res["idx"].cpu().numpy().reshape(G, nb, nb)
         gmask = lists_to_mask(cnt, idx)
-        mism_tot = 0
-        band_tot = 0
+        assert np.array_equal(lists_to_mask(cnt, ras[1].cpu().numpy().reshape(G, nb, nb)), gmask)
+        del ras
+        # the window-free mask of the same inputs (the CDF part alone)
+        nabla_only = None
+        if cfg.sta is not None:
+            c2, i2 = nab.build_mask(res["qf"], res["kf"], cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, None)
+            torch.cuda.synchronize()
+            nabla_only = lists_to_mask(c2.cpu().numpy().reshape(G, nb), i2.cpu().numpy().reshape(G, nb, nb))
+            assert np.all(gmask >= nabla_only) and np.all(gmask >= sta_part[None])
+            assert np.array_equal(gmask, nabla_only | sta_part[None])
+        counts, counts_nabla = {}, {}
         # oracle mask, a few heads at a time to bound host memory
         for g0 in range(0, G, 8):
             sl = slice(g0, min(G, g0 + 8))
@@ -303,27 +352,30 @@ def test_full_config_parity(cfg):
             qf = O.reorder(qn, cfg.T, cfg.H, cfg.W, cfg.P)
             kf = O.reorder(kn, cfg.T, cfg.H, cfg.W, cfg.P)
             ref = O.block_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, cfg.sta)
-            mism, band = check_mask(gmask[sl], ref["mask"], ref["A"], thr)
-            mism_tot += mism
-            band_tot += band
-            say(f"  heads {g0}..{sl.stop - 1}: mask mismatches {mism}, band {band}")
-        assert mism_tot <= 1e-3 * gmask.size
-        say(f"  thr {thr}: kept {gmask.mean():.4f}  mismatches {mism_tot}  band {band_tot}")
+            check_mask(gmask[sl], ref["mask"], ref["A"], thr, ref["F"], counts)
+            if nabla_only is not None:
+                check_mask(nabla_only[sl], ref["mask_nabla"], ref["A"], thr, ref["F"], counts_nabla)
+        say(f"  thr {thr}: kept {gmask.mean():.4f}; mask mismatches {counts['mismatches']} of {counts['blocks']} "
+            f"(plain band {counts['plain']}, near-tie only {counts['tie_only']}), band population {counts['band']}")
+        if nabla_only is not None:
+            say(f"  thr {thr}: kept fractions: CDF part {nabla_only.mean():.4f}, window {sta_part.mean():.4f}, "
+                f"union {gmask.mean():.4f}; CDF-part mismatches {counts_nabla['mismatches']} "
+                f"(plain band {counts_nabla['plain']}, near-tie only {counts_nabla['tie_only']})")
         rng = np.random.default_rng(cfg.index)
-        blocks = _sample_blocks(G, cfg.nb, cnt, rng)
+        blocks = _full_sample(G, nb, cnt, rng)
         of = res["of"].reshape(G, cfg.L, cfg.d)
         worst = 0.0
         heads = sorted({g for g, _ in blocks})
         for g in heads:
             qf, kf, vf = (O.reorder(to_np(t.reshape(G, cfg.L, cfg.d)[g]), cfg.T, cfg.H, cfg.W, cfg.P)
                           for t in (q, k, v))
+            got_h = to_np(of[g])
             for gg, i in blocks:
                 if gg != g:
                     continue
-                ref_o = O.attention_block(qf, kf, vf, gmask[g, i], i, cfg.N, 1.0 / np.sqrt(cfg.d))
-                got = to_np(of[g, i * cfg.N:(i + 1) * cfg.N])
-                worst = max(worst, max_abs(got, ref_o))
-        say(f"  attention on {len(blocks)} sampled blocks: max-abs {worst:.3e}")
+                ref_o = O.attention_block(qf, kf, vf, gmask[g, i], i, cfg.N, 1.0 / np.sqrt(cfg.d), np.float32)
+                worst = max(worst, max_abs(got_h[i * cfg.N:(i + 1) * cfg.N], ref_o))
+        say(f"  attention on {len(blocks)} query blocks ({len(heads)} heads): max-abs {worst:.3e}")
         assert worst <= TOL_BF16
         del res
         torch.cuda.empty_cache()
