@@ -51,7 +51,12 @@ PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_blockmean_amd", "csrc", "attn_bf16.hip")
 ATTN_TILE = os.path.join(ROOT, "block_sparse_attention_blockmean_amd", "csrc", "attn_tile.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_file(workload: str) -> str:
+    """The committed --pmc summary of the attention kernel on one workload."""
+    return os.path.join(PROFILES, f"attn_fwd_bf16_{workload}_traffic.txt")
 
 
 def kernel_source_hash() -> str:
@@ -66,10 +71,11 @@ def kernel_source_hash() -> str:
 def read_traffic(workload: str, kernel: str):
     """HBM bytes per attention launch from the committed --pmc summary, valid only
     if it was taken on the current kernel source, for this workload and this kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for ln in open(TRAFFIC_FILE):
+    for ln in open(path):
         if ":" in ln and not ln.lstrip().startswith("#"):
             key, val = ln.split(":", 1)
             kv[key.strip()] = val.strip()

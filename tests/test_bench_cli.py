@@ -1,6 +1,7 @@
 """bench.py's command-line contract on a machine without a GPU: more than one GPU is
 refused with exit status 2 and a message naming the reason, and a run with no GPU fails
 loudly rather than falling back to the CPU."""
+import glob
 import os
 import subprocess
 import sys
@@ -32,22 +33,31 @@ def test_no_gpu_fails_loudly():
 
 
 def test_traffic_figure_only_for_its_workload_and_kernel():
-    """The committed counter figure belongs to one kernel on one workload: any other
+    """Each committed counter figure belongs to one kernel on one workload: any other
     bench line reports its traffic as unknown rather than borrowing it."""
     sys.path.insert(0, ROOT)
     import bench
-    kv = {}
-    for ln in open(bench.TRAFFIC_FILE):
-        if ":" in ln and not ln.lstrip().startswith("#"):
-            key, val = ln.split(":", 1)
-            kv[key.strip()] = val.strip()
-    own = (kv["workload"], kv["kernel"])
-    t = bench.read_traffic(*own)
-    assert t is None or t > 0
+    files = sorted(glob.glob(os.path.join(bench.PROFILES, "attn_fwd_bf16_*_traffic.txt")))
+    assert files, "no committed traffic summary"
+    owners = []
+    for path in files:
+        kv = {}
+        for ln in open(path):
+            if ":" in ln and not ln.lstrip().startswith("#"):
+                key, val = ln.split(":", 1)
+                kv[key.strip()] = val.strip()
+        assert path == bench.traffic_file(kv["workload"])
+        owners.append((kv["workload"], kv["kernel"]))
+        t = bench.read_traffic(kv["workload"], kv["kernel"])
+        # valid only while the kernel source is the one the counters were taken on
+        if kv["kernel_source_sha256"] == bench.kernel_source_hash():
+            assert t == float(kv["hbm_bytes_per_launch"]) > 0
+        else:
+            assert t is None
     for other in [("tiny", "attn_fwd_f32_kernel<64, raster>"), ("wan14b_720p_cfg", "attn_fwd_bf16_kernel<128, fractal>"),
                   ("hunyuan_720p_sta", "attn_fwd_bf16_kernel<128, raster>"), ("wan1.3b_480p", "attn_fwd_bf16_kernel<128, fractal>"),
                   ("wan14b_720p_cfg", "attn_fwd_bf16_kernel<128, raster>"), ("wan1.3b_480p", "attn_fwd_bf16_kernel<128, raster>")]:
-        if other != own:
+        if other not in owners:
             assert bench.read_traffic(*other) is None, other
 
 
