@@ -101,71 +101,6 @@ struct BlockRows {
     __device__ uint32_t operator()(int r) const { return base + attn::row_in_block<RASTER>(grid, r); }
 };
 
-// Mean of query block b of one head (one wave) into the LDS row xr (float32, the same
-// arithmetic as pool_kernel, so the pooled rows do not depend on which kernel forms them).
-template <typename T, int D>
-__device__ inline void pool_row(const T* __restrict__ head, const attn::RasterGrid& grid, bool raster, uint32_t b,
-                                int lane, float* xr) {
-    constexpr int EPC = Elem<T>::kPerChunk;
-    constexpr int CHUNKS = D / EPC;
-    float acc[EPC];
-    if (raster) block_sum_wave<T, D, 64, 2>(head, BlockRows<true, 64>(grid, b), lane, acc);
-    else block_sum_wave<T, D, 64, 2>(head, BlockRows<false, 64>(grid, b), lane, acc);
-    if (lane < CHUNKS) {
-        constexpr float inv = 1.0f / 64;
-#pragma unroll
-        for (int e = 0; e < EPC; e += 4)
-            *reinterpret_cast<f32x4*>(xr + lane * EPC + e) =
-                f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
-    }
-}
-
-// Block means of K (and of Q for callers that want them stored): one wave per (tensor,
-// head, block), float32 means stored as [block][D].
-template <typename T, int D, int N, bool RASTER>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
-                                                    const T* __restrict__ k,
-                                                    float* __restrict__ qp,
-                                                    float* __restrict__ kp, int total_blocks, int nb,
-                                                    int L, attn::RasterGrid grid, int first_wave) {
-    constexpr int EPC = Elem<T>::kPerChunk;
-    constexpr int CHUNKS = D / EPC;
-    const int wave = first_wave + ((blockIdx.x * 256 + threadIdx.x) >> 6);
-    const int lane = threadIdx.x & 63;
-    if (wave >= 2 * total_blocks) return;
-    const bool is_k = wave >= total_blocks;
-    const int blk = is_k ? wave - total_blocks : wave;
-    const int bh = blk / nb;
-    const T* head = (is_k ? k : q) + (size_t)bh * L * D;
-    float acc[EPC];
-    block_sum_wave<T, D, N, 64>(head, BlockRows<RASTER, N>(grid, blk - bh * nb), lane, acc);
-    if (lane < CHUNKS) {
-        constexpr float inv = 1.0f / N;      // N is a power of two: exact
-        float* o = (is_k ? kp : qp) + (size_t)blk * D + lane * EPC;
-#pragma unroll
-        for (int e = 0; e < EPC; e += 4) {
-            *reinterpret_cast<f32x4*>(o + e) =
-                f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Reduced map, then the cut.
-// The map kernels hold kRows = 16 rows of S per workgroup (the M of the 16x16 float32
-//   MFMA).
-// The cut (select_row) takes one row in one wave.  Keeping block j iff F_j > thr is the
-//   same as keeping every block whose probability is at least v*, the smallest row
-//   value with g(v*) > thr, where g(u) = sum of the row values <= u.  g only grows with
-//   u, and non-negative floats order like their bit patterns, so v* is found by
-//   bisection over bit patterns.  The search starts at u0 = thr / nb (g(u0) <= nb u0 =
-//   thr) and keeps only the values still inside the bracket (compacted into a per-wave
-//   LDS buffer), so each step touches fewer values and the search stops once a single
-//   candidate is left.  All sums run in a fixed order, so the result is deterministic.
-// ---------------------------------------------------------------------------
-constexpr int kRows = 16;
-constexpr int kCap = 256;   // candidates per wave held in LDS
-
 // Wave-wide reductions on DPP: shifts of 1, 2, 4, 8 lanes inside each 16-lane row, then
 // the row broadcasts of lanes 15 and 31 (a fixed order, so the result is deterministic);
 // lane 63 ends with the total, which every lane then reads.  VALU latency only, no LDS.
@@ -196,6 +131,143 @@ __device__ inline float wave_max(float x) {
 __device__ inline uint32_t wave_max_u(uint32_t x) {
     return (uint32_t)wave_reduce_bits((int)x, 0, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
 }
+
+// ---------------------------------------------------------------------------
+// Two-term half-precision form of a pooled row, for the map on the fp16 MFMA (the split
+// of Ootomo & Yokota, "Recovering single precision accuracy from Tensor Cores while
+// surpassing the FP32 theoretical peak performance", IJHPCA 2022, with the low term
+// scaled by 2^11).  The row is scaled by 2^-e, e = floor(log2 of its largest magnitude),
+// which is exact and brings every element into the half range; then x = hi + lo 2^-11
+// with hi = fp16(x) and lo = fp16((x - hi) 2^11), the subtraction and the scaling being
+// exact.  That keeps x to about 2^-22 of itself (2^-35 of the row's largest element where
+// x is tiny).  A dot product of two split rows is hi.hi + (hi.lo + lo.hi) 2^-11 with the
+// lo.lo term dropped: three fp16 products accumulated in float32, as close to the float64
+// value as one float32 product pass.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// e for a row whose elements c * EPC .. c * EPC + EPC - 1 every lane holds (for some c):
+// the exponent of the largest magnitude, -126 for a zero or subnormal row
+template <int EPC>
+__device__ inline int split_exponent(const float (&m)[EPC]) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) mx = max(mx, __float_as_uint(m[i]) & 0x7fffffffu);
+    mx = wave_max_u(mx);
+    return max((int)(mx >> 23), 1) - 127;
+}
+
+// hi and lo halves of m * 2^-e, EPC consecutive elements each
+template <int EPC>
+__device__ inline void split_store(const float (&m)[EPC], int e, _Float16* __restrict__ hi, _Float16* __restrict__ lo) {
+    static_assert(EPC == 4 || EPC == 8, "one 8- or 16-byte store per term");
+    _Float16 h[EPC], l[EPC];
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) {
+        const float x = ldexpf(m[i], -e);
+        h[i] = (_Float16)x;
+        l[i] = (_Float16)((x - (float)h[i]) * 2048.0f);
+    }
+    if constexpr (EPC == 8) {
+        *reinterpret_cast<f16x8*>(hi) = f16x8{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+        *reinterpret_cast<f16x8*>(lo) = f16x8{l[0], l[1], l[2], l[3], l[4], l[5], l[6], l[7]};
+    } else {
+        *reinterpret_cast<f16x4*>(hi) = f16x4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<f16x4*>(lo) = f16x4{l[0], l[1], l[2], l[3]};
+    }
+}
+
+// Layout of the split Kp in the workspace, in the order the map's MFMA operands are read:
+// per head, tiles of 16 blocks (the last one padded; its extra columns are never read
+// back); inside a tile, for each step s of 32 coordinates and each term (hi, lo), the
+// 16-byte pieces of the 64 lanes: lane l = 16 g + (j % 16) holds coordinates
+// 32 s + 8 g .. + 7 of block j.  One load instruction of a wave then reads 1 KiB of
+// consecutive memory.  kKpTileHalves halves per tile.
+template <int D>
+constexpr int kKpTileHalves = 16 * D * 2;
+
+template <int D>
+__device__ inline size_t kp_piece(int bh, int ntiles, int j, int e, int term) {
+    const int st = e >> 5, g = (e >> 3) & 3;
+    return ((size_t)bh * ntiles + (j >> 4)) * kKpTileHalves<D> + (size_t)((st * 2 + term) * 64 + 16 * g + (j & 15)) * 8 +
+           (e & 7);
+}
+
+// Mean of query block b of one head (one wave), with pool_kernel's arithmetic, in the
+// two-term half form (split_store) into the LDS rows hi, lo, its exponent in *e_out.
+template <typename T, int D, int BATCH>
+__device__ inline void pool_row_split(const T* __restrict__ head, const attn::RasterGrid& grid, bool raster,
+                                      uint32_t b, int lane, _Float16* hi, _Float16* lo, int* e_out) {
+    constexpr int EPC = Elem<T>::kPerChunk;
+    constexpr int CHUNKS = D / EPC;
+    float acc[EPC];
+    if (raster) block_sum_wave<T, D, 64, BATCH>(head, BlockRows<true, 64>(grid, b), lane, acc);
+    else block_sum_wave<T, D, 64, BATCH>(head, BlockRows<false, 64>(grid, b), lane, acc);
+    constexpr float inv = 1.0f / 64;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] *= inv;
+    const int ex = split_exponent(acc);
+    if (lane < CHUNKS) split_store(acc, ex, hi + lane * EPC, lo + lane * EPC);
+    if (lane == 0) *e_out = ex;
+}
+
+// Block means of K (and of Q for callers that want them stored): one wave per (tensor,
+// head, block).  SPLIT = false: float32 means stored as [block][D] (the IBCS scores read
+// them).  SPLIT = true (K only): the two-term half form in the tiled layout of kp_piece, with the
+// block's exponent in kexp[block] (NABLA's map).
+template <typename T, int D, int N, bool RASTER, bool SPLIT>
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
+                                                    const T* __restrict__ k,
+                                                    float* __restrict__ qp,
+                                                    float* __restrict__ kp, int32_t* __restrict__ kexp,
+                                                    int total_blocks, int nb, int L, attn::RasterGrid grid,
+                                                    int first_wave) {
+    constexpr int EPC = Elem<T>::kPerChunk;
+    constexpr int CHUNKS = D / EPC;
+    const int wave = first_wave + ((blockIdx.x * 256 + threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wave >= 2 * total_blocks) return;
+    const bool is_k = wave >= total_blocks;
+    const int blk = is_k ? wave - total_blocks : wave;
+    const int bh = blk / nb;
+    const T* head = (is_k ? k : q) + (size_t)bh * L * D;
+    float acc[EPC];
+    block_sum_wave<T, D, N, 64>(head, BlockRows<RASTER, N>(grid, blk - bh * nb), lane, acc);
+    constexpr float inv = 1.0f / N;      // N is a power of two: exact
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] *= inv;
+    if constexpr (SPLIT) {
+        // K only (first_wave = total_blocks): the tiled layout of kp_piece
+        const int ex = split_exponent(acc);
+        _Float16* base = reinterpret_cast<_Float16*>(kp);
+        const int j = blk - bh * nb, ntiles = (nb + 15) >> 4;
+        if (lane < CHUNKS)
+            split_store(acc, ex, base + kp_piece<D>(bh, ntiles, j, lane * EPC, 0),
+                        base + kp_piece<D>(bh, ntiles, j, lane * EPC, 1));
+        if (lane == 0) kexp[blk] = ex;
+    } else if (lane < CHUNKS) {
+        float* o = (is_k ? kp : qp) + (size_t)blk * D + lane * EPC;
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) *reinterpret_cast<f32x4*>(o + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reduced map, then the cut.
+// The map kernels hold kRows = 16 rows of S per workgroup (the M of the 16x16 float32
+//   MFMA).
+// The cut (select_row) takes one row in one wave.  Keeping block j iff F_j > thr is the
+//   same as keeping every block whose probability is at least v*, the smallest row
+//   value with g(v*) > thr, where g(u) = sum of the row values <= u.  g only grows with
+//   u, and non-negative floats order like their bit patterns, so v* is found by
+//   bisection over bit patterns.  The search starts at u0 = thr / nb (g(u0) <= nb u0 =
+//   thr) and keeps only the values still inside the bracket (compacted into a per-wave
+//   LDS buffer), so each step touches fewer values and the search stops once a single
+//   candidate is left.  All sums run in a fixed order, so the result is deterministic.
+// ---------------------------------------------------------------------------
+constexpr int kRows = 16;
+constexpr int kCap = 256;   // candidates per wave held in LDS
 
 // Writes the values of src[0..len) whose bit pattern lies in (lo, hi] to dst, in
 // order; src may equal dst (each write lands at or before its source).
@@ -821,57 +893,137 @@ constexpr int kChunkCols = 16 * kWaves;     // one 16-column tile per wave
 constexpr int kChunkLd = kChunkCols + 4;    // padded row: the 16 x 16 tile stores hit distinct banks
 constexpr int kRowCand = kCap;              // a wave's compacted candidates
 
-// One 16 x 16 tile of X Kp^T (unscaled): the kRows X rows staged in x_lds, columns
-// j0 .. j0 + 15 of the head's Kp [nb, D] (columns past nb read as zeros).  Lane (row/col
-// l % 16, group g = l / 16) supplies coordinate 16 m + 4 g + i at MFMA step 4 m + i in
-// both operands, so each 16-byte load reads 64 contiguous bytes of 16 rows.  The Kp
-// operand is loaded in two halves of d (two load round trips per tile, 16 VGPRs at
-// d = 128), leaving the registers to the wave's row.
+// LDS row of a split pooled query: D halves and a 16-byte pad, so the 16-byte reads of
+// 8 consecutive lanes (8 rows) fall on distinct banks
 template <int D>
-__device__ inline f32x4 map_tile(const float* __restrict__ x_lds, const float* __restrict__ kh, int nb, int j0,
-                                 int lane) {
-    constexpr int KC = D / 4;   // 16-byte chunks per row
+constexpr int kQld = D + 8;
+
+// One 16 x 16 tile of S = scale * Qp Kp^T: rows row0 .. row0 + 15 of the workgroup (split
+// halves q_hi, q_lo in LDS, exponents eq), columns j0 .. j0 + 15 (j0 a multiple of 16,
+// below nb) of the head's split Kp (tiled layout of kp_piece, exponents kexp; columns
+// past nb hold padding, and their S values are never read).  Three
+// v_mfma_f32_16x16x32_f16 per 32 coordinates: hi.hi into one accumulator, hi.lo and lo.hi
+// into another, combined as hh + x 2^-11 and scaled back by 2^(eq + ek).  Lane (row/col
+// l % 16, group g = l / 16) supplies coordinates 32 s + 8 g .. + 7 at step s in both
+// operands (one 16-byte load per term, 1 KiB per wave).  The Kp operand comes in two
+// rounds of half the steps (16 VGPRs at d = 128), leaving the registers to the wave's row.
+template <int D>
+__device__ inline f32x4 map_tile(const _Float16* __restrict__ q_hi, const _Float16* __restrict__ q_lo,
+                                 const int* __restrict__ eq, const _Float16* __restrict__ kh,
+                                 const int32_t* __restrict__ kexp, int nb, int j0, float scale, int lane) {
+    constexpr int KS = D / 32;           // MFMA steps
+    constexpr int H = KS / 2;            // steps per load round
     const int li = lane & 15;
     const int kq = lane >> 4;
     const int j = j0 + li;
-    const f32x4* xa = reinterpret_cast<const f32x4*>(x_lds + li * kXld<D>) + kq;
-    const f32x4* src = reinterpret_cast<const f32x4*>(kh + (size_t)min(j, nb - 1) * D) + kq;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    constexpr int H = KC / 8;   // chunks per half: two load round trips per tile
+    const _Float16* src = kh + (size_t)(j0 >> 4) * kKpTileHalves<D> + lane * 8;
+    const _Float16* qa = q_hi + li * kQld<D> + 8 * kq;
+    const _Float16* qb = q_lo + li * kQld<D> + 8 * kq;
+    f32x4 hh = {0.f, 0.f, 0.f, 0.f};
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
-        f32x4 b[H];
+        f16x8 bh[H], bl[H];
 #pragma unroll
         for (int m = 0; m < H; ++m) {
-            b[m] = src[4 * (h * H + m)];
-            if (j >= nb) b[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int st = h * H + m;
+            bh[m] = *reinterpret_cast<const f16x8*>(src + (st * 2) * 512);
+            bl[m] = *reinterpret_cast<const f16x8*>(src + (st * 2 + 1) * 512);
         }
 #pragma unroll
         for (int m = 0; m < H; ++m) {
-            const f32x4 a = xa[4 * (h * H + m)];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[m][i], acc, 0, 0, 0);
+            const int st = h * H + m;
+            const f16x8 ah = *reinterpret_cast<const f16x8*>(qa + 32 * st);
+            const f16x8 al = *reinterpret_cast<const f16x8*>(qb + 32 * st);
+            hh = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh[m], hh, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[m], x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh[m], x, 0, 0, 0);
         }
     }
-    return acc;
+    const int ek = kexp[min(j, nb - 1)];
+    f32x4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[r] = ldexpf(fmaf(x[r], 1.0f / 2048.0f, hh[r]) * scale, eq[4 * kq + r] + ek);
+    return out;
 }
 
-// Rows of up to 24 register blocks (1536 KV blocks) run eight waves per SIMD (two
+// The Kp operand of one tile, whole: columns j0 + l % 16, coordinates 32 s + 8 (l / 16)
+// .. + 7 of both terms for every step s (eight 1 KiB reads of the tiled layout), and the
+// column's exponent.  Columns past nb hold padding: their S values are never read (the
+// rows take -inf there), and not zeroing the loaded registers keeps the loads in flight
+// until they are used.
+template <int D>
+struct KpTile {
+    f16x8 hi[D / 32], lo[D / 32];
+    int ek;
+};
+
+template <int D>
+__device__ inline void load_kp_tile(const _Float16* __restrict__ kh, const int32_t* __restrict__ kexp, int nb,
+                                    int j0, int lane, KpTile<D>& t) {
+    // j0 is a multiple of 16; past the last tile the last one is read again
+    const int tile = min(j0, nb - 1) >> 4;
+    const _Float16* src = kh + (size_t)tile * kKpTileHalves<D> + lane * 8;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+        t.hi[st] = *reinterpret_cast<const f16x8*>(src + (st * 2) * 512);
+        t.lo[st] = *reinterpret_cast<const f16x8*>(src + (st * 2 + 1) * 512);
+    }
+    t.ek = kexp[min(j0 + (lane & 15), nb - 1)];
+}
+
+// hi.hi + (hi.lo + lo.hi) 2^-11 for the workgroup's 16 split query rows against a
+// loaded Kp tile, scaled to S (see map_tile)
+template <int D>
+__device__ inline f32x4 tile_products(const _Float16* __restrict__ q_hi, const _Float16* __restrict__ q_lo,
+                                      const int* __restrict__ eq, const KpTile<D>& t, float scale, int lane) {
+    const int li = lane & 15;
+    const int kq = lane >> 4;
+    const _Float16* qa = q_hi + li * kQld<D> + 8 * kq;
+    const _Float16* qb = q_lo + li * kQld<D> + 8 * kq;
+    f32x4 hh = {0.f, 0.f, 0.f, 0.f};
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+        const f16x8 ah = *reinterpret_cast<const f16x8*>(qa + 32 * st);
+        const f16x8 al = *reinterpret_cast<const f16x8*>(qb + 32 * st);
+        hh = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, t.hi[st], hh, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, t.lo[st], x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, t.hi[st], x, 0, 0, 0);
+    }
+    f32x4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[r] = ldexpf(fmaf(x[r], 1.0f / 2048.0f, hh[r]) * scale, eq[4 * kq + r] + t.ek);
+    return out;
+}
+
+// Rows of up to 20 register blocks (1280 KV blocks) run eight waves per SIMD (two
 // workgroups per CU) within 64 VGPRs; longer rows four waves per SIMD with 128, and so
 // does the SIP form from rows of 12 registers on (it keeps more values live across its
 // water-level loop).
 template <int NREG, bool SIP>
-constexpr int kMapSelectWaves = (NREG > 24 || (SIP && NREG >= 12)) ? 4 : 8;
+constexpr int kMapSelectWaves = (NREG > 20 || (SIP && NREG >= 12)) ? 4 : 8;
+// Where the registers allow (four waves per SIMD), a wave loads the next
+// chunk's Kp tile whole while the current chunk is exchanged and read, so the load's
+// latency is hidden behind the barrier; otherwise the tile comes in two rounds per chunk
+// (map_tile).  With four waves per SIMD the query block's mean also keeps eight loads in
+// flight instead of two.
+template <int NREG, bool SIP>
+constexpr bool kMapPrefetch = kMapSelectWaves<NREG, SIP> == 4;
+template <int NREG, bool SIP>
+constexpr int kPoolBatch = kMapSelectWaves<NREG, SIP> == 4 ? 8 : 2;
 
 template <int D, int NREG, bool SIP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMapSelectWaves<NREG, SIP>,
                                                                              kMapSelectWaves<NREG, SIP>))) void
 map_select_kernel(const void* __restrict__ q, int bf16, int raster, attn::RasterGrid grid, int L,
-                  const float* __restrict__ kp, int nb, float scale, float thr, int sta,
+                  const _Float16* __restrict__ kp, const int32_t* __restrict__ kexp, int nb, float scale,
+                  float thr, int sta,
                   FastDiv fd_pf, FastDiv fd_nw, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
                   int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int sip_budget,
                   const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
-    // [2][kRows][kChunkLd] chunk buffers, [kWaves][kRowCand] candidates, [kRows][kXld] pooled queries
+    // [2][kRows][kChunkLd] chunk buffers, [kWaves][kRowCand] candidates, then the split
+    // pooled queries: [kRows][kQld] hi halves, [kRows][kQld] lo halves, [kRows] exponents
     extern __shared__ __align__(16) float s_lds[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -879,20 +1031,34 @@ map_select_kernel(const void* __restrict__ q, int bf16, int raster, attn::Raster
     const int row0 = blockIdx.x * kRows;
     const int row = row0 + wave;
     float* cand = s_lds + 2 * kRows * kChunkLd + wave * kRowCand;
-    float* x_lds = s_lds + 2 * kRows * kChunkLd + kWaves * kRowCand;
-    const float* kh = kp + (size_t)bh * nb * D;
+    _Float16* q_hi = reinterpret_cast<_Float16*>(s_lds + 2 * kRows * kChunkLd + kWaves * kRowCand);
+    _Float16* q_lo = q_hi + kRows * kQld<D>;
+    int* eq = reinterpret_cast<int*>(q_lo + kRows * kQld<D>);
+    const _Float16* kh = kp + (size_t)bh * ((nb + 15) >> 4) * kKpTileHalves<D>;
+    const int32_t* kexp_h = kexp + (size_t)bh * nb;
+    // the first chunk's Kp tile, in flight while the query block is pooled
+    constexpr bool kPf = kMapPrefetch<NREG, SIP>;
+    KpTile<D> kt;
+    if constexpr (kPf) load_kp_tile<D>(kh, kexp_h, nb, 16 * wave, lane, kt);
     // the workgroup's pooled query rows: wave w forms the mean of query block row0 + w
     // from Q itself (zeros past nb), so Q is read once, here, beside other workgroups' work
     {
-        float* xr = x_lds + wave * kXld<D>;
+        _Float16* hr = q_hi + wave * kQld<D>;
+        _Float16* lr = q_lo + wave * kQld<D>;
         if (row < nb) {
-            if (bf16) pool_row<__bf16, D>((const __bf16*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row, lane, xr);
-            else pool_row<float, D>((const float*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row, lane, xr);
+            constexpr int kB = kPoolBatch<NREG, SIP>;
+            if (bf16)
+                pool_row_split<__bf16, D, kB>((const __bf16*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row,
+                                              lane, hr, lr, eq + wave);
+            else
+                pool_row_split<float, D, kB>((const float*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row,
+                                             lane, hr, lr, eq + wave);
         } else {
-            for (int e = lane; e < D; e += 64) xr[e] = 0.f;
+            for (int e = lane; e < D; e += 64) hr[e] = lr[e] = (_Float16)0.f;
+            if (lane == 0) eq[wave] = 0;
         }
     }
-    __syncthreads();
+    attn::lds_barrier();   // LDS only: prefetched tiles stay in flight
 
     float v[NREG];
     const int li = lane & 15;
@@ -903,11 +1069,20 @@ map_select_kernel(const void* __restrict__ q, int bf16, int raster, attn::Raster
             float* buf = s_lds + (c & 1) * kRows * kChunkLd;
             const int j0 = c * kChunkCols + 16 * wave;
             if (j0 < nb) {
-                const f32x4 acc = map_tile<D>(x_lds, kh, nb, j0, lane);
+                f32x4 sv;
+                if constexpr (kPf) {
+                    sv = tile_products<D>(q_hi, q_lo, eq, kt, scale, lane);
+                    // the next chunk's tile, in flight across this chunk's exchange (past the
+                    // last chunk a clamped, unused one: an unconditional load is not copied
+                    // between registers, which would wait for it here)
+                    load_kp_tile<D>(kh, kexp_h, nb, j0 + kChunkCols, lane, kt);
+                } else {
+                    sv = map_tile<D>(q_hi, q_lo, eq, kh, kexp_h, nb, j0, scale, lane);
+                }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) buf[(4 * kq + r) * kChunkLd + 16 * wave + li] = acc[r] * scale;
+                for (int r = 0; r < 4; ++r) buf[(4 * kq + r) * kChunkLd + 16 * wave + li] = sv[r];
             }
-            __syncthreads();
+            attn::lds_barrier();   // LDS only: prefetched tiles stay in flight
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int j = c * kChunkCols + lane + 64 * m;
@@ -1087,32 +1262,44 @@ __global__ __launch_bounds__(64) void pair_schedule_kernel(const int32_t* __rest
     if (single && lane == 0) schedule[(size_t)BH * (nb - 1) + h] = h * nb + nb - 1;
 }
 
+template <typename T, int D, bool RASTER, bool SPLIT>
+void launch_pool_form(const MaskArgs& a, const attn::RasterGrid& grid, hipStream_t s) {
+    const int total = a.BH * a.nb;
+    const int first = total;   // K only: NABLA's map pools Q itself, IBCS clusters Q
+    hipLaunchKernelGGL((pool_kernel<T, D, 64, RASTER, SPLIT>), dim3((2 * total - first + 3) / 4), dim3(256), 0, s,
+                       (const T*)a.q, (const T*)a.k, a.qp, a.kp, a.kexp, total, a.nb, a.nb * 64, grid, first);
+}
+
 template <typename T, int D>
 hipError_t launch_pool(const MaskArgs& a, hipStream_t s) {
-    const int total = a.BH * a.nb;
-    const int waves = 2 * total;
-    const int first = total;   // K only: NABLA's map pools Q itself, IBCS clusters Q
     attn::RasterGrid grid{};
     if (a.raster) {
         grid.W = (uint32_t)a.W;
         grid.HW = (uint32_t)(a.H * a.W);
         grid.nHW = FastDiv((uint32_t)(a.nH * a.nW));
         grid.nW = FastDiv((uint32_t)a.nW);
-        hipLaunchKernelGGL((pool_kernel<T, D, 64, true>), dim3((waves - first + 3) / 4), dim3(256), 0, s,
-                           (const T*)a.q, (const T*)a.k, a.qp, a.kp, total, a.nb, a.nb * 64, grid, first);
+    }
+    // the IBCS scores read float32 means, NABLA's map the half form
+    if (a.raster) {
+        if (a.ibcs) launch_pool_form<T, D, true, false>(a, grid, s);
+        else launch_pool_form<T, D, true, true>(a, grid, s);
     } else {
-        hipLaunchKernelGGL((pool_kernel<T, D, 64, false>), dim3((waves - first + 3) / 4), dim3(256), 0, s,
-                           (const T*)a.q, (const T*)a.k, a.qp, a.kp, total, a.nb, a.nb * 64, grid, first);
+        if (a.ibcs) launch_pool_form<T, D, false, false>(a, grid, s);
+        else launch_pool_form<T, D, false, true>(a, grid, s);
     }
     return hipGetLastError();
 }
 
+template <int D>
+constexpr size_t map_select_lds_bytes() {
+    return ((size_t)2 * kRows * kChunkLd + (size_t)kWaves * kRowCand) * sizeof(float) +
+           (size_t)2 * kRows * kQld<D> * sizeof(_Float16) + (size_t)kRows * sizeof(int);
+}
+static_assert(map_select_lds_bytes<128>() <= 64 * 1024, "map/select LDS within the default dynamic limit");
+
 template <int D, int NREG>
 hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
-    const size_t lds = ((size_t)2 * kRows * kChunkLd + (size_t)kWaves * kRowCand + (size_t)kRows * kXld<D>) *
-                       sizeof(float);
-    static_assert((2 * kRows * kChunkLd + kWaves * kRowCand + kRows * kXld<128>) * sizeof(float) <= 64 * 1024,
-                  "map/select LDS within the default dynamic limit, two workgroups per CU");
+    const size_t lds = map_select_lds_bytes<D>();
     dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
     const FastDiv fd_pf((uint32_t)(a.nH * a.nW)), fd_nw((uint32_t)a.nW);   // block -> (frame, patch row, column)
     attn::RasterGrid rg{};
@@ -1122,14 +1309,15 @@ hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
         rg.nHW = FastDiv((uint32_t)(a.nH * a.nW));
         rg.nW = FastDiv((uint32_t)a.nW);
     }
+    const _Float16* kp = reinterpret_cast<const _Float16*>(a.kp);
     if (a.sip_budget > 0) {
         hipLaunchKernelGGL((map_select_kernel<D, NREG, true>), grid, dim3(kWaves * 64), lds, s, a.q, a.bf16, a.raster,
-                           rg, a.nb * 64, a.kp, a.nb, a.scale, a.thr, a.sta, fd_pf, fd_nw, a.rt, a.rh, a.rw,
+                           rg, a.nb * 64, kp, a.kexp, a.nb, a.scale, a.thr, a.sta, fd_pf, fd_nw, a.rt, a.rh, a.rw,
                            a.kv_count, a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
     } else {
         hipLaunchKernelGGL((map_select_kernel<D, NREG, false>), grid, dim3(kWaves * 64), lds, s, a.q, a.bf16,
-                           a.raster, rg, a.nb * 64, a.kp, a.nb, a.scale, a.thr, a.sta, fd_pf, fd_nw, a.rt, a.rh,
-                           a.rw, a.kv_count, a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
+                           a.raster, rg, a.nb * 64, kp, a.kexp, a.nb, a.scale, a.thr, a.sta, fd_pf, fd_nw, a.rt,
+                           a.rh, a.rw, a.kv_count, a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
     }
     return hipGetLastError();
 }

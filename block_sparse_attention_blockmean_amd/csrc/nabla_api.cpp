@@ -87,12 +87,14 @@ size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // The NABLA workspace: the pooled K (the map kernel pools Q itself).
 struct NablaSections {
-    size_t kp;
-    size_t total() const { return kp; }
+    size_t kp, kexp;
+    size_t total() const { return kp + kexp; }
 };
 
 NablaSections nabla_sections(long long BH, long long nb, int d) {
-    return {up256((size_t)BH * nb * d * sizeof(float))};
+    // split Kp in tiles of 16 blocks (the last one padded), then one exponent per block
+    const long long nb16 = (nb + 15) / 16 * 16;
+    return {up256((size_t)BH * nb16 * d * sizeof(float)), up256((size_t)BH * nb * sizeof(int32_t))};
 }
 
 }  // namespace
@@ -269,8 +271,10 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     // the launches cover up to 256 threads per block of every head with 32-bit thread ids
     if ((long long)batch * heads > 65535 || L * d >= kMaxHeadElems || (long long)batch * heads * nb >= (1ll << 24))
         return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
-    // pooled K of one head (a multiple of 256 bytes for d = 64, 128)
-    const size_t head_pool_bytes = (size_t)nb * d * sizeof(float);
+    // pooled K of one head in the split half form, and its exponents (the first part a
+    // multiple of 256 bytes for d = 64, 128)
+    const size_t head_kp_bytes = (size_t)((nb + 15) / 16 * 16) * d * sizeof(float);
+    const size_t head_pool_bytes = head_kp_bytes + (size_t)nb * sizeof(int32_t);
     if (use_scratch && head_pool_bytes > nabla::kScratchBytes)
         return fail(NABLA_E_UNSUPPORTED, "%s: one head's pooled K needs %zu bytes, the scratch holds %zu", who,
                     head_pool_bytes, nabla::kScratchBytes);
@@ -319,9 +323,11 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
         a.ibcs = 1;
         a.ibcs_group = ibcs_q_group / N;
     } else {
-        // [Kp]
+        // [split Kp | exponents]
+        const NablaSections sec = nabla_sections(a.BH, nb, d);
         a.qp = nullptr;
         a.kp = (float*)workspace;
+        a.kexp = (int32_t*)((char*)workspace + sec.kp);
     }
     a.bf16 = dtype == NABLA_BF16;
     a.raster = raster;
@@ -347,6 +353,7 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
         c.bitmap = bitmap ? bitmap + (size_t)h0 * nb * words : nullptr;
         c.schedule = nullptr;
         c.kp = (float*)workspace;
+        c.kexp = (int32_t*)((char*)workspace + (size_t)per_chunk * head_kp_bytes);
         nabla_status st = hip_status(nabla::launch_build_mask(c, stream), who);
         if (st != NABLA_OK) return st;
     }

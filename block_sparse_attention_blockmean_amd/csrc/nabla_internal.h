@@ -78,8 +78,10 @@ struct MaskArgs {
     int32_t* kv_index;
     uint32_t* bitmap;       // may be null
     int32_t* schedule;      // may be null
-    float* qp;              // workspace [BH, nb, d]
-    float* kp;              // workspace [BH, nb, d]
+    float* qp;              // unused (Q is pooled inside the map kernel); null
+    float* kp;              // workspace: pooled K, [BH, nb, d] float32 (IBCS) or the split
+                            // half form [BH, nb][hi d | lo d] (NABLA's map), 4 nb d bytes per head
+    int32_t* kexp;          // workspace [BH, nb]: exponents of the split form (NABLA)
     float* scores;          // IBCS workspace [BH, groups, nb] score rows (rows sum to one)
     int bf16;
     int raster;             // 0: q, k in fractal order; 1: raster order, 8 x 8 patches per block

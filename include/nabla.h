@@ -79,10 +79,13 @@ nabla_status nabla_reorder(const void* src, void* dst, int batch, int heads, int
 
 /*
  * nabla_build_mask_workspace_size - bytes of device workspace nabla_build_mask (and its
- * raster and SIP forms) needs (BH = batch*heads, nb = L/N): the pooled K, BH*nb*d floats,
- * rounded up to 256 bytes.  After a call it holds those means, float32, row-major (the
- * pooled Q is formed inside the map kernel and not stored).  Returns 0 for non-positive
- * sizes or L not a multiple of N.
+ * raster and SIP forms) needs (BH = batch*heads, nb = L/N, nb16 = nb rounded up to a
+ * multiple of 16): the pooled K, BH*nb16*d*4 bytes, then one 4-byte exponent per block,
+ * each part rounded up to 256 bytes.  After a call it holds the block means of K in a
+ * two-term half-precision form (mean = (hi + lo / 2048) * 2^e, e the block's exponent),
+ * laid out in tiles of 16 blocks in the order the map kernel reads them; the pooled Q is
+ * formed inside the map kernel and not stored.  Returns 0 for non-positive sizes or L
+ * not a multiple of N.
  */
 size_t nabla_build_mask_workspace_size(int batch, int heads, int L, int d, int N);
 
@@ -193,7 +196,7 @@ nabla_status nabla_build_mask_raster(const void* q, const void* k, int batch, in
  * that forbid hipMalloc): no workspace argument, and no allocation of any kind.  The
  * pooled K lives in a device array of the library, NABLA_NOALLOC_SCRATCH_BYTES per
  * GPU, held from the library's load until the process ends; heads are processed in
- * chunks whose pooled K fits in it (nb * d * 4 bytes per head), one launch
+ * chunks whose pooled K fits in it (nb16 * d * 4 + nb * 4 bytes per head), one launch
  * sequence per chunk on `stream`.  Results (counts, lists, bitmap, schedule) are those of
  * nabla_build_mask_raster on the same arguments.
  * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on

@@ -52,12 +52,17 @@ def test_status_strings(lib):
                      "NABLA_E_WORKSPACE"]
 
 
+def up256(n):
+    return (n + 255) // 256 * 256
+
+
 def test_workspace_size(lib):
-    # pooled K, B*H*nb*d floats, rounded up to 256
-    assert lib.nabla_build_mask_workspace_size(1, 12, 32256, 128, 64) == 12 * 504 * 128 * 4
-    assert lib.nabla_build_mask_workspace_size(1, 2, 1024, 64, 64) == 2 * 16 * 64 * 4
-    # 3 blocks, d = 16: 192 B, rounded up to 256
-    assert lib.nabla_build_mask_workspace_size(1, 1, 192, 16, 64) == 256
+    # pooled K in the split half form (4 d bytes per block, blocks padded to a multiple
+    # of 16 per head), then one 4-byte exponent per block, each part rounded up to 256
+    assert lib.nabla_build_mask_workspace_size(1, 12, 32256, 128, 64) == 12 * 512 * 128 * 4 + up256(12 * 504 * 4)
+    assert lib.nabla_build_mask_workspace_size(1, 2, 1024, 64, 64) == 2 * 16 * 64 * 4 + up256(2 * 16 * 4)
+    # 3 blocks (padded to 16), d = 16: 1024 B, and 12 B rounded up to 256
+    assert lib.nabla_build_mask_workspace_size(1, 1, 192, 16, 64) == 16 * 16 * 4 + 256
     assert lib.nabla_build_mask_workspace_size(1, 1, 1000, 64, 64) == 0
     assert lib.nabla_build_mask_workspace_size(0, 1, 1024, 64, 64) == 0
 
