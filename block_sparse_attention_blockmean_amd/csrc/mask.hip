@@ -754,8 +754,9 @@ __device__ inline int compact_regs(const float (&v)[NV], uint32_t lo, uint32_t h
     return len;
 }
 
-// One bisection step over the values in registers: narrows (lo, hi] to the half that
-// holds the cut, keeping g_lo (mass of the values <= lo) and n_in (values in the bracket).
+// One bisection step over the compacted candidates (the values in (lo, hi]): narrows
+// the bracket to the half that holds the cut, keeping g_lo (mass of the row's values
+// <= lo) and n_in (values in the bracket).
 template <int NV>
 __device__ inline void bisect_step(const float (&v)[NV], uint32_t& lo, uint32_t& hi, float& g_lo, int& n_in,
                                    float thr) {
@@ -777,6 +778,32 @@ __device__ inline void bisect_step(const float (&v)[NV], uint32_t& lo, uint32_t&
         lo = mid;
         g_lo += s_;
         n_in -= c;
+    }
+}
+
+// The same step over the whole row: g(mid) is summed afresh over every value <= mid (one
+// compare, one select and one add per value, no lower bound to test), and the counts of
+// values <= lo and <= hi give the bracket's population.
+template <int NV>
+__device__ inline void bisect_step_row(const float (&v)[NV], uint32_t& lo, uint32_t& hi, float& g_lo, int& c_lo,
+                                       int& c_hi, float thr) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    float s_ = 0.f;
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const bool le = __float_as_uint(v[i]) <= mid;
+        s_ += le ? v[i] : 0.f;
+        c += __popcll(__ballot(le));
+    }
+    s_ = wave_sum(s_);
+    if (s_ > thr) {
+        hi = mid;
+        c_hi = c;
+    } else {
+        lo = mid;
+        g_lo = s_;
+        c_lo = c;
     }
 }
 
@@ -812,7 +839,11 @@ __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int
     uint32_t hi = maxb;
     // bracket (lo, hi]: g(lo) = g_lo <= thr and, unless the whole row sums to at most
     // thr, g(hi) > thr; n_in values lie inside it (always >= 1: the maximum)
-    while (hi - lo > 1 && n_in > kCap) bisect_step(v, lo, hi, g_lo, n_in, thr);
+    {
+        int c_lo = NREG * 64 - n_in, c_hi = NREG * 64;   // values <= lo, <= hi (padding included)
+        while (hi - lo > 1 && c_hi - c_lo > kCap) bisect_step_row(v, lo, hi, g_lo, c_lo, c_hi, thr);
+        n_in = c_hi - c_lo;
+    }
     uint32_t cut = hi;
     if (n_in <= kCap) {
         float c4[kCap / 64];
@@ -839,6 +870,7 @@ __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int
     }
 
     int qt = 0, qh_ = 0, qw = 0;
+    int jlo = 0, jhi = 0;   // the blocks of the frames the window reaches
     if (sta) {
         uint32_t t_, rem_, h_, w_;
         fd_pf.divmod((uint32_t)row, t_, rem_);
@@ -846,6 +878,8 @@ __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int
         qt = (int)t_;
         qh_ = (int)h_;
         qw = (int)w_;
+        jlo = max(qt - rt, 0) * (int)fd_pf.d;
+        jhi = (qt + rt + 1) * (int)fd_pf.d;
     }
     int32_t* out_idx = kv_index + ((size_t)bh * nb + row) * nb;
     uint32_t* out_bits = bitmap ? bitmap + ((size_t)bh * nb + row) * nwords : nullptr;
@@ -853,10 +887,11 @@ __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int
 #pragma unroll
     for (int i = 0; i < NREG; ++i) {
         const int j = lane + 64 * i;
-        bool keep = false;
-        if (j < nb) {
-            keep = __float_as_uint(v[i]) >= cut;
-            if (sta && !keep) {
+        bool keep = j < nb && __float_as_uint(v[i]) >= cut;
+        // the window test only where this register's 64 blocks meet the window's frames
+        // (a uniform branch)
+        if (sta && 64 * i < jhi && 64 * i + 64 > jlo) {
+            if (!keep && j < nb && j >= jlo && j < jhi) {
                 uint32_t kt, rem, kh_, kw;
                 fd_pf.divmod((uint32_t)j, kt, rem);
                 fd_nw.divmod(rem, kh_, kw);
@@ -1003,15 +1038,16 @@ __device__ inline f32x4 tile_products(const _Float16* __restrict__ q_hi, const _
 // water-level loop).
 template <int NREG, bool SIP>
 constexpr int kMapSelectWaves = (NREG > 20 || (SIP && NREG >= 12)) ? 4 : 8;
-// Where the registers allow (four waves per SIMD), a wave loads the next
-// chunk's Kp tile whole while the current chunk is exchanged and read, so the load's
-// latency is hidden behind the barrier; otherwise the tile comes in two rounds per chunk
-// (map_tile).  With four waves per SIMD the query block's mean also keeps eight loads in
-// flight instead of two.
+// Where the registers allow (four waves per SIMD, rows of at most 32 registers), a wave
+// loads the next chunk's Kp tile whole while the current chunk is exchanged and read, so
+// the load's latency is hidden behind the barrier; otherwise the tile comes in two rounds
+// per chunk (map_tile).  There the query block's mean also keeps all sixteen loads in
+// flight instead of two.  Rows of 48 and 64 registers (up to 4096 blocks) fit in 128
+// VGPRs only without both.
 template <int NREG, bool SIP>
-constexpr bool kMapPrefetch = kMapSelectWaves<NREG, SIP> == 4;
+constexpr bool kMapPrefetch = kMapSelectWaves<NREG, SIP> == 4 && NREG <= 32;
 template <int NREG, bool SIP>
-constexpr int kPoolBatch = kMapSelectWaves<NREG, SIP> == 4 ? 8 : 2;
+constexpr int kPoolBatch = kMapSelectWaves<NREG, SIP> == 4 && NREG <= 32 ? 16 : 2;
 
 template <int D, int NREG, bool SIP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMapSelectWaves<NREG, SIP>,
@@ -1326,14 +1362,16 @@ hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
 // covering nb / 64
 template <int D>
 hipError_t launch_map_select_nreg(const MaskArgs& a, hipStream_t s) {
-    static_assert(NABLA_MAX_BLOCKS <= 32 * 64, "rows of at most 32 registers per lane");
+    static_assert(NABLA_MAX_BLOCKS <= 64 * 64, "rows of at most 64 registers per lane");
     if (a.nb <= 4 * 64) return launch_map_select<D, 4>(a, s);
     if (a.nb <= 8 * 64) return launch_map_select<D, 8>(a, s);
     if (a.nb <= 12 * 64) return launch_map_select<D, 12>(a, s);
     if (a.nb <= 16 * 64) return launch_map_select<D, 16>(a, s);
     if (a.nb <= 20 * 64) return launch_map_select<D, 20>(a, s);
     if (a.nb <= 24 * 64) return launch_map_select<D, 24>(a, s);
-    return launch_map_select<D, 32>(a, s);
+    if (a.nb <= 32 * 64) return launch_map_select<D, 32>(a, s);
+    if (a.nb <= 48 * 64) return launch_map_select<D, 48>(a, s);
+    return launch_map_select<D, 64>(a, s);
 }
 
 hipError_t launch_map_select_for(const MaskArgs& a, hipStream_t s) {
@@ -1344,7 +1382,7 @@ hipError_t launch_select(const MaskArgs& a, hipStream_t s) {
     const int ld_s = ((a.nb + 63) / 64) * 64 + 16;
     const size_t lds = ((size_t)kSelWaves * ld_s + (size_t)kSelWaves * kCap) * sizeof(float);
     static std::atomic<uint64_t> lds_set{0};
-    const int max_lds = (kSelWaves * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kSelWaves * kCap) * (int)sizeof(float);
+    const int max_lds = (kSelWaves * (((NABLA_IBCS_MAX_BLOCKS + 63) / 64) * 64 + 16) + kSelWaves * kCap) * (int)sizeof(float);
     hipError_t e = set_max_dynamic_lds((const void*)select_kernel, max_lds, lds_set);
     if (e != hipSuccess) return e;
     dim3 grid((a.nb + kSelWaves - 1) / kSelWaves, a.BH);
@@ -1359,7 +1397,7 @@ hipError_t launch_ibcs_score(const MaskArgs& a, hipStream_t s) {
     const int ld_s = ((a.nb + 63) / 64) * 64 + 16;
     const size_t lds = ((size_t)kRows * ld_s + (size_t)kRows * kXld<D>) * sizeof(float);
     static std::atomic<uint64_t> lds_set{0};
-    const int max_lds = (kRows * (((NABLA_MAX_BLOCKS + 63) / 64) * 64 + 16) + kRows * kXld<D>) * (int)sizeof(float);
+    const int max_lds = (kRows * (((NABLA_IBCS_MAX_BLOCKS + 63) / 64) * 64 + 16) + kRows * kXld<D>) * (int)sizeof(float);
     hipError_t e = set_max_dynamic_lds((const void*)ibcs_score_kernel<D>, max_lds, lds_set);
     if (e != hipSuccess) return e;
     const int groups = a.nb / a.ibcs_group;

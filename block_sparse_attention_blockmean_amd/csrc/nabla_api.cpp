@@ -268,6 +268,9 @@ nabla_status build_mask_impl(const char* who, int raster, const void* q, const v
     const long long nb = L / N;
     if (nb > NABLA_MAX_BLOCKS)
         return fail(NABLA_E_UNSUPPORTED, "%s: %lld blocks per head exceed %d", who, nb, NABLA_MAX_BLOCKS);
+    if (ibcs_q_group && nb > NABLA_IBCS_MAX_BLOCKS)
+        return fail(NABLA_E_UNSUPPORTED, "%s: %lld blocks per head exceed %d (IBCS score rows are held in LDS)",
+                    who, nb, NABLA_IBCS_MAX_BLOCKS);
     // the launches cover up to 256 threads per block of every head with 32-bit thread ids
     if ((long long)batch * heads > 65535 || L * d >= kMaxHeadElems || (long long)batch * heads * nb >= (1ll << 24))
         return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);

@@ -56,8 +56,12 @@ typedef enum { NABLA_F32 = 0, NABLA_BF16 = 1 } nabla_dtype;
  * truncated at the grid border. */
 typedef struct { int wt, wh, ww; } nabla_sta_window;
 
-/* Largest number of N-token blocks per head that nabla_build_mask accepts. */
-#define NABLA_MAX_BLOCKS 2048
+/* Largest number of N-token blocks per head that nabla_build_mask (and its raster, SIP
+ * and allocation-free forms), the attention entry points and the backward accept (4096
+ * blocks of 64: 262,144 tokens per head), and the smaller limit of the IBCS entry points,
+ * whose score rows are held in LDS. */
+#define NABLA_MAX_BLOCKS 4096
+#define NABLA_IBCS_MAX_BLOCKS 2048
 
 /*
  * nabla_reorder - fractal flattening of the token axis ("Metodologia: NABLA", item 1,
@@ -294,7 +298,7 @@ size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, 
  * Arguments, outputs and errors as nabla_build_mask, plus q_group and the workspace of
  * nabla_build_mask_ibcs_workspace_size(); NABLA_E_INVAL when q_group is not a positive
  * multiple of N or does not divide L, NABLA_E_UNSUPPORTED when q_group is not 64 or
- * 128.
+ * 128 or nb exceeds NABLA_IBCS_MAX_BLOCKS.
  */
 nabla_status nabla_build_mask_ibcs(const void* q, const void* k, int batch, int heads, int T, int H,
                                    int W, int d, int P, int N, int q_group, float thr,

@@ -124,7 +124,7 @@ def build_mask(lib, q=A, k=B_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=6
     (dict(dt=5), NABLA_E_INVAL),
     (dict(N=32, T=4), NABLA_E_UNSUPPORTED),
     (dict(d=96), NABLA_E_UNSUPPORTED),
-    (dict(T=129, H=32, W=32), NABLA_E_UNSUPPORTED),     # 2064 blocks > NABLA_MAX_BLOCKS
+    (dict(T=257, H=32, W=32), NABLA_E_UNSUPPORTED),     # 4112 blocks > NABLA_MAX_BLOCKS
     (dict(schedule=ctypes.c_void_p(0x100002)), NABLA_E_INVAL),
     (dict(ws=None), NABLA_E_WORKSPACE),
     (dict(ws_bytes=100), NABLA_E_WORKSPACE),
@@ -223,7 +223,7 @@ def attn_bwd(lib, **kw):
     (dict(dt=4), NABLA_E_INVAL),
     (dict(N=32), NABLA_E_UNSUPPORTED),
     (dict(d=32), NABLA_E_UNSUPPORTED),
-    (dict(L=64 * 2049), NABLA_E_UNSUPPORTED),
+    (dict(L=64 * 4097), NABLA_E_UNSUPPORTED),          # nb > NABLA_MAX_BLOCKS
     (dict(L=1 << 23, d=128), NABLA_E_UNSUPPORTED),
     (dict(ws=None), NABLA_E_WORKSPACE),
     (dict(ws_bytes=1000), NABLA_E_WORKSPACE),
@@ -333,7 +333,8 @@ def test_build_mask_ibcs_validation(lib):
                    (dict(ws_bytes=small_ws), NABLA_E_WORKSPACE),
                    (dict(qg=0), NABLA_E_INVAL), (dict(qg=96), NABLA_E_INVAL),
                    (dict(T=3, H=8, W=8), NABLA_E_INVAL),          # 3 blocks: L = 192 not a multiple of 128
-                   (dict(qg=256), NABLA_E_UNSUPPORTED)):
+                   (dict(qg=256), NABLA_E_UNSUPPORTED),
+                   (dict(T=129, H=32, W=32), NABLA_E_UNSUPPORTED)):   # 2064 blocks > NABLA_IBCS_MAX_BLOCKS
         assert call(**kw) == st, kw
         assert lib.nabla_last_error().decode().startswith("nabla_build_mask_ibcs")
 
@@ -413,6 +414,6 @@ def test_build_mask_raster_noalloc_validation(lib):
                                                    a["cnt"], a["idx"], None, None, None)
     for kw, st in ((dict(q=None), NABLA_E_INVAL), (dict(idx=None), NABLA_E_INVAL), (dict(thr=1.5), NABLA_E_INVAL),
                    (dict(P=4, H=16, W=16), NABLA_E_INVAL), (dict(H=20), NABLA_E_INVAL),
-                   (dict(d=96), NABLA_E_UNSUPPORTED), (dict(T=129, H=32, W=32), NABLA_E_UNSUPPORTED)):
+                   (dict(d=96), NABLA_E_UNSUPPORTED), (dict(T=257, H=32, W=32), NABLA_E_UNSUPPORTED)):
         assert call(**kw) == st, kw
         assert lib.nabla_last_error().decode().startswith("nabla_build_mask_raster_noalloc")
