@@ -1045,92 +1045,25 @@ constexpr int kMapSelectWaves = (NREG > 20 || (SIP && NREG >= 12)) ? 4 : 8;
 // flight instead of two.  Rows of 48 and 64 registers (up to 4096 blocks) fit in 128
 // VGPRs only without both.
 template <int NREG, bool SIP>
-constexpr bool kMapPrefetch = kMapSelectWaves<NREG, SIP> == 4 && NREG <= 32;
+constexpr bool kMapPrefetch = kMapSelectWaves<NREG, SIP> == 4 && NREG <= 32 && !(!SIP && NREG > 20);
 template <int NREG, bool SIP>
 constexpr int kPoolBatch = kMapSelectWaves<NREG, SIP> == 4 && NREG <= 32 ? 16 : 2;
+// Rows of 24 and 32 registers (NABLA's cut, not SIP) take two rows per wave in eight-wave
+// workgroups, so two workgroups share a CU at four waves per SIMD: one's pooling and map
+// overlap the other's cut, where one sixteen-wave workgroup per CU would leave the
+// SIMDs idle through its own pooling.
+template <int NREG, bool SIP>
+constexpr int kRowsPerWave = (!SIP && NREG > 20 && NREG <= 32) ? 2 : 1;
+template <int NREG, bool SIP>
+constexpr int kMapThreads = 64 * kRows / kRowsPerWave<NREG, SIP>;
 
-template <int D, int NREG, bool SIP>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMapSelectWaves<NREG, SIP>,
-                                                                             kMapSelectWaves<NREG, SIP>))) void
-map_select_kernel(const void* __restrict__ q, int bf16, int raster, attn::RasterGrid grid, int L,
-                  const _Float16* __restrict__ kp, const int32_t* __restrict__ kexp, int nb, float scale,
-                  float thr, int sta,
-                  FastDiv fd_pf, FastDiv fd_nw, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
-                  int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int sip_budget,
-                  const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
-    // [2][kRows][kChunkLd] chunk buffers, [kWaves][kRowCand] candidates, then the split
-    // pooled queries: [kRows][kQld] hi halves, [kRows][kQld] lo halves, [kRows] exponents
-    extern __shared__ __align__(16) float s_lds[];
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int bh = blockIdx.y;
-    const int row0 = blockIdx.x * kRows;
-    const int row = row0 + wave;
-    float* cand = s_lds + 2 * kRows * kChunkLd + wave * kRowCand;
-    _Float16* q_hi = reinterpret_cast<_Float16*>(s_lds + 2 * kRows * kChunkLd + kWaves * kRowCand);
-    _Float16* q_lo = q_hi + kRows * kQld<D>;
-    int* eq = reinterpret_cast<int*>(q_lo + kRows * kQld<D>);
-    const _Float16* kh = kp + (size_t)bh * ((nb + 15) >> 4) * kKpTileHalves<D>;
-    const int32_t* kexp_h = kexp + (size_t)bh * nb;
-    // the first chunk's Kp tile, in flight while the query block is pooled
-    constexpr bool kPf = kMapPrefetch<NREG, SIP>;
-    KpTile<D> kt;
-    if constexpr (kPf) load_kp_tile<D>(kh, kexp_h, nb, 16 * wave, lane, kt);
-    // the workgroup's pooled query rows: wave w forms the mean of query block row0 + w
-    // from Q itself (zeros past nb), so Q is read once, here, beside other workgroups' work
-    {
-        _Float16* hr = q_hi + wave * kQld<D>;
-        _Float16* lr = q_lo + wave * kQld<D>;
-        if (row < nb) {
-            constexpr int kB = kPoolBatch<NREG, SIP>;
-            if (bf16)
-                pool_row_split<__bf16, D, kB>((const __bf16*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row,
-                                              lane, hr, lr, eq + wave);
-            else
-                pool_row_split<float, D, kB>((const float*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row,
-                                             lane, hr, lr, eq + wave);
-        } else {
-            for (int e = lane; e < D; e += 64) hr[e] = lr[e] = (_Float16)0.f;
-            if (lane == 0) eq[wave] = 0;
-        }
-    }
-    attn::lds_barrier();   // LDS only: prefetched tiles stay in flight
-
-    float v[NREG];
-    const int li = lane & 15;
-    const int kq = lane >> 4;
-#pragma unroll
-    for (int c = 0; c < NREG / 4; ++c) {
-        if (c * kChunkCols < nb) {              // uniform over the workgroup
-            float* buf = s_lds + (c & 1) * kRows * kChunkLd;
-            const int j0 = c * kChunkCols + 16 * wave;
-            if (j0 < nb) {
-                f32x4 sv;
-                if constexpr (kPf) {
-                    sv = tile_products<D>(q_hi, q_lo, eq, kt, scale, lane);
-                    // the next chunk's tile, in flight across this chunk's exchange (past the
-                    // last chunk a clamped, unused one: an unconditional load is not copied
-                    // between registers, which would wait for it here)
-                    load_kp_tile<D>(kh, kexp_h, nb, j0 + kChunkCols, lane, kt);
-                } else {
-                    sv = map_tile<D>(q_hi, q_lo, eq, kh, kexp_h, nb, j0, scale, lane);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) buf[(4 * kq + r) * kChunkLd + 16 * wave + li] = sv[r];
-            }
-            attn::lds_barrier();   // LDS only: prefetched tiles stay in flight
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int j = c * kChunkCols + lane + 64 * m;
-                v[4 * c + m] = j < nb ? buf[wave * kChunkLd + lane + 64 * m] : -INFINITY;
-            }
-        } else {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) v[4 * c + m] = -INFINITY;
-        }
-    }
-    if (row >= nb) return;
-
+// The softmax of one row held in registers and its cut (or SIP sampling).
+template <int NREG, bool SIP>
+__device__ __attribute__((always_inline)) inline void cut_row(float (&v)[NREG], float* cand, int nb, int bh, int row, float thr,
+                               int sta, FastDiv fd_pf, FastDiv fd_nw, int rt, int rh, int rw,
+                               int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
+                               uint32_t* __restrict__ bitmap, int sip_budget, const float* __restrict__ uniforms,
+                               float* __restrict__ kv_logw, int lane) {
     // softmax in place: A = exp2((S - max) log2 e) / sum, the sum in block order per lane
     float mx = -INFINITY;
 #pragma unroll
@@ -1155,6 +1088,131 @@ map_select_kernel(const void* __restrict__ q, int bf16, int raster, attn::Raster
     } else {
         select_row_regs<NREG>(v, cand, nb, bh, row, thr, sta, fd_pf, fd_nw, rt, rh, rw, kv_count, kv_index, bitmap,
                               lane);
+    }
+}
+
+template <int D, int NREG, bool SIP>
+__global__ __launch_bounds__((kMapThreads<NREG, SIP>)) __attribute__((amdgpu_waves_per_eu(kMapSelectWaves<NREG, SIP>,
+                                                                                       kMapSelectWaves<NREG, SIP>))) void
+map_select_kernel(const void* __restrict__ q, int bf16, int raster, attn::RasterGrid grid, int L,
+                  const _Float16* __restrict__ kp, const int32_t* __restrict__ kexp, int nb, float scale,
+                  float thr, int sta,
+                  FastDiv fd_pf, FastDiv fd_nw, int rt, int rh, int rw, int32_t* __restrict__ kv_count,
+                  int32_t* __restrict__ kv_index, uint32_t* __restrict__ bitmap, int sip_budget,
+                  const float* __restrict__ uniforms, float* __restrict__ kv_logw) {
+    constexpr int RPW = kRowsPerWave<NREG, SIP>;   // rows (and map tiles per chunk) per wave
+    // [2][kRows][kChunkLd] chunk buffers, [waves][kRowCand] candidates, then the split
+    // pooled queries: [kRows][kQld] hi halves, [kRows][kQld] lo halves, [kRows] exponents
+    extern __shared__ __align__(16) float s_lds[];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.y;
+    const int row0 = blockIdx.x * kRows;
+    float* cand = s_lds + 2 * kRows * kChunkLd + wave * kRowCand;
+    _Float16* q_hi = reinterpret_cast<_Float16*>(s_lds + 2 * kRows * kChunkLd + kWaves * kRowCand);
+    _Float16* q_lo = q_hi + kRows * kQld<D>;
+    int* eq = reinterpret_cast<int*>(q_lo + kRows * kQld<D>);
+    const _Float16* kh = kp + (size_t)bh * ((nb + 15) >> 4) * kKpTileHalves<D>;
+    const int32_t* kexp_h = kexp + (size_t)bh * nb;
+    // the first chunk's Kp tile, in flight while the query block is pooled
+    constexpr bool kPf = kMapPrefetch<NREG, SIP>;
+    KpTile<D> kt;
+    if constexpr (kPf) load_kp_tile<D>(kh, kexp_h, nb, 16 * wave, lane, kt);
+    // the workgroup's pooled query rows: wave w forms the mean of query block row0 + w
+    // from Q itself (zeros past nb), so Q is read once, here, beside other workgroups' work
+    if constexpr (RPW == 1) {
+        const int row = row0 + wave;
+        _Float16* hr = q_hi + wave * kQld<D>;
+        _Float16* lr = q_lo + wave * kQld<D>;
+        if (row < nb) {
+            constexpr int kB = kPoolBatch<NREG, SIP>;
+            if (bf16)
+                pool_row_split<__bf16, D, kB>((const __bf16*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row,
+                                              lane, hr, lr, eq + wave);
+            else
+                pool_row_split<float, D, kB>((const float*)q + (size_t)bh * L * D, grid, raster, (uint32_t)row,
+                                             lane, hr, lr, eq + wave);
+        } else {
+            for (int e = lane; e < D; e += 64) hr[e] = lr[e] = (_Float16)0.f;
+            if (lane == 0) eq[wave] = 0;
+        }
+    } else {
+        // the same for local rows RPW wave + u
+#pragma unroll
+        for (int u = 0; u < RPW; ++u) {
+            const int r = RPW * wave + u;
+            const int row = row0 + r;
+            _Float16* hr = q_hi + r * kQld<D>;
+            _Float16* lr = q_lo + r * kQld<D>;
+            if (row < nb) {
+                constexpr int kB = kPoolBatch<NREG, SIP>;
+                if (bf16)
+                    pool_row_split<__bf16, D, kB>((const __bf16*)q + (size_t)bh * L * D, grid, raster,
+                                                  (uint32_t)row, lane, hr, lr, eq + r);
+                else
+                    pool_row_split<float, D, kB>((const float*)q + (size_t)bh * L * D, grid, raster,
+                                                 (uint32_t)row, lane, hr, lr, eq + r);
+            } else {
+                for (int e = lane; e < D; e += 64) hr[e] = lr[e] = (_Float16)0.f;
+                if (lane == 0) eq[r] = 0;
+            }
+        }
+    }
+    attn::lds_barrier();   // LDS only: prefetched tiles stay in flight
+
+    // the rows in registers: va for local row RPW wave, vb for RPW wave + 1 (two rows per
+    // wave only)
+    float va[NREG];
+    float vb[RPW == 2 ? NREG : 1];
+    const int li = lane & 15;
+    const int kq = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < NREG / 4; ++c) {
+        if (c * kChunkCols < nb) {              // uniform over the workgroup
+            float* buf = s_lds + (c & 1) * kRows * kChunkLd;
+#pragma unroll
+            for (int u = 0; u < RPW; ++u) {
+                const int t = RPW * wave + u;      // the chunk's 16-column tile this wave computes
+                const int j0 = c * kChunkCols + 16 * t;
+                if (j0 < nb) {
+                    f32x4 sv;
+                    if constexpr (kPf) {
+                        sv = tile_products<D>(q_hi, q_lo, eq, kt, scale, lane);
+                        // the next chunk's tile, in flight across this chunk's exchange (past the
+                        // last chunk a clamped, unused one: an unconditional load is not copied
+                        // between registers, which would wait for it here)
+                        load_kp_tile<D>(kh, kexp_h, nb, j0 + kChunkCols, lane, kt);
+                    } else {
+                        sv = map_tile<D>(q_hi, q_lo, eq, kh, kexp_h, nb, j0, scale, lane);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) buf[(4 * kq + r) * kChunkLd + 16 * t + li] = sv[r];
+                }
+            }
+            attn::lds_barrier();   // LDS only: prefetched tiles stay in flight
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int j = c * kChunkCols + lane + 64 * m;
+                va[4 * c + m] = j < nb ? buf[(RPW * wave) * kChunkLd + lane + 64 * m] : -INFINITY;
+                if constexpr (RPW == 2)
+                    vb[4 * c + m] = j < nb ? buf[(RPW * wave + 1) * kChunkLd + lane + 64 * m] : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                va[4 * c + m] = -INFINITY;
+                if constexpr (RPW == 2) vb[4 * c + m] = -INFINITY;
+            }
+        }
+    }
+    const int row_a = row0 + RPW * wave;
+    if (row_a < nb)
+        cut_row<NREG, SIP>(va, cand, nb, bh, row_a, thr, sta, fd_pf, fd_nw, rt, rh, rw, kv_count, kv_index, bitmap,
+                           sip_budget, uniforms, kv_logw, lane);
+    if constexpr (RPW == 2) {
+        if (row_a + 1 < nb)
+            cut_row<NREG, SIP>(vb, cand, nb, bh, row_a + 1, thr, sta, fd_pf, fd_nw, rt, rh, rw, kv_count, kv_index,
+                               bitmap, sip_budget, uniforms, kv_logw, lane);
     }
 }
 
@@ -1347,11 +1405,11 @@ hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
     }
     const _Float16* kp = reinterpret_cast<const _Float16*>(a.kp);
     if (a.sip_budget > 0) {
-        hipLaunchKernelGGL((map_select_kernel<D, NREG, true>), grid, dim3(kWaves * 64), lds, s, a.q, a.bf16, a.raster,
+        hipLaunchKernelGGL((map_select_kernel<D, NREG, true>), grid, dim3((kMapThreads<NREG, true>)), lds, s, a.q, a.bf16, a.raster,
                            rg, a.nb * 64, kp, a.kexp, a.nb, a.scale, a.thr, a.sta, fd_pf, fd_nw, a.rt, a.rh, a.rw,
                            a.kv_count, a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
     } else {
-        hipLaunchKernelGGL((map_select_kernel<D, NREG, false>), grid, dim3(kWaves * 64), lds, s, a.q, a.bf16,
+        hipLaunchKernelGGL((map_select_kernel<D, NREG, false>), grid, dim3((kMapThreads<NREG, false>)), lds, s, a.q, a.bf16,
                            a.raster, rg, a.nb * 64, kp, a.kexp, a.nb, a.scale, a.thr, a.sta, fd_pf, fd_nw, a.rt,
                            a.rh, a.rw, a.kv_count, a.kv_index, a.bitmap, a.sip_budget, a.uniforms, a.kv_logw);
     }
