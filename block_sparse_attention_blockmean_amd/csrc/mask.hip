@@ -194,6 +194,19 @@ __device__ inline size_t kp_piece(int bh, int ntiles, int j, int e, int term) {
            (e & 7);
 }
 
+// The float32 means for the IBCS scores in the same spirit, for the float32 MFMA's
+// operand order (map_rows): per head, tiles of 16 blocks; inside a tile, for each group m
+// of 16 coordinates, the 16-byte pieces of the 64 lanes (lane 16g + (j mod 16) holds
+// coordinates 16m + 4g .. + 3 of block j).  kKpF32TileFloats floats per tile.
+template <int D>
+constexpr int kKpF32TileFloats = 16 * D;
+
+template <int D>
+__device__ inline size_t kpf_piece(int bh, int ntiles, int j, int e) {
+    return ((size_t)bh * ntiles + (j >> 4)) * kKpF32TileFloats<D> +
+           (size_t)((e >> 4) * 64 + 16 * ((e >> 2) & 3) + (j & 15)) * 4 + (e & 3);
+}
+
 // Mean of query block b of one head (one wave), with pool_kernel's arithmetic, in the
 // two-term half form (split_store) into the LDS rows hi, lo, its exponent in *e_out.
 template <typename T, int D, int BATCH>
@@ -212,10 +225,11 @@ __device__ inline void pool_row_split(const T* __restrict__ head, const attn::Ra
     if (lane == 0) *e_out = ex;
 }
 
-// Block means of K (and of Q for callers that want them stored): one wave per (tensor,
-// head, block).  SPLIT = false: float32 means stored as [block][D] (the IBCS scores read
-// them).  SPLIT = true (K only): the two-term half form in the tiled layout of kp_piece, with the
-// block's exponent in kexp[block] (NABLA's map).
+// Block means of K: one wave per (head, block) (the launch starts at first_wave =
+// total_blocks, past the Q waves, which no caller needs any more).  SPLIT = false: float32
+// means in the tiled layout of kpf_piece (the IBCS scores read them).  SPLIT = true: the
+// two-term half form in the tiled layout of kp_piece, with the block's exponent in
+// kexp[block] (NABLA's map).
 template <typename T, int D, int N, bool RASTER, bool SPLIT>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
                                                     const T* __restrict__ k,
@@ -247,9 +261,12 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
                         base + kp_piece<D>(bh, ntiles, j, lane * EPC, 1));
         if (lane == 0) kexp[blk] = ex;
     } else if (lane < CHUNKS) {
-        float* o = (is_k ? kp : qp) + (size_t)blk * D + lane * EPC;
+        // K only (IBCS): float32 means in the tiled layout of kpf_piece
+        const int j = blk - bh * nb, ntiles = (nb + 15) >> 4;
 #pragma unroll
-        for (int e = 0; e < EPC; e += 4) *reinterpret_cast<f32x4*>(o + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+        for (int e = 0; e < EPC; e += 4)
+            *reinterpret_cast<f32x4*>(kp + kpf_piece<D>(bh, ntiles, j, lane * EPC + e)) =
+                f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
     }
 }
 
@@ -410,17 +427,16 @@ __device__ inline void map_rows(const float* __restrict__ x_lds, const float* __
     const int n_ct = (nb + 15) / 16;
     for (int ct = wave; ct < n_ct; ct += NW) {
         const int j = ct * 16 + li;
-        const f32x4* src = reinterpret_cast<const f32x4*>(kh + (size_t)min(j, nb - 1) * D) + kq;
+        // the tile's operand pieces, one 1 KiB read per 16 coordinates (the padding columns
+        // past nb are read but never stored)
+        const float* src = kh + (size_t)ct * kKpF32TileFloats<D> + lane * 4;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         // the K operand in two halves of d (16 values per lane each)
 #pragma unroll 1
         for (int h = 0; h < 2; ++h) {
             f32x4 b[KC / 8];
 #pragma unroll
-            for (int v = 0; v < KC / 8; ++v) {
-                b[v] = src[4 * (h * (KC / 8) + v)];
-                if (j >= nb) b[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int v = 0; v < KC / 8; ++v) b[v] = *reinterpret_cast<const f32x4*>(src + (h * (KC / 8) + v) * 256);
 #pragma unroll
             for (int v = 0; v < KC / 8; ++v) {
                 const f32x4 a = xa[4 * (h * (KC / 8) + v)];
@@ -462,7 +478,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) __attribute__((amdgpu_waves_per_e
     float* x_lds = s_lds + kRows * ld_s;
     stage_rows<D, kScoreWaves * 64>(cent + (size_t)bh * n_rows * D, n_rows, row0, x_lds);
     __syncthreads();
-    map_rows<D, kScoreWaves>(x_lds, kp + (size_t)bh * nb * D, nb, ld_s, scale, s_lds, wave, lane);
+    map_rows<D, kScoreWaves>(x_lds, kp + (size_t)bh * ((nb + 15) >> 4) * kKpF32TileFloats<D>, nb, ld_s, scale,
+                             s_lds, wave, lane);
     __syncthreads();
     // per centroid row: the maximum m_c and the factor w_c / sum_j exp(S_cj - m_c)
     __shared__ float fac[kRows], mx2[kRows];

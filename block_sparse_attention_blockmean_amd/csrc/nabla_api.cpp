@@ -114,7 +114,9 @@ struct IbcsSections {
 };
 
 IbcsSections ibcs_sections(long long BH, long long nb, long long groups, int d) {
-    return {up256((size_t)BH * nb * d * sizeof(float)),
+    // float32 pooled K in tiles of 16 blocks (the last one padded), then centroids, weights, scores
+    const long long nb16 = (nb + 15) / 16 * 16;
+    return {up256((size_t)BH * nb16 * d * sizeof(float)),
             up256((size_t)BH * groups * nabla::kIbcsClusters * d * sizeof(float)),
             up256((size_t)BH * groups * nabla::kIbcsClusters * sizeof(float)),
             up256((size_t)BH * groups * nb * sizeof(float))};

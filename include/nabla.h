@@ -263,12 +263,14 @@ nabla_status nabla_build_mask_sip(const void* q, const void* k, int batch, int h
 
 /*
  * nabla_build_mask_ibcs_workspace_size - bytes of device workspace nabla_build_mask_ibcs
- * needs (BH = batch*heads, nb = L/N, groups = L/q_group), four sections in this order,
- * each rounded up to 256 bytes: the pooled K (BH*nb*d floats), 8 centroids per query
- * group (BH*groups*8*d floats), their weights (BH*groups*8 floats) and the score rows
- * A (BH*groups*nb floats).  After a call the sections hold those values, float32,
- * row-major [batch, heads, ...].  Returns 0 for non-positive sizes, L not a multiple of
- * N or of q_group, or q_group not a multiple of N.
+ * needs (BH = batch*heads, nb = L/N, nb16 = nb rounded up to a multiple of 16,
+ * groups = L/q_group), four sections in this order, each rounded up to 256 bytes: the
+ * pooled K (BH*nb16*d floats, in tiles of 16 blocks laid out in the order the score
+ * kernel's MFMA reads them), 8 centroids per query group (BH*groups*8*d floats), their
+ * weights (BH*groups*8 floats) and the score rows A (BH*groups*nb floats).  After a call
+ * the sections hold those values, float32; the last three row-major [batch, heads, ...].
+ * Returns 0 for non-positive sizes, L not a multiple of N or of q_group, or q_group not a
+ * multiple of N.
  */
 size_t nabla_build_mask_ibcs_workspace_size(int batch, int heads, int L, int d, int N, int q_group);
 

@@ -301,15 +301,15 @@ def test_attn_weighted_validation(lib):
 # ------------------------------------------------------------- IBCS entry points
 
 def test_ibcs_workspace_size(lib):
-    # pooled K per block; 8 centroids, 8 weights and one nb-long score row per query
-    # group; sections rounded up to 256
+    # pooled K per block (blocks padded to a multiple of 16 per head); 8 centroids, 8
+    # weights and one nb-long score row per query group; sections rounded up to 256
     blocks = 12 * 504
     for qg in (64, 128):
         groups = blocks * 64 // qg
-        want = blocks * 128 * 4 + groups * 8 * 128 * 4 + groups * 8 * 4 + groups * 504 * 4
+        want = 12 * 512 * 128 * 4 + groups * 8 * 128 * 4 + groups * 8 * 4 + groups * 504 * 4
         assert lib.nabla_build_mask_ibcs_workspace_size(1, 12, 32256, 128, 64, qg) == want
-    # 3 blocks, d = 64, one block per group: 768 B, 6144 B, 96 B, 36 B
-    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 192, 64, 64, 64) == 768 + 6144 + 256 + 256
+    # 3 blocks (padded to 16), d = 64, one block per group: 4096 B, 6144 B, 96 B, 36 B
+    assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 192, 64, 64, 64) == 4096 + 6144 + 256 + 256
     assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 192, 64, 64, 128) == 0     # 192 % 128
     assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 256, 64, 64, 96) == 0      # 96 % 64
     assert lib.nabla_build_mask_ibcs_workspace_size(1, 1, 1000, 64, 64, 64) == 0

@@ -60,7 +60,7 @@ def gpu_ibcs(cfg, qf, kf, thr, sta=None, qn=128):
     cnt, idx, bm = nab.build_mask(qf, kf, cfg.T, cfg.H, cfg.W, cfg.P, cfg.N, thr, sta, with_bitmap=True,
                                   workspace=ws, ibcs=True, ibcs_group=qn)
     torch.cuda.synchronize()
-    o_cent = _up256(G * nb * d * 4)
+    o_cent = _up256(G * ((nb + 15) // 16 * 16) * d * 4)   # pooled K in tiles of 16 blocks
     o_w = o_cent + _up256(G * ng * K * d * 4)
     o_a = o_w + _up256(G * ng * K * 4)
     assert o_a + _up256(G * ng * nb * 4) == nbytes
