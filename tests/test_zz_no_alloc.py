@@ -10,7 +10,6 @@ import pytest
 import torch
 
 import block_sparse_attention_blockmean_amd as nab
-from parity import lists_to_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -33,9 +32,11 @@ def structured(B, heads, T, H, W, d, dtype, seed):
 
 
 CASES = [
-    # 2 x 11 heads of 2048 blocks at d = 128: the pooled Q and K of 16 heads fill the
-    # 32 MiB array, so this call runs in two chunks
-    dict(B=2, heads=11, T=16, H=64, W=128, d=128, dtype=torch.bfloat16, thr=0.2, sta=None),
+    # 2 x 8 heads of 4096 blocks at d = 128 (the longest rows): one head's pooled K takes
+    # 2.1 MB of the 32 MiB array, 15 heads fit, so this call runs in two chunks
+    dict(B=2, heads=8, T=64, H=64, W=64, d=128, dtype=torch.bfloat16, thr=0.2, sta=None),
+    # 2 x 11 heads of 2048 blocks, window: one chunk of 22 heads
+    dict(B=2, heads=11, T=16, H=64, W=128, d=128, dtype=torch.bfloat16, thr=0.2, sta=(3, 3, 3)),
     # smaller: 75 blocks per head (ragged against 16-row and 64-column tiles), window
     dict(B=1, heads=3, T=5, H=24, W=40, d=64, dtype=torch.bfloat16, thr=0.2, sta=(3, 3, 3)),
     # smaller still, float32
@@ -63,9 +64,10 @@ def test_noalloc_matches_workspace_entry():
         assert torch.equal(cnt, ref_cnt), "counts differ"
         G = B * NH
         cn = cnt.cpu().numpy().reshape(G, nb)
-        m = lists_to_mask(cn, idx.cpu().numpy().reshape(G, nb, nb))
-        m_ref = lists_to_mask(ref_cnt.cpu().numpy().reshape(G, nb), ref_idx.cpu().numpy().reshape(G, nb, nb))
-        assert np.array_equal(m, m_ref), "lists differ"
+        # the lists are ascending and duplicate-free, so equal masks mean equal written
+        # prefixes; compared on the GPU (a list holds only its first count entries)
+        valid = torch.arange(nb, device="cuda")[None, None, None, :] < cnt[..., None]
+        assert torch.equal(idx[valid], ref_idx[valid]), "lists differ"
         assert torch.equal(bm, ref_bm), "bitmaps differ"
         # the start order: each head's blocks once, by non-increasing count (ties in any order)
         s = sched.cpu().numpy().reshape(G, nb)
@@ -73,6 +75,6 @@ def test_noalloc_matches_workspace_entry():
         for g in range(G):
             assert np.array_equal(np.sort(s[g]), np.sort(s_ref[g]))
             assert np.array_equal(cn.reshape(-1)[s[g]], cn.reshape(-1)[s_ref[g]])
-        say(f"  kept {m.mean():.4f}: counts, lists, bitmap and order agree")
-        del q, k, ref_idx, idx
+        say(f"  kept {cn.sum() / (G * nb * nb):.4f}: counts, lists, bitmap and order agree")
+        del q, k, ref_idx, idx, valid
         torch.cuda.empty_cache()
