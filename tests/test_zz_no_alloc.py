@@ -1,8 +1,8 @@
 """The mask entry point that allocates nothing (nabla_build_mask_raster_noalloc) against
 the workspace entry point it mirrors (nabla_build_mask_raster), through the C ABI: counts,
-lists, bitmap and start order must agree bit for bit, on calls in a row whose second and
-third inputs are smaller than the first (the device array keeps the previous call's
-contents, which must not leak into the next)."""
+lists, bitmap and start order must agree bit for bit, on calls in a row each smaller than
+the one before (the device array keeps the previous call's contents, which must not leak
+into the next); the first runs in two chunks of heads."""
 import sys
 
 import numpy as np
