@@ -225,44 +225,35 @@ __device__ inline void pool_row_split(const T* __restrict__ head, const attn::Ra
     if (lane == 0) *e_out = ex;
 }
 
-// Block means of K: one wave per (head, block) (the launch starts at first_wave =
-// total_blocks, past the Q waves, which no caller needs any more).  SPLIT = false: float32
-// means in the tiled layout of kpf_piece (the IBCS scores read them).  SPLIT = true: the
-// two-term half form in the tiled layout of kp_piece, with the block's exponent in
-// kexp[block] (NABLA's map).
+// Block means of K: one wave per (head, block).  SPLIT = false: float32 means in the
+// tiled layout of kpf_piece (the IBCS scores read them).  SPLIT = true: the two-term half
+// form in the tiled layout of kp_piece, with the block's exponent in kexp[block] (NABLA's
+// map).  (The query blocks are pooled where they are used: in the map kernel for NABLA,
+// by the clustering for IBCS.)
 template <typename T, int D, int N, bool RASTER, bool SPLIT>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q,
-                                                    const T* __restrict__ k,
-                                                    float* __restrict__ qp,
-                                                    float* __restrict__ kp, int32_t* __restrict__ kexp,
-                                                    int total_blocks, int nb, int L, attn::RasterGrid grid,
-                                                    int first_wave) {
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k, float* __restrict__ kp,
+                                                    int32_t* __restrict__ kexp, int total_blocks, int nb, int L,
+                                                    attn::RasterGrid grid) {
     constexpr int EPC = Elem<T>::kPerChunk;
     constexpr int CHUNKS = D / EPC;
-    const int wave = first_wave + ((blockIdx.x * 256 + threadIdx.x) >> 6);
+    const int blk = (blockIdx.x * 256 + threadIdx.x) >> 6;
     const int lane = threadIdx.x & 63;
-    if (wave >= 2 * total_blocks) return;
-    const bool is_k = wave >= total_blocks;
-    const int blk = is_k ? wave - total_blocks : wave;
+    if (blk >= total_blocks) return;
     const int bh = blk / nb;
-    const T* head = (is_k ? k : q) + (size_t)bh * L * D;
+    const int j = blk - bh * nb, ntiles = (nb + 15) >> 4;
     float acc[EPC];
-    block_sum_wave<T, D, N, 64>(head, BlockRows<RASTER, N>(grid, blk - bh * nb), lane, acc);
+    block_sum_wave<T, D, N, 64>(k + (size_t)bh * L * D, BlockRows<RASTER, N>(grid, j), lane, acc);
     constexpr float inv = 1.0f / N;      // N is a power of two: exact
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] *= inv;
     if constexpr (SPLIT) {
-        // K only (first_wave = total_blocks): the tiled layout of kp_piece
         const int ex = split_exponent(acc);
         _Float16* base = reinterpret_cast<_Float16*>(kp);
-        const int j = blk - bh * nb, ntiles = (nb + 15) >> 4;
         if (lane < CHUNKS)
             split_store(acc, ex, base + kp_piece<D>(bh, ntiles, j, lane * EPC, 0),
                         base + kp_piece<D>(bh, ntiles, j, lane * EPC, 1));
         if (lane == 0) kexp[blk] = ex;
     } else if (lane < CHUNKS) {
-        // K only (IBCS): float32 means in the tiled layout of kpf_piece
-        const int j = blk - bh * nb, ntiles = (nb + 15) >> 4;
 #pragma unroll
         for (int e = 0; e < EPC; e += 4)
             *reinterpret_cast<f32x4*>(kp + kpf_piece<D>(bh, ntiles, j, lane * EPC + e)) =
@@ -1376,9 +1367,8 @@ __global__ __launch_bounds__(64) void pair_schedule_kernel(const int32_t* __rest
 template <typename T, int D, bool RASTER, bool SPLIT>
 void launch_pool_form(const MaskArgs& a, const attn::RasterGrid& grid, hipStream_t s) {
     const int total = a.BH * a.nb;
-    const int first = total;   // K only: NABLA's map pools Q itself, IBCS clusters Q
-    hipLaunchKernelGGL((pool_kernel<T, D, 64, RASTER, SPLIT>), dim3((2 * total - first + 3) / 4), dim3(256), 0, s,
-                       (const T*)a.q, (const T*)a.k, a.qp, a.kp, a.kexp, total, a.nb, a.nb * 64, grid, first);
+    hipLaunchKernelGGL((pool_kernel<T, D, 64, RASTER, SPLIT>), dim3((total + 3) / 4), dim3(256), 0, s, (const T*)a.k,
+                       a.kp, a.kexp, total, a.nb, a.nb * 64, grid);
 }
 
 template <typename T, int D>
