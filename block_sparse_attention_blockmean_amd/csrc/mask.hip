@@ -1,14 +1,20 @@
 // Adaptive block mask (NABLA technical summary, "Metodologia: NABLA", item 2, with the
 // STA union of item 3):
-//   pool_kernel        block means of Q and K (one HBM pass over both, float32 sums)
-//   map_select_kernel  reduced map S = Qp Kp^T * scale on float32 MFMA, row softmax,
-//                      then per row (select_row) the CDF cutoff found by bisection on
-//                      float32 bit patterns (or SIP sampling), the STA OR, and
-//                      compaction into an ascending kept list
+//   pool_kernel           block means of K (one HBM pass, float32 sums), stored in a
+//                         two-term half-precision form in the map's operand order
+//   map_select_kernel     per workgroup 16 query blocks: their means pooled from Q, the
+//                         reduced map S = Qp Kp^T * scale on the fp16 MFMA (three
+//                         products of the split terms, float32 accumulation) into the
+//                         waves' registers, row softmax, then per row (select_row_regs)
+//                         the CDF cutoff found by bisection on float32 bit patterns (or
+//                         SIP sampling), the STA OR, and compaction into an ascending list
+//   pair_schedule_kernel  the attention's start order: pairs of blocks of neighbouring
+//                         frames, each head's pairs by decreasing combined count
 // With IBCS block scores the rows of the map are the 8 cluster centroids of each query
-// group (ibcs.hip) instead of its mean: ibcs_score_kernel writes each group's score row,
-// the weighted sum of its centroids' softmax rows, and select_kernel applies select_row
-// to those rows; the cut and the lists are the same.
+// group (ibcs.hip) instead of its mean: ibcs_score_kernel (float32 MFMA on float32 means)
+// writes each group's score row, the weighted sum of its centroids' softmax rows, and
+// select_kernel applies select_row (the same cut on an LDS row) to those rows; the cut
+// and the lists are the same.
 #include <math.h>
 
 #include "attn_tile.h"
@@ -263,9 +269,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k, floa
 
 // ---------------------------------------------------------------------------
 // Reduced map, then the cut.
-// The map kernels hold kRows = 16 rows of S per workgroup (the M of the 16x16 float32
-//   MFMA).
-// The cut (select_row) takes one row in one wave.  Keeping block j iff F_j > thr is the
+// The map kernels hold kRows = 16 rows of S per workgroup (the M of the 16 x 16 MFMA).
+// The cut (select_row on an LDS row, select_row_regs on a row in registers) takes one row
+//   in one wave.  Keeping block j iff F_j > thr is the
 //   same as keeping every block whose probability is at least v*, the smallest row
 //   value with g(v*) > thr, where g(u) = sum of the row values <= u.  g only grows with
 //   u, and non-negative floats order like their bit patterns, so v* is found by
@@ -919,17 +925,18 @@ __device__ void select_row_regs(const float (&v)[NREG], float* cand, int nb, int
 }
 
 // ---------------------------------------------------------------------------
-// NABLA's reduced map and cut in one kernel.  A workgroup (16 waves) owns kRows = 16
-// query blocks of one head; wave r pools block r from Q (block_sum_wave, as pool_kernel
-// does for K) and owns row r of the map: the row ends up in the wave's
-// registers (v[i] = S_j of block j = lane + 64 i), so the softmax and the cut run without
-// touching LDS.  The map runs in chunks of 256 columns: each wave computes one 16 x 16
-// tile of the chunk on the float32 MFMA (map_tile) into an LDS chunk buffer, and after
-// one barrier every wave copies its row's 256 values into registers.  Two chunk buffers
-// alternate, so one barrier per chunk suffices (a wave writes chunk c + 2 only after the
-// barrier of chunk c + 1, which every wave reaches after reading chunk c).  LDS per
-// workgroup is then ~46 KiB whatever nb, and two workgroups share a CU: one's loads and
-// barriers overlap the other's cut.
+// NABLA's reduced map and cut in one kernel.  A workgroup owns kRows = 16 query blocks of
+// one head (16 waves, one row each; for rows of 24 and 32 registers 8 waves, two rows
+// each).  A wave pools its blocks from Q (block_sum_wave, as pool_kernel does for K) and
+// owns their rows of the map: a row ends up in the wave's registers (v[i] = S_j of block
+// j = lane + 64 i), so the softmax and the cut run without touching LDS.  The map runs in
+// chunks of 256 columns: each wave computes its 16 x 16 tile(s) of the chunk on the fp16
+// MFMA (map_tile / tile_products) into an LDS chunk buffer, and after one barrier every
+// wave copies its rows' 256 values into registers.  Two chunk buffers alternate, so one
+// barrier per chunk suffices (a wave writes chunk c + 2 only after the barrier of chunk
+// c + 1, which every wave reaches after reading chunk c).  LDS per workgroup is 58 KiB
+// whatever nb, and two workgroups share a CU: one's loads and barriers overlap the
+// other's cut.
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 16;
 constexpr int kChunkCols = 16 * kWaves;     // one 16-column tile per wave
