@@ -145,22 +145,30 @@ def cpu_baseline(cfg, q, k, v, kept_flops_total, budget_s=20.0, blocks_per_head=
 
 
 def bench_backward(args, cfg, qd, kd, vd) -> int:
-    """Gradient of the attention step on the same workload: the mask and the forward
-    (with its log-sum-exp) run once untimed; then K calls of block_sparse_attn_bwd (row
-    dots, transposed lists, start orders, the dQ sweep and the dK/dV sweep), each
-    bracketed by HIP events on the launch stream."""
+    """Gradient of the attention step on the same workload, in the step's token order
+    (raster in and out, the flattening applied in the addressing, when N == P*P): the
+    mask and the forward (with its log-sum-exp) run once untimed; then K calls of
+    block_sparse_attn_bwd(_raster) (row dots, transposed lists, start orders, the dQ
+    sweep and the dK/dV sweep), each bracketed by HIP events on the launch stream."""
     T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
-    qf, kf, vf = (nab.reorder(t, T, H, W, P) for t in (qd, kd, vd))
-    cnt, idx, sched = nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True)
-    o, lse = nab.attn_fwd(qf, kf, vf, cnt, idx, N, schedule=sched, with_lse=True)
+    raster = N == P * P
     g = torch.Generator(device="cuda").manual_seed(1234)
-    dout = torch.randn(qf.shape, device="cuda", generator=g).to(qf.dtype)
+    dout = torch.randn(qd.shape, device="cuda", generator=g).to(qd.dtype)
+    if raster:
+        qf, kf, vf, dof = qd, kd, vd, dout
+        cnt, idx, sched = nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True, raster=True)
+        o, lse = nab.attn_fwd_raster(qf, kf, vf, cnt, idx, T, H, W, P, N, schedule=sched, with_lse=True)
+    else:
+        qf, kf, vf, dof = (nab.reorder(t, T, H, W, P) for t in (qd, kd, vd, dout))
+        cnt, idx, sched = nab.build_mask(qf, kf, T, H, W, P, N, cfg.thr, cfg.sta, with_schedule=True)
+        o, lse = nab.attn_fwd(qf, kf, vf, cnt, idx, N, schedule=sched, with_lse=True)
     ws = torch.empty(nab.attn_bwd_workspace_size(cfg.B, cfg.heads, cfg.L, N), dtype=torch.uint8,
                      device="cuda")
     dq, dk, dv = (torch.empty_like(qf) for _ in range(3))
 
     def call():
-        nab.attn_bwd(qf, kf, vf, o, dout, lse, cnt, idx, N, workspace=ws, dq=dq, dk=dk, dv=dv)
+        nab.attn_bwd(qf, kf, vf, o, dof, lse, cnt, idx, N, workspace=ws, dq=dq, dk=dk, dv=dv,
+                     raster=(T, H, W, P) if raster else None)
 
     for _ in range(args.warmup):
         call()
@@ -197,6 +205,7 @@ def bench_backward(args, cfg, qd, kd, vd) -> int:
         "ms_bwd": round(ms, 4),
         "kept_fraction": round(kept / (cfg.BH * cfg.nb * cfg.nb), 5),
         "flop_convention": "algorithmic 10 N^2 d per kept tile (5 products); executed 14 N^2 d",
+        "order": "raster, flattening in the addressing" if raster else "fractal (explicit reorder before)",
         "executed_tflops": round(exe / (ms * 1e-3) / 1e12, 2),
         "executed_frac_of_peak": round(exe / (ms * 1e-3) / 1e12 / peak, 4),
     }

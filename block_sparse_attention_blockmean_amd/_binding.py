@@ -34,8 +34,10 @@ EXPORTS = (
     "block_sparse_attn_fwd",
     "block_sparse_attn_fwd_raster",
     "block_sparse_attn_fwd_lse",
+    "block_sparse_attn_fwd_lse_raster",
     "nabla_attn_bwd_workspace_size",
     "block_sparse_attn_bwd",
+    "block_sparse_attn_bwd_raster",
     "nabla_status_string",
     "nabla_last_error",
 )
@@ -95,11 +97,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.block_sparse_attn_fwd.restype = i
     lib.block_sparse_attn_fwd_lse.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, f, i, vp, vp]
     lib.block_sparse_attn_fwd_lse.restype = i
+    lib.block_sparse_attn_fwd_lse_raster.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, f, i, vp,
+                                                     vp]
+    lib.block_sparse_attn_fwd_lse_raster.restype = i
     lib.nabla_attn_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.nabla_attn_bwd_workspace_size.restype = sz
     lib.block_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, f, i,
                                           vp, sz, vp]
     lib.block_sparse_attn_bwd.restype = i
+    lib.block_sparse_attn_bwd_raster.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp,
+                                                 f, i, vp, sz, vp]
+    lib.block_sparse_attn_bwd_raster.restype = i
     lib.nabla_status_string.argtypes = [i]
     lib.nabla_status_string.restype = ctypes.c_char_p
     lib.nabla_last_error.argtypes = []
@@ -395,9 +403,14 @@ def attn_fwd_weighted(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_coun
 def attn_fwd_raster(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.Tensor,
                     kv_index: torch.Tensor, T: int, H: int, W: int, P: int, N: int = 64,
                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                    schedule: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    schedule: Optional[torch.Tensor] = None, with_lse: bool = False,
+                    lse: Optional[torch.Tensor] = None):
     """Block-sparse attention of raster-ordered Q, K, V (output in raster order) under
-    lists that number blocks in fractal order (``build_mask(..., raster=True)``)."""
+    lists that number blocks in fractal order (``build_mask(..., raster=True)``).
+
+    With ``with_lse`` (or an ``lse`` tensor) it also returns the float32 [B, heads, L]
+    log-sum-exp of every query row in raster order, as (out, lse), which
+    ``attn_bwd_raster`` needs."""
     lib = load_library()
     B, NH, L, d = q.shape
     if L != T * H * W:
@@ -410,11 +423,21 @@ def attn_fwd_raster(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count:
         raise ValueError("schedule must hold batch*heads*nb int32 entries")
     if out is None:
         out = torch.empty_like(q)
+    sched = _dev(schedule, "schedule") if schedule is not None else None
+    scale_arg = float(scale) if scale is not None else 0.0
+    if with_lse or lse is not None:
+        if lse is None:
+            lse = torch.empty((B, NH, L), dtype=torch.float32, device=q.device)
+        if lse.dtype != torch.float32 or lse.numel() != B * NH * L:
+            raise ValueError("lse must hold batch*heads*L float32 values")
+        _check(lib.block_sparse_attn_fwd_lse_raster(
+            _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, NH, T, H, W, d, P, N,
+            _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), sched, scale_arg, _dtype_code(q),
+            _dev(lse, "lse"), _stream()), lib)
+        return out, lse
     _check(lib.block_sparse_attn_fwd_raster(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, NH, T, H, W, d, P, N,
-        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
-        _dev(schedule, "schedule") if schedule is not None else None,
-        float(scale) if scale is not None else 0.0, _dtype_code(q), _stream()), lib)
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), sched, scale_arg, _dtype_code(q), _stream()), lib)
     return out
 
 
@@ -426,11 +449,18 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              lse: torch.Tensor, kv_count: torch.Tensor, kv_index: torch.Tensor, N: int = 64,
              scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None):
+             dv: Optional[torch.Tensor] = None, raster: Optional[tuple] = None):
     """Gradients (dq, dk, dv) of sum(o * dout) for o = attn_fwd(q, k, v, ...) under the
-    same lists; ``o`` and ``lse`` come from ``attn_fwd(..., with_lse=True)``."""
+    same lists; ``o`` and ``lse`` come from ``attn_fwd(..., with_lse=True)``.
+
+    ``raster=(T, H, W, P)``: every tensor (gradients too) is in raster order, ``o`` and
+    ``lse`` from ``attn_fwd_raster(..., with_lse=True)``."""
     lib = load_library()
     B, NH, L, d = q.shape
+    if raster is not None:
+        T, H, W, P = (int(x) for x in raster)
+        if L != T * H * W:
+            raise ValueError(f"L={L} does not match T*H*W={T * H * W}")
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError(f"{name} must match q in shape and dtype")
@@ -443,10 +473,13 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     ws_bytes = int(lib.nabla_attn_bwd_workspace_size(B, NH, L, N))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    _check(lib.block_sparse_attn_bwd(
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(dout, "dout"), _dev(lse, "lse"),
-        _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), B, NH, L, d, N,
-        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
-        float(scale) if scale is not None else 0.0, _dtype_code(q),
-        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()), lib)
+    ptrs = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(dout, "dout"), _dev(lse, "lse"),
+            _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"))
+    rest = (_dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+            float(scale) if scale is not None else 0.0, _dtype_code(q),
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream())
+    if raster is not None:
+        _check(lib.block_sparse_attn_bwd_raster(*ptrs, B, NH, T, H, W, d, P, N, *rest), lib)
+    else:
+        _check(lib.block_sparse_attn_bwd(*ptrs, B, NH, L, d, N, *rest), lib)
     return dq, dk, dv

@@ -13,6 +13,12 @@
 //
 // bf16: MFMA v_mfma_f32_32x32x16_bf16 with float32 accumulation; P and dS are rounded
 // to bf16 as MFMA operands; gradients are written in bf16.  float32: plain FMAs.
+//
+// Token order: every kernel takes the blocks either as runs of 64 rows (fractal order)
+// or, with RASTER, as 8 x 8 patches of a raster T x H x W grid (the fractal reorder of
+// the NABLA summary, "Metodologia: NABLA", item 1, folded into the addressing: a patch
+// is eight runs of eight consecutive tokens).  Lists number blocks the same way in both;
+// the arithmetic, and so every result bit, is the same.
 #include <math.h>
 
 #include <algorithm>
@@ -117,17 +123,16 @@ __global__ __launch_bounds__(64) void bwd_qlist_kernel(const uint32_t* __restric
 // K and V tiles are double-buffered through the LDS DMA, both with the row-read
 // swizzle.  The two key halves are summed through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool RASTER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                         const __bf16* __restrict__ dout, const float* __restrict__ lse,
                         const float* __restrict__ drow, __bf16* __restrict__ dq, int L, int nb,
                         const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_index,
-                        const int32_t* __restrict__ schedule, float scale_log2e, float scale) {
+                        const int32_t* __restrict__ schedule, RasterGrid grid, float scale_log2e, float scale) {
     using G = Tile<D>;
     constexpr int KS = D / 16;
     constexpr int DT = D / 32;
-    constexpr uint32_t kTileBytes = kBlk * D * 2;
     __shared__ __attribute__((aligned(1024))) char k_lds0[G::kBytes];
     __shared__ __attribute__((aligned(1024))) char k_lds1[G::kBytes];
     __shared__ __attribute__((aligned(1024))) char v_lds0[G::kBytes];
@@ -151,16 +156,18 @@ void bwd_dq_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         __builtin_amdgcn_make_buffer_rsrc((void*)(k + head_off), 0, head_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t v_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(v + head_off), 0, head_bytes, kBufferFlags);
-    const uint32_t lane_copy = copy_lane_offset<D, false>(wave, lane);
+    const uint32_t lane_copy = copy_lane_offset_in<D, false, RASTER>(grid, wave, lane);
+    const uint32_t stride = copy_stride<RASTER>(grid);   // between a tile's 4 KiB copies
 
     const int count = kv_count[(size_t)bh * nb + qb];
     const int32_t* list = kv_index + ((size_t)bh * nb + qb) * nb;
     if (count > 0) {
-        copy_tile<D>(k_rsrc, list[0] * kTileBytes, k_lds0, wave, lane_copy);
-        copy_tile<D>(v_rsrc, list[0] * kTileBytes, v_lds0, wave, lane_copy);
+        const uint32_t first = block_row<RASTER>(grid, list[0]) * G::kRowBytes;
+        copy_tile<D>(k_rsrc, first, k_lds0, wave, lane_copy, stride);
+        copy_tile<D>(v_rsrc, first, v_lds0, wave, lane_copy, stride);
     }
 
-    const int qrow = qb * kBlk + 32 * qhalf + c32;
+    const int qrow = block_row<RASTER>(grid, qb) + row_in_block<RASTER>(grid, 32 * qhalf + c32);
     bf16x8 qreg[KS], doreg[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -200,7 +207,7 @@ void bwd_dq_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         // tile i has landed; after the barrier every wave is done with tile i - 1
         wait_vmcnt<0>();
         lds_barrier();
-        const uint32_t nxt = next_tile * kTileBytes;
+        const uint32_t nxt = block_row<RASTER>(grid, next_tile) * G::kRowBytes;
         char* k_dst = PAR ? k_lds0 : k_lds1;
         char* v_dst = PAR ? v_lds0 : v_lds1;
         constexpr int kEvery = KS / G::kCopiesPerWave;
@@ -222,7 +229,7 @@ void bwd_dq_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qreg[s], sacc, 0, 0, 0);
             if (s % kEvery == 0)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(k_dst + (kWaves * (s / kEvery) + wave) * 1024),
-                                                         16, lane_copy, nxt + (s / kEvery) * (kWaves * 1024), 0, 0);
+                                                         16, lane_copy, nxt + (s / kEvery) * stride, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -230,7 +237,7 @@ void bwd_dq_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
             dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], doreg[s], dpacc, 0, 0, 0);
             if (s % kEvery == 0)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)(v_dst + (kWaves * (s / kEvery) + wave) * 1024),
-                                                         16, lane_copy, nxt + (s / kEvery) * (kWaves * 1024), 0, 0);
+                                                         16, lane_copy, nxt + (s / kEvery) * stride, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -315,17 +322,16 @@ void bwd_dq_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 // behind, and the next Q copy has the whole block.  The two query halves are summed
 // through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool RASTER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                           const __bf16* __restrict__ dout, const float* __restrict__ lse,
                           const float* __restrict__ drow, __bf16* __restrict__ dk, __bf16* __restrict__ dv, int L,
                           int nb, const int32_t* __restrict__ q_count, const int32_t* __restrict__ q_index,
-                          const int32_t* __restrict__ schedule, float scale_log2e, float scale) {
+                          const int32_t* __restrict__ schedule, RasterGrid grid, float scale_log2e, float scale) {
     using G = Tile<D>;
     constexpr int KS = D / 16;
     constexpr int DT = D / 32;
-    constexpr uint32_t kTileBytes = kBlk * D * 2;
     // vector-memory operations a wave issues per query block, in issue order: the row
     // statistics (two groups of four 16-byte loads), the next Q copy, the next dO copy
     constexpr int kStatLoads = 8;
@@ -359,15 +365,18 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         __builtin_amdgcn_make_buffer_rsrc((void*)(v + head_off), 0, head_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t do_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(dout + head_off), 0, head_bytes, kBufferFlags);
-    const uint32_t lane_copy = copy_lane_offset<D, false>(wave, lane);
+    const uint32_t lane_copy = copy_lane_offset_in<D, false, RASTER>(grid, wave, lane);
+    const uint32_t stride = copy_stride<RASTER>(grid);   // between a tile's 4 KiB copies
 
     const int count = q_count[(size_t)bh * nb + kb];
     const int32_t* list = q_index + ((size_t)bh * nb + kb) * nb;
-    copy_tile<D>(k_rsrc, kb * kTileBytes, k_t, wave, lane_copy);
-    copy_tile<D>(v_rsrc, kb * kTileBytes, v_t, wave, lane_copy);
+    const uint32_t kv_first = block_row<RASTER>(grid, kb);
+    copy_tile<D>(k_rsrc, kv_first * G::kRowBytes, k_t, wave, lane_copy, stride);
+    copy_tile<D>(v_rsrc, kv_first * G::kRowBytes, v_t, wave, lane_copy, stride);
     if (count > 0) {
-        copy_tile<D>(q_rsrc, list[0] * kTileBytes, q_t0, wave, lane_copy);
-        copy_tile<D>(do_rsrc, list[0] * kTileBytes, do_t, wave, lane_copy);
+        const uint32_t first = block_row<RASTER>(grid, list[0]) * G::kRowBytes;
+        copy_tile<D>(q_rsrc, first, q_t0, wave, lane_copy, stride);
+        copy_tile<D>(do_rsrc, first, do_t, wave, lane_copy, stride);
     }
 
     f32x16 dvacc[DT], dkacc[DT];
@@ -400,8 +409,11 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
             const int d = 32 * t + 16 * (g16 & 1) + 4 * (j16 & 3);
             t_off[t][p] = row * G::kRowBytes + (((d >> 3) ^ G::k_swz(row)) * 16) + ((d >> 2) & 1) * 8;
         }
-    // the lane's 16 query rows of a block: 32 qh + 8 g + 4 h + c for accumulator entry 4 g + c
-    const size_t stat_off = (size_t)bh * L + 32 * qhalf + 4 * h;
+    // the lane's 16 query rows of a block: 32 qh + 8 g + 4 h + c for accumulator entry 4 g + c,
+    // four consecutive rows per g in either order (a raster patch row holds 8), g's rows
+    // stat_g rows after g - 1's
+    const size_t stat_off = (size_t)bh * L + row_in_block<RASTER>(grid, 32 * qhalf + 4 * h);
+    const uint32_t stat_g = RASTER ? grid.W : 8u;
 
     auto step = [&](auto par, int i) {
         constexpr int PAR = decltype(par)::value;
@@ -416,16 +428,17 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         // wait for the statistics never waits for that copy.  The copy is unconditional
         // (the last block copies its own Q again into a buffer nothing reads), so the
         // compiler's waits stay exact.
+        const size_t qrow0 = block_row<RASTER>(grid, qblk);
         float4 ls[4], dr[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-            ls[g] = *reinterpret_cast<const float4*>(lse + stat_off + (size_t)qblk * kBlk + 8 * g);
+            ls[g] = *reinterpret_cast<const float4*>(lse + stat_off + qrow0 + g * stat_g);
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-            dr[g] = *reinterpret_cast<const float4*>(drow + stat_off + (size_t)qblk * kBlk + 8 * g);
-        const uint32_t nxt = list[min(i + 1, count - 1)] * kTileBytes;
+            dr[g] = *reinterpret_cast<const float4*>(drow + stat_off + qrow0 + g * stat_g);
+        const uint32_t nxt = block_row<RASTER>(grid, list[min(i + 1, count - 1)]) * G::kRowBytes;
         __builtin_amdgcn_sched_barrier(0);
-        copy_tile<D>(q_rsrc, nxt, q_next, wave, lane_copy);
+        copy_tile<D>(q_rsrc, nxt, q_next, wave, lane_copy, stride);
         __builtin_amdgcn_sched_barrier(0);
 
         // S, then P (the log-sum-exp and S die here)
@@ -482,7 +495,7 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
                 dsb[g / 2][4 * (g % 2) + c] = (__bf16)(p[4 * g + c] * (dpacc[4 * g + c] - dr[g][c]));
         // every wave has read this dO: its buffer takes the next block's dO
         lds_barrier();
-        copy_tile<D>(do_rsrc, nxt, do_t, wave, lane_copy);
+        copy_tile<D>(do_rsrc, nxt, do_t, wave, lane_copy, stride);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -520,7 +533,7 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     }
     lds_barrier();
     if (qhalf == 0) {
-        const size_t key = (size_t)kb * kBlk + brow;
+        const size_t key = (size_t)kv_first + row_in_block<RASTER>(grid, brow);
         __bf16* vrow = dv + head_off + key * D;
         __bf16* krow_out = dk + head_off + key * D;
 #pragma unroll
@@ -543,14 +556,15 @@ void bwd_dkdv_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
 // ---------------------------------------------------------------------------
 // float32 versions: plain FMAs, four threads per row, tiles in LDS (accuracy first).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool RASTER>
 __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                          const float* __restrict__ v, const float* __restrict__ dout,
                                                          const float* __restrict__ lse,
                                                          const float* __restrict__ drow, float* __restrict__ dq,
                                                          int L, int nb, const int32_t* __restrict__ kv_count,
                                                          const int32_t* __restrict__ kv_index,
-                                                         const int32_t* __restrict__ schedule, float scale) {
+                                                         const int32_t* __restrict__ schedule, RasterGrid grid,
+                                                         float scale) {
     constexpr int LD = D + 1;
     extern __shared__ float lds[];
     float* q_s = lds;                  // [64][LD]
@@ -566,25 +580,28 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(const float* __restrict
     const int row = tid >> 2;
     const int part = tid & 3;
     const size_t head_off = (size_t)bh * L * D;
-    const size_t base = head_off + (size_t)qb * kBlk * D;
+    const uint32_t qbase = block_row<RASTER>(grid, qb);
     for (int i = tid; i < kBlk * D; i += 256) {
-        q_s[(i / D) * LD + i % D] = q[base + i];
-        do_s[(i / D) * LD + i % D] = dout[base + i];
+        const size_t src = head_off + (size_t)(qbase + row_in_block<RASTER>(grid, i / D)) * D + i % D;
+        q_s[(i / D) * LD + i % D] = q[src];
+        do_s[(i / D) * LD + i % D] = dout[src];
     }
     const int count = kv_count[(size_t)bh * nb + qb];
     const int32_t* list = kv_index + ((size_t)bh * nb + qb) * nb;
-    const float lse_r = count > 0 ? lse[(size_t)bh * L + (size_t)qb * kBlk + row] : 0.f;
-    const float d_r = drow[(size_t)bh * L + (size_t)qb * kBlk + row];
+    const uint32_t my_row = qbase + row_in_block<RASTER>(grid, row);
+    const float lse_r = count > 0 ? lse[(size_t)bh * L + my_row] : 0.f;
+    const float d_r = drow[(size_t)bh * L + my_row];
     float acc[D / 4];
 #pragma unroll
     for (int c = 0; c < D / 4; ++c) acc[c] = 0.f;
 
     for (int it = 0; it < count; ++it) {
-        const size_t tb = head_off + (size_t)list[it] * kBlk * D;
+        const uint32_t tb = block_row<RASTER>(grid, list[it]);
         __syncthreads();
         for (int i = tid; i < kBlk * D; i += 256) {
-            k_s[(i / D) * LD + i % D] = k[tb + i];
-            v_s[(i / D) * LD + i % D] = v[tb + i];
+            const size_t src = head_off + (size_t)(tb + row_in_block<RASTER>(grid, i / D)) * D + i % D;
+            k_s[(i / D) * LD + i % D] = k[src];
+            v_s[(i / D) * LD + i % D] = v[src];
         }
         __syncthreads();
 #pragma unroll 4
@@ -607,12 +624,12 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(const float* __restrict
             acc[c] = a;
         }
     }
-    float* out = dq + base + (size_t)row * D;
+    float* out = dq + head_off + (size_t)my_row * D;
 #pragma unroll
     for (int c = 0; c < D / 4; ++c) out[part + 4 * c] = acc[c] * scale;
 }
 
-template <int D>
+template <int D, bool RASTER>
 __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                            const float* __restrict__ v,
                                                            const float* __restrict__ dout,
@@ -621,7 +638,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restri
                                                            float* __restrict__ dv, int L, int nb,
                                                            const int32_t* __restrict__ q_count,
                                                            const int32_t* __restrict__ q_index,
-                                                           const int32_t* __restrict__ schedule, float scale) {
+                                                           const int32_t* __restrict__ schedule, RasterGrid grid,
+                                                           float scale) {
     constexpr int LD = D + 1;
     extern __shared__ float lds[];
     float* k_s = lds;                  // [64][LD]
@@ -638,10 +656,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restri
     const int key = tid >> 2;
     const int part = tid & 3;
     const size_t head_off = (size_t)bh * L * D;
-    const size_t kbase = head_off + (size_t)kb * kBlk * D;
+    const uint32_t kbase = block_row<RASTER>(grid, kb);
     for (int i = tid; i < kBlk * D; i += 256) {
-        k_s[(i / D) * LD + i % D] = k[kbase + i];
-        v_s[(i / D) * LD + i % D] = v[kbase + i];
+        const size_t src = head_off + (size_t)(kbase + row_in_block<RASTER>(grid, i / D)) * D + i % D;
+        k_s[(i / D) * LD + i % D] = k[src];
+        v_s[(i / D) * LD + i % D] = v[src];
     }
     const int count = q_count[(size_t)bh * nb + kb];
     const int32_t* list = q_index + ((size_t)bh * nb + kb) * nb;
@@ -652,16 +671,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restri
         acck[c] = 0.f;
     }
     for (int it = 0; it < count; ++it) {
-        const size_t qrow0 = (size_t)list[it] * kBlk;
-        const size_t qbase = head_off + qrow0 * D;
+        const uint32_t qrow0 = block_row<RASTER>(grid, list[it]);
         __syncthreads();
         for (int i = tid; i < kBlk * D; i += 256) {
-            q_s[(i / D) * LD + i % D] = q[qbase + i];
-            do_s[(i / D) * LD + i % D] = dout[qbase + i];
+            const size_t src = head_off + (size_t)(qrow0 + row_in_block<RASTER>(grid, i / D)) * D + i % D;
+            q_s[(i / D) * LD + i % D] = q[src];
+            do_s[(i / D) * LD + i % D] = dout[src];
         }
         if (tid < kBlk) {
-            st[tid] = lse[(size_t)bh * L + qrow0 + tid];
-            st[kBlk + tid] = drow[(size_t)bh * L + qrow0 + tid];
+            const size_t r = (size_t)bh * L + qrow0 + row_in_block<RASTER>(grid, tid);
+            st[tid] = lse[r];
+            st[kBlk + tid] = drow[r];
         }
         __syncthreads();
         float ds[16];
@@ -697,8 +717,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restri
             acck[c] = a;
         }
     }
-    float* vout = dv + kbase + (size_t)key * D;
-    float* kout = dk + kbase + (size_t)key * D;
+    const size_t out_off = head_off + (size_t)(kbase + row_in_block<RASTER>(grid, key)) * D;
+    float* vout = dv + out_off;
+    float* kout = dk + out_off;
 #pragma unroll
     for (int c = 0; c < D / 4; ++c) {
         vout[part + 4 * c] = accv[c];
@@ -735,37 +756,58 @@ hipError_t launch_qlists(const AttnBwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D>
+// The raster grid of 8 x 8 patches (unused in fractal order).
+RasterGrid raster_grid(const AttnBwdArgs& a) {
+    RasterGrid g{};
+    if (a.raster) {
+        g.W = (uint32_t)a.W;
+        g.HW = (uint32_t)(a.H * a.W);
+        g.nHW = FastDiv((uint32_t)((a.H / 8) * (a.W / 8)));
+        g.nW = FastDiv((uint32_t)(a.W / 8));
+    }
+    return g;
+}
+
+template <int D, bool RASTER>
 hipError_t launch_bf16(const AttnBwdArgs& a, hipStream_t s) {
     const float sl2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D>), dim3(a.BH * a.nb), dim3(kThreads), 0, s, (const __bf16*)a.q,
+    const RasterGrid grid = raster_grid(a);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, RASTER>), dim3(a.BH * a.nb), dim3(kThreads), 0, s, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, a.drow, (__bf16*)a.dq,
-                       a.L, a.nb, a.kv_count, a.kv_index, a.sched_q, sl2, a.scale);
+                       a.L, a.nb, a.kv_count, a.kv_index, a.sched_q, grid, sl2, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D>), dim3(a.BH * a.nb), dim3(kThreads), 0, s, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, a.drow, (__bf16*)a.dk,
-                       (__bf16*)a.dv, a.L, a.nb, a.q_count, a.q_index, a.sched_k, sl2, a.scale);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RASTER>), dim3(a.BH * a.nb), dim3(kThreads), 0, s,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
+                       a.drow, (__bf16*)a.dk, (__bf16*)a.dv, a.L, a.nb, a.q_count, a.q_index, a.sched_k, grid, sl2,
+                       a.scale);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool RASTER>
 hipError_t launch_f32(const AttnBwdArgs& a, hipStream_t s) {
     const size_t lds = (4 * kBlk * (D + 1) + kBlk * 65 + 2 * kBlk) * sizeof(float);
     static std::atomic<uint64_t> set_q{0}, set_k{0};
-    hipError_t e = set_max_dynamic_lds((const void*)bwd_dq_f32_kernel<D>, (int)lds, set_q);
+    hipError_t e = set_max_dynamic_lds((const void*)bwd_dq_f32_kernel<D, RASTER>, (int)lds, set_q);
     if (e != hipSuccess) return e;
-    e = set_max_dynamic_lds((const void*)bwd_dkdv_f32_kernel<D>, (int)lds, set_k);
+    e = set_max_dynamic_lds((const void*)bwd_dkdv_f32_kernel<D, RASTER>, (int)lds, set_k);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), dim3(a.BH * a.nb), dim3(256), lds, s, (const float*)a.q,
+    const RasterGrid grid = raster_grid(a);
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, RASTER>), dim3(a.BH * a.nb), dim3(256), lds, s, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse, a.drow, (float*)a.dq, a.L,
-                       a.nb, a.kv_count, a.kv_index, a.sched_q, a.scale);
+                       a.nb, a.kv_count, a.kv_index, a.sched_q, grid, a.scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3(a.BH * a.nb), dim3(256), lds, s, (const float*)a.q,
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, RASTER>), dim3(a.BH * a.nb), dim3(256), lds, s, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse, a.drow, (float*)a.dk,
-                       (float*)a.dv, a.L, a.nb, a.q_count, a.q_index, a.sched_k, a.scale);
+                       (float*)a.dv, a.L, a.nb, a.q_count, a.q_index, a.sched_k, grid, a.scale);
     return hipGetLastError();
+}
+
+template <bool RASTER>
+hipError_t launch_sweeps(const AttnBwdArgs& a, hipStream_t s) {
+    if (a.bf16) return a.d == 128 ? launch_bf16<128, RASTER>(a, s) : launch_bf16<64, RASTER>(a, s);
+    return a.d == 128 ? launch_f32<128, RASTER>(a, s) : launch_f32<64, RASTER>(a, s);
 }
 
 }  // namespace
@@ -780,8 +822,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     e = launch_schedule(a.q_count, a.BH, a.nb, a.sched_k, s);
     if (e != hipSuccess) return e;
-    if (a.bf16) return a.d == 128 ? launch_bf16<128>(a, s) : launch_bf16<64>(a, s);
-    return a.d == 128 ? launch_f32<128>(a, s) : launch_f32<64>(a, s);
+    return a.raster ? launch_sweeps<true>(a, s) : launch_sweeps<false>(a, s);
 }
 
 }  // namespace nabla

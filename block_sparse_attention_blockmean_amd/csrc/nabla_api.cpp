@@ -36,6 +36,18 @@ constexpr long long kMaxHeadElems = 1ll << 33;
 // byte offsets (signed in the tile arithmetic), so a head must stay below 2^31 bytes.
 constexpr long long kMaxHeadBytes = 1ll << 31;
 
+// Checks a raster grid of one P x P patch per N-token block; sets L = T H W.
+nabla_status raster_tokens(const char* who, int T, int H, int W, int P, int N, int* L) {
+    if (T <= 0 || H <= 0 || W <= 0 || P <= 0 || N <= 0) return fail(NABLA_E_INVAL, "%s: sizes must be positive", who);
+    if (H % P || W % P) return fail(NABLA_E_INVAL, "%s: H=%d and W=%d must be multiples of P=%d", who, H, W, P);
+    if (N != P * P)
+        return fail(NABLA_E_INVAL, "%s: raster order needs one P x P patch per block (N == P*P)", who);
+    const long long tokens = (long long)T * H * W;
+    if (tokens >= (1ll << 31)) return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
+    *L = (int)tokens;
+    return NABLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -405,16 +417,11 @@ nabla_status block_sparse_attn_fwd_raster(const void* q, const void* k, const vo
                                           const int32_t* schedule, float scale, nabla_dtype dtype,
                                           hipStream_t stream) {
     const char* who = "block_sparse_attn_fwd_raster";
-    if (T <= 0 || H <= 0 || W <= 0 || P <= 0 || N <= 0)
-        return fail(NABLA_E_INVAL, "%s: sizes must be positive", who);
-    if (H % P || W % P)
-        return fail(NABLA_E_INVAL, "%s: H=%d and W=%d must be multiples of P=%d", who, H, W, P);
-    if (N != P * P)
-        return fail(NABLA_E_INVAL, "%s: raster order needs one P x P patch per block (N == P*P)", who);
-    const long long L = (long long)T * H * W;
-    if (L >= (1ll << 31)) return fail(NABLA_E_UNSUPPORTED, "%s: tensor too large", who);
-    return attn_fwd_impl(who, q, k, v, o, batch, heads, (int)L, d, N, kv_count, kv_index, schedule, scale,
-                         dtype, nullptr, 1, H, W, stream);
+    int L = 0;
+    const nabla_status st = raster_tokens(who, T, H, W, P, N, &L);
+    if (st != NABLA_OK) return st;
+    return attn_fwd_impl(who, q, k, v, o, batch, heads, L, d, N, kv_count, kv_index, schedule, scale, dtype,
+                         nullptr, 1, H, W, stream);
 }
 
 nabla_status block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v, void* o,
@@ -428,6 +435,21 @@ nabla_status block_sparse_attn_fwd_lse(const void* q, const void* k, const void*
                          kv_index, schedule, scale, dtype, lse, 0, 0, 0, stream);
 }
 
+nabla_status block_sparse_attn_fwd_lse_raster(const void* q, const void* k, const void* v, void* o,
+                                              int batch, int heads, int T, int H, int W, int d, int P, int N,
+                                              const int32_t* kv_count, const int32_t* kv_index,
+                                              const int32_t* schedule, float scale, nabla_dtype dtype,
+                                              float* lse, hipStream_t stream) {
+    const char* who = "block_sparse_attn_fwd_lse_raster";
+    if (!lse) return fail(NABLA_E_INVAL, "%s: null lse", who);
+    if (!aligned16(lse)) return fail(NABLA_E_INVAL, "%s: misaligned lse", who);
+    int L = 0;
+    const nabla_status st = raster_tokens(who, T, H, W, P, N, &L);
+    if (st != NABLA_OK) return st;
+    return attn_fwd_impl(who, q, k, v, o, batch, heads, L, d, N, kv_count, kv_index, schedule, scale, dtype,
+                         lse, 1, H, W, stream);
+}
+
 size_t nabla_attn_bwd_workspace_size(int batch, int heads, int L, int N) {
     if (batch <= 0 || heads <= 0 || L <= 0 || N <= 0 || L % N) return 0;
     const size_t BH = (size_t)batch * heads, nb = (size_t)(L / N), words = (nb + 31) / 32;
@@ -436,13 +458,13 @@ size_t nabla_attn_bwd_workspace_size(int batch, int heads, int L, int N) {
            2 * up(BH * nb * 4);
 }
 
-nabla_status block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                                   int batch, int heads, int L, int d, int N,
-                                   const int32_t* kv_count, const int32_t* kv_index, float scale,
-                                   nabla_dtype dtype, void* workspace, size_t workspace_bytes,
-                                   hipStream_t stream) {
-    const char* who = "block_sparse_attn_bwd";
+namespace {
+
+nabla_status attn_bwd_impl(const char* who, const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int batch,
+                           int heads, int L, int d, int N, const int32_t* kv_count, const int32_t* kv_index,
+                           float scale, nabla_dtype dtype, void* workspace, size_t workspace_bytes, int raster,
+                           int H, int W, hipStream_t stream) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !kv_count || !kv_index)
         return fail(NABLA_E_INVAL, "%s: null pointer", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
@@ -491,6 +513,9 @@ nabla_status block_sparse_attn_bwd(const void* q, const void* k, const void* v, 
     a.kv_index = kv_index;
     a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
     a.bf16 = dtype == NABLA_BF16;
+    a.raster = raster;
+    a.H = H;
+    a.W = W;
     const size_t BH = (size_t)a.BH, nb = (size_t)a.nb, words = (nb + 31) / 32;
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
     char* w = (char*)workspace;
@@ -506,6 +531,32 @@ nabla_status block_sparse_attn_bwd(const void* q, const void* k, const void* v, 
     w += up(BH * nb * 4);
     a.sched_k = (int32_t*)w;
     return hip_status(nabla::launch_attn_bwd(a, stream), who);
+}
+
+}  // namespace
+
+nabla_status block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                   int batch, int heads, int L, int d, int N,
+                                   const int32_t* kv_count, const int32_t* kv_index, float scale,
+                                   nabla_dtype dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    return attn_bwd_impl("block_sparse_attn_bwd", q, k, v, o, dout, lse, dq, dk, dv, batch, heads, L, d, N,
+                         kv_count, kv_index, scale, dtype, workspace, workspace_bytes, 0, 0, 0, stream);
+}
+
+nabla_status block_sparse_attn_bwd_raster(const void* q, const void* k, const void* v, const void* o,
+                                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                          int batch, int heads, int T, int H, int W, int d, int P, int N,
+                                          const int32_t* kv_count, const int32_t* kv_index, float scale,
+                                          nabla_dtype dtype, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+    const char* who = "block_sparse_attn_bwd_raster";
+    int L = 0;
+    const nabla_status st = raster_tokens(who, T, H, W, P, N, &L);
+    if (st != NABLA_OK) return st;
+    return attn_bwd_impl(who, q, k, v, o, dout, lse, dq, dk, dv, batch, heads, L, d, N, kv_count, kv_index, scale,
+                         dtype, workspace, workspace_bytes, 1, H, W, stream);
 }
 
 namespace {

@@ -143,6 +143,8 @@ struct AttnBwdArgs {
     const int32_t* kv_index;
     float scale;
     int bf16;
+    int raster;                // 0: blocks are runs of 64 rows; 1: raster T x H x W with 8 x 8 patches
+    int H, W;                  // grid of the raster order
     // workspace
     float* drow;               // [BH, L]   rowsum(dO * O)
     uint32_t* bits;            // [BH, nb, ceil(nb/32)]  transposed mask

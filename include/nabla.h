@@ -373,6 +373,21 @@ nabla_status block_sparse_attn_fwd_lse(const void* q, const void* k, const void*
                                        float* lse, hipStream_t stream);
 
 /*
+ * block_sparse_attn_fwd_lse_raster - block_sparse_attn_fwd_raster that also writes the
+ * log-sum-exp of block_sparse_attn_fwd_lse, in raster order like O: lse[b,h,l] belongs
+ * to raster token l.  Equals nabla_reorder of Q, K, V, block_sparse_attn_fwd_lse and the
+ * inverse reorder of O and of lse, bit for bit (the fractal reorder of the NABLA summary,
+ * "Metodologia: NABLA", item 1, folded into the addressing).
+ * Arguments, results and errors as block_sparse_attn_fwd_raster and
+ * block_sparse_attn_fwd_lse.
+ */
+nabla_status block_sparse_attn_fwd_lse_raster(const void* q, const void* k, const void* v, void* o,
+                                              int batch, int heads, int T, int H, int W, int d, int P,
+                                              int N, const int32_t* kv_count, const int32_t* kv_index,
+                                              const int32_t* schedule, float scale, nabla_dtype dtype,
+                                              float* lse, hipStream_t stream);
+
+/*
  * nabla_attn_bwd_workspace_size - bytes of device workspace block_sparse_attn_bwd needs
  * (nb = L/N, BH = batch*heads): the row dots D (BH*L floats), the transposed mask
  * (BH*nb*ceil(nb/32) words), the transposed lists (BH*nb counts, BH*nb*nb entries) and
@@ -416,6 +431,25 @@ nabla_status block_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                                    const int32_t* kv_count, const int32_t* kv_index, float scale,
                                    nabla_dtype dtype, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/*
+ * block_sparse_attn_bwd_raster - block_sparse_attn_bwd for Q, K, V, O, dO, lse and the
+ * gradients in raster order (lse from block_sparse_attn_fwd_lse_raster), with blocks
+ * numbered as fractal order numbers them (the lists of nabla_build_mask_raster).  The
+ * permutation is applied while reading tiles and rows and writing gradients, so no
+ * reorder pass runs before or after; the gradients equal those of block_sparse_attn_bwd
+ * on the reordered tensors, inverse-reordered, bit for bit.
+ * T, H, W     token grid, L = T*H*W; P patch size with N == P*P.
+ * workspace   nabla_attn_bwd_workspace_size(batch, heads, T*H*W, N) bytes.
+ * Errors: as block_sparse_attn_bwd, plus NABLA_E_INVAL for non-positive T, H, W, P, H or
+ * W not a multiple of P, or N != P*P.
+ */
+nabla_status block_sparse_attn_bwd_raster(const void* q, const void* k, const void* v, const void* o,
+                                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                          int batch, int heads, int T, int H, int W, int d, int P, int N,
+                                          const int32_t* kv_count, const int32_t* kv_index, float scale,
+                                          nabla_dtype dtype, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
 
 /* Static name of a status code ("NABLA_OK", ...). */
 const char* nabla_status_string(nabla_status status);

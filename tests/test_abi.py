@@ -267,6 +267,39 @@ def test_attn_raster_validation(lib):
         assert lib.nabla_last_error().decode().startswith("block_sparse_attn_fwd_raster")
 
 
+def test_attn_lse_raster_validation(lib):
+    def call(**kw):
+        a = dict(q=A, k=B_, v=C, o=D_, batch=1, heads=2, T=4, H=16, W=16, d=64, P=8, N=64, cnt=E, idx=F_,
+                 scale=0.0, dt=NABLA_BF16, lse=G)
+        a.update(kw)
+        return lib.block_sparse_attn_fwd_lse_raster(a["q"], a["k"], a["v"], a["o"], a["batch"], a["heads"],
+                                                    a["T"], a["H"], a["W"], a["d"], a["P"], a["N"], a["cnt"],
+                                                    a["idx"], None, a["scale"], a["dt"], a["lse"], None)
+    for kw, st in ((dict(lse=None), NABLA_E_INVAL), (dict(lse=ctypes.c_void_p(0x100008)), NABLA_E_INVAL),
+                   (dict(o=None), NABLA_E_INVAL), (dict(P=4), NABLA_E_INVAL), (dict(W=12), NABLA_E_INVAL),
+                   (dict(T=0), NABLA_E_INVAL), (dict(d=96), NABLA_E_UNSUPPORTED)):
+        assert call(**kw) == st, kw
+        assert lib.nabla_last_error().decode().startswith("block_sparse_attn_fwd_lse_raster")
+
+
+def test_attn_bwd_raster_validation(lib):
+    need = lib.nabla_attn_bwd_workspace_size(1, 2, 4 * 16 * 16, 64)
+    def call(**kw):
+        a = dict(q=A, k=B_, v=C, o=D_, dout=E, lse=F_, dq=G, dk=H_, dv=I_, batch=1, heads=2, T=4, H=16, W=16,
+                 d=64, P=8, N=64, cnt=J_, idx=K_, scale=0.0, dt=NABLA_BF16, ws=M_, ws_bytes=need)
+        a.update(kw)
+        return lib.block_sparse_attn_bwd_raster(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"],
+                                                a["dk"], a["dv"], a["batch"], a["heads"], a["T"], a["H"], a["W"],
+                                                a["d"], a["P"], a["N"], a["cnt"], a["idx"], a["scale"], a["dt"],
+                                                a["ws"], a["ws_bytes"], None)
+    for kw, st in ((dict(q=None), NABLA_E_INVAL), (dict(lse=None), NABLA_E_INVAL), (dict(dq=A), NABLA_E_INVAL),
+                   (dict(P=4), NABLA_E_INVAL), (dict(N=32), NABLA_E_INVAL), (dict(H=20), NABLA_E_INVAL),
+                   (dict(T=-1), NABLA_E_INVAL), (dict(d=32), NABLA_E_UNSUPPORTED),
+                   (dict(ws_bytes=need - 1), NABLA_E_WORKSPACE), (dict(ws=None), NABLA_E_WORKSPACE)):
+        assert call(**kw) == st, kw
+        assert lib.nabla_last_error().decode().startswith("block_sparse_attn_bwd_raster")
+
+
 # ------------------------------------------------------------- SIP entry points
 
 def test_build_mask_sip_validation(lib):
