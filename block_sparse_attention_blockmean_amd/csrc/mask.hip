@@ -1121,8 +1121,16 @@ map_select_kernel(const void* __restrict__ q, int bf16, int raster, attn::Raster
     extern __shared__ __align__(16) float s_lds[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int bh = blockIdx.y;
-    const int row0 = blockIdx.x * kRows;
+    // Workgroups are dealt round-robin to the 8 XCDs; XCD x takes the x-th eighth of the
+    // (head, row group) items in order, so the workgroups on one XCD's L2 read the pooled
+    // K of one or two heads at a time instead of all the heads in flight on the GPU.
+    const int groups = (nb + kRows - 1) / kRows;
+    const int nwg = gridDim.x;
+    const int full = (nwg / 8) * 8;
+    const int w = blockIdx.x;
+    const int item = w < full ? (w % 8) * (nwg / 8) + w / 8 : w;
+    const int bh = item / groups;
+    const int row0 = (item - bh * groups) * kRows;
     float* cand = s_lds + 2 * kRows * kChunkLd + wave * kRowCand;
     _Float16* q_hi = reinterpret_cast<_Float16*>(s_lds + 2 * kRows * kChunkLd + kWaves * kRowCand);
     _Float16* q_lo = q_hi + kRows * kQld<D>;
@@ -1261,17 +1269,28 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_kernel(
 // to the 8 XCDs, so all of them work on the same one or two heads at any time: the
 // K/V tiles in flight are those of one or two heads (tens of MB at the 720p shapes),
 // which the last-level cache holds, and each head's short lists run last, which keeps
-// the tail of the launch short.  One wave per head (counting sort on nb + 1 bins).
+// the tail of the launch short.  One wave per head (counting sort on nb + 1 bins); the
+// blocks' bins are read from the counts once, with the loads batched, and kept in LDS.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict__ kv_count, int nb,
                                                       int32_t* __restrict__ schedule) {
-    extern __shared__ int bins[];   // nb + 1 counters
+    extern __shared__ int bins[];   // nb + 1 counters, then the nb blocks' bins
+    int* keyl = bins + nb + 1;
     const int h = blockIdx.x;
     const int lane = threadIdx.x;
     const int32_t* cnt = kv_count + (size_t)h * nb;
     for (int b = lane; b <= nb; b += 64) bins[b] = 0;
+    // eight blocks per lane per round: eight count loads in flight
+    for (int i0 = lane; i0 < nb; i0 += 512) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = cnt[min(i0 + 64 * u, nb - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (i0 + 64 * u < nb) keyl[i0 + 64 * u] = nb - min(max(c[u], 0), nb);
+    }
     __syncthreads();
-    for (int i = lane; i < nb; i += 64) atomicAdd(&bins[nb - min(max(cnt[i], 0), nb)], 1);
+    for (int i = lane; i < nb; i += 64) atomicAdd(&bins[keyl[i]], 1);
     __syncthreads();
     // exclusive prefix sum over the nb + 1 bins: one contiguous chunk per lane
     const int per = (nb + 1 + 63) / 64;
@@ -1292,7 +1311,7 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
     }
     __syncthreads();
     for (int i = lane; i < nb; i += 64) {
-        const int pos = atomicAdd(&bins[nb - min(max(cnt[i], 0), nb)], 1);
+        const int pos = atomicAdd(&bins[keyl[i]], 1);
         schedule[(size_t)h * nb + pos] = h * nb + i;
     }
 }
@@ -1309,7 +1328,8 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
 // or two heads at a time and each head's short lists run last.  The single blocks of all
 // heads go at the very end, so that every head's pairs stay aligned to even positions.
 // `fpf` is the number of blocks per frame (1 when frames do not hold whole blocks, which
-// pairs blocks 2j and 2j + 1).
+// pairs blocks 2j and 2j + 1).  The pairs' bins are computed once, with the count loads
+// batched, and kept in LDS.
 // ---------------------------------------------------------------------------
 __device__ inline void pair_members(int j, int fpf, int tpairs, int& a, int& b) {
     if (j < tpairs * fpf) {
@@ -1324,7 +1344,7 @@ __device__ inline void pair_members(int j, int fpf, int tpairs, int& a, int& b) 
 
 __global__ __launch_bounds__(64) void pair_schedule_kernel(const int32_t* __restrict__ kv_count, int nb, int fpf,
                                                            int BH, int32_t* __restrict__ schedule) {
-    extern __shared__ int bins[];   // 2 nb + 1 counters
+    extern __shared__ int bins[];   // 2 nb + 1 counters, then the nb / 2 pairs' bins
     const int h = blockIdx.x;
     const int lane = threadIdx.x;
     const int32_t* cnt = kv_count + (size_t)h * nb;
@@ -1333,14 +1353,25 @@ __global__ __launch_bounds__(64) void pair_schedule_kernel(const int32_t* __rest
     const int single = (frames & 1) & (fpf & 1);      // a block left without a partner
     const int npairs = (nb - single) / 2;
     const int nbins = 2 * nb + 1;
+    int* keyl = bins + nbins;
     for (int b = lane; b < nbins; b += 64) bins[b] = 0;
+    // four pairs per lane per round: eight count loads in flight (indices past the pairs
+    // clamped to a valid block, their bins unused)
+    for (int j0 = lane; j0 < npairs; j0 += 256) {
+        int ca[4], cb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            int a, b;
+            pair_members(min(j0 + 64 * u, npairs - 1), fpf, tpairs, a, b);
+            ca[u] = cnt[a];
+            cb[u] = cnt[b];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (j0 + 64 * u < npairs) keyl[j0 + 64 * u] = 2 * nb - (min(max(ca[u], 0), nb) + min(max(cb[u], 0), nb));
+    }
     __syncthreads();
-    auto key = [&](int j) {
-        int a, b;
-        pair_members(j, fpf, tpairs, a, b);
-        return 2 * nb - (min(max(cnt[a], 0), nb) + min(max(cnt[b], 0), nb));
-    };
-    for (int j = lane; j < npairs; j += 64) atomicAdd(&bins[key(j)], 1);
+    for (int j = lane; j < npairs; j += 64) atomicAdd(&bins[keyl[j]], 1);
     __syncthreads();
     // exclusive prefix sum over the bins: one contiguous chunk per lane
     const int per = (nbins + 63) / 64;
@@ -1364,7 +1395,7 @@ __global__ __launch_bounds__(64) void pair_schedule_kernel(const int32_t* __rest
     for (int j = lane; j < npairs; j += 64) {
         int a, b;
         pair_members(j, fpf, tpairs, a, b);
-        const int pos = atomicAdd(&bins[key(j)], 1);
+        const int pos = atomicAdd(&bins[keyl[j]], 1);
         out[2 * pos] = h * nb + a;
         out[2 * pos + 1] = h * nb + b;
     }
@@ -1408,7 +1439,7 @@ static_assert(map_select_lds_bytes<128>() <= 64 * 1024, "map/select LDS within t
 template <int D, int NREG>
 hipError_t launch_map_select(const MaskArgs& a, hipStream_t s) {
     const size_t lds = map_select_lds_bytes<D>();
-    dim3 grid((a.nb + kRows - 1) / kRows, a.BH);
+    dim3 grid(((a.nb + kRows - 1) / kRows) * a.BH);   // (head, row group) items, see the kernel
     const FastDiv fd_pf((uint32_t)(a.nH * a.nW)), fd_nw((uint32_t)a.nW);   // block -> (frame, patch row, column)
     attn::RasterGrid rg{};
     if (a.raster) {
@@ -1504,14 +1535,16 @@ hipError_t launch_pair_schedule(const MaskArgs& a, const int32_t* counts, int32_
     // blocks per frame when frames hold whole N-token blocks, else 1 (blocks 2j, 2j + 1)
     const long long hw = (long long)a.H * a.W;
     const int fpf = (hw % a.N == 0 && a.nb % (int)(hw / a.N) == 0) ? (int)(hw / a.N) : 1;
-    // one wave per head; its 2 nb + 1 bins fit the default LDS limit
-    hipLaunchKernelGGL(pair_schedule_kernel, dim3(a.BH), dim3(64), (size_t)(2 * a.nb + 1) * sizeof(int), s, counts,
-                       a.nb, fpf, a.BH, schedule);
+    // one wave per head; its 2 nb + 1 bins and nb / 2 pair bins fit the default LDS limit
+    static_assert((2 * NABLA_MAX_BLOCKS + 1 + NABLA_MAX_BLOCKS / 2) * 4 <= 64 * 1024, "schedule LDS");
+    hipLaunchKernelGGL(pair_schedule_kernel, dim3(a.BH), dim3(64), (size_t)(2 * a.nb + 1 + a.nb / 2) * sizeof(int), s,
+                       counts, a.nb, fpf, a.BH, schedule);
     return hipGetLastError();
 }
 
 hipError_t launch_schedule(const int32_t* counts, int BH, int nb, int32_t* schedule, hipStream_t s) {
-    hipLaunchKernelGGL(schedule_kernel, dim3(BH), dim3(64), (size_t)(nb + 1) * sizeof(int), s, counts, nb,
+    static_assert((2 * NABLA_MAX_BLOCKS + 1) * 4 <= 64 * 1024, "schedule LDS");
+    hipLaunchKernelGGL(schedule_kernel, dim3(BH), dim3(64), (size_t)(2 * nb + 1) * sizeof(int), s, counts, nb,
                        schedule);
     return hipGetLastError();
 }
