@@ -200,3 +200,69 @@ def test_backward_full_size():
     say("  sampled: " + "  ".join(f"{n} {e:.3e}" for n, e in worst.items()))
     for n, e in worst.items():
         assert e <= TOL_GRAD["bf16"], n
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["hunyuan_720p_sta", "wan14b_720p_cfg"])
+def test_backward_full_size_720p(name):
+    """The 720p workloads at full size through the raster-order entry points (the form
+    the bench times): the closed-form sums over every head and dQ of sampled query
+    blocks against the oracle; dK and dV of a sampled head's least-kept KV block too
+    when at most 48 query blocks keep it (each of them needs its whole row in the
+    oracle; on these inputs every KV block is kept by hundreds, so there dK and dV are
+    checked by the sums, and against the oracle block by block at the Wan-1.3B size)."""
+    cfg = get_config(name)
+    T, H, W, P, N = cfg.T, cfg.H, cfg.W, cfg.P, cfg.N
+    G, nb, L, d = cfg.BH, cfg.nb, cfg.L, cfg.d
+    say(f"backward full size {cfg.name}: {G} heads L{L} nb{nb}")
+    q, k, v = make_qkv(cfg)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    dout = torch.randn(qd.shape, generator=torch.Generator().manual_seed(7)).to(qd.dtype).cuda()
+    cnt, idx = nab.build_mask(qd, kd, T, H, W, P, N, cfg.thr, cfg.sta, raster=True)
+    o, lse = nab.attn_fwd_raster(qd, kd, vd, cnt, idx, T, H, W, P, N, with_lse=True)
+    dq, dk, dv = nab.attn_bwd(qd, kd, vd, o, dout, lse, cnt, idx, N, raster=(T, H, W, P))
+    torch.cuda.synchronize()
+    say("  gradients computed")
+    m = lists_to_mask(cnt.cpu().numpy().reshape(G, nb), idx.cpu().numpy().reshape(G, nb, nb))
+    # closed-form sums, every head (token order does not matter for them)
+    pi = torch.from_numpy(O.fractal_index(T, H, W, P)).long().cuda()
+    live_f = torch.from_numpy(np.repeat(m.any(axis=2), N, axis=1)).cuda()   # fractal order
+    live = torch.empty_like(live_f)
+    live[:, :] = live_f[:, pi]                                                 # raster token l
+    dkn, dvn, don = (t.float().reshape(G, L, d) for t in (dk, dv, dout))
+    sum_dk = dkn.sum(dim=1).abs().max().item()
+    sum_dv = (dvn.sum(dim=1) - (don * live[..., None]).sum(dim=1)).abs().max().item()
+    scale_k = dkn.abs().max().item()
+    say(f"  |sum dK| {sum_dk:.3e} (max |dK| {scale_k:.3e}), |sum dV - sum dO| {sum_dv:.3e}")
+    assert sum_dk <= L * 2.0 ** -9 * max(1.0, scale_k)
+    assert sum_dv <= L * 2.0 ** -9 * max(1.0, dvn.abs().max().item())
+    rng = np.random.default_rng(17)
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for g in (0, G - 1):
+        qn, kn, vn, dn = (O.reorder(to_np(t.reshape(G, L, d)[g]), T, H, W, P) for t in (qd, kd, vd, dout))
+        gq, gk, gv = (O.reorder(to_np(t.reshape(G, L, d)[g]), T, H, W, P) for t in (dq, dk, dv))
+        qb_s = sorted({0, nb - 1, int(rng.integers(nb))})
+        col = m[g].sum(axis=0)
+        kb = int(np.argmin(np.where(col > 0, col, nb + 1)))
+        # the oracle's cost grows with the rows that keep the block (each needs its whole
+        # row): check dK, dV only where few rows keep it
+        check_kv = col[kb] <= 48
+        rows = sorted(set(qb_s) | (set(np.nonzero(m[g][:, kb])[0].tolist()) if check_kv else set()))
+        sub = np.zeros_like(m[g])
+        sub[rows] = m[g][rows]
+        dmask = np.zeros((L, 1))
+        for i in rows:
+            dmask[i * N:(i + 1) * N] = 1.0
+        say(f"  head {g}: query blocks {qb_s}, KV block {kb} kept by {int(col[kb])} rows"
+            + ("" if check_kv else " (too many for the oracle: dK, dV by the sums only)"))
+        rq, rk, rv = O.masked_attention_backward(qn[None], kn[None], vn[None], (dn * dmask)[None], sub[None], N)
+        for i in qb_s:
+            sl = slice(i * N, (i + 1) * N)
+            worst["dq"] = max(worst["dq"], grad_err(gq[sl], rq[0, sl]))
+        if check_kv:
+            sl = slice(kb * N, (kb + 1) * N)
+            worst["dk"] = max(worst["dk"], grad_err(gk[sl], rk[0, sl]))
+            worst["dv"] = max(worst["dv"], grad_err(gv[sl], rv[0, sl]))
+    say("  sampled: " + "  ".join(f"{n} {e:.3e}" for n, e in worst.items()))
+    for n, e in worst.items():
+        assert e <= TOL_GRAD["bf16"], n
